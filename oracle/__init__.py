@@ -1,0 +1,241 @@
+"""CPU oracle of the sparse MoE layer forward (ctypes wrapper around liboracle.so).
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The HIP library
+and its Python binding never import it, and the two share no code: the only
+common module is ``workloads`` (seeded random inputs, no layer arithmetic).
+
+The arithmetic lives in ``moe_oracle.c`` (plain loops, fp64 accumulation,
+``-ffp-contract=off``); this file only marshals numpy arrays and chains the
+steps in the order the layer defines them:
+logits -> exact top-k + softmax gates -> counts / offsets / stable expert-major
+permutation / LIS -> per-row expert FFN -> weighted combine (+ shared experts).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+OK, ERR_ARG, ERR_NONFINITE = 0, 1, 2
+F32, BF16 = 0, 1
+ROUND_NONE, ROUND_BF16, ROUND_F32 = 0, 1, 2
+SWIGLU, RELU = 0, 1
+INT4_GROUP = 128
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = False) -> str:
+    """Compile liboracle.so with gcc (plain C11 + OpenMP, no contraction)."""
+    if force or not os.path.exists(_LIB_PATH) or \
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            L = C.CDLL(_LIB_PATH)
+            p, i, i64, d = C.c_void_p, C.c_int, C.c_int64, C.c_double
+            L.orc_router_logits.argtypes = [p, i, p, p, i, i, i, p]
+            L.orc_topk_gates.argtypes = [p, i, i, i, p, p]
+            L.orc_permute.argtypes = [p, i, i, i, p, p, p, p, p]
+            L.orc_expert_rows.argtypes = [p, i, i, i, i, p, p, p, i, i, p, p, i, p]
+            L.orc_combine.argtypes = [p, p, p, p, i, i, i, p]
+            L.orc_dequant_int4.argtypes = [p, p, p, i64, i, i, p]
+            L.orc_round_bf16.argtypes = [d]
+            L.orc_round_bf16.restype = d
+            for f in ("orc_router_logits", "orc_topk_gates", "orc_permute", "orc_expert_rows",
+                      "orc_combine", "orc_dequant_int4"):
+                getattr(L, f).restype = C.c_int
+            _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _check(rc, what):
+    if rc != OK:
+        raise OracleError("%s failed with code %d" % (what, rc))
+
+
+def _dt(a):
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float32:
+        return F32
+    raise TypeError("expected bf16 bits (uint16) or float32, got %s" % a.dtype)
+
+
+def round_bf16(v: float) -> float:
+    return lib().orc_round_bf16(float(v))
+
+
+# --- steps ---------------------------------------------------------------
+
+def router_logits(x, w_r, b_r=None):
+    x = np.ascontiguousarray(x)
+    w_r = np.ascontiguousarray(w_r)
+    assert _dt(x) == _dt(w_r)
+    T, d = x.shape
+    E = w_r.shape[0]
+    out = np.empty((T, E), np.float32)
+    b = None if b_r is None else np.ascontiguousarray(b_r, np.float32)
+    _check(lib().orc_router_logits(_ptr(x), _dt(x), _ptr(w_r), _ptr(b), T, d, E, _ptr(out)),
+           "router_logits")
+    return out
+
+
+def topk_gates(logits, k):
+    logits = np.ascontiguousarray(logits, np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, k), np.int32)
+    gate = np.empty((T, k), np.float32)
+    _check(lib().orc_topk_gates(_ptr(logits), T, E, k, _ptr(idx), _ptr(gate)), "topk_gates")
+    return idx, gate
+
+
+def permute(idx, E):
+    idx = np.ascontiguousarray(idx, np.int32)
+    T, k = idx.shape
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    row_assign = np.empty(T * k, np.int32)
+    assign_row = np.empty(T * k, np.int32)
+    lis = np.empty(1, np.float64)
+    _check(lib().orc_permute(_ptr(idx), T, E, k, _ptr(counts), _ptr(offsets), _ptr(row_assign),
+                             _ptr(assign_row), _ptr(lis)), "permute")
+    return counts, offsets, row_assign, assign_row, float(lis[0])
+
+
+def expert_rows(x, w_gate, w_up, w_down, act, h_round, tok, exp_id):
+    """fp64 expert outputs for (token, expert) pairs.  Weights [E,F,d] / [E,d,F]."""
+    x = np.ascontiguousarray(x)
+    w_up = np.ascontiguousarray(w_up)
+    w_down = np.ascontiguousarray(w_down)
+    w_gate = None if w_gate is None else np.ascontiguousarray(w_gate)
+    T, d = x.shape
+    F = w_up.shape[-2]
+    assert w_up.shape[-1] == d and w_down.shape[-2:] == (d, F)
+    tok = np.ascontiguousarray(tok, np.int32)
+    exp_id = np.ascontiguousarray(exp_id, np.int32)
+    n = tok.shape[0]
+    Y = np.empty((n, d), np.float64)
+    a = SWIGLU if act == "swiglu" else RELU
+    _check(lib().orc_expert_rows(_ptr(x), _dt(x), d, F, a, _ptr(w_gate), _ptr(w_up),
+                                 _ptr(w_down), _dt(w_up), h_round, _ptr(tok), _ptr(exp_id), n,
+                                 _ptr(Y)), "expert_rows")
+    return Y
+
+
+def combine(Y, assign_row, gate, Ys=None):
+    gate = np.ascontiguousarray(gate, np.float32)
+    T, k = gate.shape
+    Y = np.ascontiguousarray(Y, np.float64)
+    d = Y.shape[1]
+    ar = None if assign_row is None else np.ascontiguousarray(assign_row, np.int32)
+    Ys = None if Ys is None else np.ascontiguousarray(Ys, np.float64)
+    y = np.empty((T, d), np.float32)
+    _check(lib().orc_combine(_ptr(Y), _ptr(ar), _ptr(gate), _ptr(Ys), T, k, d, _ptr(y)),
+           "combine")
+    return y
+
+
+def dequant_int4(q, scale, zero, group=INT4_GROUP):
+    """INT4 words [.., N, K/8] + fp16 scale/zero [.., N, K/group] -> bf16 bits [.., N, K]."""
+    q = np.ascontiguousarray(q, np.int32)
+    scale = np.ascontiguousarray(scale, np.uint16)
+    zero = np.ascontiguousarray(zero, np.uint16)
+    K = q.shape[-1] * 8
+    rows = int(np.prod(q.shape[:-1]))
+    out = np.empty(q.shape[:-1] + (K,), np.uint16)
+    _check(lib().orc_dequant_int4(_ptr(q), _ptr(scale), _ptr(zero), rows, K, group, _ptr(out)),
+           "dequant_int4")
+    return out
+
+
+# --- the layer -----------------------------------------------------------
+
+def _h_round(wl):
+    return ROUND_BF16 if wl.cfg.dtype == "bf16" else ROUND_F32
+
+
+def dense_expert_weights(wl, experts=None):
+    """Routed expert weights as dense arrays (INT4 decoded with the oracle's rule)."""
+    if not wl.cfg.int4:
+        return wl.w_gate, wl.w_up, wl.w_down
+    E = wl.cfg.E
+    sel = range(E) if experts is None else experts
+    out = []
+    for qw, shape_src in ((wl.q_gate, wl.w_gate), (wl.q_up, wl.w_up), (wl.q_down, wl.w_down)):
+        full = np.zeros(shape_src.shape, np.uint16)
+        for e in sel:
+            full[e] = dequant_int4(qw.q[e], qw.scale[e], qw.zero[e])
+        out.append(full)
+    return tuple(out)
+
+
+def layer_forward(wl, logits=None, tokens=None, routing_only=False):
+    """Run the whole layer on the CPU.
+
+    ``logits``: if given (e.g. the GPU's fp32 logits), routing uses them instead
+    of the oracle's own; that pins every integer output to one fp32 input.
+    ``tokens``: optional subset of token ids whose y is computed (routing,
+    counts, permutation and LIS always cover all T tokens).
+    Returns a dict of every intermediate and output.
+    """
+    cfg = wl.cfg
+    T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    own_logits = router_logits(wl.x, wl.w_router, wl.b_router)
+    lg = own_logits if logits is None else np.ascontiguousarray(logits, np.float32)
+    idx, gate = topk_gates(lg, k)
+    counts, offsets, row_assign, assign_row, lis = permute(idx, E)
+    out = dict(logits=own_logits, idx=idx, gate=gate, counts=counts, offsets=offsets,
+               row_assign=row_assign, assign_row=assign_row, lis=lis)
+    if routing_only:
+        return out
+    if tokens is None:
+        # every row in expert-major order, recombined through assign_row
+        toks = np.arange(T, dtype=np.int32)
+        pt = (row_assign // k).astype(np.int32)
+        pe = idx.reshape(-1)[row_assign]
+        ar = assign_row
+    else:
+        # a token subset, in its own flat slot order
+        toks = np.asarray(tokens, np.int32)
+        pt = np.repeat(toks, k)
+        pe = idx[toks].reshape(-1)
+        ar = None
+    needed = sorted(set(int(e) for e in pe))
+    wg, wu, wd = dense_expert_weights(wl, needed)
+    Y = expert_rows(wl.x, wg, wu, wd, cfg.act, _h_round(wl), pt, pe)
+    Ys = None
+    if cfg.n_shared:
+        Ys = expert_rows(wl.x, wl.ws_gate[None], wl.ws_up[None], wl.ws_down[None], "swiglu",
+                         _h_round(wl), toks, np.zeros_like(toks))
+    out["tokens"] = toks
+    out["Y"] = Y
+    out["Ys"] = Ys
+    out["y"] = combine(Y, ar, gate[toks], Ys)
+    return out

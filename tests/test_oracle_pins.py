@@ -1,0 +1,433 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test ties one oracle step to a closed form, an invariant, brute force on
+tiny inputs, a hand-worked fixture under tests/golden/, or an independent
+library routine (numpy fp64 matmul / argsort / bincount, torch's bf16 cast).
+The mutation test at the end plants plausible mistakes in a copy of the oracle
+and checks that this file catches each of them.
+"""
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import get_config, make_workload
+from workloads.gen import bf16_bits_to_f32, f32_to_bf16_bits, quantize_int4_rows
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _topk_brute(l, k):
+    """Full sort by (value descending, id ascending); -0.0 == +0.0 under IEEE."""
+    order = sorted(range(len(l)), key=lambda e: (-float(l[e]) + 0.0, e))
+    return order[:k]
+
+
+# ---------------------------------------------------------------- bf16 rounding
+
+def test_round_bf16_table_matches_torch_cast():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([
+        rng.standard_normal(4000).astype(np.float32),
+        (rng.standard_normal(4000) * 1e-30).astype(np.float32),
+        (rng.standard_normal(4000) * 1e30).astype(np.float32),
+        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 257.0, 259.0, 2 ** -130,
+                  0.0, -0.0], np.float32),
+    ])
+    ref = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float32).numpy()
+    got = np.array([oracle.round_bf16(float(v)) for v in vals], np.float64).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    # the generator's fp32 -> bf16 conversion follows the same rule
+    assert np.array_equal(bf16_bits_to_f32(f32_to_bf16_bits(vals)).view(np.uint32),
+                          ref.view(np.uint32))
+
+
+def test_round_bf16_is_a_single_rounding_from_fp64():
+    # 1 + 2^-8 + 2^-40 lies above the bf16 midpoint 1 + 2^-8: one rounding gives
+    # 1 + 2^-7; rounding through fp32 first would land on the midpoint and tie to 1.
+    assert oracle.round_bf16(1 + 2 ** -8 + 2 ** -40) == 1 + 2 ** -7
+    assert oracle.round_bf16(1 + 2 ** -8) == 1.0          # tie -> even
+    assert oracle.round_bf16(1 + 3 * 2 ** -8) == 1 + 2 ** -6  # tie -> even
+
+
+# ---------------------------------------------------------------- logits
+
+def test_router_logits_match_numpy_fp64():
+    rng = np.random.default_rng(1)
+    T, d, E = 37, 24, 5
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    w = (rng.standard_normal((E, d)) * 0.3).astype(np.float32)
+    b = rng.standard_normal(E).astype(np.float32)
+    got = oracle.router_logits(x, w, b)
+    ref = (x.astype(np.float64) @ w.astype(np.float64).T + b.astype(np.float64)).astype(np.float32)
+    np.testing.assert_allclose(got, ref, rtol=2e-7, atol=1e-7)
+    # bf16 inputs are widened exactly
+    xb, wb = f32_to_bf16_bits(x), f32_to_bf16_bits(w)
+    got = oracle.router_logits(xb, wb, None)
+    ref = (bf16_bits_to_f32(xb).astype(np.float64) @ bf16_bits_to_f32(wb).astype(np.float64).T)
+    np.testing.assert_allclose(got, ref.astype(np.float32), rtol=2e-7, atol=1e-7)
+
+
+# ---------------------------------------------------------------- top-k
+
+@pytest.mark.parametrize("E,k", [(1, 1), (2, 1), (5, 2), (8, 2), (16, 5), (64, 6), (64, 64)])
+def test_topk_matches_full_sort(E, k):
+    rng = np.random.default_rng(E * 100 + k)
+    T = 60
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    # exact ties and signed zeros in half the rows
+    alphabet = np.array([-1.0, -0.0, 0.0, 0.5, 1.0], np.float32)
+    l[::2] = alphabet[rng.integers(0, 5, size=(T // 2, E))]
+    idx, _ = oracle.topk_gates(l, k)
+    for t in range(T):
+        assert list(idx[t]) == _topk_brute(l[t], k), (t, l[t])
+
+
+@pytest.mark.parametrize("E", [1, 2, 3, 4])
+def test_topk_exhaustive_small_alphabet(E):
+    alphabet = [-1.0, -0.0, 0.0, 1.0]
+    rows = np.array(list(itertools.product(alphabet, repeat=E)), np.float32)
+    for k in range(1, E + 1):
+        idx, gate = oracle.topk_gates(rows, k)
+        for t in range(rows.shape[0]):
+            assert list(idx[t]) == _topk_brute(rows[t], k)
+        assert np.all(np.abs(gate.astype(np.float64).sum(1) - 1.0) <= 1e-6)
+
+
+def test_topk_shift_invariance():
+    rng = np.random.default_rng(3)
+    l = (rng.integers(-64, 64, size=(200, 16)) / 8.0).astype(np.float32)  # exact grid
+    i1, g1 = oracle.topk_gates(l, 4)
+    i2, g2 = oracle.topk_gates(l + np.float32(2.5), 4)
+    assert np.array_equal(i1, i2)
+    assert np.array_equal(g1, g2)
+
+
+def test_topk_rejects_nonfinite():
+    l = np.zeros((2, 4), np.float32)
+    l[1, 2] = np.nan
+    with pytest.raises(oracle.OracleError):
+        oracle.topk_gates(l, 2)
+    l[1, 2] = np.inf
+    with pytest.raises(oracle.OracleError):
+        oracle.topk_gates(l, 2)
+
+
+# ---------------------------------------------------------------- gates
+
+def test_gates_closed_forms():
+    rng = np.random.default_rng(4)
+    l = rng.standard_normal((500, 8)).astype(np.float32) * 3
+    i1, g1 = oracle.topk_gates(l, 1)
+    assert np.all(g1 == 1.0)                      # k = 1: exactly one
+    i2, g2 = oracle.topk_gates(l, 2)
+    l0 = np.take_along_axis(l, i2[:, :1], 1)[:, 0].astype(np.float64)
+    l1 = np.take_along_axis(l, i2[:, 1:2], 1)[:, 0].astype(np.float64)
+    sig = 1.0 / (1.0 + np.exp(l1 - l0))           # k = 2: g0 = sigmoid(l0 - l1)
+    np.testing.assert_allclose(g2[:, 0], sig, rtol=0, atol=1e-7)
+    np.testing.assert_allclose(g2[:, 1], 1 - sig, rtol=0, atol=1e-7)
+    assert np.all(g2[:, 0] >= g2[:, 1])
+    eq = np.zeros((3, 6), np.float32)            # equal logits: 1/k each
+    for k in (1, 2, 3, 6):
+        _, g = oracle.topk_gates(eq, k)
+        assert np.all(g == np.float32(1.0 / k))
+    # k = E: the full softmax, in sorted order
+    i8, g8 = oracle.topk_gates(l, 8)
+    lf = l.astype(np.float64)
+    sm = np.exp(lf - lf.max(1, keepdims=True))
+    sm /= sm.sum(1, keepdims=True)
+    np.testing.assert_allclose(g8, np.take_along_axis(sm, i8, 1), rtol=0, atol=1e-7)
+    assert np.all(np.abs(g8.astype(np.float64).sum(1) - 1) <= 1e-6)
+
+
+# ---------------------------------------------------------------- counts / permutation / LIS
+
+def _check_permutation(idx, E):
+    T, k = idx.shape
+    counts, offsets, row_assign, assign_row, lis = oracle.permute(idx, E)
+    flat = idx.reshape(-1)
+    assert np.array_equal(counts, np.bincount(flat, minlength=E))
+    assert counts.sum() == T * k
+    assert offsets[0] == 0 and np.array_equal(np.diff(offsets), counts)
+    assert np.array_equal(row_assign, np.argsort(flat, kind="stable"))
+    assert np.array_equal(assign_row[row_assign], np.arange(T * k))
+    assert np.array_equal(np.sort(row_assign), np.arange(T * k))
+    for e in range(E):
+        seg = row_assign[offsets[e]:offsets[e + 1]]
+        assert np.all(flat[seg] == e)
+        assert np.all(np.diff(seg // k) > 0)      # token order inside an expert
+    if T:
+        exact = Fraction(E * int(counts.max()), T * k)
+        assert lis == float(exact)                 # one correctly rounded division
+        assert 1.0 <= lis <= E / k
+    else:
+        assert math.isnan(lis)
+    return counts, offsets, row_assign, assign_row, lis
+
+
+def test_permutation_golden_worked_example():
+    fields = {}
+    with open(os.path.join(GOLDEN, "lis_worked_example.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                key, *vals = line.split()
+                fields[key] = vals
+    E, k = int(fields["E"][0]), int(fields["K"][0])
+    idx = np.array(fields["IDX"], np.int32).reshape(-1, k)
+    counts, offsets, row_assign, assign_row, lis = oracle.permute(idx, E)
+    assert list(counts) == [int(v) for v in fields["COUNTS"]]
+    assert list(offsets) == [int(v) for v in fields["OFFSETS"]]
+    assert list(row_assign) == [int(v) for v in fields["ROW_ASSIGN"]]
+    assert list(assign_row) == [int(v) for v in fields["ASSIGN_ROW"]]
+    assert lis == float(fields["LIS"][0])
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (7, 8, 2), (100, 64, 6), (333, 8, 1), (50, 3, 3)])
+def test_permutation_invariants_random(T, E, k):
+    rng = np.random.default_rng(T * E + k)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    _check_permutation(idx, E)
+
+
+def test_permutation_empty_and_degenerate():
+    _check_permutation(np.zeros((0, 2), np.int32), 8)           # T = 0: LIS NaN
+    E, k, T = 8, 2, 64
+    rr = np.array([[(t * k + j) % E for j in range(k)] for t in range(T)], np.int32)
+    assert _check_permutation(rr, E)[4] == 1.0                  # round-robin: balanced
+    same = np.tile(np.array([[5, 2]], np.int32), (T, 1))
+    c = _check_permutation(same, E)
+    assert c[4] == E / k                                        # all on the same k
+    assert list(np.nonzero(c[0])[0]) == [2, 5]                 # empty experts elsewhere
+
+
+# ---------------------------------------------------------------- expert FFN and layer
+
+def _silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+def _np_ffn(x, wg, wu, wd, act, h_round):
+    """numpy fp64 matmul formulation of one expert on a block of tokens."""
+    x = x.astype(np.float64)
+    u = x @ wu.astype(np.float64).T
+    h = _silu(x @ wg.astype(np.float64).T) * u if act == "swiglu" else np.maximum(u, 0.0)
+    if h_round == oracle.ROUND_F32:
+        h = h.astype(np.float32).astype(np.float64)
+    return h @ wd.astype(np.float64).T
+
+
+@pytest.mark.parametrize("act", ["swiglu", "relu"])
+def test_expert_rows_dense_ffn(act):
+    rng = np.random.default_rng(5)
+    T, d, F, E = 9, 24, 40, 3                    # d != F catches a transposed operand
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wg = (rng.standard_normal((E, F, d)) * 0.2).astype(np.float32)
+    wu = (rng.standard_normal((E, F, d)) * 0.2).astype(np.float32)
+    wd = (rng.standard_normal((E, d, F)) * 0.2).astype(np.float32)
+    tok = np.repeat(np.arange(T), E).astype(np.int32)
+    ex = np.tile(np.arange(E), T).astype(np.int32)
+    Y = oracle.expert_rows(x, wg if act == "swiglu" else None, wu, wd, act, oracle.ROUND_NONE,
+                           tok, ex)
+    for e in range(E):
+        ref = _np_ffn(x, wg[e], wu[e], wd[e], act, oracle.ROUND_NONE)
+        np.testing.assert_allclose(Y[ex == e], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_expert_rows_scalar_closed_form_and_silu_zero():
+    x = np.array([[0.75], [0.0], [-1.5]], np.float32)
+    wg = np.array([[[2.0]]], np.float32)
+    wu = np.array([[[-0.5]]], np.float32)
+    wd = np.array([[[3.0]]], np.float32)
+    Y = oracle.expert_rows(x, wg, wu, wd, "swiglu", oracle.ROUND_NONE,
+                           np.arange(3, dtype=np.int32), np.zeros(3, np.int32))
+    for t in range(3):
+        xv = float(x[t, 0])
+        g = 2.0 * xv
+        ref = (g / (1 + math.exp(-g))) * (-0.5 * xv) * 3.0
+        assert abs(Y[t, 0] - ref) <= 1e-15
+    assert Y[1, 0] == 0.0                                      # silu(0) = 0
+
+
+def _tiny_f32(T=48, d=32, F=40, E=6, k=2, **kw):
+    return make_workload(get_config("tiny_fp32", T=T, d=d, F=F, E=E, k=k, **kw))
+
+
+def _dense_masked_y(wl, idx, gate):
+    """Every expert on every token, times a one-hot gate matrix (no permutation)."""
+    cfg = wl.cfg
+    G = np.zeros((cfg.T, cfg.E))
+    for t in range(cfg.T):
+        for j in range(cfg.k):
+            G[t, idx[t, j]] += float(gate[t, j])
+    y = np.zeros((cfg.T, cfg.d))
+    for e in range(cfg.E):
+        Ye = _np_ffn(wl.x, wl.w_gate[e], wl.w_up[e], wl.w_down[e], cfg.act, oracle.ROUND_F32)
+        y += G[:, e:e + 1] * Ye
+    return y
+
+
+def test_layer_matches_dense_masked_formulation():
+    wl = _tiny_f32()
+    out = oracle.layer_forward(wl)
+    ref = _dense_masked_y(wl, out["idx"], out["gate"])
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-6, atol=1e-9)
+    sub = oracle.layer_forward(wl, tokens=[5, 0, 47])          # token subset path agrees
+    np.testing.assert_allclose(sub["y"], out["y"][[5, 0, 47]], rtol=1e-7, atol=1e-12)
+
+
+def test_layer_single_expert_is_dense_ffn():
+    wl = _tiny_f32(E=1, k=1)
+    out = oracle.layer_forward(wl)
+    assert np.all(out["gate"] == 1.0) and np.all(out["idx"] == 0)
+    ref = _np_ffn(wl.x, wl.w_gate[0], wl.w_up[0], wl.w_down[0], "swiglu", oracle.ROUND_F32)
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-6, atol=1e-9)
+
+
+def test_layer_all_experts_is_dense_softmax_mixture():
+    wl = _tiny_f32(E=4, k=4)
+    out = oracle.layer_forward(wl)
+    lf = out["logits"].astype(np.float64)
+    sm = np.exp(lf - lf.max(1, keepdims=True))
+    sm /= sm.sum(1, keepdims=True)
+    y = np.zeros((wl.cfg.T, wl.cfg.d))
+    for e in range(4):
+        y += sm[:, e:e + 1] * _np_ffn(wl.x, wl.w_gate[e], wl.w_up[e], wl.w_down[e], "swiglu",
+                                     oracle.ROUND_F32)
+    np.testing.assert_allclose(out["y"], y, rtol=1e-5, atol=1e-8)
+
+
+def test_layer_token_permutation_equivariance():
+    wl = _tiny_f32()
+    out = oracle.layer_forward(wl)
+    perm = np.random.default_rng(6).permutation(wl.cfg.T)
+    wl.x = wl.x[perm].copy()
+    out2 = oracle.layer_forward(wl)
+    assert np.array_equal(out2["idx"], out["idx"][perm])
+    assert np.array_equal(out2["counts"], out["counts"])
+    assert out2["lis"] == out["lis"]
+    np.testing.assert_array_equal(out2["y"], out["y"][perm])
+
+
+def test_layer_shared_experts_add_dense_term():
+    wl = _tiny_f32(n_shared=2, F_shared=16)
+    assert wl.ws_gate.shape == (32, wl.cfg.d)
+    out = oracle.layer_forward(wl)
+    routed = _dense_masked_y(wl, out["idx"], out["gate"])
+    shared = _np_ffn(wl.x, wl.ws_gate, wl.ws_up, wl.ws_down, "swiglu", oracle.ROUND_F32)
+    np.testing.assert_allclose(out["y"], routed + shared, rtol=1e-6, atol=1e-9)
+    assert out["counts"].sum() == wl.cfg.T * wl.cfg.k           # shared not counted
+
+
+def test_tiny_workload_bias_skews_load():
+    out = oracle.layer_forward(make_workload("tiny_fp32"), routing_only=True)
+    # b_0 exceeds b_1 by 0.35 against logit noise of ~0.23 std: expert 0 nearly always wins
+    assert out["counts"][0] >= 0.85 * 64 and out["lis"] > 3.0
+
+
+# ---------------------------------------------------------------- INT4 decode
+
+def _pack(nibbles):
+    nib = np.asarray(nibbles, np.uint32).reshape(-1, 8)
+    return np.bitwise_or.reduce(nib << (np.arange(8, dtype=np.uint32) * 4), axis=1) \
+        .astype(np.uint32).view(np.int32)
+
+
+def test_int4_golden_table():
+    rows = []
+    with open(os.path.join(GOLDEN, "int4_dequant_table.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                q, s, z, v = line.split()
+                rows.append((int(q), int(s, 16), int(z, 16), float(v)))
+    for q, s, z, v in rows:
+        K = 128
+        words = _pack([q] * K)[None]                       # one row, one group
+        out = oracle.dequant_int4(words, np.array([[s]], np.uint16), np.array([[z]], np.uint16))
+        vals = bf16_bits_to_f32(out)
+        assert np.all(vals == np.float32(v)), (q, hex(s), hex(z), vals[0, 0], v)
+
+
+def test_int4_nibble_order_and_groups():
+    K, N = 256, 3
+    rng = np.random.default_rng(7)
+    q = rng.integers(0, 16, size=(N, K))
+    words = _pack(q.reshape(-1)).reshape(N, K // 8)
+    s = np.full((N, K // 128), 0x3C00, np.uint16)          # s = 1
+    z = np.zeros((N, K // 128), np.uint16)
+    z[:, 1] = 0x4000                                       # z = 2 on the second group only
+    out = bf16_bits_to_f32(oracle.dequant_int4(words, s, z))
+    exp = q.astype(np.float32)
+    exp[:, 128:] -= 2
+    assert np.array_equal(out, exp)
+
+
+def test_int4_quantization_error_bound():
+    rng = np.random.default_rng(8)
+    w = f32_to_bf16_bits((rng.standard_normal((16, 512)) * 0.02).astype(np.float32))
+    for frac in (False, True):
+        q, s, z = quantize_int4_rows(w, fractional_zero=frac)
+        wh = bf16_bits_to_f32(oracle.dequant_int4(q, s, z)).astype(np.float64)
+        wf = bf16_bits_to_f32(w).astype(np.float64).reshape(16, 4, 128)
+        s64 = np.frombuffer(s.tobytes(), np.float16).astype(np.float64).reshape(16, 4, 1)
+        err = np.abs(wh.reshape(16, 4, 128) - wf)
+        # half a quantisation step, plus half a bf16 ulp of the decoded value, plus
+        # one step where the top of the group is clipped at 15
+        bound = 0.5 * s64 + np.abs(wf) * 2.0 ** -8 + 1e-9
+        inside = err <= bound
+        assert inside.mean() > 0.97, inside.mean()
+        assert np.all(err <= 1.0 * s64 + np.abs(wf) * 2.0 ** -8 + 1e-9)
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+MUTANTS = [
+    ("topk tie to higher id", "if (best < 0 || l[e] > l[best]) best = e;",
+     "if (best < 0 || l[e] >= l[best]) best = e;"),
+    ("bias dropped", "if (b_r) s += (double)b_r[e];", "(void)b_r;"),
+    ("gate not normalised", "(float)(exp((double)l[out[j]] - m) / sum);",
+     "(float)(exp((double)l[out[j]] - m));"),
+    ("lis uses k twice", "(double)((int64_t)T * k);", "(double)((int64_t)T * k * k);"),
+    ("unstable permutation", "int32_t row = offsets[e] + seen[e]++;",
+     "int32_t row = offsets[e + 1] - 1 - seen[e]++;"),
+    ("silu sign", "v = (g / (1.0 + exp(-g))) * u;", "v = (g / (1.0 + exp(g))) * u;"),
+    ("down operand transposed",
+     "size_t wo = (e * (size_t)d + (size_t)i) * (size_t)F;\n        double s = 0.0;\n"
+     "        for (int f = 0; f < F; ++f) s += h[f] * elem(w_down, wdt, wo + f);",
+     "size_t wo = e * (size_t)d * (size_t)F;\n        double s = 0.0;\n"
+     "        for (int f = 0; f < F; ++f) s += h[f] * elem(w_down, wdt, wo + (size_t)f * d + i);"),
+    ("combine drops shared term", "if (Ys) s += Ys[(size_t)t * d + i];", "(void)Ys;"),
+    ("int4 high nibble first", "(word >> (4 * (kk % 8))) & 0xFu;",
+     "(word >> (4 * (7 - kk % 8))) & 0xFu;"),
+    ("int4 zero added", "float a = (float)nib - z;", "float a = (float)nib + z;"),
+    ("bf16 rounding truncates", "double r = nearbyint(ldexp(v, -q));",
+     "double r = trunc(ldexp(v, -q));"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(name, old, new, tmp_path):
+    """A copy of the oracle with one plausible mistake must fail this file's pins."""
+    import subprocess
+    import sys
+    src = open(oracle._SRC).read()
+    assert old in src, "mutation anchor not found: " + name
+    mdir = tmp_path / "oracle"
+    mdir.mkdir()
+    (mdir / "moe_oracle.c").write_text(src.replace(old, new, 1))
+    (mdir / "__init__.py").write_text(open(os.path.join(os.path.dirname(oracle._SRC),
+                                                        "__init__.py")).read())
+    env = dict(os.environ)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env["PYTHONPATH"] = str(tmp_path) + os.pathsep + root
+    env["ORACLE_MUTANT_RUN"] = "1"
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.abspath(__file__), "-k", "not planted_mistake"],
+                       cwd=str(tmp_path), env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, "pins did not catch mutant: %s\n%s" % (name, r.stdout[-2000:])
+    assert "failed" in r.stdout or "error" in r.stdout.lower()

@@ -1,0 +1,191 @@
+"""Seeded tensor generation for the MoE workloads.
+
+Every tensor is drawn from its own ``numpy.random.Generator(PCG64(SeedSequence(
+[cfg_id, tensor_id, expert])))`` so any tensor regenerates on its own, on any
+machine, bit for bit.  Values are drawn in fp32 (x ~ N(0,1), every weight ~
+N(0, 0.02^2)) and, for bf16 workloads, rounded to bf16 with round-to-nearest-
+even.  bf16 arrays are returned as ``uint16`` bit patterns.
+
+Nothing here computes any part of the layer: the INT4 *encoding* below is
+input preparation (it turns bf16 weights into nibbles, scales and zero points);
+the *decoding* that the layer performs lives separately in the oracle and in
+the HIP kernels.
+"""
+from __future__ import annotations
+
+import math
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from .configs import CONFIGS, WorkloadConfig
+
+# tensor ids inside a workload's seed space
+TID_X, TID_WR, TID_WGATE, TID_WUP, TID_WDOWN = 0, 1, 2, 3, 4
+TID_SGATE, TID_SUP, TID_SDOWN, TID_ZIPF = 5, 6, 7, 8
+
+W_STD = 0.02
+INT4_GROUP = 128
+
+
+def _rng(cfg_id: int, tid: int, expert: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg_id, tid, expert])))
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round-to-nearest-even (finite inputs)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).copy()
+    u += np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal(cfg_id, tid, expert, shape, scale, bf16):
+    a = _rng(cfg_id, tid, expert).standard_normal(shape, dtype=np.float32)
+    if scale != 1.0:
+        a *= np.float32(scale)
+    return f32_to_bf16_bits(a) if bf16 else a
+
+
+def _per_expert(fn, n, threads=8):
+    with ThreadPoolExecutor(max(1, min(threads, n))) as ex:
+        return np.stack(list(ex.map(fn, range(n))))
+
+
+def quantize_int4_rows(w_bits: np.ndarray, fractional_zero: bool = False):
+    """Asymmetric group-wise INT4 encoding of bf16 weight rows.
+
+    ``w_bits``: [N, K] bf16 bits, K a multiple of 128.  Returns (q [N, K/8] int32
+    with nibble i of word j holding K-index 8j+i, low nibble first; scale and
+    zero as fp16 bits [N, K/128]).  Per group of 128 along K: s = fp16((hi-lo)/15),
+    z = fp16(clamp(rint(-lo/s), 0, 15)) and q = clamp(rint(w/s) + z, 0, 15);
+    a constant group gets s = 1, z = 0.  With ``fractional_zero`` the zero
+    point keeps its fraction (z = fp16(clamp(-lo/s, 0, 15)), q = clamp(rint(w/s + z),
+    0, 15)), which exercises the decode rule with non-integer z.
+    """
+    N, K = w_bits.shape
+    assert K % INT4_GROUP == 0
+    w = bf16_bits_to_f32(w_bits).reshape(N, K // INT4_GROUP, INT4_GROUP)
+    lo = w.min(axis=2)
+    hi = w.max(axis=2)
+    const = hi == lo
+    s16 = ((hi - lo) / np.float32(15.0)).astype(np.float16)
+    s16[const] = np.float16(1.0)
+    s = s16.astype(np.float32)
+    if fractional_zero:
+        z16 = np.clip(-lo / s, 0.0, 15.0).astype(np.float16)
+    else:
+        z16 = np.clip(np.rint(-lo / s), 0.0, 15.0).astype(np.float16)
+    z16[const] = np.float16(0.0)
+    z = z16.astype(np.float32)
+    if fractional_zero:
+        q = np.clip(np.rint(w / s[..., None] + z[..., None]), 0, 15)
+    else:
+        q = np.clip(np.rint(w / s[..., None]) + z[..., None], 0, 15)
+    q = q.astype(np.uint32).reshape(N, K // 8, 8)
+    shifts = (np.arange(8, dtype=np.uint32) * np.uint32(4))[None, None, :]
+    words = np.bitwise_or.reduce(q << shifts, axis=2).astype(np.uint32)
+    return words.view(np.int32), s16.view(np.uint16), z16.view(np.uint16)
+
+
+@dataclass
+class Int4Weights:
+    q: np.ndarray       # [E, N, K/8] int32
+    scale: np.ndarray   # [E, N, K/128] fp16 bits (uint16)
+    zero: np.ndarray    # [E, N, K/128] fp16 bits (uint16)
+
+
+@dataclass
+class Workload:
+    cfg: WorkloadConfig
+    x: np.ndarray                    # [T, d]   bf16 bits (uint16) or fp32
+    w_router: np.ndarray             # [E, d]   activation dtype
+    b_router: np.ndarray             # [E]      fp32
+    w_gate: Optional[np.ndarray]     # [E, F, d] (None for ReLU)
+    w_up: np.ndarray                 # [E, F, d] (W_in for ReLU)
+    w_down: np.ndarray               # [E, d, F]
+    ws_gate: Optional[np.ndarray] = None   # [S*F_s, d] shared experts, concatenated along F
+    ws_up: Optional[np.ndarray] = None
+    ws_down: Optional[np.ndarray] = None   # [d, S*F_s]
+    q_gate: Optional[Int4Weights] = None
+    q_up: Optional[Int4Weights] = None
+    q_down: Optional[Int4Weights] = None
+
+    @property
+    def bf16(self) -> bool:
+        return self.cfg.dtype == "bf16"
+
+
+def router_bias(cfg: WorkloadConfig, beta: Optional[float] = None) -> np.ndarray:
+    """Router bias per the config's recipe (fp32)."""
+    E = cfg.E
+    beta = cfg.beta if beta is None else beta
+    e = np.arange(E, dtype=np.float64)
+    if cfg.bias == "zero":
+        b = np.zeros(E)
+    elif cfg.bias == "log_inv":           # b_e = 0.5 ln(1/(e+1))
+        b = 0.5 * np.log(1.0 / (e + 1.0))
+    elif cfg.bias == "neg_log":           # b_e = -beta ln(e+1)
+        b = -beta * np.log(e + 1.0)
+    elif cfg.bias == "zipf":              # b_e = -1.1 beta ln(r_e), r_e a seeded rank in 1..E
+        ranks = _rng(cfg.cfg_id, TID_ZIPF).permutation(E) + 1
+        b = -1.1 * beta * np.log(ranks.astype(np.float64))
+    else:
+        raise ValueError(cfg.bias)
+    return b.astype(np.float32)
+
+
+def make_workload(cfg, beta: Optional[float] = None, fractional_zero: bool = False,
+                  threads: int = 8) -> Workload:
+    """Draw every tensor of a workload.  ``cfg`` is a WorkloadConfig or a name."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    bf16 = cfg.dtype == "bf16"
+    T, d, E, F = cfg.T, cfg.d, cfg.E, cfg.F
+    wid = CONFIGS[cfg.weights_of].cfg_id if cfg.weights_of else cfg.cfg_id
+    if cfg.x_rows_of:
+        src = CONFIGS[cfg.x_rows_of]
+        assert src.d == d and T <= src.T
+        x = _normal(src.cfg_id, TID_X, 0, (src.T, d), 1.0, bf16)[:T].copy()
+    else:
+        x = _normal(cfg.cfg_id, TID_X, 0, (T, d), 1.0, bf16)
+    w_router = _normal(wid, TID_WR, 0, (E, d), W_STD, bf16)
+    b_router = router_bias(cfg, beta)
+
+    def mk(tid, shape):
+        return _per_expert(lambda e: _normal(wid, tid, e, shape, W_STD, bf16), E, threads)
+
+    w_gate = mk(TID_WGATE, (F, d)) if cfg.act == "swiglu" else None
+    w_up = mk(TID_WUP, (F, d))
+    w_down = mk(TID_WDOWN, (d, F))
+    wl = Workload(cfg, x, w_router, b_router, w_gate, w_up, w_down)
+    if cfg.n_shared:
+        Fs = cfg.n_shared * cfg.F_shared
+        wl.ws_gate = _normal(wid, TID_SGATE, 0, (Fs, d), W_STD, bf16)
+        wl.ws_up = _normal(wid, TID_SUP, 0, (Fs, d), W_STD, bf16)
+        wl.ws_down = _normal(wid, TID_SDOWN, 0, (d, Fs), W_STD, bf16)
+    if cfg.int4:
+        assert bf16, "INT4 experts carry bf16 activations"
+
+        def q4(w):
+            parts = [None] * E
+
+            def one(e):
+                parts[e] = quantize_int4_rows(w[e], fractional_zero)
+            with ThreadPoolExecutor(max(1, min(threads, E))) as ex:
+                list(ex.map(one, range(E)))
+            return Int4Weights(np.stack([p[0] for p in parts]),
+                               np.stack([p[1] for p in parts]),
+                               np.stack([p[2] for p in parts]))
+        wl.q_gate = q4(w_gate)
+        wl.q_up = q4(w_up)
+        wl.q_down = q4(w_down)
+    return wl
+
