@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one full layer call (router logits, top-k + gates, permutation with
+counts and LIS, grouped gate/up GEMM, grouped down GEMM, shared experts when
+the layer has them, combine) on one batch of seeded synthetic input that is
+already resident in HBM.  The primary line is the Mixtral-8x7B-shaped prefill
+(T=4096, d=4096, E=8, top-2, SwiGLU d_ff=14336, bf16); the Mixtral decode
+(T=16) and the INT4-expert decode (T=64) are reported alongside in the same
+JSON line.  One JSON line is printed.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import dataclasses
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP32_VALU_PEAK_TFLOPS = 157.3
+
+
+def _hip():
+    h = C.CDLL("libamdhip64.so")
+    h.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+    h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+    h.hipEventSynchronize.argtypes = [C.c_void_p]
+    h.hipEventDestroy.argtypes = [C.c_void_p]
+    return h
+
+
+def work(cfg, counts):
+    """Algorithmic FLOPs and bytes of the layer and of its two GEMM kernels.
+
+    Counts only active experts' weights; excludes the H and y_rows round trips
+    (implementation traffic, reported by the counters instead)."""
+    T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F
+    rows = T * k
+    active = int(np.count_nonzero(counts))
+    swiglu = cfg.act == "swiglu"
+    esz = 4 if cfg.dtype == "f32" else 2
+    wsz = (0.5 + 2 * 2 / 128) if cfg.int4 else esz     # INT4: nibble + fp16 s,z per 128
+    gu_mats = 2 if swiglu else 1
+    gu_flops = 2.0 * rows * d * F * gu_mats
+    dn_flops = 2.0 * rows * d * F
+    gu_bytes = active * gu_mats * F * d * wsz + T * d * esz
+    dn_bytes = active * F * d * wsz + rows * d * 4
+    flops = gu_flops + dn_flops + 2.0 * T * d * E
+    wbytes = active * (gu_mats + 1) * F * d * wsz
+    if cfg.n_shared:
+        Fs = cfg.n_shared * cfg.F_shared
+        flops += 2.0 * T * d * Fs * 3
+        wbytes += 3.0 * Fs * d * esz
+    total_bytes = wbytes + E * d * esz + T * d * esz + T * d * 4
+    return dict(flops=flops, bytes=total_bytes, gu_flops=gu_flops, dn_flops=dn_flops,
+                gu_bytes=gu_bytes, dn_bytes=dn_bytes, active=active)
+
+
+def run_gpu(name, steps, warmup):
+    import torch
+    import sparse_mixture_experts_wavefront_amd as moe
+    from sparse_mixture_experts_wavefront_amd.device_inputs import to_device
+    from workloads import make_workload
+    wl = make_workload(name)
+    cfg = wl.cfg
+    layer, x = to_device(wl)
+    runner = moe.LayerRunner(layer, cfg.T)
+    for _ in range(warmup):
+        runner(x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        runner(x)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1000.0 / steps
+    counts = runner.aux_t["counts"].cpu().numpy()
+    lis = float(runner.aux_t["lis"].cpu().numpy()[0])
+
+    # per-stage durations from HIP events recorded by the library on this stream
+    hip = _hip()
+    handles = []
+    for i in range(7):
+        h = C.c_void_p()
+        assert hip.hipEventCreate(C.byref(h)) == 0
+        handles.append(h.value)
+    evs = (C.c_void_p * 7)(*handles)
+    st = np.zeros(6)
+    B = moe.lib()
+    B.moe_set_stage_events(C.cast(evs, C.POINTER(C.c_void_p)), 7)
+    try:
+        for _ in range(steps):
+            runner(x)
+            hip.hipEventSynchronize(evs[6])
+            for i in range(6):
+                f = C.c_float(0)
+                hip.hipEventElapsedTime(C.byref(f), evs[i], evs[i + 1])
+                st[i] += f.value
+    finally:
+        B.moe_set_stage_events(None, 0)
+        for i in range(7):
+            hip.hipEventDestroy(evs[i])
+    st /= steps
+    w = work(cfg, counts)
+    stages = dict(zip(["route_topk", "permute", "gate_up_gemm", "down_gemm", "shared_experts",
+                       "combine"], [round(v * 1000.0, 2) for v in st]))
+    return wl, dict(ms=ms, counts=counts, lis=lis, stages_us=stages, work=w)
+
+
+def roofline(cfg, r):
+    w = r["work"]
+    t = r["stages_us"]["gate_up_gemm"] * 1e-6
+    if cfg.T * cfg.k >= 1024:          # many rows per expert: the GEMM is MFMA-bound
+        ach = w["gu_flops"] / t / 1e12
+        return dict(kernel="grouped_gemm gate/up (SwiGLU epilogue)", bound="mfma",
+                    achieved=round(ach, 1), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None,
+                    per_launch=dict(flops=w["gu_flops"], us=round(t * 1e6, 2)))
+    ach = w["gu_bytes"] / t / 1e9
+    return dict(kernel="grouped_gemm gate/up (weight streaming)", bound="hbm",
+                achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                per_launch=dict(bytes=w["gu_bytes"], us=round(t * 1e6, 2)))
+
+
+def cpu_baseline(wl, target_s=15.0):
+    """The oracle (as it stands) on a bounded sample: the first S tokens as a batch."""
+    import oracle
+    cfg = wl.cfg
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+    def sample(S):
+        c = dataclasses.replace(cfg, T=S)
+        return dataclasses.replace(wl, cfg=c, x=wl.x[:S].copy())
+    S = min(cfg.T, 8)
+    t0 = time.perf_counter()
+    oracle.layer_forward(sample(S))
+    dt = time.perf_counter() - t0
+    S2 = int(min(cfg.T, max(S, S * target_s / max(dt, 1e-3))))
+    if S2 > S:
+        S = S2
+        t0 = time.perf_counter()
+        oracle.layer_forward(sample(S))
+        dt = time.perf_counter() - t0
+    return dict(value=round(S / dt, 3), unit="tokens/s", cores=threads, kind="oracle",
+                sample="first %d of %d tokens as one batch, whole layer (router, top-k, "
+                       "permutation, FFN, combine), fp64 C oracle, %.1f s" % (S, cfg.T, dt))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill_bf16")
+    ap.add_argument("--secondary", default="mixtral_decode_bf16,mixtral_int4_decode",
+                    help="comma-separated extra workloads reported in the same line ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    wl, r = run_gpu(args.workload, args.steps, args.warmup)
+    cfg = wl.cfg
+    value = cfg.T / (r["ms"] / 1000.0)
+    out = {
+        "metric": "MoE-layer tokens/sec at Mixtral shape; % MFMA peak (prefill) / % HBM BW (decode)",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["ms"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) random-init weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E,
+                   "top_k": cfg.k, "d_ff": cfg.F, "act": cfg.act, "int4": cfg.int4,
+                   "n_shared": cfg.n_shared, "parallelism": "none (1 GPU)"},
+        "lis": r["lis"], "active_experts": r["work"]["active"],
+        "layer_tflops": round(r["work"]["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
+        "stages_us": r["stages_us"],
+        "roofline": roofline(cfg, r),
+    }
+    sec = []
+    for name in [s for s in args.secondary.split(",") if s]:
+        wl2, r2 = run_gpu(name, args.steps, args.warmup)
+        c2 = wl2.cfg
+        sec.append({"workload": name, "T": c2.T, "tokens_per_s": round(c2.T / (r2["ms"] / 1e3), 1),
+                    "ms_per_step": round(r2["ms"], 4), "lis": r2["lis"],
+                    "layer_GBps": round(r2["work"]["bytes"] / (r2["ms"] * 1e-3) / 1e9, 1),
+                    "layer_hbm_frac": round(r2["work"]["bytes"] / (r2["ms"] * 1e-3) / 1e9
+                                            / HBM_PEAK_GBS, 4),
+                    "stages_us": r2["stages_us"], "roofline": roofline(c2, r2)})
+        del wl2
+    if sec:
+        out["secondary"] = sec
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

