@@ -189,6 +189,9 @@ def dense_expert_weights(wl, experts=None):
     sel = range(E) if experts is None else experts
     out = []
     for qw, shape_src in ((wl.q_gate, wl.w_gate), (wl.q_up, wl.w_up), (wl.q_down, wl.w_down)):
+        if qw is None:          # ReLU experts have no gate projection
+            out.append(None)
+            continue
         full = np.zeros(shape_src.shape, np.uint16)
         for e in sel:
             full[e] = dequant_int4(qw.q[e], qw.scale[e], qw.zero[e])

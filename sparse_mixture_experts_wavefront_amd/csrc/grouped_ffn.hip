@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(TileArgs p) {
 // column strip and XCD-contiguous, so the concurrent blocks of one XCD share
 // A and B slices in its L2.
 
-constexpr int kV2BM = 256, kV2BN = 256, kV2BK = 32, kV2Stages = 4, kV2GroupM = 8;
+constexpr int kV2BM = 256, kV2BN = 256, kV2BK = 32, kV2GroupM = 8;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ void dma16(const void* g, u16* lds) {
@@ -324,7 +324,8 @@ __device__ __forceinline__ int v2_off(int row, int chunk) {
 template <int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_v2_kernel(TileArgs p) {
-  constexpr int BM = kV2BM, BN = kV2BN, BK = kV2BK;
+  constexpr int BM = kV2BM, BK = kV2BK;
+  static_assert(kV2BM == kV2BN, "square stage buffers");
   constexpr int STAGE = BM * BK;  // elements per operand per stage (BM == BN)
   __shared__ __align__(16) u16 sA0[STAGE], sA1[STAGE], sA2[STAGE], sA3[STAGE];
   __shared__ __align__(16) u16 sB0[STAGE], sB1[STAGE], sB2[STAGE], sB3[STAGE];
@@ -807,6 +808,7 @@ size_t ffn_ws_bytes(int rows, int F, moe_dtype dt) {
 
 hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid) {
   if (p.rows == 0) return hipSuccess;
+  if (stream_ffn_applies(p)) return launch_stream_ffn(p, s, mid);
   const bool relu = p.act == MOE_ACT_RELU;
   const int E = p.offsets ? p.E : 1;
   if (p.dt == MOE_DT_F32) {

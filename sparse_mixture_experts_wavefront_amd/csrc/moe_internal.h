@@ -67,6 +67,11 @@ struct FfnProblem {
 size_t ffn_ws_bytes(int rows, int F, moe_dtype dt);
 hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid = nullptr);
 
+// Weight-streaming variant for few rows per expert (decode); same contract as
+// launch_grouped_ffn.
+bool stream_ffn_applies(const FfnProblem& p);
+hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid = nullptr);
+
 hipError_t launch_combine(const float* y_rows, const int32_t* assign_row, int T, int k, int d,
                           const float* y_shared, void* y, moe_dtype ydt, hipStream_t s);
 

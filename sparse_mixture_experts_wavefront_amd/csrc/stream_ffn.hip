@@ -1,0 +1,462 @@
+// stream_ffn.hip -- grouped expert FFN for few rows per expert (decode).
+//
+// With a handful of token rows per expert the FFN is a weight stream: every
+// weight byte is read once and each feeds only a few multiply-adds, so HBM
+// bandwidth bounds it ("FloE: On-the-Fly MoE Inference on Memory-constrained
+// GPU" -- What carries the argument: decode time goes to moving expert weights;
+// "D^2MoE: Dual Routing and Dynamic Scheduling for Efficient On-Device
+// MoE-based LLM Serving" -- What carries the argument and Figure 8: low-bit
+// expert weights are decoded inside the GEMM kernel).
+//
+// One block = one expert x one strip of 32 output columns (64 weight rows for
+// gate/up: 32 gate + 32 up, the same f-values; 32 rows for ReLU W_in and for
+// down).  Weights stream in chunks of 512 K values (bf16: 16 rows x 1 KB;
+// INT4: all rows x 256 B) with non-temporal 16-byte loads laid out so one wave
+// instruction reads whole contiguous row pieces (measured on MI355X: ~7 TB/s
+// from HBM this way, ~5-5.6 TB/s when each instruction reads 64 B of 16 rows
+// as the MFMA operand layout would, ~5.5 TB/s through LDS DMA).  Chunks are
+// loaded three ahead into registers, written to one of two LDS slots in the
+// 16x16x32 MFMA operand layout, and multiplied by the 4 waves, each taking a
+// quarter of the chunk's K range, against the expert's token rows (up to 16
+// per B operand, zero-padded).  The four K-partial sums meet in LDS at the end;
+// the epilogue applies SiLU(gate)*up (to bf16 H) or the gate scale (fp32 rows).
+//
+// INT4 weights (group 128 along K, fp16 scale s and zero z, 8 nibbles per
+// int32, low nibble first) are decoded after the LDS read:
+//   W = bf16_RNE( fp32( fp32(q) - z ) * s )
+// When fp32(q) - z is exact for every q in 0..15 (z == 0 or |z| >= 2^-10), this
+// equals bf16_RNE( fma(q, s, -(z*s)) ): z*s is exact in fp32 (11+11 bits) and
+// the fma rounds the exact (q - z)*s once.  Each wave checks its zero points
+// per chunk and takes the two-operation form otherwise.
+// Within a chunk, lane (r, g) of wave w feeds MFMA step s with K values
+// [w*128 + g*32 + s*8, +8); the token operand uses the same map, so the MFMA
+// sums over the same K set (the order of K inside one accumulation is free).
+// LDS rows keep 16-byte unit u of row r at position u ^ (r & 15), so the 16 rows
+// one read pass touches fall on 16 different bank groups.
+#include <type_traits>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kSModeGateUp = 0, kSModeRelu = 1, kSModeDown = 2;
+
+
+struct StreamArgs {
+  const u16* X;            // gate/up: x [T][ldx]; down: H [rows][ldx]
+  int ldx;
+  const int32_t* gather;   // gate/up: row -> flat assignment (token = a / k); NULL: row
+  int k;
+  const unsigned char* W0; // dense bf16 or INT4 words, [E][N][K] elements
+  const unsigned char* W1;
+  const u16* s0; const u16* s1; const u16* z0; const u16* z1;   // INT4 fp16 [E][N][K/128]
+  int N, K;
+  const int32_t* offsets;  // [E+1] or NULL (one expert, `rows` rows)
+  int rows;
+  u16* H;                  // gate/up output [rows][N]
+  float* Y;                // down output [rows][N]
+  const int32_t* gate_map;
+  const float* gate;
+  int nblk_per_expert;
+};
+
+__device__ __forceinline__ float h2f(u16 h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// fp32(q) - z is exact for all q in 0..15 when z == 0 or |z| >= 2^-10 (finite).
+__device__ __forceinline__ bool zero_point_fma_exact(u16 z) {
+  const unsigned ex = (z >> 10) & 0x1f;
+  return (z & 0x7fff) == 0 || (ex >= 5 && ex != 31);
+}
+
+// byte b of v as fp32 (v_cvt_f32_ubyte{b}; plain VALU, no memory access)
+__device__ __forceinline__ float ub0(uint32_t v) { float f; asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(v)); return f; }
+__device__ __forceinline__ float ub1(uint32_t v) { float f; asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(v)); return f; }
+__device__ __forceinline__ float ub2(uint32_t v) { float f; asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(v)); return f; }
+__device__ __forceinline__ float ub3(uint32_t v) { float f; asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(v)); return f; }
+// two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// 8 nibbles (low first) -> 8 bf16, fused form: fma(q, s, nzs), nzs = -(z*s) exact.
+__device__ __forceinline__ bf16x8 dq8_fma(uint32_t w, float s, float nzs) {
+  const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;  // nibbles 0,2,4,6 / 1,3,5,7
+  u32x4 o;
+  o[0] = pk_bf16(__builtin_fmaf(ub0(lo), s, nzs), __builtin_fmaf(ub0(hi), s, nzs));
+  o[1] = pk_bf16(__builtin_fmaf(ub1(lo), s, nzs), __builtin_fmaf(ub1(hi), s, nzs));
+  o[2] = pk_bf16(__builtin_fmaf(ub2(lo), s, nzs), __builtin_fmaf(ub2(hi), s, nzs));
+  o[3] = pk_bf16(__builtin_fmaf(ub3(lo), s, nzs), __builtin_fmaf(ub3(hi), s, nzs));
+  return as_bf16x8(o);
+}
+// the defining two-operation form (any zero point)
+__device__ __forceinline__ bf16x8 dq8_exact(uint32_t w, float s, float z) {
+  const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+  auto f = [&](float q) { return __fmul_rn(__fsub_rn(q, z), s); };
+  u32x4 o;
+  o[0] = pk_bf16(f(ub0(lo)), f(ub0(hi)));
+  o[1] = pk_bf16(f(ub1(lo)), f(ub1(hi)));
+  o[2] = pk_bf16(f(ub2(lo)), f(ub2(hi)));
+  o[3] = pk_bf16(f(ub3(lo)), f(ub3(hi)));
+  return as_bf16x8(o);
+}
+
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int gcd_c(int a, int b) { return b ? gcd_c(b, a % b) : a; }
+constexpr int lcm3(int a, int b, int c) {
+  const int ab = a / gcd_c(a, b) * b;
+  return ab / gcd_c(ab, c) * c;
+}
+
+template <int MODE, bool INT4, int MB>
+__global__ __launch_bounds__(256) void stream_ffn_kernel(StreamArgs p) {
+  constexpr int R = (MODE == kSModeGateUp) ? 64 : 32;  // weight rows per block
+  constexpr int RBLK = R / 16;
+  constexpr int NOUT = 32;                              // output columns per block
+  constexpr int KC = 512, KW = 128, NS = 4, KL = 32;    // K per chunk / wave / MFMA steps / lane
+  constexpr int CR = INT4 ? R : 16;                     // weight rows per chunk
+  constexpr int RBYTES = INT4 ? KC / 2 : KC * 2;        // bytes per row per chunk (256 | 1024)
+  constexpr int CBYTES = CR * RBYTES;                   // 16 KB (8 KB for INT4 ReLU/down)
+  constexpr int NRC = R / CR;                           // chunks per K slice
+  constexpr int CRB = CR / 16;                          // 16-row blocks per chunk
+  constexpr int UPR = RBYTES / 16;                      // 16-byte units per row per chunk
+  constexpr int NLD = CBYTES / 1024 / 4;                // 16-byte weight loads per lane per chunk
+  constexpr int WU = INT4 ? 1 : 4;                      // 16-byte units per lane per row block
+  constexpr int D = (INT4 && MB > 1) ? 1 : 2;           // chunks loaded ahead
+  constexpr int NSET = D + 1;
+  // unroll: a common multiple of the register sets, the 2 LDS slots and the
+  // chunks per K slice, so set, slot and row block are compile-time in the body
+  constexpr int U = lcm3(NSET, 2, NRC);
+  static_assert(UPR >= 16 && NLD >= 1, "geometry");
+
+  __shared__ __align__(16) unsigned char sW0[CBYTES], sW1[CBYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int e = blockIdx.x / p.nblk_per_expert;
+  const int nb = blockIdx.x - e * p.nblk_per_expert;
+  int row0 = 0, cnt = p.rows;
+  if (p.offsets) {
+    row0 = p.offsets[e];
+    cnt = p.offsets[e + 1] - row0;
+  }
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  cnt = __builtin_amdgcn_readfirstlane(cnt);
+  if (cnt <= 0) return;
+  const int n0 = nb * NOUT;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nchunks = (p.K / KC) * NRC;
+  const int kgroups = p.K >> 7;
+  const size_t row_bytes = INT4 ? (size_t)p.K / 2 : (size_t)p.K * 2;
+
+  // block row r (0..R-1) -> weight matrix and row
+  auto wsel = [&](int r, const unsigned char*& W, int& n) {
+    if constexpr (MODE == kSModeGateUp) {
+      W = (r < 32) ? p.W0 : p.W1;
+      n = n0 + (r & 31);
+    } else {
+      W = p.W0;
+      n = n0 + r;
+    }
+    n = min(n, p.N - 1);
+  };
+  // Loads: load j of wave w covers chunk units (w*NLD+j)*64 + lane, i.e. chunk
+  // row u / UPR, unit u % UPR: one wave instruction reads RBYTES-long contiguous
+  // row pieces (1 KB for bf16).  N is a multiple of the strip width (checked by
+  // the launcher), so a chunk's rows are a fixed offset from chunk 0's rows.
+  const unsigned char* lsrc[NLD];
+  const unsigned char* lsrc_up[NLD];
+  int ldst[NLD];  // LDS byte offset of the unit (chunk row r, unit pos ^ (r & 15))
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int u = (w * NLD + j) * 64 + lane;
+    const int r = u / UPR, pos = u % UPR;
+    const unsigned char* W;
+    int n;
+    wsel(r, W, n);
+    lsrc[j] = W + ((size_t)e * p.N + n) * row_bytes + pos * 16;
+    if constexpr (MODE == kSModeGateUp && NRC > 1) {
+      wsel(32 + r, W, n);
+      lsrc_up[j] = W + ((size_t)e * p.N + n) * row_bytes + pos * 16;
+    } else {
+      lsrc_up[j] = lsrc[j];
+    }
+    ldst[j] = r * RBYTES + ((pos ^ (r & 15)) * 16);
+  }
+
+  const u16* sz_s[RBLK];
+  const u16* sz_z[RBLK];
+  if constexpr (INT4) {
+#pragma unroll
+    for (int rb = 0; rb < RBLK; ++rb) {
+      const int r = rb * 16 + r16;
+      const unsigned char* W;
+      int n;
+      wsel(r, W, n);
+      const bool second = (MODE == kSModeGateUp) && r >= 32;
+      sz_s[rb] = (second ? p.s1 : p.s0) + ((size_t)e * p.N + n) * kgroups;
+      sz_z[rb] = (second ? p.z1 : p.z0) + ((size_t)e * p.N + n) * kgroups;
+    }
+  }
+
+  for (int mbase = 0; mbase < cnt; mbase += MB * 16) {
+    const int mrows = min(MB * 16, cnt - mbase);
+    const int mb_act = (mrows + 15) >> 4;
+    const u16* xrow[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = mb * 16 + r16;
+      const int rr = row0 + mbase + min(m, mrows - 1);
+      const int src = p.gather ? p.gather[rr] / p.k : rr;
+      xrow[mb] = p.X + (size_t)src * p.ldx + w * KW + g * KL;
+    }
+    f32x4 acc[RBLK][MB];
+#pragma unroll
+    for (int rb = 0; rb < RBLK; ++rb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    struct Set {
+      u32x4 wv[NLD];
+      u32x4 x[MB][NS];
+      u16 s[CRB], z[CRB];
+    };
+    // chunk c = (kc, rc): rows rc*CR.., K [kc*KC, +KC); lane (r, g) feeds MFMA
+    // step s with K [w*KW + g*KL + s*8, +8) of it (weights and tokens alike)
+    auto load = [&](Set& st, int c) {
+      const int kc = c / NRC, rc = c - kc * NRC;
+      const bool up = (MODE == kSModeGateUp && NRC > 1) && rc >= NRC / 2;
+      const size_t roff = (size_t)kc * RBYTES + (size_t)((NRC > 1 ? rc : 0) & 1) * 16 * row_bytes;
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+        st.wv[j] = __builtin_nontemporal_load((const u32x4*)((up ? lsrc_up[j] : lsrc[j]) + roff));
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)  // rows past the count are clamped copies
+#pragma unroll
+        for (int s = 0; s < NS; ++s) st.x[mb][s] = *(const u32x4*)(xrow[mb] + (size_t)kc * KC + s * 8);
+      if constexpr (INT4) {
+        const int grp = (kc * KC + w * KW + g * KL) >> 7;
+#pragma unroll
+        for (int i = 0; i < CRB; ++i) {
+          st.s[i] = sz_s[rc * CRB + i][grp];
+          st.z[i] = sz_z[rc * CRB + i][grp];
+        }
+      }
+    };
+    auto store = [&](unsigned char* slot, const Set& st) {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) *(u32x4*)(slot + ldst[j]) = st.wv[j];
+    };
+    auto compute = [&](const unsigned char* slot, const Set& st, int rc) {
+      const int ubase = INT4 ? (w * KW + g * KL) / 32 : (w * KW + g * KL) / 8;
+      u32x4 wv[CRB][WU];
+#pragma unroll
+      for (int i = 0; i < CRB; ++i) {
+        const int r = i * 16 + r16;
+#pragma unroll
+        for (int q = 0; q < WU; ++q)
+          wv[i][q] = *(const u32x4*)(slot + r * RBYTES + (((ubase + q) ^ (r & 15)) * 16));
+      }
+      if constexpr (!INT4) {
+#pragma unroll
+        for (int i = 0; i < CRB; ++i)
+#pragma unroll
+          for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+              acc[rc * CRB + i][mb] = mfma16(as_bf16x8(wv[i][s]), as_bf16x8(st.x[mb][s]),
+                                             acc[rc * CRB + i][mb]);
+      } else {
+        float sf[CRB], zf[CRB], nzs[CRB];
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < CRB; ++i) {
+          sf[i] = h2f(st.s[i]);
+          zf[i] = h2f(st.z[i]);
+          nzs[i] = -(zf[i] * sf[i]);
+          ok = ok && zero_point_fma_exact(st.z[i]);
+        }
+        // one uniform choice per chunk: the fused decode when every zero point
+        // of the chunk allows it (the usual case), else the two-operation form
+        const bool fast =
+            __builtin_amdgcn_readfirstlane((int)(__ballot(!ok) == 0ull)) != 0;
+        auto run = [&](auto fused) {
+#pragma unroll
+          for (int i = 0; i < CRB; ++i) {
+            bf16x8 a[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              if constexpr (decltype(fused)::value)
+                a[s] = dq8_fma(wv[i][0][s], sf[i], nzs[i]);
+              else
+                a[s] = dq8_exact(wv[i][0][s], sf[i], zf[i]);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+              for (int mb = 0; mb < MB; ++mb)
+                acc[rc * CRB + i][mb] = mfma16(a[s], as_bf16x8(st.x[mb][s]), acc[rc * CRB + i][mb]);
+          }
+        };
+        if (fast)
+          run(std::true_type{});
+        else
+          run(std::false_type{});
+      }
+    };
+
+    // ---- pipeline: chunk c sits in register set c % NSET (loaded D chunks
+    // ahead), goes to LDS slot c % 2, is published by the barrier and multiplied.
+    // Slot c % 2 was last read in iteration c - 2, which every wave finished
+    // before the barrier of iteration c - 1.
+    Set st[NSET];
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (d < nchunks) load(st[d], d);
+    for (int c0 = 0; c0 < nchunks; c0 += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u;
+        if (c < nchunks) {  // uniform
+          unsigned char* slot = (u & 1) ? sW1 : sW0;
+          store(slot, st[u % NSET]);
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+          block_barrier();
+          if (c + D < nchunks) load(st[(u + D) % NSET], c + D);
+          compute(slot, st[u % NSET], u % NRC);  // c0 is a multiple of U, so rc = u % NRC
+        }
+      }
+    }
+
+    // ---- cross-wave reduction and epilogue, one 16-row token block at a time ----
+    float* red = (float*)sW0;  // [4 waves][RBLK][64 lanes][4]
+    static_assert(4 * RBLK * 64 * 16 <= CBYTES, "reduction buffer");
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if (mb >= mb_act) break;
+      __syncthreads();
+#pragma unroll
+      for (int rb = 0; rb < RBLK; ++rb)
+        *(f32x4*)(red + (((w * RBLK) + rb) * 64 + lane) * 4) = acc[rb][mb];
+      __syncthreads();
+      for (int o = tid; o < 16 * NOUT; o += 256) {
+        const int m = o / NOUT, col = o % NOUT;
+        const int row = mbase + mb * 16 + m;
+        if (row >= cnt || n0 + col >= p.N) continue;
+        // C layout of 16x16 MFMA: weight row 4*(lane/16)+i, token column lane%16
+        auto part = [&](int wr) {
+          const int rb = wr >> 4, rr = wr & 15;
+          const int ln = (rr >> 2) * 16 + m, i = rr & 3;
+          float sacc = 0.0f;
+#pragma unroll
+          for (int ww = 0; ww < 4; ++ww) sacc += red[((ww * RBLK + rb) * 64 + ln) * 4 + i];
+          return sacc;
+        };
+        const size_t orow = (size_t)(row0 + row);
+        if constexpr (MODE == kSModeGateUp) {
+          const float gv = part(col), uv = part(32 + col);
+          p.H[orow * p.N + n0 + col] = f32_to_bf16(silu_f32(gv) * uv);
+        } else if constexpr (MODE == kSModeRelu) {
+          p.H[orow * p.N + n0 + col] = f32_to_bf16(fmaxf(part(col), 0.0f));
+        } else {
+          const float gs = p.gate ? p.gate[p.gate_map ? p.gate_map[orow] : orow] : 1.0f;
+          p.Y[orow * p.N + n0 + col] = gs * part(col);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int MODE, bool INT4>
+hipError_t launch_mode(const StreamArgs& a, int E, int mb, hipStream_t s) {
+  const dim3 grid((unsigned)(E * a.nblk_per_expert)), block(256);
+  // up to 32 token rows per pass; an expert with more rows takes further passes
+  if (mb <= 1)
+    hipLaunchKernelGGL((stream_ffn_kernel<MODE, INT4, 1>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((stream_ffn_kernel<MODE, INT4, 2>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool stream_ffn_applies(const FfnProblem& p) {
+  if (p.dt != MOE_DT_BF16) return false;
+  // few rows per expert: every expert has at most T rows (a token picks an
+  // expert once); beyond 64 the tiled kernels win
+  if (p.T > 64) return false;
+  const bool int4 = p.w->q_up != nullptr;
+  (void)int4;
+  // chunking needs both reduction lengths to be multiples of 512
+  return (p.d % 512) == 0 && (p.F % 512) == 0;
+}
+
+hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid) {
+  const bool int4 = p.w->q_up != nullptr;
+  const bool relu = p.act == MOE_ACT_RELU;
+  const int E = p.offsets ? p.E : 1;
+  const int mb = (p.T + 15) / 16;
+  StreamArgs a{};
+  a.k = p.k;
+  a.offsets = p.offsets;
+  a.rows = p.rows;
+  // gate/up (or ReLU W_in): weights [E][F][d], tokens x
+  a.X = (const u16*)p.x;
+  a.ldx = p.d;
+  a.gather = p.row_assign;
+  a.N = p.F;
+  a.K = p.d;
+  a.H = (u16*)p.H;
+  a.nblk_per_expert = (p.F + 31) / 32;
+  if (int4) {
+    const moe_w4* g = relu ? p.w->q_up : p.w->q_gate;
+    const moe_w4* u = p.w->q_up;
+    a.W0 = (const unsigned char*)g->q; a.s0 = g->scale; a.z0 = g->zero;
+    a.W1 = (const unsigned char*)u->q; a.s1 = u->scale; a.z1 = u->zero;
+  } else {
+    a.W0 = (const unsigned char*)(relu ? p.w->w_up : p.w->w_gate);
+    a.W1 = (const unsigned char*)p.w->w_up;
+  }
+  hipError_t e;
+  if (relu)
+    e = int4 ? launch_mode<kSModeRelu, true>(a, E, mb, s) : launch_mode<kSModeRelu, false>(a, E, mb, s);
+  else
+    e = int4 ? launch_mode<kSModeGateUp, true>(a, E, mb, s)
+             : launch_mode<kSModeGateUp, false>(a, E, mb, s);
+  if (e != hipSuccess) return e;
+  if (mid) {
+    e = hipEventRecord(mid, s);
+    if (e != hipSuccess) return e;
+  }
+  // down: weights [E][d][F], operand H
+  StreamArgs b{};
+  b.k = p.k;
+  b.offsets = p.offsets;
+  b.rows = p.rows;
+  b.X = (const u16*)p.H;
+  b.ldx = p.F;
+  b.gather = nullptr;
+  b.N = p.d;
+  b.K = p.F;
+  b.Y = p.y_rows;
+  b.gate_map = p.row_assign;
+  b.gate = p.gate;
+  b.nblk_per_expert = (p.d + 31) / 32;
+  if (int4) {
+    b.W0 = (const unsigned char*)p.w->q_down->q; b.s0 = p.w->q_down->scale; b.z0 = p.w->q_down->zero;
+  } else {
+    b.W0 = (const unsigned char*)p.w->w_down;
+  }
+  return int4 ? launch_mode<kSModeDown, true>(b, E, mb, s) : launch_mode<kSModeDown, false>(b, E, mb, s);
+}
+
+}  // namespace moe

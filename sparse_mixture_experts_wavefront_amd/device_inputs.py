@@ -25,8 +25,8 @@ def to_device(wl, device="cuda"):
     cfg = wl.cfg
     bf = cfg.dtype == "bf16"
     if cfg.int4:
-        routed = ExpertWeights(q_gate=_q(wl.q_gate, device), q_up=_q(wl.q_up, device),
-                               q_down=_q(wl.q_down, device))
+        routed = ExpertWeights(q_gate=None if wl.q_gate is None else _q(wl.q_gate, device),
+                               q_up=_q(wl.q_up, device), q_down=_q(wl.q_down, device))
     else:
         routed = ExpertWeights(
             w_gate=None if wl.w_gate is None else _t(wl.w_gate, device, bf),

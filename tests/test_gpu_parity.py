@@ -99,11 +99,20 @@ SMALL = {
     "tiny_fp32": ("tiny_fp32", {}),
     "switch_small": ("switch_bf16", dict(T=300, d=256, F=384)),
     "mixtral_small": ("mixtral_prefill_bf16", dict(T=333, d=512, F=640)),
-    "decode_small": ("mixtral_decode_bf16", dict(T=16, d=512, F=640, x_rows_of=None,
+    "decode_small": ("mixtral_decode_bf16", dict(T=16, d=512, F=1024, x_rows_of=None,
                                                  weights_of=None)),
+    # several K slices per weight strip in the streaming kernels (regression:
+    # row-block selection must stay compile-time there)
+    "decode_multi_kslice": ("mixtral_decode_bf16", dict(T=16, d=2048, F=1536, x_rows_of=None,
+                                                        weights_of=None)),
+    "int4_multi_kslice": ("mixtral_int4_decode", dict(T=48, d=2048, F=1536, x_rows_of=None,
+                                                      weights_of=None)),
+    "decode_relu_small": ("switch_bf16", dict(T=40, d=512, F=1024)),
     "deepseek_small": ("deepseek_v2_lite_bf16", dict(T=257, d=256, F=192, F_shared=64)),
-    "int4_small": ("mixtral_int4_decode", dict(T=64, d=512, F=768, x_rows_of=None,
+    "int4_small": ("mixtral_int4_decode", dict(T=64, d=512, F=1024, x_rows_of=None,
                                                weights_of=None)),
+    "int4_relu_small": ("mixtral_int4_decode", dict(T=33, d=512, F=1024, act="relu",
+                                                    x_rows_of=None, weights_of=None)),
     "int4_prefill_small": ("mixtral_int4_decode", dict(T=300, d=256, F=384, x_rows_of=None,
                                                        weights_of=None)),
     "single_token": ("mixtral_prefill_bf16", dict(T=1, d=512, F=640)),
@@ -122,7 +131,7 @@ def test_layer_parity_small(case):
 
 def test_int4_fractional_zero_point():
     _say("int4 fractional zero point")
-    cfg = get_config("mixtral_int4_decode", T=40, d=256, F=384, x_rows_of=None, weights_of=None)
+    cfg = get_config("mixtral_int4_decode", T=40, d=512, F=1024, x_rows_of=None, weights_of=None)
     wl = make_workload(cfg, fractional_zero=True)
     assert np.any(wl.q_up.zero.view(np.float16) % 1 != 0)
     g = run_layer(wl)
@@ -130,14 +139,15 @@ def test_int4_fractional_zero_point():
     check_y(wl, g)
 
 
-def test_all_tokens_one_expert_and_empty_experts():
-    _say("all tokens routed to expert 3 (k=1), seven empty experts")
-    wl = make_workload(get_config("switch_bf16", T=200, d=128, F=256))
+@pytest.mark.parametrize("T", [200, 64])
+def test_all_tokens_one_expert_and_empty_experts(T):
+    _say("all tokens routed to expert 3 (k=1), seven empty experts, T=%d" % T)
+    wl = make_workload(get_config("switch_bf16", T=T, d=512, F=512))
     wl.b_router = np.zeros(8, np.float32)
     wl.b_router[3] = 100.0
     g = run_layer(wl)
     ref = check_routing(wl, g)
-    assert ref["counts"][3] == 200 and ref["lis"] == 8.0
+    assert ref["counts"][3] == T and ref["lis"] == 8.0
     check_y(wl, g)
 
 
@@ -165,9 +175,14 @@ def test_empty_batch():
     assert counts.cpu().numpy().sum() == 0 and math.isnan(float(lis.cpu()[0]))
 
 
-def test_deterministic_rerun():
-    _say("bitwise determinism")
-    wl = _workload("deepseek_v2_lite_bf16", T=257, d=256, F=192, F_shared=64)
+@pytest.mark.parametrize("name,over", [
+    ("deepseek_v2_lite_bf16", dict(T=257, d=256, F=192, F_shared=64)),
+    ("mixtral_decode_bf16", dict(T=16, d=2048, F=1536, x_rows_of=None, weights_of=None)),
+    ("mixtral_int4_decode", dict(T=64, d=1024, F=1024, x_rows_of=None, weights_of=None)),
+])
+def test_deterministic_rerun(name, over):
+    _say("bitwise determinism %s %s" % (name, over))
+    wl = _workload(name, **over)
     a = run_layer(wl)
     b = run_layer(wl)
     assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["logits"], b["logits"])

@@ -184,7 +184,7 @@ def make_workload(cfg, beta: Optional[float] = None, fractional_zero: bool = Fal
             return Int4Weights(np.stack([p[0] for p in parts]),
                                np.stack([p[1] for p in parts]),
                                np.stack([p[2] for p in parts]))
-        wl.q_gate = q4(w_gate)
+        wl.q_gate = q4(w_gate) if w_gate is not None else None
         wl.q_up = q4(w_up)
         wl.q_down = q4(w_down)
     return wl
