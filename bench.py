@@ -16,6 +16,7 @@ from __future__ import annotations
 import argparse
 import ctypes as C
 import dataclasses
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +27,13 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 FP32_VALU_PEAK_TFLOPS = 157.3
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "sparse_mixture_experts_wavefront_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_hbm_traffic.md")
+# sources whose text fixes each dominant kernel; a counter record taken from other text is void
+KERNEL_SOURCES = {"grouped_gemm": ("grouped_ffn.hip", "moe_internal.h"),
+                  "stream_ffn": ("stream_ffn.hip", "moe_internal.h")}
+COPY_CAL_BYTES = 1 << 30
 
 
 def _hip():
@@ -85,34 +93,79 @@ def run_gpu(name, steps, warmup):
     counts = runner.aux_t["counts"].cpu().numpy()
     lis = float(runner.aux_t["lis"].cpu().numpy()[0])
 
-    # per-stage durations from HIP events recorded by the library on this stream
+    # Per-stage durations from HIP events that the library records on the stream it
+    # launches on (torch's current stream).  One event set per step, no host sync
+    # inside the loop, so the stages run back to back as in the timed loop above.
     hip = _hip()
-    handles = []
-    for i in range(7):
-        h = C.c_void_p()
-        assert hip.hipEventCreate(C.byref(h)) == 0
-        handles.append(h.value)
-    evs = (C.c_void_p * 7)(*handles)
-    st = np.zeros(6)
+    sets = []
+    for _ in range(steps):
+        hs = []
+        for i in range(7):
+            h = C.c_void_p()
+            assert hip.hipEventCreate(C.byref(h)) == 0
+            hs.append(h.value)
+        sets.append((C.c_void_p * 7)(*hs))
     B = moe.lib()
-    B.moe_set_stage_events(C.cast(evs, C.POINTER(C.c_void_p)), 7)
+    per = np.zeros((steps, 7))
     try:
-        for _ in range(steps):
+        for evs in sets:
+            B.moe_set_stage_events(C.cast(evs, C.POINTER(C.c_void_p)), 7)
             runner(x)
-            hip.hipEventSynchronize(evs[6])
+        B.moe_set_stage_events(None, 0)
+        torch.cuda.synchronize()
+        for n, evs in enumerate(sets):
             for i in range(6):
                 f = C.c_float(0)
-                hip.hipEventElapsedTime(C.byref(f), evs[i], evs[i + 1])
-                st[i] += f.value
+                assert hip.hipEventElapsedTime(C.byref(f), evs[i], evs[i + 1]) == 0
+                per[n, i] = f.value
+            f = C.c_float(0)
+            assert hip.hipEventElapsedTime(C.byref(f), evs[0], evs[6]) == 0
+            per[n, 6] = f.value
     finally:
         B.moe_set_stage_events(None, 0)
-        for i in range(7):
-            hip.hipEventDestroy(evs[i])
-    st /= steps
+        for evs in sets:
+            for i in range(7):
+                hip.hipEventDestroy(evs[i])
+    st = per[:, :6].mean(axis=0)
+    layer_ms = per[:, 6]
     w = work(cfg, counts)
     stages = dict(zip(["route_topk", "permute", "gate_up_gemm", "down_gemm", "shared_experts",
                        "combine"], [round(v * 1000.0, 2) for v in st]))
-    return wl, dict(ms=ms, counts=counts, lis=lis, stages_us=stages, work=w)
+    timing = dict(event_ms_p10=round(float(np.percentile(layer_ms, 10)), 4),
+                  event_ms_p50=round(float(np.percentile(layer_ms, 50)), 4),
+                  event_ms_p90=round(float(np.percentile(layer_ms, 90)), 4))
+    return wl, dict(ms=ms, counts=counts, lis=lis, stages_us=stages, work=w, timing=timing)
+
+
+def sources_sha256(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of the gate/up kernel from committed rocprofv3 counter runs.
+
+    Records are lines 'traffic_record {json}' in the profile summary; each holds
+    FETCH_SIZE and WRITE_SIZE per dispatch already scaled by the copy-kernel factor,
+    and the sha256 of the kernel's sources when the counters were taken.  A record
+    whose hash differs from the current sources is stale and gives None."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    cur = sources_sha256(kernel)
+    for ln in lines:
+        if not ln.startswith("traffic_record "):
+            continue
+        rec = json.loads(ln[len("traffic_record "):])
+        if rec.get("workload") == workload and rec.get("kernel") == kernel:
+            if rec.get("sources_sha256") != cur:
+                return None
+            return round(float(rec["read_bytes"]) + float(rec["write_bytes"]))
+    return None
 
 
 def roofline(cfg, r):
@@ -122,12 +175,14 @@ def roofline(cfg, r):
         ach = w["gu_flops"] / t / 1e12
         return dict(kernel="grouped_gemm gate/up (SwiGLU epilogue)", bound="mfma",
                     achieved=round(ach, 1), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None,
+                    frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                    traffic=measured_traffic(cfg.name, "grouped_gemm"),
                     per_launch=dict(flops=w["gu_flops"], us=round(t * 1e6, 2)))
     ach = w["gu_bytes"] / t / 1e9
     return dict(kernel="grouped_gemm gate/up (weight streaming)", bound="hbm",
                 achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                frac=round(ach / HBM_PEAK_GBS, 4),
+                traffic=measured_traffic(cfg.name, "stream_ffn"),
                 per_launch=dict(bytes=w["gu_bytes"], us=round(t * 1e6, 2)))
 
 
@@ -164,6 +219,9 @@ def main():
     ap.add_argument("--secondary", default="mixtral_decode_bf16,mixtral_int4_decode",
                     help="comma-separated extra workloads reported in the same line ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device-to-device copy 5 times (the known-size kernel "
+                         "that scales the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -173,6 +231,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        import torch as _t
+        a = _t.empty(COPY_CAL_BYTES, dtype=_t.uint8, device="cuda").fill_(1)
+        b = _t.empty_like(a)
+        _t.cuda.synchronize()
+        for _ in range(5):
+            b.copy_(a)
+        _t.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": COPY_CAL_BYTES, "copies": 5}), flush=True)
+        return
 
     wl, r = run_gpu(args.workload, args.steps, args.warmup)
     cfg = wl.cfg
@@ -189,6 +258,7 @@ def main():
         "lis": r["lis"], "active_experts": r["work"]["active"],
         "layer_tflops": round(r["work"]["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
         "stages_us": r["stages_us"],
+        "timing": r["timing"],
         "roofline": roofline(cfg, r),
     }
     sec = []
@@ -200,7 +270,8 @@ def main():
                     "layer_GBps": round(r2["work"]["bytes"] / (r2["ms"] * 1e-3) / 1e9, 1),
                     "layer_hbm_frac": round(r2["work"]["bytes"] / (r2["ms"] * 1e-3) / 1e9
                                             / HBM_PEAK_GBS, 4),
-                    "stages_us": r2["stages_us"], "roofline": roofline(c2, r2)})
+                    "stages_us": r2["stages_us"], "timing": r2["timing"],
+                    "roofline": roofline(c2, r2)})
         del wl2
     if sec:
         out["secondary"] = sec
