@@ -10,25 +10,33 @@
 //
 // One block = one expert x one strip of 32 output columns (64 weight rows for
 // gate/up: 32 gate + 32 up, the same f-values; 32 rows for ReLU W_in and for
-// down).  Weights stream in chunks of 512 K values (bf16: 16 rows x 1 KB;
-// INT4: all rows x 256 B) with non-temporal 16-byte loads laid out so one wave
-// instruction reads whole contiguous row pieces (measured on MI355X: ~7 TB/s
-// from HBM this way, ~5-5.6 TB/s when each instruction reads 64 B of 16 rows
-// as the MFMA operand layout would, ~5.5 TB/s through LDS DMA).  Chunks are
-// loaded three ahead into registers, written to one of two LDS slots in the
-// 16x16x32 MFMA operand layout, and multiplied by the 4 waves, each taking a
-// quarter of the chunk's K range, against the expert's token rows (up to 16
-// per B operand, zero-padded).  The four K-partial sums meet in LDS at the end;
-// the epilogue applies SiLU(gate)*up (to bf16 H) or the gate scale (fp32 rows).
+// down); its 4 waves split K and their partial sums meet in LDS at the end,
+// where the epilogue applies SiLU(gate)*up (to bf16 H) or the gate scale (fp32
+// rows).  Two ways to feed the 16x16x32 MFMA from the weight stream:
+//   register-direct (gate/up, ReLU W_in, INT4 down): each wave loads its MFMA
+//     operands straight into registers, 16 row pieces of 64 bytes per
+//     instruction, with ordinary cached loads (the other half of each 128-byte
+//     line is the next instruction's piece and hits L2; measured ~12% faster
+//     than non-temporal loads for this pattern on MI355X);
+//   LDS-staged (bf16 down, K = d_ff long rows): non-temporal 16-byte loads laid
+//     out so one wave instruction reads whole 1 KB row pieces (~7 TB/s from HBM
+//     for this pattern, ~5-5.6 TB/s for the MFMA-shaped one, ~5.5 TB/s through
+//     LDS DMA), written to one of two LDS slots in the MFMA operand layout.
+// LDS-staged details: weights stream in chunks of 512 K values (bf16: 16 rows x
+// 1 KB; INT4: all rows x 256 B), loaded two chunks ahead into registers, stored
+// to the slot, published by a barrier and multiplied by the 4 waves, each taking
+// a quarter of the chunk's K range, against the expert's token rows (up to 16
+// per B operand, zero-padded).
 //
 // INT4 weights (group 128 along K, fp16 scale s and zero z, 8 nibbles per
-// int32, low nibble first) are decoded after the LDS read:
+// int32, low nibble first) are decoded in registers right before the MFMA:
 //   W = bf16_RNE( fp32( fp32(q) - z ) * s )
 // When fp32(q) - z is exact for every q in 0..15 (z == 0 or |z| >= 2^-10), this
 // equals bf16_RNE( fma(q, s, -(z*s)) ): z*s is exact in fp32 (11+11 bits) and
-// the fma rounds the exact (q - z)*s once.  Each wave checks its zero points
-// per chunk and takes the two-operation form otherwise.
-// Within a chunk, lane (r, g) of wave w feeds MFMA step s with K values
+// the fma rounds the exact (q - z)*s once.  The fused form is used only where
+// every zero point involved allows it (per chunk in the LDS-staged kernel, per
+// block in the register-direct one), the two-operation form otherwise.
+// LDS-staged K map: within a chunk, lane (r, g) of wave w feeds MFMA step s with K values
 // [w*128 + g*32 + s*8, +8); the token operand uses the same map, so the MFMA
 // sums over the same K set (the order of K inside one accumulation is free).
 // LDS rows keep 16-byte unit u of row r at position u ^ (r & 15), so the 16 rows
@@ -59,6 +67,7 @@ struct StreamArgs {
   const int32_t* gate_map;
   const float* gate;
   int nblk_per_expert;
+  uint32_t xbytes;         // bytes of X (register-direct kernel: buffer size)
 };
 
 __device__ __forceinline__ float h2f(u16 h) { return (float)__builtin_bit_cast(_Float16, h); }
@@ -376,6 +385,262 @@ __global__ __launch_bounds__(256) void stream_ffn_kernel(StreamArgs p) {
   }
 }
 
+// ---- register-direct variant ------------------------------------------------
+// Each wave owns a contiguous quarter of K for all of the block's weight rows
+// and loads its MFMA operands straight into registers (lane (r, g) of a wave
+// instruction reads 16 bytes of weight row r; the 4 lanes of a row are
+// adjacent, so one instruction reads 16 row pieces of 64 bytes), D iterations
+// ahead, with no LDS staging and no barrier until the final K reduction.
+// Iteration = 128 K values = one INT4 group.  K map inside an iteration, the
+// same for weights and tokens: bf16 lane (r, g) step s takes K [s*32 + g*8, +8);
+// INT4 lane (r, g) holds K [g*32, +32) in one 16-byte load and feeds step s
+// with its word s, i.e. K [g*32 + s*8, +8).  INT4 scales and zero points of the
+// block's rows are staged once in LDS (row stride G+1 words: 16 rows hit 16
+// different banks).
+// The loop has no data-dependent branch: loads run through buffer resources,
+// and an iteration past the wave's K range loads from an offset past the
+// resource's size, which returns zeros without touching memory; its MFMAs then
+// add zeros.  A straight-line loop lets the compiler wait for exactly the
+// oldest register set (vmcnt = loads of the D-1 younger sets) instead of all.
+
+template <int MODE, bool INT4, int MB, int D>
+__global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
+  constexpr int R = (MODE == kSModeGateUp) ? 64 : 32;  // weight rows per block
+  constexpr int RB = R / 16;
+  constexpr int NOUT = 32;
+  constexpr int KI = 128, NS = 4;
+  constexpr int WL = INT4 ? 1 : NS;                  // 16-byte weight loads per row block
+  constexpr int IT_BYTES = INT4 ? KI / 2 : KI * 2;    // weight bytes per row per iteration
+  constexpr int XS = INT4 ? 8 : 32;                  // token K offset between MFMA steps
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* red = (float*)smem;                                 // [4][RB][64][4]
+  uint32_t* sz = (uint32_t*)(smem + 4 * RB * 64 * 16);       // [R][G+1]: s | z << 16
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int e = blockIdx.x / p.nblk_per_expert;
+  const int nb = blockIdx.x - e * p.nblk_per_expert;
+  int row0 = 0, cnt = p.rows;
+  if (p.offsets) {
+    row0 = p.offsets[e];
+    cnt = p.offsets[e + 1] - row0;
+  }
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  cnt = __builtin_amdgcn_readfirstlane(cnt);
+  if (cnt <= 0) return;
+  const int n0 = nb * NOUT;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int Kq = p.K >> 2;            // per wave; a multiple of KI (K % 512 == 0)
+  const int kw0 = w * Kq;
+  const int iters = Kq / KI;
+  const int G = p.K >> 7, GP = G + 1;
+  const uint32_t row_bytes = INT4 ? (uint32_t)p.K / 2 : (uint32_t)p.K * 2;
+
+  // weight resources: the block's strip of 32 rows in each matrix (the launcher
+  // checks that 32 rows and the token matrix fit 32-bit offsets)
+  const uint32_t strip_bytes = 32u * row_bytes;
+  const __amdgpu_buffer_rsrc_t wres0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.W0 + ((size_t)e * p.N + n0) * row_bytes), (short)0, (int)strip_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wres1 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((MODE == kSModeGateUp ? p.W1 : p.W0) + ((size_t)e * p.N + n0) * row_bytes), (short)0,
+      (int)strip_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t xres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.X, (short)0, (int)p.xbytes, 0x00020000);
+  // row block rb covers block rows rb*16..+15: matrix 0 for rows < 32, 1 above
+  uint32_t wvoff[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+    wvoff[rb] = (uint32_t)((rb * 16 + r16) & 31) * row_bytes +
+                (INT4 ? (uint32_t)(kw0 + g * 32) / 2 : (uint32_t)(kw0 + g * 8) * 2);
+
+  auto wsel = [&](int r, int& n, bool& second) {
+    if constexpr (MODE == kSModeGateUp) {
+      second = r >= 32;
+      n = n0 + (r & 31);
+    } else {
+      second = false;
+      n = n0 + r;
+    }
+  };
+  bool fused_ok = true;
+  if constexpr (INT4) {
+    bool ok = true;
+    for (int i = tid; i < R * G; i += 256) {
+      const int r = i / G, gi = i - r * G;
+      int n;
+      bool second;
+      wsel(r, n, second);
+      const size_t o = ((size_t)e * p.N + n) * G + gi;
+      const u16 s = (second ? p.s1 : p.s0)[o], z = (second ? p.z1 : p.z0)[o];
+      ok = ok && zero_point_fma_exact(z);
+      sz[r * GP + gi] = (uint32_t)s | ((uint32_t)z << 16);
+    }
+    // the fused decode when every zero point of the block allows it (the usual
+    // case), else the two-operation form; uniform over the block
+    fused_ok = __syncthreads_and(ok) != 0;
+  }
+
+  auto body = [&](auto fused) {
+    for (int mbase = 0; mbase < cnt; mbase += MB * 16) {
+      const int mrows = min(MB * 16, cnt - mbase);
+      const int mb_act = (mrows + 15) >> 4;
+      uint32_t xvoff[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int m = mb * 16 + r16;
+        const int rr = row0 + mbase + min(m, mrows - 1);  // rows past the count: clamped copies
+        const int src = p.gather ? p.gather[rr] / p.k : rr;
+        xvoff[mb] = ((uint32_t)src * (uint32_t)p.ldx + (uint32_t)(kw0 + (INT4 ? g * 32 : g * 8))) * 2u;
+      }
+      f32x4 acc[RB][MB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+      struct Set {
+        u32x4 wv[RB][WL];
+        u32x4 x[MB][NS];
+      };
+      auto load = [&](Set& S, int it) {
+        const bool live = it < iters;  // uniform
+        const uint32_t wo = live ? (uint32_t)it * IT_BYTES : strip_bytes;
+        const uint32_t xo = live ? (uint32_t)it * KI * 2 : p.xbytes;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int q = 0; q < WL; ++q)
+            S.wv[rb][q] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128((rb * 16 < 32) ? wres0 : wres1,
+                                                             (int)(wvoff[rb] + wo + q * 64), 0, 0));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int s = 0; s < NS; ++s)
+            S.x[mb][s] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, (int)(xvoff[mb] + xo + s * XS * 2),
+                                                             0, 0));
+        // sets are issued whole and in order (prologue and loop alike), so the
+        // oldest set is complete once vmcnt <= the loads of the younger sets
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto compute = [&](const Set& S, int it) {
+        if constexpr (!INT4) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+              for (int mb = 0; mb < MB; ++mb)
+                acc[rb][mb] = mfma16(as_bf16x8(S.wv[rb][s]), as_bf16x8(S.x[mb][s]), acc[rb][mb]);
+        } else {
+          // past the K range the tokens are zeros; any finite scale will do
+          const int grp = (kw0 >> 7) + min(it, iters - 1);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const uint32_t v = sz[(rb * 16 + r16) * GP + grp];
+            const float sf = h2f((u16)(v & 0xffffu)), zf = h2f((u16)(v >> 16));
+            const float nzs = -(zf * sf);
+            bf16x8 a[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              if constexpr (decltype(fused)::value)
+                a[s] = dq8_fma(S.wv[rb][0][s], sf, nzs);
+              else
+                a[s] = dq8_exact(S.wv[rb][0][s], sf, zf);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+              for (int mb = 0; mb < MB; ++mb)
+                acc[rb][mb] = mfma16(a[s], as_bf16x8(S.x[mb][s]), acc[rb][mb]);
+          }
+        }
+      };
+
+      // iteration it lives in register set it % D, loaded D iterations ahead;
+      // its set is refilled with iteration it + D once its MFMAs are issued
+      Set st[D];
+#pragma unroll
+      for (int d = 0; d < D; ++d) load(st[d], d);
+      for (int it0 = 0; it0 < iters; it0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+          compute(st[u], it0 + u);
+          load(st[u], it0 + u + D);
+          // keep the scheduler from hoisting the next set's MFMAs (and their
+          // waits) above this set's refill
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // cross-wave K reduction and epilogue, one 16-row token block at a time
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        if (mb >= mb_act) break;
+        __syncthreads();
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          *(f32x4*)(red + (((w * RB) + rb) * 64 + lane) * 4) = acc[rb][mb];
+        __syncthreads();
+        for (int o = tid; o < 16 * NOUT; o += 256) {
+          const int m = o / NOUT, col = o % NOUT;
+          const int row = mbase + mb * 16 + m;
+          if (row >= cnt || n0 + col >= p.N) continue;
+          // C layout of the 16x16 MFMA: weight row 4*(lane/16)+i, token column lane%16
+          auto part = [&](int wr) {
+            const int rb = wr >> 4, rr = wr & 15;
+            const int ln = (rr >> 2) * 16 + m, i = rr & 3;
+            float sacc = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < 4; ++ww) sacc += red[((ww * RB + rb) * 64 + ln) * 4 + i];
+            return sacc;
+          };
+          const size_t orow = (size_t)(row0 + row);
+          if constexpr (MODE == kSModeGateUp) {
+            const float gv = part(col), uv = part(32 + col);
+            p.H[orow * p.N + n0 + col] = f32_to_bf16(silu_f32(gv) * uv);
+          } else if constexpr (MODE == kSModeRelu) {
+            p.H[orow * p.N + n0 + col] = f32_to_bf16(fmaxf(part(col), 0.0f));
+          } else {
+            const float gs = p.gate ? p.gate[p.gate_map ? p.gate_map[orow] : orow] : 1.0f;
+            p.Y[orow * p.N + n0 + col] = gs * part(col);
+          }
+        }
+      }
+      __syncthreads();
+    }
+  };
+  if constexpr (INT4) {
+    if (fused_ok)
+      body(std::true_type{});
+    else
+      body(std::false_type{});
+  } else {
+    body(std::true_type{});
+  }
+}
+
+template <int MODE, bool INT4>
+size_t stream_reg_lds_bytes(int K) {
+  constexpr int R = (MODE == kSModeGateUp) ? 64 : 32;
+  return (size_t)4 * (R / 16) * 64 * 16 + (INT4 ? (size_t)R * ((K >> 7) + 1) * 4 : 0);
+}
+
+template <int MODE, bool INT4>
+hipError_t launch_reg_mode(const StreamArgs& a, int E, int mb, hipStream_t s) {
+  const dim3 grid((unsigned)(E * a.nblk_per_expert)), block(256);
+  const size_t lds = stream_reg_lds_bytes<MODE, INT4>(a.K);
+  // two register sets in flight: deeper prefetch measured no faster here (the
+  // INT4 decode is bound by its VALU work, bf16 by the access pattern)
+  if (mb <= 1)
+    hipLaunchKernelGGL((stream_reg_kernel<MODE, INT4, 1, 2>), grid, block, lds, s, a);
+  else
+    hipLaunchKernelGGL((stream_reg_kernel<MODE, INT4, 2, 2>), grid, block, lds, s, a);
+  return hipGetLastError();
+}
+
 template <int MODE, bool INT4>
 hipError_t launch_mode(const StreamArgs& a, int E, int mb, hipStream_t s) {
   const dim3 grid((unsigned)(E * a.nblk_per_expert)), block(256);
@@ -417,6 +682,12 @@ hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid)
   a.K = p.d;
   a.H = (u16*)p.H;
   a.nblk_per_expert = (p.F + 31) / 32;
+  // the register-direct kernel addresses the token matrix (x, then H) and a
+  // 32-row weight strip with 32-bit buffer offsets
+  const size_t xb = (size_t)p.T * p.d * 2, hb = (size_t)p.rows * p.F * 2;
+  const size_t strip = 32 * (size_t)(p.d > p.F ? p.d : p.F) * (int4 ? 1 : 4) / 2;
+  const bool reg = xb < (1u << 31) && hb < (1u << 31) && strip < (1u << 31);
+  a.xbytes = (uint32_t)xb;
   if (int4) {
     const moe_w4* g = relu ? p.w->q_up : p.w->q_gate;
     const moe_w4* u = p.w->q_up;
@@ -428,10 +699,15 @@ hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid)
   }
   hipError_t e;
   if (relu)
-    e = int4 ? launch_mode<kSModeRelu, true>(a, E, mb, s) : launch_mode<kSModeRelu, false>(a, E, mb, s);
+    e = int4 ? (reg ? launch_reg_mode<kSModeRelu, true>(a, E, mb, s)
+                    : launch_mode<kSModeRelu, true>(a, E, mb, s))
+             : (reg ? launch_reg_mode<kSModeRelu, false>(a, E, mb, s)
+                    : launch_mode<kSModeRelu, false>(a, E, mb, s));
   else
-    e = int4 ? launch_mode<kSModeGateUp, true>(a, E, mb, s)
-             : launch_mode<kSModeGateUp, false>(a, E, mb, s);
+    e = int4 ? (reg ? launch_reg_mode<kSModeGateUp, true>(a, E, mb, s)
+                    : launch_mode<kSModeGateUp, true>(a, E, mb, s))
+             : (reg ? launch_reg_mode<kSModeGateUp, false>(a, E, mb, s)
+                    : launch_mode<kSModeGateUp, false>(a, E, mb, s));
   if (e != hipSuccess) return e;
   if (mid) {
     e = hipEventRecord(mid, s);
@@ -448,6 +724,7 @@ hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid)
   b.N = p.d;
   b.K = p.F;
   b.Y = p.y_rows;
+  b.xbytes = (uint32_t)hb;
   b.gate_map = p.row_assign;
   b.gate = p.gate;
   b.nblk_per_expert = (p.d + 31) / 32;
@@ -456,6 +733,9 @@ hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid)
   } else {
     b.W0 = (const unsigned char*)p.w->w_down;
   }
+  // bf16 down rows are long (K = d_ff): whole contiguous row pieces staged
+  // through LDS stream faster there than MFMA-shaped register loads
+  if (int4 && reg) return launch_reg_mode<kSModeDown, true>(b, E, mb, s);
   return int4 ? launch_mode<kSModeDown, true>(b, E, mb, s) : launch_mode<kSModeDown, false>(b, E, mb, s);
 }
 
