@@ -59,6 +59,8 @@ struct TileArgs {
   const int32_t* gate_map; // down: row -> flat assignment for the gate; NULL: gate index = row
   const float* gate;       // gate per flat assignment; NULL: 1
   int m_tiles_max, n_tiles;
+  int ksplit;              // K slices (down only): slice s covers K [s*K/ksplit, +K/ksplit)
+  size_t ystride;          // elements between the partial outputs of two slices
 };
 
 // LDS rows of 64 bf16 (128 B).  The LDS has 64 banks of 4 bytes and serves a
@@ -708,22 +710,229 @@ void grouped_gemm_v3_kernel(TileArgs p) {
     }
 }
 
+// ---- v4: v3's tile, LDS layout and DMA staging, with a finer schedule ---------------
+// v3 issues each quarter's 8 fragment reads as a group and, after the stage
+// barrier, all 16 DMA instructions back to back, so with one wave per SIMD the
+// MFMA pipe drains at every stage.  Here every MFMA is followed by at most one
+// other memory instruction: the next quarter's fragment reads sit between the
+// current quarter's MFMAs, and after the barrier the 16 DMA instructions of the
+// stage two ahead and the next stage's first fragment reads sit between the
+// last quarter's MFMAs, which keeps the MFMA pipe fed while they issue.
+template <int MODE>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void grouped_gemm_v4_kernel(TileArgs p) {
+  constexpr int BM = 256, BK = 64;
+  constexpr int STAGE = BM * BK;
+  __shared__ __align__(16) u16 sA0[STAGE], sA1[STAGE];
+  __shared__ __align__(16) u16 sB0[STAGE], sB1[STAGE];
+  __shared__ int s_tile[3];
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+
+  const int nb = gridDim.x;
+  const int bid = blockIdx.x;
+  int t = (bid & 7) * (nb >> 3) + (bid >> 3);
+  // K slice outermost: slice ks covers K [ks*K/ksplit, +K/ksplit) and writes
+  // its partial sums to Y + ks*ystride (the combine adds the slices)
+  const int slice_tiles = p.m_tiles_max * p.n_tiles;
+  const int ks = t / slice_tiles;
+  if (ks >= p.ksplit) return;
+  t -= ks * slice_tiles;
+  const int kslice = p.K / p.ksplit;
+  const int per_group = kV2GroupM * p.n_tiles;
+  const int g = t / per_group;
+  const int first_m = g * kV2GroupM;
+  const int gm = min(p.m_tiles_max - first_m, kV2GroupM);
+  const int in_g = t - g * per_group;
+  const int m_tile = first_m + in_g % gm;
+  const int n_tile = in_g / gm;
+
+  if (wid == 0) {
+    int cnt = 0, first = 0;
+    if (p.offsets) {
+      if (lane < p.E) {
+        first = p.offsets[lane];
+        cnt = p.offsets[lane + 1] - first;
+      }
+    } else if (lane == 0) {
+      cnt = p.rows;
+    }
+    const int tiles = (cnt + BM - 1) / BM;
+    int incl = tiles;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    const int excl = incl - tiles;
+    if (lane == 0) s_tile[0] = -1;
+    if (m_tile >= excl && m_tile < incl) {
+      s_tile[0] = lane;
+      s_tile[1] = first + (m_tile - excl) * BM;
+      s_tile[2] = min(BM, cnt - (m_tile - excl) * BM);
+    }
+  }
+  __syncthreads();
+  const int expert = __builtin_amdgcn_readfirstlane(s_tile[0]);
+  if (expert < 0) return;
+  const int row0 = __builtin_amdgcn_readfirstlane(s_tile[1]);
+  const int rvalid = __builtin_amdgcn_readfirstlane(s_tile[2]);
+
+  // DMA: instruction j (0..7 A, 8..15 B) of wave w fills LDS rows (w*8+j%8)*8 ..
+  // +8 (1 KB); lane L feeds row (w*8+j%8)*8 + L/8 at 16-byte position L%8.
+  const u16* src[16];
+  const size_t wstride = (size_t)p.N * p.K;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (wid * 8 + j) * 8 + (lane >> 3);
+    const int c = v3_pos(r, lane & 7);
+    const int gr = row0 + min(r, rvalid - 1);
+    const int sr = p.gather ? (p.gather[gr] / p.k) : gr;
+    src[j] = p.A + (size_t)sr * p.lda + c * 8;
+    const u16* Bm;
+    int n;
+    if constexpr (MODE == kGateUpSwiglu) {
+      Bm = (r < 128) ? p.B0 : p.B1;
+      n = n_tile * 128 + (r & 127);
+    } else {
+      Bm = p.B0;
+      n = n_tile * 256 + r;
+    }
+    n = min(n, p.N - 1);
+    src[8 + j] = Bm + (size_t)expert * wstride + (size_t)n * p.K + c * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) src[j] += (size_t)ks * kslice;
+  const int nk = kslice / BK;
+  const int wbase = __builtin_amdgcn_readfirstlane(wid) * 8 * 512;
+  auto dma = [&](u16* sa, u16* sb, int kt, int j) {
+    const int k0 = min(kt, nk - 1) * BK;  // past the end: reload the last slice (never read)
+    dma16(src[j] + k0, (j < 8 ? sa : sb) + wbase + (j & 7) * 512);
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int fr = lane & 31, fk = lane >> 5;
+  auto brow = [&](int j) {
+    if constexpr (MODE == kGateUpSwiglu) return (j < 2 ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32);
+    else return wn * 128 + j * 32;
+  };
+  // fragment f (0..3 A rows, 4..7 B rows) of K quarter kk
+  auto read1 = [&](const u16* sa, const u16* sb, int kk, int f, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
+    const int c = kk * 2 + fk;
+    if (f < 4)
+      af[f] = as_bf16x8(*(const u32x4*)(sa + v3_off(wm * 128 + f * 32 + fr, c)));
+    else
+      bfr[f - 4] = as_bf16x8(*(const u32x4*)(sb + v3_off(brow(f - 4) + fr, c)));
+  };
+  // read order A0 B0 B1 B2 B3 A1 A2 A3: MFMAs 0..3 (A0 x B0..B3) need only the
+  // first five reads
+  constexpr int kRead[8] = {0, 4, 5, 6, 7, 1, 2, 3};
+  // MFMA m (0..15) of a quarter: A fragment m/4, B fragment m%4
+  auto mfma1 = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], int m) {
+    acc[m >> 2][m & 3] = mfma32(af[m >> 2], bfr[m & 3], acc[m >> 2][m & 3]);
+  };
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  // quarter with the next quarter's 8 fragment reads after its first 8 MFMAs,
+  // so the last read has 8 MFMAs (~256 cycles) to land before it is needed
+  auto quarter = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], const u16* sa, const u16* sb,
+                     int kk_next, bf16x8 (&an)[4], bf16x8 (&bn)[4]) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      mfma1(af, bfr, m);
+      if (m < 8) read1(sa, sb, kk_next, kRead[m], an, bn);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto stage = [&](u16* sa, u16* sb, u16* na, u16* nb_, int kt) {
+    quarter(a0, b0, sa, sb, 1, a1, b1);
+    quarter(a1, b1, sa, sb, 2, a0, b0);
+    quarter(a0, b0, sa, sb, 3, a1, b1);
+    wait_vm_lgkm0<0>();
+    block_barrier();
+    // last quarter: one DMA (stage kt+2 into the buffer just consumed) after
+    // each MFMA, and the next stage's first fragments after the odd ones
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      mfma1(a1, b1, m);
+      dma(sa, sb, kt + 2, m);
+      if (m < 8) read1(na, nb_, 0, kRead[m], a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < 16; ++j) dma(sA0, sB0, 0, j);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) dma(sA1, sB1, 1, j);
+  wait_vm_lgkm0<16>();
+  block_barrier();
+#pragma unroll
+  for (int f = 0; f < 8; ++f) read1(sA0, sB0, 0, f, a0, b0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    stage(sA0, sB0, sA1, sB1, kt);
+    stage(sA1, sB1, sA0, sB0, kt + 1);
+  }
+  wait_vm_lgkm0<0>();
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
+      if (row >= rvalid) continue;
+      const int grow = row0 + row;
+      if constexpr (MODE == kGateUpSwiglu) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = n_tile * 128 + wn * 64 + j * 32 + fr;
+          if (col < p.N)
+            p.H[(size_t)grow * p.N + col] = f32_to_bf16(silu_f32(acc[i][j][r]) * acc[i][j + 2][r]);
+        }
+      } else if constexpr (MODE == kUpRelu) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = n_tile * 256 + wn * 128 + j * 32 + fr;
+          if (col < p.N) p.H[(size_t)grow * p.N + col] = f32_to_bf16(fmaxf(acc[i][j][r], 0.0f));
+        }
+      } else {
+        const float gscale = p.gate ? p.gate[p.gate_map ? p.gate_map[grow] : grow] : 1.0f;
+        float* Y = p.Y + (size_t)ks * p.ystride;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = n_tile * 256 + wn * 128 + j * 32 + fr;
+          if (col < p.N) Y[(size_t)grow * p.N + col] = gscale * acc[i][j][r];
+        }
+      }
+    }
+}
+
 template <int MODE>
 hipError_t run_tiles_v2(TileArgs a, hipStream_t s) {
   const int m_tiles_max = (a.rows + kV2BM - 1) / kV2BM + min(a.E, a.rows);
   a.m_tiles_max = m_tiles_max;
   const int ncols = (MODE == kGateUpSwiglu) ? 128 : 256;
   a.n_tiles = (a.N + ncols - 1) / ncols;
-  long long nblk = (long long)m_tiles_max * a.n_tiles;
+  if (a.ksplit < 1) a.ksplit = 1;
+  long long nblk = (long long)m_tiles_max * a.n_tiles * a.ksplit;
   nblk = (nblk + 7) / 8 * 8;
   static const int variant = [] {
     const char* v = getenv("MOE_GEMM_VARIANT");
-    return v ? atoi(v) : 3;
+    return v ? atoi(v) : 4;
   }();
-  if (variant == 2 || (a.K / 64) % 2 != 0)
-    hipLaunchKernelGGL(grouped_gemm_v2_kernel<MODE>, dim3((unsigned)nblk), dim3(256), 0, s, a);
-  else
+  // K slices exist only in v4; each slice needs an even number of 64-wide steps
+  const int steps = a.K / a.ksplit / 64;
+  if (a.ksplit > 1 || (variant != 2 && variant != 3 && steps % 2 == 0))
+    hipLaunchKernelGGL(grouped_gemm_v4_kernel<MODE>, dim3((unsigned)nblk), dim3(256), 0, s, a);
+  else if (variant == 3 && steps % 2 == 0)
     hipLaunchKernelGGL(grouped_gemm_v3_kernel<MODE>, dim3((unsigned)nblk), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(grouped_gemm_v2_kernel<MODE>, dim3((unsigned)nblk), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -806,6 +1015,30 @@ size_t ffn_ws_bytes(int rows, int F, moe_dtype dt) {
   return (size_t)rows * F * (dt == MOE_DT_F32 ? 4 : 2);
 }
 
+int ffn_down_splits(int T, int d, int F, int E, int k, moe_dtype dt, bool int4) {
+  if (dt != MOE_DT_BF16 || int4 || T <= 0) return 1;
+  FfnProblem q{};
+  q.T = T; q.d = d; q.F = F; q.dt = dt; q.rows = T * k;
+  if (stream_ffn_applies(q)) return 1;
+  // tiles of one slice (upper bound, as the launcher sizes the grid), in rounds
+  // of one tile per CU (256 CUs); a slice costs 1/S of a full-K tile, and each
+  // extra slice adds a partial-row write and read (charged as 0.1 round)
+  constexpr int kCUs = 256;
+  const int rows = T * k;
+  const long long tiles = (long long)((rows + kV2BM - 1) / kV2BM + min(E, rows)) * ((d + 255) / 256);
+  int best = 1;
+  double best_cost = 1e30;
+  for (int S = 1; S <= 4; S *= 2) {
+    if (F % (128 * S) != 0) break;
+    const double cost = (double)((tiles * S + kCUs - 1) / kCUs) / S + 0.1 * (S - 1);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = S;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid) {
   if (p.rows == 0) return hipSuccess;
   if (stream_ffn_applies(p)) return launch_stream_ffn(p, s, mid);
@@ -879,12 +1112,15 @@ hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid
   b.Y = p.y_rows;
   b.gate_map = p.row_assign;
   b.gate = p.gate;
+  b.ksplit = p.down_splits > 1 ? p.down_splits : 1;
+  b.ystride = (size_t)p.rows * p.d;
   if (int4) {
     b.q0 = p.w->q_down->q; b.s0 = p.w->q_down->scale; b.z0 = p.w->q_down->zero;
     return run_tiles<128, 128, kDown, true>(b, s);
   }
   b.B0 = (const u16*)p.w->w_down;
   if (p.F % (4 * kV2BK) == 0) return run_tiles_v2<kDown>(b, s);
+  if (b.ksplit > 1) return hipErrorInvalidValue;  // slices exist only on the tiled v4 path
   return run_tiles<128, 128, kDown, false>(b, s);
 }
 

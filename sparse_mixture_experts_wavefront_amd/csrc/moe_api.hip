@@ -126,7 +126,8 @@ struct LayerWs {
   double* lis;
   void* perm_ws;
   void* H;
-  float* y_rows;
+  float* y_rows;           // down_splits partial copies of [T*k][d]
+  int down_splits;
   void* Hs;
   float* y_shared;
   size_t total;
@@ -148,7 +149,8 @@ LayerWs carve_layer(const moe_layer_desc* L, int T, void* ws) {
   w.lis = (double*)c.take(8);
   w.perm_ws = c.take(permute_ws_bytes(T, E, k));
   w.H = c.take(n * F * esz);
-  w.y_rows = (float*)c.take(n * d * 4);
+  w.down_splits = ffn_down_splits(T, d, F, E, k, L->act_dtype, L->routed.q_up != nullptr);
+  w.y_rows = (float*)c.take(n * d * 4 * w.down_splits);
   const int Fs = L->n_shared * L->d_ff_shared;
   w.Hs = L->n_shared ? c.take((size_t)T * Fs * esz) : nullptr;
   w.y_shared = L->n_shared ? (float*)c.take((size_t)T * d * 4) : nullptr;
@@ -371,6 +373,7 @@ moe_status moe_layer_forward(const moe_layer_desc* L, const void* x, int T, void
   p.T = T; p.d = d; p.F = L->d_ff; p.E = E; p.k = k; p.act = L->act;
   p.dt = L->act_dtype; p.x = x; p.w = &L->routed; p.offsets = offsets;
   p.row_assign = row_assign; p.gate = gates; p.y_rows = w.y_rows; p.H = w.H; p.rows = T * k;
+  p.down_splits = w.down_splits;
   e = launch_grouped_ffn(p, st, g_stage_on ? g_stage_ev[3] : nullptr);
   if (e != hipSuccess) return hip_status(e, "grouped_ffn");
   stage(4, st);
@@ -384,7 +387,8 @@ moe_status moe_layer_forward(const moe_layer_desc* L, const void* x, int T, void
     if (e != hipSuccess) return hip_status(e, "shared experts");
   }
   stage(5, st);
-  e = launch_combine(w.y_rows, assign_row, T, k, d, w.y_shared, y, ydt, st);
+  e = launch_combine(w.y_rows, assign_row, T, k, d, w.y_shared, y, ydt, st, w.down_splits,
+                     (size_t)T * k * d);
   stage(6, st);
   return hip_status(e, "combine");
 }

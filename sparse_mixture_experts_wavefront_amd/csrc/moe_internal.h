@@ -63,8 +63,14 @@ struct FfnProblem {
   float* y_rows;                 // [rows][d]
   void* H;                       // [rows][F] scratch (bf16 or fp32)
   int rows;                      // T * k
+  int down_splits;               // K slices of the down pass (0 or 1: none); slice s
+                                 // writes its partial sums to y_rows + s * rows * d
 };
 size_t ffn_ws_bytes(int rows, int F, moe_dtype dt);
+// K slices for the down pass of a layer-sized problem: more, smaller tiles when
+// one slice would leave the last round of tiles mostly idle.  Pure function of
+// the shapes (the workspace size depends on it).
+int ffn_down_splits(int T, int d, int F, int E, int k, moe_dtype dt, bool int4);
 hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid = nullptr);
 
 // Weight-streaming variant for few rows per expert (decode); same contract as
@@ -72,7 +78,10 @@ hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid
 bool stream_ffn_applies(const FfnProblem& p);
 hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid = nullptr);
 
+// y[t] = sum over slots j, then over K slices s, of y_rows[s * split_stride +
+// assign_row[t*k+j] * d], plus y_shared[t]; fixed order, so deterministic.
 hipError_t launch_combine(const float* y_rows, const int32_t* assign_row, int T, int k, int d,
-                          const float* y_shared, void* y, moe_dtype ydt, hipStream_t s);
+                          const float* y_shared, void* y, moe_dtype ydt, hipStream_t s,
+                          int nsplit = 1, size_t split_stride = 0);
 
 }  // namespace moe
