@@ -21,13 +21,9 @@
 // (expert, row tile); blocks past the last tile exit.  Block ids are remapped
 // so that consecutive ids on one XCD (ids that differ by 8) take the row tiles
 // of one weight panel, which then stays in that XCD's L2.
-// Tile: BM x BN x 64, 256 threads as 2x2 waves, 32x32x16 MFMA.  Operands are
-// K-contiguous in both A and B; LDS rows are 64 bf16 with 16-byte chunks
-// XOR-swizzled by (row & 7) so MFMA fragment reads do not collide on banks.
-// Global->LDS staging is double buffered: the loads of tile k+1 are in flight
-// while the MFMAs of tile k run.
-#include <stdlib.h>
-
+// Two tiled kernels: the 256x256x64 DMA-staged kernel (bf16, K % 128 == 0: the
+// layer path) and a 128x128x64 register-staged kernel (INT4 weights decoded
+// while staged, and any other shape).
 #include "moe_internal.h"
 
 namespace moe {
@@ -284,24 +280,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(TileArgs p) {
     }
 }
 
-// ---- v2: 256x256x32 tiles, direct-to-LDS loads, 4-stage pipeline --------------------
-//
-// Measured on MI355X: LDS reads reach ~128 B/clk/CU and bf16 MFMA ~1.95 PFLOP/s,
-// so the tile is chosen for LDS traffic: 4 waves each own a 128x128 quarter
-// (256 fp32 accumulators per lane), which needs 16 B/clk/SIMD of fragment reads
-// plus 32 B/clk/CU of staging writes.  Staging uses global_load_lds_dwordx4
-// (each lane's 16 bytes land at base + 16*lane), so no registers hold tiles in
-// flight; four LDS stages keep three K-slices of loads in flight behind the
-// MFMAs.  LDS rows are 32 bf16 (64 bytes).  The LDS has 64 banks of 4 bytes
-// and serves 16-byte-per-lane reads 16 lanes (256 bytes) per pass; a fragment
-// read has those 16 lanes on 16 consecutive rows at one chunk, so chunk c of row
-// r is stored at position c ^ ((r >> 2) & 3), which puts the 16 rows on 16
-// distinct 16-byte bank groups (measured: the (r >> 1) variant left half the
-// LDS cycles in bank conflicts).  Blocks are ordered in groups of 8 row tiles per
-// column strip and XCD-contiguous, so the concurrent blocks of one XCD share
-// A and B slices in its L2.
-
-constexpr int kV2BM = 256, kV2BN = 256, kV2BK = 32, kV2GroupM = 8;
+// ---- shared pieces of the 256x256 tiled kernel ---------------------------------------
+constexpr int kV2BM = 256, kV2GroupM = 8;  // tile rows; row tiles per column-strip group
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ void dma16(const void* g, u16* lds) {
@@ -318,409 +298,32 @@ __device__ __forceinline__ void block_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-__device__ __forceinline__ int v2_pos(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
-__device__ __forceinline__ int v2_off(int row, int chunk) {
-  return row * kV2BK + (v2_pos(row, chunk) << 3);
-}
-
-template <int MODE>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void grouped_gemm_v2_kernel(TileArgs p) {
-  constexpr int BM = kV2BM, BK = kV2BK;
-  static_assert(kV2BM == kV2BN, "square stage buffers");
-  constexpr int STAGE = BM * BK;  // elements per operand per stage (BM == BN)
-  __shared__ __align__(16) u16 sA0[STAGE], sA1[STAGE], sA2[STAGE], sA3[STAGE];
-  __shared__ __align__(16) u16 sB0[STAGE], sB1[STAGE], sB2[STAGE], sB3[STAGE];
-  __shared__ int s_tile[3];
-
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
-
-  // ---- block -> (row tile, column strip): XCD-contiguous, grouped by 8 row tiles ----
-  const int nb = gridDim.x;
-  const int bid = blockIdx.x;
-  const int t = (bid & 7) * (nb >> 3) + (bid >> 3);
-  if (t >= p.m_tiles_max * p.n_tiles) return;
-  const int per_group = kV2GroupM * p.n_tiles;
-  const int g = t / per_group;
-  const int first_m = g * kV2GroupM;
-  const int gm = min(p.m_tiles_max - first_m, kV2GroupM);
-  const int in_g = t - g * per_group;
-  const int m_tile = first_m + in_g % gm;
-  const int n_tile = in_g / gm;
-
-  if (wid == 0) {
-    int cnt = 0, first = 0;
-    if (p.offsets) {
-      if (lane < p.E) {
-        first = p.offsets[lane];
-        cnt = p.offsets[lane + 1] - first;
-      }
-    } else if (lane == 0) {
-      cnt = p.rows;
-    }
-    const int tiles = (cnt + BM - 1) / BM;
-    int incl = tiles;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    const int excl = incl - tiles;
-    if (lane == 0) s_tile[0] = -1;
-    if (m_tile >= excl && m_tile < incl) {
-      s_tile[0] = lane;
-      s_tile[1] = first + (m_tile - excl) * BM;
-      s_tile[2] = min(BM, cnt - (m_tile - excl) * BM);
-    }
-  }
-  __syncthreads();
-  // wave-uniform values in scalar registers (branches on them stay scalar)
-  const int expert = __builtin_amdgcn_readfirstlane(s_tile[0]);
-  if (expert < 0) return;
-  const int row0 = __builtin_amdgcn_readfirstlane(s_tile[1]);
-  const int rvalid = __builtin_amdgcn_readfirstlane(s_tile[2]);
-
-  // ---- DMA sources: this lane feeds LDS row (wid*4+j)*16 + lane/4, 16-byte unit lane&3 ----
-  const u16* a_src[4];
-  const u16* b_src[4];
-  const size_t wstride = (size_t)p.N * p.K;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = (wid * 4 + j) * 16 + (lane >> 2);
-    const int c = v2_pos(r, lane & 3);  // position lane&3 holds chunk c (the map is an involution)
-    const int gr = row0 + min(r, rvalid - 1);
-    const int src = p.gather ? (p.gather[gr] / p.k) : gr;
-    a_src[j] = p.A + (size_t)src * p.lda + c * 8;
-    const u16* Bm;
-    int n;
-    if constexpr (MODE == kGateUpSwiglu) {
-      Bm = (r < 128) ? p.B0 : p.B1;
-      n = n_tile * 128 + (r & 127);
-    } else {
-      Bm = p.B0;
-      n = n_tile * 256 + r;
-    }
-    n = min(n, p.N - 1);
-    b_src[j] = Bm + (size_t)expert * wstride + (size_t)n * p.K + c * 8;
-  }
-  const int nk = p.K / BK;  // a multiple of the stage count (checked by the launcher)
-  const int wbase = __builtin_amdgcn_readfirstlane(wid) * 4 * 512;  // this wave's LDS slice
-  auto issue = [&](u16* sa, u16* sb, int kt) {
-    const int k0 = min(kt, nk - 1) * BK;  // past the end: reload the last slice (never read)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(a_src[j] + k0, sa + wbase + j * 512);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(b_src[j] + k0, sb + wbase + j * 512);
-  };
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  const int fr = lane & 31, fk = lane >> 5;
-  auto brow = [&](int j) {
-    if constexpr (MODE == kGateUpSwiglu) return (j < 2 ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32);
-    else return wn * 128 + j * 32;
-  };
-  // fragments of one 16-wide K half of a stage
-  auto read = [&](const u16* sa, const u16* sb, int kk, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
-    const int c = kk * 2 + fk;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = as_bf16x8(*(const u32x4*)(sa + v2_off(wm * 128 + i * 32 + fr, c)));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bfr[j] = as_bf16x8(*(const u32x4*)(sb + v2_off(brow(j) + fr, c)));
-  };
-  auto mma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], int i0) {
-#pragma unroll
-    for (int i = i0; i < i0 + 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
-  };
-  bf16x8 a0[4], b0[4], a1[4], b1[4];
-  // One stage = two 16-wide K halves.  Each half's 16 MFMAs are split in two
-  // and the other half's fragment reads are issued between them, so an LDS
-  // wait only ever covers reads issued a full MFMA group earlier.  The block
-  // barrier sits where the next stage has landed and every wave has finished
-  // reading the buffer the next DMA will overwrite.
-  auto step = [&](u16* sa, u16* sb, u16* na, u16* nb_, u16* da, u16* db, int s) {
-    issue(da, db, s + 3);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a0, b0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    read(sa, sb, 1, a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a0, b0, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vm_lgkm0<16>();
-    block_barrier();
-    mma(a1, b1, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    read(na, nb_, 0, a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a1, b1, 2);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  issue(sA0, sB0, 0);
-  issue(sA1, sB1, 1);
-  issue(sA2, sB2, 2);
-  wait_vm_lgkm0<16>();
-  block_barrier();
-  read(sA0, sB0, 0, a0, b0);
-  for (int kt = 0; kt < nk; kt += 4) {
-    step(sA0, sB0, sA1, sB1, sA3, sB3, kt);
-    step(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
-    step(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
-    step(sA3, sB3, sA0, sB0, sA2, sB2, kt + 3);
-  }
-  wait_vm_lgkm0<0>();
-
-  // ---- epilogue (32x32 C layout: reg r -> row 8*(r/4) + 4*(lane/32) + r%4, col lane%32) ----
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
-      if (row >= rvalid) continue;
-      const int grow = row0 + row;
-      if constexpr (MODE == kGateUpSwiglu) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n_tile * 128 + wn * 64 + j * 32 + fr;
-          if (col < p.N)
-            p.H[(size_t)grow * p.N + col] = f32_to_bf16(silu_f32(acc[i][j][r]) * acc[i][j + 2][r]);
-        }
-      } else if constexpr (MODE == kUpRelu) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n_tile * 256 + wn * 128 + j * 32 + fr;
-          if (col < p.N) p.H[(size_t)grow * p.N + col] = f32_to_bf16(fmaxf(acc[i][j][r], 0.0f));
-        }
-      } else {
-        const float gscale = p.gate ? p.gate[p.gate_map ? p.gate_map[grow] : grow] : 1.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n_tile * 256 + wn * 128 + j * 32 + fr;
-          if (col < p.N) p.Y[(size_t)grow * p.N + col] = gscale * acc[i][j][r];
-        }
-      }
-    }
-}
-
-// ---- v3: 256x256x64 tiles, two 64 KB LDS stages ------------------------------------
-// Same wave layout and DMA staging as v2, but each stage covers 64 K-values, so
-// every row contributes one full 128-byte line per stage (half as many memory
-// requests per byte as v2's 64-byte pieces).  Rows are 128 bytes; chunk c of
-// row r sits at position c ^ ((r >> 1) & 7), conflict-free for the 16 rows one
-// 256-byte LDS pass serves.
 
 __device__ __forceinline__ int v3_pos(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 __device__ __forceinline__ int v3_off(int row, int chunk) { return row * 64 + (v3_pos(row, chunk) << 3); }
 
+// ---- tiled grouped GEMM for many rows per expert: 256x256x64 tiles -------------------
+//
+// 256 threads as 2x2 waves, each owning a 128x128 quarter of the output tile with
+// 32x32x16 bf16 MFMAs (16 fp32x16 accumulators, 256 registers per lane).  A and B
+// stage through two 64 KB LDS buffers with global_load_lds_dwordx4 (each lane's
+// 16 bytes land at base + 16*lane: no registers hold tiles in flight); each
+// stage covers 64 K values, so every row contributes one full 128-byte line.
+// LDS rows are 128 bytes; chunk c of row r sits at position c ^ ((r >> 1) & 7),
+// which puts the 16 rows one 256-byte LDS pass serves on 16 distinct bank
+// groups (the LDS has 64 banks of 4 bytes and serves 16-byte reads 16 lanes per
+// pass).  Measured on MI355X: LDS reads reach ~80 B/clk/CU from 4 waves and bf16
+// MFMA ~1.95 PFLOP/s, so the schedule is built around the LDS: every MFMA is
+// followed by at most one other memory instruction, fragment reads run two K
+// quarters ahead (four register sets), and one barrier per stage, after its
+// second quarter, publishes the next stage and frees the current buffer for the
+// DMA of the stage two ahead, issued during the third and fourth quarters.
+// Blocks are ordered in groups of 8 row tiles per column strip and remapped so
+// consecutive ids on one XCD share A and B slices in its L2.  The down pass may
+// split K into slices (partial rows reduced by the combine).
 template <int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void grouped_gemm_v3_kernel(TileArgs p) {
-  constexpr int BM = 256, BK = 64;
-  constexpr int STAGE = BM * BK;
-  __shared__ __align__(16) u16 sA0[STAGE], sA1[STAGE];
-  __shared__ __align__(16) u16 sB0[STAGE], sB1[STAGE];
-  __shared__ int s_tile[3];
-
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
-
-  const int nb = gridDim.x;
-  const int bid = blockIdx.x;
-  const int t = (bid & 7) * (nb >> 3) + (bid >> 3);
-  if (t >= p.m_tiles_max * p.n_tiles) return;
-  const int per_group = kV2GroupM * p.n_tiles;
-  const int g = t / per_group;
-  const int first_m = g * kV2GroupM;
-  const int gm = min(p.m_tiles_max - first_m, kV2GroupM);
-  const int in_g = t - g * per_group;
-  const int m_tile = first_m + in_g % gm;
-  const int n_tile = in_g / gm;
-
-  if (wid == 0) {
-    int cnt = 0, first = 0;
-    if (p.offsets) {
-      if (lane < p.E) {
-        first = p.offsets[lane];
-        cnt = p.offsets[lane + 1] - first;
-      }
-    } else if (lane == 0) {
-      cnt = p.rows;
-    }
-    const int tiles = (cnt + BM - 1) / BM;
-    int incl = tiles;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    const int excl = incl - tiles;
-    if (lane == 0) s_tile[0] = -1;
-    if (m_tile >= excl && m_tile < incl) {
-      s_tile[0] = lane;
-      s_tile[1] = first + (m_tile - excl) * BM;
-      s_tile[2] = min(BM, cnt - (m_tile - excl) * BM);
-    }
-  }
-  __syncthreads();
-  const int expert = __builtin_amdgcn_readfirstlane(s_tile[0]);
-  if (expert < 0) return;
-  const int row0 = __builtin_amdgcn_readfirstlane(s_tile[1]);
-  const int rvalid = __builtin_amdgcn_readfirstlane(s_tile[2]);
-
-  // DMA: instruction j of wave w fills LDS rows (w*8+j)*8 .. +8 (1 KB); lane L
-  // feeds row (w*8+j)*8 + L/8 at 16-byte position L%8.
-  const u16* a_src[8];
-  const u16* b_src[8];
-  const size_t wstride = (size_t)p.N * p.K;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = (wid * 8 + j) * 8 + (lane >> 3);
-    const int c = v3_pos(r, lane & 7);
-    const int gr = row0 + min(r, rvalid - 1);
-    const int src = p.gather ? (p.gather[gr] / p.k) : gr;
-    a_src[j] = p.A + (size_t)src * p.lda + c * 8;
-    const u16* Bm;
-    int n;
-    if constexpr (MODE == kGateUpSwiglu) {
-      Bm = (r < 128) ? p.B0 : p.B1;
-      n = n_tile * 128 + (r & 127);
-    } else {
-      Bm = p.B0;
-      n = n_tile * 256 + r;
-    }
-    n = min(n, p.N - 1);
-    b_src[j] = Bm + (size_t)expert * wstride + (size_t)n * p.K + c * 8;
-  }
-  const int nk = p.K / BK;
-  const int wbase = __builtin_amdgcn_readfirstlane(wid) * 8 * 512;
-  auto issue = [&](u16* sa, u16* sb, int kt) {
-    const int k0 = min(kt, nk - 1) * BK;  // past the end: reload the last slice (never read)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dma16(a_src[j] + k0, sa + wbase + j * 512);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dma16(b_src[j] + k0, sb + wbase + j * 512);
-  };
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  const int fr = lane & 31, fk = lane >> 5;
-  auto brow = [&](int j) {
-    if constexpr (MODE == kGateUpSwiglu) return (j < 2 ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32);
-    else return wn * 128 + j * 32;
-  };
-  auto read = [&](const u16* sa, const u16* sb, int kk, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
-    const int c = kk * 2 + fk;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = as_bf16x8(*(const u32x4*)(sa + v3_off(wm * 128 + i * 32 + fr, c)));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bfr[j] = as_bf16x8(*(const u32x4*)(sb + v3_off(brow(j) + fr, c)));
-  };
-  auto mma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], int i0) {
-#pragma unroll
-    for (int i = i0; i < i0 + 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
-  };
-  bf16x8 a0[4], b0[4], a1[4], b1[4];
-  // One stage = four 16-wide K quarters.  The fragments of quarter q+1 are
-  // read before the 16 MFMAs of quarter q, so each LDS read has a full MFMA
-  // group to land.  The barrier that publishes the next stage sits before the
-  // last quarter's MFMAs; the next stage's first fragments are read right after
-  // it, and the next DMA (into the stage just consumed) is issued there too.
-  auto stage = [&](u16* sa, u16* sb, u16* na, u16* nb_, int kt) {
-    read(sa, sb, 1, a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a0, b0, 0);
-    mma(a0, b0, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    read(sa, sb, 2, a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a1, b1, 0);
-    mma(a1, b1, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    read(sa, sb, 3, a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a0, b0, 0);
-    mma(a0, b0, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vm_lgkm0<0>();
-    block_barrier();
-    issue(sa, sb, kt + 2);
-    read(na, nb_, 0, a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a1, b1, 0);
-    mma(a1, b1, 2);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  issue(sA0, sB0, 0);
-  issue(sA1, sB1, 1);
-  wait_vm_lgkm0<16>();
-  block_barrier();
-  read(sA0, sB0, 0, a0, b0);
-  for (int kt = 0; kt < nk; kt += 2) {
-    // stage kt (buffer 0): its successor kt+1 is in buffer 1 (in flight)
-    stage(sA0, sB0, sA1, sB1, kt);
-    stage(sA1, sB1, sA0, sB0, kt + 1);
-  }
-  wait_vm_lgkm0<0>();
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
-      if (row >= rvalid) continue;
-      const int grow = row0 + row;
-      if constexpr (MODE == kGateUpSwiglu) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n_tile * 128 + wn * 64 + j * 32 + fr;
-          if (col < p.N)
-            p.H[(size_t)grow * p.N + col] = f32_to_bf16(silu_f32(acc[i][j][r]) * acc[i][j + 2][r]);
-        }
-      } else if constexpr (MODE == kUpRelu) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n_tile * 256 + wn * 128 + j * 32 + fr;
-          if (col < p.N) p.H[(size_t)grow * p.N + col] = f32_to_bf16(fmaxf(acc[i][j][r], 0.0f));
-        }
-      } else {
-        const float gscale = p.gate ? p.gate[p.gate_map ? p.gate_map[grow] : grow] : 1.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n_tile * 256 + wn * 128 + j * 32 + fr;
-          if (col < p.N) p.Y[(size_t)grow * p.N + col] = gscale * acc[i][j][r];
-        }
-      }
-    }
-}
-
-// ---- v4: v3's tile, LDS layout and DMA staging, with a finer schedule ---------------
-// v3 issues each quarter's 8 fragment reads as a group and, after the stage
-// barrier, all 16 DMA instructions back to back, so with one wave per SIMD the
-// MFMA pipe drains at every stage.  Here every MFMA is followed by at most one
-// other memory instruction: the next quarter's fragment reads sit between the
-// current quarter's MFMAs, and after the barrier the 16 DMA instructions of the
-// stage two ahead and the next stage's first fragment reads sit between the
-// last quarter's MFMAs, which keeps the MFMA pipe fed while they issue.
-template <int MODE>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void grouped_gemm_v4_kernel(TileArgs p) {
+void grouped_gemm_tile_kernel(TileArgs p) {
   constexpr int BM = 256, BK = 64;
   constexpr int STAGE = BM * BK;
   __shared__ __align__(16) u16 sA0[STAGE], sA1[STAGE];
@@ -838,33 +441,27 @@ void grouped_gemm_v4_kernel(TileArgs p) {
   auto mfma1 = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], int m) {
     acc[m >> 2][m & 3] = mfma32(af[m >> 2], bfr[m & 3], acc[m >> 2][m & 3]);
   };
-  bf16x8 a0[4], b0[4], a1[4], b1[4];
-  // quarter with the next quarter's 8 fragment reads after its first 8 MFMAs,
-  // so the last read has 8 MFMAs (~256 cycles) to land before it is needed
-  auto quarter = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], const u16* sa, const u16* sb,
-                     int kk_next, bf16x8 (&an)[4], bf16x8 (&bn)[4]) {
+  bf16x8 fa[4][4], fb[4][4];  // [quarter set][fragment]
+  // quarter q: MFMAs on set q; reads for (sa_r, sb_r, kk_r) into set r after
+  // its first 8 MFMAs; DMA j0..j0+7 of stage kt_dma (when j0 >= 0) after its
+  // even MFMAs
+  auto quarter = [&](int q, const u16* sa_r, const u16* sb_r, int kk_r, int r, u16* sa_d,
+                     u16* sb_d, int kt_dma, int j0) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
-      mfma1(af, bfr, m);
-      if (m < 8) read1(sa, sb, kk_next, kRead[m], an, bn);
+      mfma1(fa[q], fb[q], m);
+      if (m < 8) read1(sa_r, sb_r, kk_r, kRead[m], fa[r], fb[r]);
+      if (j0 >= 0 && (m & 1) == 0) dma(sa_d, sb_d, kt_dma, j0 + (m >> 1));
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto stage = [&](u16* sa, u16* sb, u16* na, u16* nb_, int kt) {
-    quarter(a0, b0, sa, sb, 1, a1, b1);
-    quarter(a1, b1, sa, sb, 2, a0, b0);
-    quarter(a0, b0, sa, sb, 3, a1, b1);
-    wait_vm_lgkm0<0>();
+  auto stage = [&](u16* sa, u16* sb, u16* na, u16* nb_, int kt) __attribute__((always_inline)) {
+    quarter(0, sa, sb, 2, 2, sa, sb, 0, -1);
+    quarter(1, sa, sb, 3, 3, sa, sb, 0, -1);
+    wait_vm_lgkm0<0>();  // own reads of this buffer done; stage kt+1 landed
     block_barrier();
-    // last quarter: one DMA (stage kt+2 into the buffer just consumed) after
-    // each MFMA, and the next stage's first fragments after the odd ones
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      mfma1(a1, b1, m);
-      dma(sa, sb, kt + 2, m);
-      if (m < 8) read1(na, nb_, 0, kRead[m], a0, b0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    quarter(2, na, nb_, 0, 0, sa, sb, kt + 2, 0);
+    quarter(3, na, nb_, 1, 1, sa, sb, kt + 2, 8);
   };
 #pragma unroll
   for (int j = 0; j < 16; ++j) dma(sA0, sB0, 0, j);
@@ -873,7 +470,9 @@ void grouped_gemm_v4_kernel(TileArgs p) {
   wait_vm_lgkm0<16>();
   block_barrier();
 #pragma unroll
-  for (int f = 0; f < 8; ++f) read1(sA0, sB0, 0, f, a0, b0);
+  for (int f = 0; f < 8; ++f) read1(sA0, sB0, 0, f, fa[0], fb[0]);
+#pragma unroll
+  for (int f = 0; f < 8; ++f) read1(sA0, sB0, 1, f, fa[1], fb[1]);
   for (int kt = 0; kt < nk; kt += 2) {
     stage(sA0, sB0, sA1, sB1, kt);
     stage(sA1, sB1, sA0, sB0, kt + 1);
@@ -919,20 +518,11 @@ hipError_t run_tiles_v2(TileArgs a, hipStream_t s) {
   const int ncols = (MODE == kGateUpSwiglu) ? 128 : 256;
   a.n_tiles = (a.N + ncols - 1) / ncols;
   if (a.ksplit < 1) a.ksplit = 1;
+  // each K slice needs an even number of 64-wide stages (callers check K % 128)
+  if ((a.K / a.ksplit) % 128 != 0) return hipErrorInvalidValue;
   long long nblk = (long long)m_tiles_max * a.n_tiles * a.ksplit;
   nblk = (nblk + 7) / 8 * 8;
-  static const int variant = [] {
-    const char* v = getenv("MOE_GEMM_VARIANT");
-    return v ? atoi(v) : 4;
-  }();
-  // K slices exist only in v4; each slice needs an even number of 64-wide steps
-  const int steps = a.K / a.ksplit / 64;
-  if (a.ksplit > 1 || (variant != 2 && variant != 3 && steps % 2 == 0))
-    hipLaunchKernelGGL(grouped_gemm_v4_kernel<MODE>, dim3((unsigned)nblk), dim3(256), 0, s, a);
-  else if (variant == 3 && steps % 2 == 0)
-    hipLaunchKernelGGL(grouped_gemm_v3_kernel<MODE>, dim3((unsigned)nblk), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(grouped_gemm_v2_kernel<MODE>, dim3((unsigned)nblk), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(grouped_gemm_tile_kernel<MODE>, dim3((unsigned)nblk), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1085,7 +675,7 @@ hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid
     a.B1 = (const u16*)p.w->w_up;
   }
   hipError_t e;
-  const bool v2_gu = !int4 && (p.d % (4 * kV2BK) == 0);
+  const bool v2_gu = !int4 && (p.d % 128 == 0);
   if (relu)
     e = int4 ? run_tiles<128, 128, kUpRelu, true>(a, s)
              : (v2_gu ? run_tiles_v2<kUpRelu>(a, s) : run_tiles<128, 128, kUpRelu, false>(a, s));
@@ -1119,8 +709,8 @@ hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid
     return run_tiles<128, 128, kDown, true>(b, s);
   }
   b.B0 = (const u16*)p.w->w_down;
-  if (p.F % (4 * kV2BK) == 0) return run_tiles_v2<kDown>(b, s);
-  if (b.ksplit > 1) return hipErrorInvalidValue;  // slices exist only on the tiled v4 path
+  if (p.F % 128 == 0) return run_tiles_v2<kDown>(b, s);
+  if (b.ksplit > 1) return hipErrorInvalidValue;  // slices exist only on the 256x256 path
   return run_tiles<128, 128, kDown, false>(b, s);
 }
 
