@@ -62,10 +62,11 @@ def lib():
             L.orc_expert_rows.argtypes = [p, i, i, i, i, p, p, p, i, i, p, p, i, p]
             L.orc_combine.argtypes = [p, p, p, p, i, i, i, p]
             L.orc_dequant_int4.argtypes = [p, p, p, i64, i, i, p]
+            L.orc_replica_split.argtypes = [p, i, i, i, i, p]
             L.orc_round_bf16.argtypes = [d]
             L.orc_round_bf16.restype = d
             for f in ("orc_router_logits", "orc_topk_gates", "orc_permute", "orc_expert_rows",
-                      "orc_combine", "orc_dequant_int4"):
+                      "orc_combine", "orc_dequant_int4", "orc_replica_split"):
                 getattr(L, f).restype = C.c_int
             _lib = L
     return _lib
@@ -127,6 +128,21 @@ def permute(idx, E):
     _check(lib().orc_permute(_ptr(idx), T, E, k, _ptr(counts), _ptr(offsets), _ptr(row_assign),
                              _ptr(assign_row), _ptr(lis)), "permute")
     return counts, offsets, row_assign, assign_row, float(lis[0])
+
+
+def replica_split(idx, E, heavy):
+    """Assignments of expert ``heavy`` alternate with the replica slot E (odd ranks)."""
+    idx = np.ascontiguousarray(idx, np.int32)
+    T, k = idx.shape
+    out = np.empty_like(idx)
+    _check(lib().orc_replica_split(_ptr(idx), T, E, k, int(heavy), _ptr(out)), "replica_split")
+    return out
+
+
+def heavy_hitter(counts):
+    """The most-loaded expert (lowest id among equal counts)."""
+    counts = np.asarray(counts)
+    return int(np.flatnonzero(counts == counts.max())[0])
 
 
 def expert_rows(x, w_gate, w_up, w_down, act, h_round, tok, exp_id):
@@ -199,7 +215,15 @@ def dense_expert_weights(wl, experts=None):
     return tuple(out)
 
 
-def layer_forward(wl, logits=None, tokens=None, routing_only=False):
+def replica_dense_weights(rep):
+    """The replica's INT4 projections ([1, N, K]) decoded with the oracle's rule."""
+    out = []
+    for qw in (rep.q_gate, rep.q_up, rep.q_down):
+        out.append(None if qw is None else dequant_int4(qw.q, qw.scale, qw.zero))
+    return tuple(out)
+
+
+def layer_forward(wl, logits=None, tokens=None, routing_only=False, replica=None):
     """Run the whole layer on the CPU.
 
     ``logits``: if given (e.g. the GPU's fp32 logits), routing uses them instead
@@ -216,6 +240,14 @@ def layer_forward(wl, logits=None, tokens=None, routing_only=False):
     counts, offsets, row_assign, assign_row, lis = permute(idx, E)
     out = dict(logits=own_logits, idx=idx, gate=gate, counts=counts, offsets=offsets,
                row_assign=row_assign, assign_row=assign_row, lis=lis)
+    if replica is not None:
+        # the replica of expert `replica.heavy` is slot E; its share of that
+        # expert's assignments and the recount over E+1 slots
+        idx2 = replica_split(idx, E, replica.heavy)
+        counts2, offsets2, row_assign2, assign_row2, lis2 = permute(idx2, E + 1)
+        out.update(base_counts=counts, base_lis=lis, idx=idx2, counts=counts2,
+                   offsets=offsets2, row_assign=row_assign2, assign_row=assign_row2, lis=lis2)
+        idx, row_assign, assign_row = idx2, row_assign2, assign_row2
     if routing_only:
         return out
     if tokens is None:
@@ -230,8 +262,13 @@ def layer_forward(wl, logits=None, tokens=None, routing_only=False):
         pt = np.repeat(toks, k)
         pe = idx[toks].reshape(-1)
         ar = None
-    needed = sorted(set(int(e) for e in pe))
+    needed = sorted(set(int(e) for e in pe if e < E))
     wg, wu, wd = dense_expert_weights(wl, needed)
+    if replica is not None:
+        rg, ru, rd = replica_dense_weights(replica)
+        wg = None if wg is None else np.concatenate([wg, rg], axis=0)
+        wu = np.concatenate([wu, ru], axis=0)
+        wd = np.concatenate([wd, rd], axis=0)
     Y = expert_rows(wl.x, wg, wu, wd, cfg.act, _h_round(wl), pt, pe)
     Ys = None
     if cfg.n_shared:

@@ -196,6 +196,33 @@ int orc_permute(const int32_t* idx, int T, int E, int k, int32_t* counts, int32_
   return ORC_OK;
 }
 
+/* ---- Replica dispatch ---------------------------------------------------
+ * "A Replicate-and-Quantize Strategy for Plug-and-Play Load Balancing of
+ * Sparse Mixture-of-Experts LLMs" -- What carries the argument (a quantized
+ * copy of the heaviest-loaded expert is appended to the layer) and the
+ * review's If-this-is-right notes: the pages never fix how the unchanged
+ * router's tokens reach the replica.  Reading taken here: the heavy expert's
+ * assignments, in ascending flat order a = t*k + j, alternate between the
+ * original (even rank 0, 2, ...) and the replica, which is expert slot E (odd
+ * rank).  Counts, offsets, the permutation and LIS are then those of
+ * orc_permute over E+1 slots (m = E+1 in the LIS). */
+int orc_replica_split(const int32_t* idx, int T, int E, int k, int heavy, int32_t* idx_out) {
+  if (T < 0 || E < 1 || k < 1 || k > E || heavy < 0 || heavy >= E || !idx_out) return ORC_ERR_ARG;
+  size_t n = (size_t)T * k;
+  int64_t rank = 0;
+  for (size_t a = 0; a < n; ++a) {
+    int e = idx[a];
+    if (e < 0 || e >= E) return ORC_ERR_ARG;
+    if (e == heavy) {
+      idx_out[a] = (rank % 2 == 1) ? E : e;
+      rank += 1;
+    } else {
+      idx_out[a] = e;
+    }
+  }
+  return ORC_OK;
+}
+
 /* ---- O8/O9: expert FFN on (token, expert) pairs ------------------------ */
 /* For pair p = (t, e):
  *   SwiGLU: H[f] = rho( silu(x_t . W_gate[e][f]) * (x_t . W_up[e][f]) ),

@@ -384,6 +384,80 @@ def test_int4_quantization_error_bound():
         assert np.all(err <= 1.0 * s64 + np.abs(wf) * 2.0 ** -8 + 1e-9)
 
 
+# ---------------------------------------------------------------- replica dispatch
+
+def _golden(name):
+    fields = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                key, *vals = line.split()
+                fields[key] = vals
+    return fields
+
+
+def test_replica_split_golden_worked_example():
+    g = _golden("replica_split_example.txt")
+    E, k, heavy = int(g["E"][0]), int(g["K"][0]), int(g["HEAVY"][0])
+    idx = np.array(g["IDX"], np.int32).reshape(-1, k)
+    counts0, _, _, _, lis0 = oracle.permute(idx, E)
+    assert oracle.heavy_hitter(counts0) == heavy
+    assert lis0 == float(g["LIS_BEFORE"][0])
+    idx2 = oracle.replica_split(idx, E, heavy)
+    assert list(idx2.reshape(-1)) == [int(v) for v in g["IDX_SPLIT"]]
+    counts, offsets, row_assign, assign_row, lis = oracle.permute(idx2, E + 1)
+    assert list(counts) == [int(v) for v in g["COUNTS"]]
+    assert list(offsets) == [int(v) for v in g["OFFSETS"]]
+    assert list(row_assign) == [int(v) for v in g["ROW_ASSIGN"]]
+    assert list(assign_row) == [int(v) for v in g["ASSIGN_ROW"]]
+    assert lis == float(g["LIS"][0])
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (37, 8, 2), (200, 64, 6), (333, 8, 1), (9, 3, 3)])
+def test_replica_split_closed_forms(T, E, k):
+    rng = np.random.default_rng(1000 + T * E + k)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    counts0, _, _, _, _ = oracle.permute(idx, E)
+    heavy = oracle.heavy_hitter(counts0)
+    n = int(counts0[heavy])
+    idx2 = oracle.replica_split(idx, E, heavy)
+    counts, offsets, row_assign, assign_row, lis = oracle.permute(idx2, E + 1)
+    # the heavy expert keeps ceil(n/2), the replica gets floor(n/2), the rest unchanged
+    assert counts[heavy] == (n + 1) // 2 and counts[E] == n // 2
+    others = [e for e in range(E) if e != heavy]
+    assert list(counts[others]) == list(counts0[others])
+    assert counts.sum() == T * k
+    # only assignments of the heavy expert move, each to the replica slot
+    moved = idx2 != idx
+    assert np.all(idx[moved] == heavy) and np.all(idx2[moved] == E)
+    # the moved ones are every second heavy assignment, counting from the second
+    heavy_flat = np.flatnonzero(idx.reshape(-1) == heavy)
+    assert list(np.flatnonzero(moved.reshape(-1))) == list(heavy_flat[1::2])
+    assert lis == (E + 1) * counts.max() / (T * k)
+    assert lis <= (E + 1) * max(counts0.max(), 1) / (T * k)
+
+
+def test_replica_of_exact_weights_leaves_the_layer_unchanged():
+    """A replica whose decoded weights equal the original expert's makes the
+    split invisible: y is the same bits with and without it."""
+    from workloads import make_replica
+    wl = make_workload(get_config("mixtral_prefill_bf16", T=48, d=256, F=256))
+    r0 = oracle.layer_forward(wl, routing_only=True)
+    heavy = oracle.heavy_hitter(r0["counts"])
+    rep = make_replica(wl, heavy)
+    # make the original expert exactly the replica's decoded weights
+    for name, qw in (("w_gate", rep.q_gate), ("w_up", rep.q_up), ("w_down", rep.q_down)):
+        getattr(wl, name)[heavy] = oracle.dequant_int4(qw.q[0], qw.scale[0], qw.zero[0])
+    base = oracle.layer_forward(wl)
+    split = oracle.layer_forward(wl, replica=rep)
+    assert split["counts"][-1] > 0
+    assert np.array_equal(base["y"], split["y"])
+    # and a lossy replica does change y (the split is really applied)
+    wl2 = make_workload(get_config("mixtral_prefill_bf16", T=48, d=256, F=256))
+    lossy = oracle.layer_forward(wl2, replica=make_replica(wl2, heavy))
+    assert not np.array_equal(oracle.layer_forward(wl2)["y"], lossy["y"])
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 MUTANTS = [
@@ -407,6 +481,10 @@ MUTANTS = [
     ("int4 zero added", "float a = (float)nib - z;", "float a = (float)nib + z;"),
     ("bf16 rounding truncates", "double r = nearbyint(ldexp(v, -q));",
      "double r = trunc(ldexp(v, -q));"),
+    ("replica takes even ranks", "idx_out[a] = (rank % 2 == 1) ? E : e;",
+     "idx_out[a] = (rank % 2 == 0) ? E : e;"),
+    ("replica split counts every expert", "    if (e == heavy) {\n      idx_out[a]",
+     "    if (e >= 0) {\n      idx_out[a]"),
 ]
 
 

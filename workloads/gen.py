@@ -189,3 +189,32 @@ def make_workload(cfg, beta: Optional[float] = None, fractional_zero: bool = Fal
         wl.q_down = q4(w_down)
     return wl
 
+
+
+@dataclass
+class Replica:
+    """An INT4 copy of one routed expert, appended to the layer as slot E.
+
+    ``heavy`` is the expert it copies; the projections hold one expert each
+    ([1, F, d] / [1, d, F] logical shapes, same packing as Int4Weights)."""
+    heavy: int
+    q_gate: Optional[Int4Weights]
+    q_up: Int4Weights
+    q_down: Int4Weights
+
+
+def make_replica(wl: Workload, heavy: int, fractional_zero: bool = False) -> Replica:
+    """Quantise expert ``heavy`` of ``wl`` with the input quantiser (INT4 layers:
+    copy its existing INT4 weights)."""
+    def one(qw, w):
+        if qw is not None:
+            return Int4Weights(qw.q[heavy:heavy + 1].copy(), qw.scale[heavy:heavy + 1].copy(),
+                               qw.zero[heavy:heavy + 1].copy())
+        if w is None:
+            return None
+        q, s, z = quantize_int4_rows(w[heavy], fractional_zero)
+        return Int4Weights(q[None], s[None], z[None])
+    if wl.cfg.dtype != "bf16":
+        raise ValueError("the INT4 replica needs bf16 activations")
+    return Replica(int(heavy), one(wl.q_gate, wl.w_gate), one(wl.q_up, wl.w_up),
+                   one(wl.q_down, wl.w_down))
