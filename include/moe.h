@@ -195,6 +195,51 @@ moe_status moe_layer_forward(const moe_layer_desc* L, const void* x, int T, void
 /* Workspace bytes moe_layer_forward needs for T tokens (host only, pure). */
 moe_status moe_workspace_size(const moe_layer_desc* L, int T, size_t* bytes);
 
+/* ---- Replica of the heaviest-loaded expert ("A Replicate-and-Quantize
+ * Strategy for Plug-and-Play Load Balancing of Sparse Mixture-of-Experts
+ * LLMs" -- What carries the argument: a quantized copy of the heavy-hitter
+ * expert is appended to the layer, the router left unchanged).  The pages do
+ * not say how that expert's tokens reach the copy; this library's rule: its
+ * assignments, in flat order a = t*k + j, alternate -- even ranks stay with
+ * the expert, odd ranks go to the replica, which is slot E.  Counts, offsets,
+ * the permutation and LIS are then those of the split routing over E + 1
+ * slots (LIS with m = E + 1). */
+
+/* The replica: INT4 weights of one expert (same layout as moe_w4 with E = 1:
+ * q_gate, q_up [1][d_ff][d_model/8], q_down [1][d_model][d_ff/8]; q_gate NULL
+ * for ReLU layers) and the expert it copies. */
+typedef struct {
+  int expert;
+  const moe_w4* q_gate;
+  const moe_w4* q_up;
+  const moe_w4* q_down;
+} moe_replica;
+
+/* Remap a permutation (the outputs of moe_permute for topk_idx) to the split
+ * routing of expert `heavy`: idx_out [T][k] (heavy's odd-ranked assignments
+ * become E), counts_out [E+1], offsets_out [E+2], row_assign_out and
+ * assign_row_out [T*k], lis_out [1].  Every output may be NULL.  Equal to
+ * moe_permute of idx_out over E+1 slots, without a second sort. */
+moe_status moe_replica_split(const int32_t* topk_idx, const int32_t* counts,
+                             const int32_t* offsets, const int32_t* assign_row, int T, int E,
+                             int k, int heavy, int32_t* idx_out, int32_t* counts_out,
+                             int32_t* offsets_out, int32_t* row_assign_out,
+                             int32_t* assign_row_out, double* lis_out, unsigned flags,
+                             void* stream);
+
+/* The layer with the replica: route, permute, split, grouped FFN of experts
+ * 0..E-1 (their own weights) and of slot E (the replica's INT4 weights),
+ * shared experts, combine.  bf16 activations only.  aux (optional) receives
+ * the split routing: counts [E+1], offsets [E+2], row_assign/assign_row, lis
+ * over E+1 slots (aux->idx keeps the router's choice); lis_base (optional)
+ * receives the LIS of the router's own routing (E slots).
+ * Workspace: moe_replica_workspace_size(L, T, &bytes). */
+moe_status moe_layer_forward_replica(const moe_layer_desc* L, const moe_replica* R,
+                                     const void* x, int T, void* y, moe_dtype ydt, moe_aux* aux,
+                                     double* lis_base, void* ws, size_t ws_bytes, unsigned flags,
+                                     void* stream);
+moe_status moe_replica_workspace_size(const moe_layer_desc* L, int T, size_t* bytes);
+
 /* Instrumentation (not part of the layer's arithmetic).  While set, every
  * moe_layer_forward call made on this thread records events[i] (hipEvent_t
  * handles created by the caller) on its stream at the stage boundaries:

@@ -22,7 +22,8 @@ MOE_F_LOGITS_GIVEN, MOE_F_VALIDATE_ONLY, MOE_F_NONDETERMINISTIC_COMBINE = 1, 2, 
 
 EXPORTED = ("moe_route_topk", "moe_permute", "moe_permute_workspace_size", "moe_grouped_ffn",
             "moe_grouped_ffn_workspace_size", "moe_combine", "moe_layer_forward",
-            "moe_workspace_size", "moe_set_stage_events", "moe_status_string",
+            "moe_workspace_size", "moe_replica_split", "moe_layer_forward_replica",
+            "moe_replica_workspace_size", "moe_set_stage_events", "moe_status_string",
             "moe_last_error")
 
 
@@ -51,6 +52,11 @@ class LayerDesc(C.Structure):
                 ("top_k", C.c_int), ("act", C.c_int), ("act_dtype", C.c_int),
                 ("w_router", C.c_void_p), ("b_router", C.c_void_p), ("routed", Experts),
                 ("n_shared", C.c_int), ("d_ff_shared", C.c_int), ("shared", Experts)]
+
+
+class Replica(C.Structure):
+    _fields_ = [("expert", C.c_int), ("q_gate", C.POINTER(W4)), ("q_up", C.POINTER(W4)),
+                ("q_down", C.POINTER(W4))]
 
 
 class Aux(C.Structure):
@@ -84,6 +90,10 @@ def lib():
             L.moe_layer_forward.argtypes = [C.POINTER(LayerDesc), p, i, p, i, C.POINTER(Aux), p,
                                             sz, u, p]
             L.moe_workspace_size.argtypes = [C.POINTER(LayerDesc), i, C.POINTER(sz)]
+            L.moe_replica_split.argtypes = [p, p, p, p, i, i, i, i, p, p, p, p, p, p, u, p]
+            L.moe_layer_forward_replica.argtypes = [C.POINTER(LayerDesc), C.POINTER(Replica), p, i,
+                                                    p, i, C.POINTER(Aux), p, p, sz, u, p]
+            L.moe_replica_workspace_size.argtypes = [C.POINTER(LayerDesc), i, C.POINTER(sz)]
             L.moe_set_stage_events.argtypes = [C.POINTER(C.c_void_p), i]
             L.moe_set_stage_events.restype = C.c_int
             L.moe_status_string.argtypes = [i]
@@ -91,7 +101,8 @@ def lib():
             L.moe_last_error.argtypes = []
             L.moe_last_error.restype = C.c_char_p
             for f in ("moe_route_topk", "moe_permute", "moe_grouped_ffn", "moe_combine",
-                      "moe_layer_forward", "moe_workspace_size"):
+                      "moe_layer_forward", "moe_workspace_size", "moe_replica_split",
+                      "moe_layer_forward_replica", "moe_replica_workspace_size"):
                 getattr(L, f).restype = C.c_int
             _lib = L
     return _lib

@@ -114,6 +114,28 @@ class MoeLayer:
         return n.value
 
 
+@dataclass
+class MoeReplica:
+    """INT4 copy of routed expert ``expert`` (one expert per projection), run as slot E."""
+    expert: int
+    q_up: Int4Proj
+    q_down: Int4Proj
+    q_gate: Optional[Int4Proj] = None
+    _keep: list = field(default_factory=list, repr=False)
+
+    def struct(self) -> B.Replica:
+        r = B.Replica()
+        r.expert = self.expert
+        self._keep = []
+        for name in ("q_gate", "q_up", "q_down"):
+            q = getattr(self, name)
+            if q is not None:
+                st = q.struct()
+                self._keep.append(st)
+                setattr(r, name, C.pointer(st))
+        return r
+
+
 # ---- the five calls -----------------------------------------------------------
 
 def route_topk(x, w_router, b_router, k, logits=None, logits_given=False, flags=0):
@@ -179,15 +201,29 @@ def combine(y_rows, assign_row, T, k, y_shared=None, out_dtype=torch.float32, fl
 
 
 class LayerRunner:
-    """Holds the descriptor, workspace and aux buffers for repeated layer calls."""
+    """Holds the descriptor, workspace and aux buffers for repeated layer calls.
 
-    def __init__(self, layer: MoeLayer, T: int, out_dtype=torch.float32, want_aux=True):
+    With ``replica`` the layer runs moe_layer_forward_replica: aux then holds
+    the split routing over E+1 slots and ``lis_base`` the router's own LIS."""
+
+    def __init__(self, layer: MoeLayer, T: int, out_dtype=torch.float32, want_aux=True,
+                 replica: Optional[MoeReplica] = None):
         self.layer = layer
         self.T = T
         dev = layer.w_router.device
         self.desc = layer.desc()
-        self.ws = _ws(layer.workspace_size(T), dev)
+        self.replica = replica
+        self.rep = None if replica is None else replica.struct()
+        if replica is None:
+            self.ws = _ws(layer.workspace_size(T), dev)
+        else:
+            n = C.c_size_t(0)
+            B.check(B.lib().moe_replica_workspace_size(C.byref(self.desc), T, C.byref(n)),
+                    "moe_replica_workspace_size")
+            self.ws = _ws(n.value, dev)
+        self.lis_base = torch.empty(1, dtype=torch.float64, device=dev)
         E, k = layer.n_experts, layer.top_k
+        S = 0 if replica is None else 1   # extra slot of the replica
         self.y = torch.empty(T, layer.d_model, dtype=out_dtype, device=dev)
         self.aux_t = None
         self.aux = None
@@ -196,8 +232,8 @@ class LayerRunner:
                 logits=torch.empty(T, E, dtype=torch.float32, device=dev),
                 idx=torch.empty(T, k, dtype=torch.int32, device=dev),
                 gates=torch.empty(T, k, dtype=torch.float32, device=dev),
-                counts=torch.empty(E, dtype=torch.int32, device=dev),
-                offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                counts=torch.empty(E + S, dtype=torch.int32, device=dev),
+                offsets=torch.empty(E + 1 + S, dtype=torch.int32, device=dev),
                 row_assign=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
                 assign_row=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
                 lis=torch.empty(1, dtype=torch.float64, device=dev))
@@ -205,18 +241,47 @@ class LayerRunner:
 
     def __call__(self, x, flags=0):
         aux = C.byref(self.aux) if self.aux is not None else None
-        B.check(B.lib().moe_layer_forward(C.byref(self.desc), _p(x), self.T, _p(self.y),
-                                          _dt(self.y), aux, _p(self.ws), self.ws.numel(), flags,
-                                          _stream()),
-                "moe_layer_forward")
+        if self.rep is None:
+            B.check(B.lib().moe_layer_forward(C.byref(self.desc), _p(x), self.T, _p(self.y),
+                                              _dt(self.y), aux, _p(self.ws), self.ws.numel(),
+                                              flags, _stream()),
+                    "moe_layer_forward")
+        else:
+            B.check(B.lib().moe_layer_forward_replica(C.byref(self.desc), C.byref(self.rep),
+                                                      _p(x), self.T, _p(self.y), _dt(self.y), aux,
+                                                      _p(self.lis_base), _p(self.ws),
+                                                      self.ws.numel(), flags, _stream()),
+                    "moe_layer_forward_replica")
         return self.y
 
 
-def layer_forward(layer: MoeLayer, x, out_dtype=torch.float32, flags=0, logits=None):
-    """One layer call; returns (y, aux dict of device tensors)."""
-    r = LayerRunner(layer, x.shape[0], out_dtype)
+def layer_forward(layer: MoeLayer, x, out_dtype=torch.float32, flags=0, logits=None,
+                  replica: Optional[MoeReplica] = None):
+    """One layer call; returns (y, aux dict of device tensors).  With ``replica``
+    aux describes the split routing and aux["lis_base"] the router's own LIS."""
+    r = LayerRunner(layer, x.shape[0], out_dtype, replica=replica)
     if logits is not None:
         r.aux_t["logits"].copy_(logits)
         flags |= B.MOE_F_LOGITS_GIVEN
     y = r(x, flags)
+    if replica is not None:
+        r.aux_t["lis_base"] = r.lis_base
     return y, r.aux_t
+
+
+def replica_split(idx, counts, offsets, assign_row, E, heavy, flags=0):
+    """Split routing of expert ``heavy`` (see moe_replica_split); returns a dict."""
+    T, k = idx.shape
+    dev = idx.device
+    out = dict(idx=torch.empty_like(idx),
+               counts=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               offsets=torch.empty(E + 2, dtype=torch.int32, device=dev),
+               row_assign=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
+               assign_row=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
+               lis=torch.empty(1, dtype=torch.float64, device=dev))
+    B.check(B.lib().moe_replica_split(_p(idx), _p(counts), _p(offsets), _p(assign_row), T, E, k,
+                                      int(heavy), _p(out["idx"]), _p(out["counts"]),
+                                      _p(out["offsets"]), _p(out["row_assign"]),
+                                      _p(out["assign_row"]), _p(out["lis"]), flags, _stream()),
+            "moe_replica_split")
+    return out

@@ -129,11 +129,14 @@ struct LayerWs {
   float* y_rows;           // down_splits partial copies of [T*k][d]
   int down_splits;
   void* Hs;
+  // replica layer: the split routing over E+1 slots
+  int32_t *counts2, *offsets2, *row_assign2, *assign_row2;
+  double* lis2;
   float* y_shared;
   size_t total;
 };
 
-LayerWs carve_layer(const moe_layer_desc* L, int T, void* ws) {
+LayerWs carve_layer(const moe_layer_desc* L, int T, void* ws, bool replica = false) {
   const int E = L->n_experts, k = L->top_k, d = L->d_model, F = L->d_ff;
   const size_t n = (size_t)T * k;
   const size_t esz = L->act_dtype == MOE_DT_F32 ? 4 : 2;
@@ -149,11 +152,22 @@ LayerWs carve_layer(const moe_layer_desc* L, int T, void* ws) {
   w.lis = (double*)c.take(8);
   w.perm_ws = c.take(permute_ws_bytes(T, E, k));
   w.H = c.take(n * F * esz);
-  w.down_splits = ffn_down_splits(T, d, F, E, k, L->act_dtype, L->routed.q_up != nullptr);
+  // a replica layer runs its slot E through a separate (INT4) pass, which
+  // writes whole rows: no K slices there
+  w.down_splits = replica ? 1 : ffn_down_splits(T, d, F, E, k, L->act_dtype, L->routed.q_up != nullptr);
   w.y_rows = (float*)c.take(n * d * 4 * w.down_splits);
   const int Fs = L->n_shared * L->d_ff_shared;
   w.Hs = L->n_shared ? c.take((size_t)T * Fs * esz) : nullptr;
   w.y_shared = L->n_shared ? (float*)c.take((size_t)T * d * 4) : nullptr;
+  w.counts2 = w.offsets2 = w.row_assign2 = w.assign_row2 = nullptr;
+  w.lis2 = nullptr;
+  if (replica) {
+    w.counts2 = (int32_t*)c.take((size_t)(E + 1) * 4);
+    w.offsets2 = (int32_t*)c.take((size_t)(E + 2) * 4);
+    w.row_assign2 = (int32_t*)c.take(n * 4);
+    w.assign_row2 = (int32_t*)c.take(n * 4);
+    w.lis2 = (double*)c.take(8);
+  }
   w.total = c.off;
   return w;
 }
@@ -323,11 +337,37 @@ moe_status moe_workspace_size(const moe_layer_desc* L, int T, size_t* bytes) {
   return ok();
 }
 
-moe_status moe_layer_forward(const moe_layer_desc* L, const void* x, int T, void* y,
-                             moe_dtype ydt, moe_aux* aux, void* ws, size_t ws_bytes,
-                             unsigned flags, void* stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status check_replica(const moe_layer_desc* L, const moe_replica* R) {
+  REQUIRE(R, "replica must not be NULL");
+  REQUIRE(R->expert >= 0 && R->expert < L->n_experts, "replica expert %d out of [0, %d)",
+          R->expert, L->n_experts);
+  if (L->act_dtype != MOE_DT_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "the INT4 replica needs bf16 activations");
+  moe_experts q{};
+  q.dtype = MOE_DT_BF16;
+  q.q_gate = R->q_gate;
+  q.q_up = R->q_up;
+  q.q_down = R->q_down;
+  REQUIRE(R->q_up, "replica q_up must not be NULL");
+  return check_experts(&q, MOE_DT_BF16, L->d_model, L->d_ff, L->act, "replica");
+}
+
+// The layer; with R, expert R->expert's odd-ranked assignments run on the
+// replica as slot E.
+moe_status layer_forward_impl(const moe_layer_desc* L, const moe_replica* R, const void* x, int T,
+                              void* y, moe_dtype ydt, moe_aux* aux, double* lis_base, void* ws,
+                              size_t ws_bytes, unsigned flags, void* stream) {
   moe_status s = check_layer(L, T, flags);
   if (s != MOE_OK) return s;
+  if (R) {
+    s = check_replica(L, R);
+    if (s != MOE_OK) return s;
+    OPT_PTR(lis_base, "lis_base");
+  }
   REQUIRE(valid_dtype(ydt), "unknown output dtype %d", (int)ydt);
   if (T > 0) {
     REQUIRE_PTR(x, "x");
@@ -341,25 +381,26 @@ moe_status moe_layer_forward(const moe_layer_desc* L, const void* x, int T, void
   }
   if ((flags & MOE_F_LOGITS_GIVEN) && !(aux && aux->logits))
     return fail(MOE_ERR_INVALID_ARG, "MOE_F_LOGITS_GIVEN needs aux->logits");
-  const size_t need = carve_layer(L, T, nullptr).total;
+  const size_t need = carve_layer(L, T, nullptr, R != nullptr).total;
   if (!ws || ws_bytes < need)
-    return fail(MOE_ERR_WORKSPACE, "moe_layer_forward needs %zu workspace bytes (got %zu)", need,
+    return fail(MOE_ERR_WORKSPACE, "the layer needs %zu workspace bytes (got %zu)", need,
                 ws ? ws_bytes : (size_t)0);
   REQUIRE(aligned(ws, 256), "ws must be 256-byte aligned");
   if (flags & MOE_F_VALIDATE_ONLY) return ok();
   if (T == 0) return ok();
 
   hipStream_t st = (hipStream_t)stream;
-  LayerWs w = carve_layer(L, T, ws);
+  LayerWs w = carve_layer(L, T, ws, R != nullptr);
   const int E = L->n_experts, k = L->top_k, d = L->d_model;
   float* logits = (aux && aux->logits) ? aux->logits : w.logits;
   int32_t* idx = (aux && aux->idx) ? aux->idx : w.idx;
   float* gates = (aux && aux->gates) ? aux->gates : w.gates;
-  int32_t* counts = (aux && aux->counts) ? aux->counts : w.counts;
-  int32_t* offsets = (aux && aux->offsets) ? aux->offsets : w.offsets;
-  int32_t* row_assign = (aux && aux->row_assign) ? aux->row_assign : w.row_assign;
-  int32_t* assign_row = (aux && aux->assign_row) ? aux->assign_row : w.assign_row;
-  double* lis = (aux && aux->lis) ? aux->lis : w.lis;
+  // the router's own routing (E slots); with a replica, aux receives the split
+  int32_t* counts = (!R && aux && aux->counts) ? aux->counts : w.counts;
+  int32_t* offsets = (!R && aux && aux->offsets) ? aux->offsets : w.offsets;
+  int32_t* row_assign = (!R && aux && aux->row_assign) ? aux->row_assign : w.row_assign;
+  int32_t* assign_row = (!R && aux && aux->assign_row) ? aux->assign_row : w.assign_row;
+  double* lis = R ? (lis_base ? lis_base : w.lis) : ((aux && aux->lis) ? aux->lis : w.lis);
 
   stage(0, st);
   hipError_t e = launch_route_topk(x, L->act_dtype, L->w_router, L->b_router, T, d, E, k, logits,
@@ -368,14 +409,47 @@ moe_status moe_layer_forward(const moe_layer_desc* L, const void* x, int T, void
   stage(1, st);
   e = launch_permute(idx, T, E, k, counts, offsets, row_assign, assign_row, lis, w.perm_ws, st);
   if (e != hipSuccess) return hip_status(e, "permute");
+  // rows of expert-major order used by the FFN and the combine
+  const int32_t* f_offsets = offsets;
+  const int32_t* f_row_assign = row_assign;
+  const int32_t* f_assign_row = assign_row;
+  if (R) {
+    int32_t* c2 = (aux && aux->counts) ? aux->counts : w.counts2;
+    int32_t* o2 = (aux && aux->offsets) ? aux->offsets : w.offsets2;
+    int32_t* ra2 = (aux && aux->row_assign) ? aux->row_assign : w.row_assign2;
+    int32_t* ar2 = (aux && aux->assign_row) ? aux->assign_row : w.assign_row2;
+    double* l2 = (aux && aux->lis) ? aux->lis : w.lis2;
+    e = launch_replica_remap(idx, counts, offsets, assign_row, T, E, k, R->expert, nullptr, c2, o2,
+                             ra2, ar2, l2, st);
+    if (e != hipSuccess) return hip_status(e, "replica split");
+    f_offsets = o2;
+    f_row_assign = ra2;
+    f_assign_row = ar2;
+  }
   stage(2, st);
   FfnProblem p{};
   p.T = T; p.d = d; p.F = L->d_ff; p.E = E; p.k = k; p.act = L->act;
-  p.dt = L->act_dtype; p.x = x; p.w = &L->routed; p.offsets = offsets;
-  p.row_assign = row_assign; p.gate = gates; p.y_rows = w.y_rows; p.H = w.H; p.rows = T * k;
+  p.dt = L->act_dtype; p.x = x; p.w = &L->routed; p.offsets = f_offsets;
+  p.row_assign = f_row_assign; p.gate = gates; p.y_rows = w.y_rows; p.H = w.H; p.rows = T * k;
   p.down_splits = w.down_splits;
   e = launch_grouped_ffn(p, st, g_stage_on ? g_stage_ev[3] : nullptr);
   if (e != hipSuccess) return hip_status(e, "grouped_ffn");
+  if (R) {
+    // slot E: one expert whose rows start at offsets[E] (absolute rows, so the
+    // same H and y_rows buffers), INT4 weights of the replica
+    moe_experts q{};
+    q.dtype = MOE_DT_BF16;
+    q.q_gate = R->q_gate;
+    q.q_up = R->q_up;
+    q.q_down = R->q_down;
+    FfnProblem r = p;
+    r.E = 1;
+    r.w = &q;
+    r.offsets = f_offsets + E;
+    r.down_splits = 1;
+    e = launch_grouped_ffn(r, st);
+    if (e != hipSuccess) return hip_status(e, "replica ffn");
+  }
   stage(4, st);
   if (L->n_shared > 0) {
     FfnProblem q{};
@@ -387,10 +461,61 @@ moe_status moe_layer_forward(const moe_layer_desc* L, const void* x, int T, void
     if (e != hipSuccess) return hip_status(e, "shared experts");
   }
   stage(5, st);
-  e = launch_combine(w.y_rows, assign_row, T, k, d, w.y_shared, y, ydt, st, w.down_splits,
+  e = launch_combine(w.y_rows, f_assign_row, T, k, d, w.y_shared, y, ydt, st, w.down_splits,
                      (size_t)T * k * d);
   stage(6, st);
   return hip_status(e, "combine");
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_forward(const moe_layer_desc* L, const void* x, int T, void* y,
+                             moe_dtype ydt, moe_aux* aux, void* ws, size_t ws_bytes,
+                             unsigned flags, void* stream) {
+  return layer_forward_impl(L, nullptr, x, T, y, ydt, aux, nullptr, ws, ws_bytes, flags, stream);
+}
+
+moe_status moe_layer_forward_replica(const moe_layer_desc* L, const moe_replica* R,
+                                     const void* x, int T, void* y, moe_dtype ydt, moe_aux* aux,
+                                     double* lis_base, void* ws, size_t ws_bytes, unsigned flags,
+                                     void* stream) {
+  REQUIRE(R, "replica must not be NULL");
+  return layer_forward_impl(L, R, x, T, y, ydt, aux, lis_base, ws, ws_bytes, flags, stream);
+}
+
+moe_status moe_replica_workspace_size(const moe_layer_desc* L, int T, size_t* bytes) {
+  REQUIRE(bytes, "bytes must not be NULL");
+  moe_status s = check_layer(L, T, 0);
+  if (s != MOE_OK) return s;
+  *bytes = carve_layer(L, T, nullptr, true).total;
+  return ok();
+}
+
+moe_status moe_replica_split(const int32_t* topk_idx, const int32_t* counts,
+                             const int32_t* offsets, const int32_t* assign_row, int T, int E,
+                             int k, int heavy, int32_t* idx_out, int32_t* counts_out,
+                             int32_t* offsets_out, int32_t* row_assign_out,
+                             int32_t* assign_row_out, double* lis_out, unsigned flags,
+                             void* stream) {
+  moe_status s = check_common(T, E, k, flags);
+  if (s != MOE_OK) return s;
+  REQUIRE(heavy >= 0 && heavy < E, "heavy expert %d out of [0, %d)", heavy, E);
+  REQUIRE_PTR(counts, "counts");
+  REQUIRE_PTR(offsets, "offsets");
+  if (T > 0) {
+    REQUIRE_PTR(topk_idx, "topk_idx");
+    REQUIRE_PTR(assign_row, "assign_row");
+  }
+  OPT_PTR(idx_out, "idx_out"); OPT_PTR(counts_out, "counts_out");
+  OPT_PTR(offsets_out, "offsets_out"); OPT_PTR(row_assign_out, "row_assign_out");
+  OPT_PTR(assign_row_out, "assign_row_out"); OPT_PTR(lis_out, "lis_out");
+  if (flags & MOE_F_VALIDATE_ONLY) return ok();
+  return hip_status(launch_replica_remap(topk_idx, counts, offsets, assign_row, T, E, k, heavy,
+                                         idx_out, counts_out, offsets_out, row_assign_out,
+                                         assign_row_out, lis_out, (hipStream_t)stream),
+                    "moe_replica_split launch");
 }
 
 }  // extern "C"

@@ -49,6 +49,15 @@ hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* coun
                           int32_t* offsets, int32_t* row_assign, int32_t* assign_row,
                           double* lis, void* ws, hipStream_t s);
 
+// Replica of expert `heavy` as slot E: its odd-ranked assignments move there;
+// maps the E-slot permutation (counts, offsets, assign_row) to the E+1-slot one.
+// Every output pointer may be NULL.
+hipError_t launch_replica_remap(const int32_t* idx, const int32_t* counts, const int32_t* offsets,
+                                const int32_t* assign_row, int T, int E, int k, int heavy,
+                                int32_t* idx_out, int32_t* counts_out, int32_t* offsets_out,
+                                int32_t* row_assign_out, int32_t* assign_row_out, double* lis_out,
+                                hipStream_t s);
+
 // Grouped expert FFN.  `mode` selects the projection: gate/up (SwiGLU or ReLU)
 // producing H, or down producing gate-scaled fp32 rows.
 struct FfnProblem {

@@ -209,4 +209,74 @@ hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* coun
   return hipGetLastError();
 }
 
+// ---- replica dispatch -------------------------------------------------------
+// "A Replicate-and-Quantize Strategy for Plug-and-Play Load Balancing of Sparse
+// Mixture-of-Experts LLMs" -- What carries the argument: a quantized copy of the
+// heaviest-loaded expert is appended to the layer.  The pages leave the split of
+// that expert's tokens open; here its assignments alternate in flat order
+// a = t*k + j: even ranks stay, odd ranks go to the replica, slot E.  The
+// expert-major layout over E+1 slots follows from the E-slot one without a new
+// sort: the heavy expert keeps its even ranks in order at its start, experts
+// after it move down by h = floor(n_heavy / 2) rows, and the odd ranks fill the
+// last h rows (slot E) in order -- the stable expert-major order of the split
+// routing, with counts, offsets and LIS (m = E + 1) to match.
+__global__ __launch_bounds__(256) void replica_remap_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ assign_row, int n, int E,
+    int heavy, int T, int k, int32_t* __restrict__ idx_out, int32_t* __restrict__ counts_out,
+    int32_t* __restrict__ offsets_out, int32_t* __restrict__ row_assign_out,
+    int32_t* __restrict__ assign_row_out, double* __restrict__ lis_out) {
+  const int nh = counts[heavy], h = nh / 2;
+  const int hstart = offsets[heavy];
+  const int rep0 = n - h;  // first row of slot E
+  if (blockIdx.x == 0) {
+    // counts and offsets over E+1 slots, LIS with m = E + 1
+    if (threadIdx.x <= E) {
+      const int e = threadIdx.x;
+      const int c = (e == E) ? h : (e == heavy ? nh - h : counts[e]);
+      if (counts_out) counts_out[e] = c;
+      if (offsets_out) offsets_out[e] = (e == E) ? rep0 : offsets[e] - (e > heavy ? h : 0);
+    }
+    if (threadIdx.x == 0) {
+      if (offsets_out) offsets_out[E + 1] = n;
+      int mx = h;
+      for (int e = 0; e < E; ++e) mx = max(mx, e == heavy ? nh - h : counts[e]);
+      if (lis_out)
+        *lis_out = (T == 0) ? __builtin_nan("") : (double)((long long)(E + 1) * mx) / (double)((long long)T * k);
+    }
+  }
+  for (int a = blockIdx.x * blockDim.x + threadIdx.x; a < n; a += gridDim.x * blockDim.x) {
+    const int e = idx[a];
+    const int row = assign_row[a];
+    int e2 = e, row2;
+    if (e == heavy) {
+      const int rank = row - hstart;
+      if (rank & 1) {
+        e2 = E;
+        row2 = rep0 + (rank >> 1);
+      } else {
+        row2 = hstart + (rank >> 1);
+      }
+    } else {
+      row2 = row - (e > heavy ? h : 0);
+    }
+    if (idx_out) idx_out[a] = e2;
+    if (assign_row_out) assign_row_out[a] = row2;
+    if (row_assign_out) row_assign_out[row2] = a;
+  }
+}
+
+hipError_t launch_replica_remap(const int32_t* idx, const int32_t* counts, const int32_t* offsets,
+                                const int32_t* assign_row, int T, int E, int k, int heavy,
+                                int32_t* idx_out, int32_t* counts_out, int32_t* offsets_out,
+                                int32_t* row_assign_out, int32_t* assign_row_out, double* lis_out,
+                                hipStream_t s) {
+  const int n = T * k;
+  const int blocks = max(1, min((n + 255) / 256, 1024));
+  hipLaunchKernelGGL(replica_remap_kernel, dim3(blocks), dim3(256), 0, s, idx, counts, offsets,
+                     assign_row, n, E, heavy, T, k, idx_out, counts_out, offsets_out,
+                     row_assign_out, assign_row_out, lis_out);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -4,7 +4,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .api import ExpertWeights, Int4Proj, MoeLayer
+from .api import ExpertWeights, Int4Proj, MoeLayer, MoeReplica
 
 
 def _t(a: np.ndarray, dev, bf16: bool):
@@ -39,3 +39,9 @@ def to_device(wl, device="cuda"):
                      torch.from_numpy(wl.b_router).to(device), routed, cfg.n_shared,
                      cfg.F_shared, shared)
     return layer, _t(wl.x, device, bf)
+
+
+def replica_to_device(rep, device="cuda"):
+    """MoeReplica for a ``workloads.Replica`` (INT4, one expert per projection)."""
+    return MoeReplica(rep.heavy, _q(rep.q_up, device), _q(rep.q_down, device),
+                      None if rep.q_gate is None else _q(rep.q_gate, device))

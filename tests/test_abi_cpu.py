@@ -193,3 +193,52 @@ def test_layer_workspace_and_validation(L, B):
 def test_status_strings(L, B):
     for s in range(5):
         assert L.moe_status_string(s).decode().startswith("MOE_")
+
+
+def _replica(B, expert=0, gate=True):
+    r = B.Replica()
+    r.expert = expert
+    keep = []
+    for name in ("q_gate", "q_up", "q_down"):
+        if name == "q_gate" and not gate:
+            continue
+        w = B.W4(_addr(30), _addr(31), _addr(32))
+        keep.append(w)
+        setattr(r, name, C.pointer(w))
+    r._keep = keep
+    return r
+
+
+def test_replica_validation_and_workspace(L, B):
+    VO = B.MOE_F_VALIDATE_ONLY
+    Ld = _desc(B)
+    n0, n1 = C.c_size_t(0), C.c_size_t(0)
+    assert L.moe_workspace_size(C.byref(Ld), 100, C.byref(n0)) == B.MOE_OK
+    assert L.moe_replica_workspace_size(C.byref(Ld), 100, C.byref(n1)) == B.MOE_OK
+    assert n1.value > 0 and n0.value > 0   # (the plain layer may hold K-slice partials instead)
+    ws = C.c_void_p(FAKE * 16)
+
+    def fwd(rep, nbytes=None, Ldesc=None):
+        return L.moe_layer_forward_replica(C.byref(Ldesc or Ld), None if rep is None else C.byref(rep),
+                                           _addr(1), 100, _addr(2), 0, None, _addr(3), ws,
+                                           n1.value if nbytes is None else nbytes, VO, None)
+    assert fwd(_replica(B, 3)) == B.MOE_OK
+    assert fwd(_replica(B, 3), n1.value - 1) == B.MOE_ERR_WORKSPACE
+    assert fwd(_replica(B, 8)) == B.MOE_ERR_INVALID_ARG          # expert out of range
+    assert fwd(_replica(B, -1)) == B.MOE_ERR_INVALID_ARG
+    assert fwd(None) == B.MOE_ERR_INVALID_ARG
+    assert fwd(_replica(B, 3, gate=False)) == B.MOE_ERR_INVALID_ARG   # SwiGLU needs q_gate
+    Lf = _desc(B)
+    Lf.act_dtype = 0
+    Lf.routed = _experts(B, dtype=0)
+    assert fwd(_replica(B, 3), Ldesc=Lf) == B.MOE_ERR_UNSUPPORTED     # bf16 activations only
+
+    def split(heavy, T=16, E=8, k=2, counts=True):
+        return L.moe_replica_split(_addr(1), _addr(2) if counts else None, _addr(3), _addr(4), T,
+                                   E, k, heavy, _addr(5), _addr(6), _addr(7), _addr(8), _addr(9),
+                                   _addr(10), VO, None)
+    assert split(0) == B.MOE_OK
+    assert split(7) == B.MOE_OK
+    assert split(8) == B.MOE_ERR_INVALID_ARG
+    assert split(0, counts=False) == B.MOE_ERR_INVALID_ARG
+    assert split(0, E=65) == B.MOE_ERR_UNSUPPORTED
