@@ -168,6 +168,43 @@ def measured_traffic(workload, kernel):
     return None
 
 
+def run_replica(name, steps, warmup):
+    """The layer with an INT4 replica of its heaviest expert (chosen by a
+    calibration call on the same batch) against the plain layer."""
+    import torch
+    import sparse_mixture_experts_wavefront_amd as moe
+    from sparse_mixture_experts_wavefront_amd.device_inputs import replica_to_device, to_device
+    from workloads import make_replica, make_workload
+    wl = make_workload(name)
+    cfg = wl.cfg
+    layer, x = to_device(wl)
+
+    def timed(runner):
+        for _ in range(warmup):
+            runner(x)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            runner(x)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1000.0 / steps
+    plain = moe.LayerRunner(layer, cfg.T)
+    ms_plain = timed(plain)
+    counts = plain.aux_t["counts"].cpu().numpy()
+    heavy = int(np.flatnonzero(counts == counts.max())[0])
+    rep = replica_to_device(make_replica(wl, heavy))
+    split = moe.LayerRunner(layer, cfg.T, replica=rep)
+    ms_rep = timed(split)
+    c2 = split.aux_t["counts"].cpu().numpy()
+    return {"workload": name, "T": cfg.T, "E": cfg.E, "top_k": cfg.k, "heavy_expert": heavy,
+            "heavy_rows": int(counts[heavy]), "rows_after": [int(c2[heavy]), int(c2[-1])],
+            "lis_before": float(split.lis_base.cpu().numpy()[0]),
+            "lis_after": float(split.aux_t["lis"].cpu().numpy()[0]),
+            "tokens_per_s_plain": round(cfg.T / (ms_plain / 1e3), 1),
+            "tokens_per_s_replica": round(cfg.T / (ms_rep / 1e3), 1),
+            "ms_plain": round(ms_plain, 4), "ms_replica": round(ms_rep, 4)}
+
+
 def roofline(cfg, r):
     w = r["work"]
     t = r["stages_us"]["gate_up_gemm"] * 1e-6
@@ -219,6 +256,9 @@ def main():
     ap.add_argument("--secondary", default="mixtral_decode_bf16,mixtral_int4_decode",
                     help="comma-separated extra workloads reported in the same line ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--replica", default="switch_bf16,deepseek_v2_lite_bf16",
+                    help="comma-separated workloads also run with an INT4 replica of their "
+                         "heaviest expert ('' for none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (the known-size kernel "
                          "that scales the FETCH_SIZE/WRITE_SIZE counters)")
@@ -275,6 +315,9 @@ def main():
         del wl2
     if sec:
         out["secondary"] = sec
+    reps = [run_replica(n, args.steps, args.warmup) for n in args.replica.split(",") if n]
+    if reps:
+        out["replica"] = reps
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     else:
