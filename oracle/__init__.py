@@ -10,6 +10,10 @@ The arithmetic lives in ``moe_oracle.c`` (plain loops, fp64 accumulation,
 steps in the order the layer defines them:
 logits -> exact top-k + softmax gates -> counts / offsets / stable expert-major
 permutation / LIS -> per-row expert FFN -> weighted combine (+ shared experts).
+Two variants of the dispatch are also here: the replica split of one heavy
+expert (odd ranks of its flat assignment order go to an extra slot), and the
+nested-width decode where each (token, slot) carries a width of 2, 3 or 4 bits
+and rows are grouped by (expert, width).
 """
 from __future__ import annotations
 
@@ -63,10 +67,11 @@ def lib():
             L.orc_combine.argtypes = [p, p, p, p, i, i, i, p]
             L.orc_dequant_int4.argtypes = [p, p, p, i64, i, i, p]
             L.orc_replica_split.argtypes = [p, i, i, i, i, p]
+            L.orc_dequant_mwq.argtypes = [p, p, p, p, p, p, p, i64, i, i, i, p]
             L.orc_round_bf16.argtypes = [d]
             L.orc_round_bf16.restype = d
             for f in ("orc_router_logits", "orc_topk_gates", "orc_permute", "orc_expert_rows",
-                      "orc_combine", "orc_dequant_int4", "orc_replica_split"):
+                      "orc_combine", "orc_dequant_int4", "orc_replica_split", "orc_dequant_mwq"):
                 getattr(L, f).restype = C.c_int
             _lib = L
     return _lib
@@ -191,6 +196,21 @@ def dequant_int4(q, scale, zero, group=INT4_GROUP):
     return out
 
 
+def dequant_mwq(m, bits, group=INT4_GROUP):
+    """Nested INT2 + residual planes (one projection, leading dims kept) decoded at
+    width ``bits`` (2, 3 or 4) -> bf16 bits [.., N, K]."""
+    q2 = np.ascontiguousarray(m.q2, np.int32)
+    K = q2.shape[-1] * 16
+    rows = int(np.prod(q2.shape[:-1]))
+    out = np.empty(q2.shape[:-1] + (K,), np.uint16)
+    arrs = [np.ascontiguousarray(a, dt) for a, dt in ((m.s2, np.uint16), (m.z2, np.uint16),
+                                                       (m.p3, np.int32), (m.a3, np.uint16),
+                                                       (m.p4, np.int32), (m.a4, np.uint16))]
+    _check(lib().orc_dequant_mwq(_ptr(q2), *[_ptr(a) for a in arrs], rows, K, group, int(bits),
+                                 _ptr(out)), "dequant_mwq")
+    return out
+
+
 # --- the layer -----------------------------------------------------------
 
 def _h_round(wl):
@@ -198,7 +218,25 @@ def _h_round(wl):
 
 
 def dense_expert_weights(wl, experts=None):
-    """Routed expert weights as dense arrays (INT4 decoded with the oracle's rule)."""
+    """Routed expert weights as dense arrays (INT4 decoded with the oracle's rule).
+
+    Nested-quantised layers have 3E virtual experts v = e*3 + (bits - 2): expert e
+    decoded at 2, 3 and 4 bits."""
+    if wl.cfg.mwq:
+        E = wl.cfg.E
+        sel = range(3 * E) if experts is None else experts
+        out = []
+        for m, shape_src in ((wl.m_gate, wl.w_gate), (wl.m_up, wl.w_up), (wl.m_down, wl.w_down)):
+            if m is None:
+                out.append(None)
+                continue
+            full = np.zeros((3 * E,) + shape_src.shape[1:], np.uint16)
+            for v in sel:
+                e, b = v // 3, v % 3 + 2
+                one = type(m)(*[a[e] for a in (m.q2, m.s2, m.z2, m.p3, m.a3, m.p4, m.a4)])
+                full[v] = dequant_mwq(one, b)
+            out.append(full)
+        return tuple(out)
     if not wl.cfg.int4:
         return wl.w_gate, wl.w_up, wl.w_down
     E = wl.cfg.E
@@ -248,6 +286,13 @@ def layer_forward(wl, logits=None, tokens=None, routing_only=False, replica=None
         out.update(base_counts=counts, base_lis=lis, idx=idx2, counts=counts2,
                    offsets=offsets2, row_assign=row_assign2, assign_row=assign_row2, lis=lis2)
         idx, row_assign, assign_row = idx2, row_assign2, assign_row2
+    if cfg.mwq:
+        # rows grouped by (expert, bit width): virtual expert v = e*3 + (bits - 2)
+        vidx = (idx * 3 + (wl.bits - 2)).astype(np.int32)
+        vcounts, voffsets, vra, var_, _ = permute(vidx, 3 * E)
+        out.update(mwq_idx=vidx, mwq_counts=vcounts, mwq_offsets=voffsets,
+                   mwq_row_assign=vra, mwq_assign_row=var_)
+        idx, row_assign, assign_row = vidx, vra, var_
     if routing_only:
         return out
     if tokens is None:
@@ -262,7 +307,7 @@ def layer_forward(wl, logits=None, tokens=None, routing_only=False, replica=None
         pt = np.repeat(toks, k)
         pe = idx[toks].reshape(-1)
         ar = None
-    needed = sorted(set(int(e) for e in pe if e < E))
+    needed = sorted(set(int(e) for e in pe if e < (3 * E if cfg.mwq else E)))
     wg, wu, wd = dense_expert_weights(wl, needed)
     if replica is not None:
         rg, ru, rd = replica_dense_weights(replica)

@@ -322,3 +322,56 @@ int orc_dequant_int4(const int32_t* q, const uint16_t* scale, const uint16_t* ze
   }
   return ORC_OK;
 }
+
+/* ---- Nested (matryoshka) weight decode -------------------------------------
+ * "D^2MoE: Dual Routing and Dynamic Scheduling for Efficient On-Device
+ * MoE-based LLM Serving" -- What carries the argument: the lowest bit width is
+ * an asymmetric quantisation of the weights, and every higher bit width adds a
+ * binary residual of the remaining error, so INT2 sits inside INT3 inside INT4;
+ * Assumptions & free parameters: group size 128.  Readings fixed here (the
+ * pages give no formula): the residual of width b is one bit r_b per weight and
+ * one fp16 magnitude a_b per group, adding +a_b (r_b = 1) or -a_b (r_b = 0).
+ *   q2 : [rows][K/16] int32, 2-bit field i of word j (bits 2i..2i+1) is K-index
+ *        16j+i;  s2, z2 : fp16 [rows][K/group]  (base scale and zero point)
+ *   p3, p4 : [rows][K/32] int32, bit i of word j is K-index 32j+i;
+ *   a3, a4 : fp16 [rows][K/group]  (residual magnitudes)
+ * Decoded at width `bits` (2, 3 or 4), each fp32 operation rounded to nearest
+ * even, no fused multiply-add, one bf16 rounding at the end:
+ *   w = fp32( fp32(q2) - z2 ) * s2 ;  bits >= 3: w = w + (r3 ? a3 : -a3) ;
+ *   bits == 4: w = w + (r4 ? a4 : -a4) ;  out = bf16_RNE(w). */
+int orc_dequant_mwq(const int32_t* q2, const uint16_t* s2, const uint16_t* z2, const int32_t* p3,
+                    const uint16_t* a3, const int32_t* p4, const uint16_t* a4, int64_t rows,
+                    int K, int group, int bits, uint16_t* out) {
+  if (rows < 0 || K < 32 || K % 32 || group < 32 || K % group || !q2 || !s2 || !z2 || !out ||
+      bits < 2 || bits > 4 || (bits >= 3 && (!p3 || !a3)) || (bits == 4 && (!p4 || !a4)))
+    return ORC_ERR_ARG;
+  int ng = K / group;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int kk = 0; kk < K; ++kk) {
+      size_t g = (size_t)r * ng + kk / group;
+      uint32_t w2 = (uint32_t)q2[r * (K / 16) + kk / 16];
+      uint32_t q = (w2 >> (2 * (kk % 16))) & 0x3u;
+      float s = fp16_to_float(s2[g]);
+      float z = fp16_to_float(z2[g]);
+      float a = (float)q - z; /* one fp32 rounding */
+      float w = a * s;        /* one fp32 rounding */
+      if (bits >= 3) {
+        uint32_t bit = ((uint32_t)p3[r * (K / 32) + kk / 32] >> (kk % 32)) & 1u;
+        float m = fp16_to_float(a3[g]);
+        w = w + (bit ? m : -m);
+      }
+      if (bits == 4) {
+        uint32_t bit = ((uint32_t)p4[r * (K / 32) + kk / 32] >> (kk % 32)) & 1u;
+        float m = fp16_to_float(a4[g]);
+        w = w + (bit ? m : -m);
+      }
+      double wr = orc_round_bf16((double)w);
+      float wf = (float)wr;
+      uint32_t u;
+      memcpy(&u, &wf, 4);
+      out[r * K + kk] = (uint16_t)(u >> 16);
+    }
+  }
+  return ORC_OK;
+}

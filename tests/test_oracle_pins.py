@@ -458,6 +458,84 @@ def test_replica_of_exact_weights_leaves_the_layer_unchanged():
     assert not np.array_equal(oracle.layer_forward(wl2)["y"], lossy["y"])
 
 
+# ---------------------------------------------------------------- nested (MWQ) decode
+
+def _mwq_one(q, r3, r4, s, z, a3, a4):
+    """One 32-wide row (K = 128 so one group) whose first weight carries the given codes."""
+    from workloads import MwqWeights
+    q2 = np.zeros((1, 8), np.uint32)
+    q2[0, 0] = q
+    p3 = np.zeros((1, 4), np.uint32)
+    p3[0, 0] = r3
+    p4 = np.zeros((1, 4), np.uint32)
+    p4[0, 0] = r4
+    g = lambda v: np.array([[v]], np.uint16)
+    return MwqWeights(q2.view(np.int32), g(s), g(z), p3.view(np.int32), g(a3), p4.view(np.int32),
+                      g(a4))
+
+
+def test_mwq_golden_table():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "mwq_dequant_table.txt"))
+            if l.strip() and not l.startswith("#") and not l.startswith("q ")]
+    assert len(rows) >= 9
+    for q, r3, r4, s, z, a3, a4, b2, b3, b4 in rows:
+        m = _mwq_one(int(q), int(r3), int(r4), int(s, 16), int(z, 16), int(a3, 16), int(a4, 16))
+        for bits, want in ((2, b2), (3, b3), (4, b4)):
+            got = oracle.dequant_mwq(m, bits)[0, 0]
+            assert got == int(want, 16), (q, r3, r4, bits, hex(got), want)
+
+
+def test_mwq_nesting_and_reductions():
+    from workloads import quantize_mwq_rows
+    rng = np.random.default_rng(31)
+    w = f32_to_bf16_bits((rng.standard_normal((24, 256)) * 0.02).astype(np.float32))
+    m1 = quantize_mwq_rows(w)
+    from workloads import MwqWeights
+    m = MwqWeights(*m1)
+    w2, w3, w4 = (oracle.dequant_mwq(m, b) for b in (2, 3, 4))
+    # width 2 reads neither plane, width 3 not the second
+    flip = MwqWeights(m.q2, m.s2, m.z2, ~m.p3, m.a3 ^ np.uint16(0x0155), ~m.p4,
+                      m.a4 ^ np.uint16(0x0133))
+    assert np.array_equal(oracle.dequant_mwq(flip, 2), w2)
+    flip4 = MwqWeights(m.q2, m.s2, m.z2, m.p3, m.a3, ~m.p4, m.a4 ^ np.uint16(0x0133))
+    assert np.array_equal(oracle.dequant_mwq(flip4, 3), w3)
+    # zero residual magnitudes: each wider decode equals the narrower one
+    zero = np.zeros_like(m.a3)
+    assert np.array_equal(oracle.dequant_mwq(MwqWeights(m.q2, m.s2, m.z2, m.p3, zero, m.p4, zero), 4), w2)
+    # the base is the INT4 rule on the same codes: spread each 2-bit field into a nibble
+    N, K = w.shape
+    q = (m.q2.view(np.uint32)[:, :, None] >> (np.arange(16, dtype=np.uint32) * 2)) & 3
+    q = q.reshape(N, K)
+    nib = np.bitwise_or.reduce(q.reshape(N, K // 8, 8) << (np.arange(8, dtype=np.uint32) * 4),
+                               axis=2).astype(np.uint32).view(np.int32)
+    assert np.array_equal(oracle.dequant_int4(nib, m.s2, m.z2), w2)
+    # the residual planes shrink the error of the input quantiser on average
+    wf = bf16_bits_to_f32(w).astype(np.float64)
+    errs = [np.abs(bf16_bits_to_f32(x) - wf).mean() for x in (w2, w3, w4)]
+    assert errs[0] > errs[1] > errs[2]
+
+
+def test_mwq_layer_at_one_width_is_the_plain_layer():
+    """All assignments at one width: rows group exactly as the plain routing and
+    y equals the plain layer on the weights decoded at that width."""
+    import dataclasses
+    wl = make_workload(get_config("mixtral_mwq_decode", T=24, d=256, F=256, x_rows_of=None,
+                                  weights_of=None))
+    for b in (2, 4):
+        wl.bits = np.full_like(wl.bits, b)
+        mw = oracle.layer_forward(wl)
+        plain = dataclasses.replace(wl, cfg=dataclasses.replace(wl.cfg, mwq=False))
+        plain.w_gate = oracle.dequant_mwq(wl.m_gate, b)
+        plain.w_up = oracle.dequant_mwq(wl.m_up, b)
+        plain.w_down = oracle.dequant_mwq(wl.m_down, b)
+        ref = oracle.layer_forward(plain)
+        assert np.array_equal(mw["counts"], ref["counts"]) and mw["lis"] == ref["lis"]
+        E = wl.cfg.E
+        assert np.array_equal(mw["mwq_counts"].reshape(E, 3)[:, b - 2], ref["counts"])
+        assert np.array_equal(mw["row_assign"], ref["row_assign"])
+        assert np.array_equal(mw["y"], ref["y"])
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 MUTANTS = [
@@ -485,6 +563,11 @@ MUTANTS = [
      "idx_out[a] = (rank % 2 == 0) ? E : e;"),
     ("replica split counts every expert", "    if (e == heavy) {\n      idx_out[a]",
      "    if (e >= 0) {\n      idx_out[a]"),
+    ("mwq residual sign flipped", "        w = w + (bit ? m : -m);\n      }\n      if (bits == 4)",
+     "        w = w + (bit ? -m : m);\n      }\n      if (bits == 4)"),
+    ("mwq second plane read from the first", "((uint32_t)p4[r * (K / 32) + kk / 32] >> (kk % 32))",
+     "((uint32_t)p3[r * (K / 32) + kk / 32] >> (kk % 32))"),
+    ("mwq 2-bit field order", "(w2 >> (2 * (kk % 16))) & 0x3u;", "(w2 >> (2 * (15 - kk % 16))) & 0x3u;"),
 ]
 
 

@@ -7,4 +7,4 @@ dequantisation), so both the CPU oracle and the HIP path may import it.
 """
 from .configs import CONFIGS, WorkloadConfig, get_config  # noqa: F401
 from .gen import Workload, make_workload, bf16_bits_to_f32, f32_to_bf16_bits  # noqa: F401
-from .gen import Replica, make_replica  # noqa: F401
+from .gen import Replica, make_replica, MwqWeights, quantize_mwq_rows  # noqa: F401

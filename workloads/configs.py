@@ -1,12 +1,13 @@
-"""The six synthetic workloads of the sparse MoE layer forward.
+"""The seven synthetic workloads of the sparse MoE layer forward.
 
 Shapes follow the model families the pages measure on: a Switch-Transformer-like
 top-1 ReLU layer, a Mixtral-8x7B-shaped top-2 SwiGLU layer (decode and prefill),
 a DeepSeek-V2-Lite-shaped layer with 64 fine-grained routed experts plus two
 always-active shared experts, and a Mixtral-shaped decode with asymmetric INT4
 expert weights (group 128 along K, fp16 scale and zero point, 8 nibbles per
-int32).  The pages print no d_model or d_ff; these sizes are those of the
-published model families.
+int32), and the same decode with nested INT2-to-INT4 weights and a bit width
+per assignment.  The pages print no d_model or d_ff; these sizes are those of
+the published model families.
 
 Router-bias constants ``beta`` were found by ``oracle/tune_router_bias.py``
 (it calls only the oracle) so that the Load Imbalance Score of the routed
@@ -34,6 +35,7 @@ class WorkloadConfig:
     bias: str = "zero"   # router-bias recipe: "zero" | "log_inv" | "neg_log" | "zipf"
     beta: float = 0.0    # bias strength for "neg_log" / "zipf"
     int4: bool = False   # expert weights as asymmetric INT4, group 128 along K
+    mwq: bool = False    # nested INT2 + binary residual planes, per-assignment bit width
     x_rows_of: Optional[str] = None   # take the first T rows of this workload's x
     weights_of: Optional[str] = None  # reuse this workload's router/expert weights
     notes: str = field(default="", compare=False)
@@ -63,6 +65,12 @@ CONFIGS = {
         "mixtral_int4_decode", 4, T=64, d=4096, E=8, k=2, F=14336, act="swiglu",
         dtype="bf16", int4=True, x_rows_of="mixtral_prefill_bf16",
         weights_of="mixtral_prefill_bf16"),
+    "mixtral_mwq_decode": WorkloadConfig(
+        "mixtral_mwq_decode", 5, T=16, d=4096, E=8, k=2, F=14336, act="swiglu",
+        dtype="bf16", mwq=True, x_rows_of="mixtral_prefill_bf16",
+        weights_of="mixtral_prefill_bf16",
+        notes="nested INT2 base + binary residual planes, bit width per assignment "
+              "uniform over {2, 3, 4}"),
 }
 
 

@@ -25,6 +25,7 @@ from .configs import CONFIGS, WorkloadConfig
 # tensor ids inside a workload's seed space
 TID_X, TID_WR, TID_WGATE, TID_WUP, TID_WDOWN = 0, 1, 2, 3, 4
 TID_SGATE, TID_SUP, TID_SDOWN, TID_ZIPF = 5, 6, 7, 8
+TID_BITS = 9   # per-assignment bit widths of the nested-quantisation workload
 
 W_STD = 0.02
 INT4_GROUP = 128
@@ -95,6 +96,66 @@ def quantize_int4_rows(w_bits: np.ndarray, fractional_zero: bool = False):
     return words.view(np.int32), s16.view(np.uint16), z16.view(np.uint16)
 
 
+def quantize_mwq_rows(w_bits: np.ndarray):
+    """Nested INT2 + two binary residual planes (group 128 along K) of bf16 rows.
+
+    ``w_bits``: [N, K] bf16 bits, K a multiple of 128.  Per group: an asymmetric
+    INT2 base (s2 = fp16((hi-lo)/3), z2 = fp16(clamp(rint(-lo/s2), 0, 3)),
+    q2 = clamp(rint(w/s2) + z2, 0, 3); a constant group gets s2 = 1, z2 = 0), then
+    for b = 3, 4 the sign bit r_b of the remaining error (1 where it is >= 0) and
+    a_b = fp16(mean |error|) -- the closed-form binary fit of the residual.  The
+    errors are taken in float64 (this is the input quantiser, not the decode).
+    Returns q2 [N, K/16] int32 (2-bit field i of word j = K-index 16j+i), s2, z2,
+    a3, a4 fp16 bits [N, K/128], p3, p4 [N, K/32] int32 (bit i of word j =
+    K-index 32j+i)."""
+    N, K = w_bits.shape
+    assert K % INT4_GROUP == 0
+    G = K // INT4_GROUP
+    w = bf16_bits_to_f32(w_bits).astype(np.float64).reshape(N, G, INT4_GROUP)
+    lo = w.min(axis=2)
+    hi = w.max(axis=2)
+    const = hi == lo
+    s16 = ((hi - lo) / 3.0).astype(np.float16)
+    s16[const] = np.float16(1.0)
+    s = s16.astype(np.float64)
+    z16 = np.clip(np.rint(-lo / s), 0.0, 3.0).astype(np.float16)
+    z16[const] = np.float16(0.0)
+    z = z16.astype(np.float64)
+    q = np.clip(np.rint(w / s[..., None]) + z[..., None], 0, 3)
+    approx = (q - z[..., None]) * s[..., None]
+    planes, mags = [], []
+    for _ in range(2):
+        err = w - approx
+        r = err >= 0
+        a16 = np.abs(err).mean(axis=2).astype(np.float16)
+        a = a16.astype(np.float64)[..., None]
+        approx = approx + np.where(r, a, -a)
+        planes.append(r.reshape(N, K))
+        mags.append(a16)
+    qv = q.astype(np.uint32).reshape(N, K // 16, 16)
+    sh2 = (np.arange(16, dtype=np.uint32) * np.uint32(2))[None, None, :]
+    q2 = np.bitwise_or.reduce(qv << sh2, axis=2).astype(np.uint32).view(np.int32)
+    sh1 = np.arange(32, dtype=np.uint32)[None, None, :]
+
+    def pack_bits(r):
+        return np.bitwise_or.reduce(r.reshape(N, K // 32, 32).astype(np.uint32) << sh1,
+                                    axis=2).astype(np.uint32).view(np.int32)
+    return (q2, s16.view(np.uint16), z16.view(np.uint16), pack_bits(planes[0]),
+            mags[0].view(np.uint16), pack_bits(planes[1]), mags[1].view(np.uint16))
+
+
+@dataclass
+class MwqWeights:
+    """Nested-quantised weights of one projection, all experts (see quantize_mwq_rows)."""
+    q2: np.ndarray      # [E, N, K/16] int32
+    s2: np.ndarray      # [E, N, K/128] fp16 bits
+    z2: np.ndarray
+    p3: np.ndarray      # [E, N, K/32] int32
+    a3: np.ndarray      # [E, N, K/128] fp16 bits
+    p4: np.ndarray
+    a4: np.ndarray
+
+
 @dataclass
 class Int4Weights:
     q: np.ndarray       # [E, N, K/8] int32
@@ -117,6 +178,10 @@ class Workload:
     q_gate: Optional[Int4Weights] = None
     q_up: Optional[Int4Weights] = None
     q_down: Optional[Int4Weights] = None
+    m_gate: Optional[MwqWeights] = None    # nested INT2+residual weights (mwq configs)
+    m_up: Optional[MwqWeights] = None
+    m_down: Optional[MwqWeights] = None
+    bits: Optional[np.ndarray] = None      # [T, k] int32 bit width of each assignment
 
     @property
     def bf16(self) -> bool:
@@ -187,6 +252,23 @@ def make_workload(cfg, beta: Optional[float] = None, fractional_zero: bool = Fal
         wl.q_gate = q4(w_gate) if w_gate is not None else None
         wl.q_up = q4(w_up)
         wl.q_down = q4(w_down)
+    if cfg.mwq:
+        assert bf16, "nested-quantised experts carry bf16 activations"
+
+        def qm(w):
+            parts = [None] * E
+
+            def one(e):
+                parts[e] = quantize_mwq_rows(w[e])
+            with ThreadPoolExecutor(max(1, min(threads, E))) as ex:
+                list(ex.map(one, range(E)))
+            return MwqWeights(*[np.stack([p[i] for p in parts]) for i in range(7)])
+        wl.m_gate = qm(w_gate) if w_gate is not None else None
+        wl.m_up = qm(w_up)
+        wl.m_down = qm(w_down)
+        # per-assignment bit widths, uniform over {2, 3, 4} (the pages' learned
+        # bit-width router is not part of this workload)
+        wl.bits = (_rng(cfg.cfg_id, TID_BITS).integers(0, 3, size=(T, cfg.k)) + 2).astype(np.int32)
     return wl
 
 
