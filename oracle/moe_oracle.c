@@ -331,14 +331,25 @@ int orc_dequant_int4(const int32_t* q, const uint16_t* scale, const uint16_t* ze
  * Assumptions & free parameters: group size 128.  Readings fixed here (the
  * pages give no formula): the residual of width b is one bit r_b per weight and
  * one fp16 magnitude a_b per group, adding +a_b (r_b = 1) or -a_b (r_b = 0).
- *   q2 : [rows][K/16] int32, 2-bit field i of word j (bits 2i..2i+1) is K-index
- *        16j+i;  s2, z2 : fp16 [rows][K/group]  (base scale and zero point)
- *   p3, p4 : [rows][K/32] int32, bit i of word j is K-index 32j+i;
+ *   q2 : [rows][K/16] int32; word j holds K-indices 16j..16j+15, byte-transposed:
+ *        K-index 16j + 4m + b sits in 2-bit field 4b + m (bits 8b+2m, 8b+2m+1);
+ *   s2, z2 : fp16 [rows][K/group]  (base scale and zero point)
+ *   p3, p4 : [rows][K/32] int32; word j holds K-indices 32j..32j+31, K-index
+ *        32j + 4i + b in bit 8b + i (b < 4, i < 8);
  *   a3, a4 : fp16 [rows][K/group]  (residual magnitudes)
  * Decoded at width `bits` (2, 3 or 4), each fp32 operation rounded to nearest
  * even, no fused multiply-add, one bf16 rounding at the end:
  *   w = fp32( fp32(q2) - z2 ) * s2 ;  bits >= 3: w = w + (r3 ? a3 : -a3) ;
  *   bits == 4: w = w + (r4 ? a4 : -a4) ;  out = bf16_RNE(w). */
+/* field of a 2-bit code and bit of a residual inside their storage words */
+static int mwq_field(int kk) {
+  int i = kk % 16;
+  return 4 * (i % 4) + i / 4;
+}
+static int mwq_bit(int kk) {
+  int i = kk % 32;
+  return 8 * (i % 4) + i / 4;
+}
 int orc_dequant_mwq(const int32_t* q2, const uint16_t* s2, const uint16_t* z2, const int32_t* p3,
                     const uint16_t* a3, const int32_t* p4, const uint16_t* a4, int64_t rows,
                     int K, int group, int bits, uint16_t* out) {
@@ -351,18 +362,18 @@ int orc_dequant_mwq(const int32_t* q2, const uint16_t* s2, const uint16_t* z2, c
     for (int kk = 0; kk < K; ++kk) {
       size_t g = (size_t)r * ng + kk / group;
       uint32_t w2 = (uint32_t)q2[r * (K / 16) + kk / 16];
-      uint32_t q = (w2 >> (2 * (kk % 16))) & 0x3u;
+      uint32_t q = (w2 >> (2 * mwq_field(kk))) & 0x3u;
       float s = fp16_to_float(s2[g]);
       float z = fp16_to_float(z2[g]);
       float a = (float)q - z; /* one fp32 rounding */
       float w = a * s;        /* one fp32 rounding */
       if (bits >= 3) {
-        uint32_t bit = ((uint32_t)p3[r * (K / 32) + kk / 32] >> (kk % 32)) & 1u;
+        uint32_t bit = ((uint32_t)p3[r * (K / 32) + kk / 32] >> mwq_bit(kk)) & 1u;
         float m = fp16_to_float(a3[g]);
         w = w + (bit ? m : -m);
       }
       if (bits == 4) {
-        uint32_t bit = ((uint32_t)p4[r * (K / 32) + kk / 32] >> (kk % 32)) & 1u;
+        uint32_t bit = ((uint32_t)p4[r * (K / 32) + kk / 32] >> mwq_bit(kk)) & 1u;
         float m = fp16_to_float(a4[g]);
         w = w + (bit ? m : -m);
       }

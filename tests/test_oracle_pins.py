@@ -485,6 +485,31 @@ def test_mwq_golden_table():
             assert got == int(want, 16), (q, r3, r4, bits, hex(got), want)
 
 
+def test_mwq_storage_positions():
+    """One non-zero code at a time lands on the K-index the storage order names:
+    q2 word j, field 4b+m -> K-index 16j+4m+b; plane word j, bit 8b+i -> 32j+4i+b."""
+    from workloads import MwqWeights
+    K = 128
+    one = lambda v: np.full((1, 1), v, np.uint16)
+    s, z, a = one(0x3C00), one(0x0000), one(0x3800)     # s = 1, z = 0, a = 0.5
+    for word, field, want in ((0, 0, 0), (0, 1, 4), (0, 4, 1), (0, 5, 5), (0, 15, 15), (1, 6, 16 + 9),
+                              (7, 11, 112 + 14)):
+        q2 = np.zeros((1, K // 16), np.uint32)
+        q2[0, word] = np.uint32(3) << np.uint32(2 * field)
+        zero_p = np.zeros((1, K // 32), np.int32)
+        m = MwqWeights(q2.view(np.int32), s, z, zero_p, a, zero_p, a)
+        w2 = oracle.dequant_mwq(m, 2)[0]
+        assert w2[want] == 0x4040 and np.count_nonzero(w2) == 1, (word, field)   # 3.0
+    for word, bit, want in ((0, 0, 0), (0, 1, 4), (0, 8, 1), (0, 9, 5), (0, 31, 31), (3, 20, 96 + 18)):
+        p = np.zeros((1, K // 32), np.uint32)
+        p[0, word] = np.uint32(1) << np.uint32(bit)
+        q2 = np.zeros((1, K // 16), np.int32)
+        zero_p = np.zeros((1, K // 32), np.int32)
+        w3 = oracle.dequant_mwq(MwqWeights(q2, s, z, p.view(np.int32), a, zero_p, a), 3)[0]
+        assert w3[want] == 0x3F00 and np.count_nonzero(w3 == 0x3F00) == 1, (word, bit)  # +0.5
+        assert np.all(np.delete(w3, want) == 0xBF00)                                   # -0.5
+
+
 def test_mwq_nesting_and_reductions():
     from workloads import quantize_mwq_rows
     rng = np.random.default_rng(31)
@@ -504,8 +529,9 @@ def test_mwq_nesting_and_reductions():
     assert np.array_equal(oracle.dequant_mwq(MwqWeights(m.q2, m.s2, m.z2, m.p3, zero, m.p4, zero), 4), w2)
     # the base is the INT4 rule on the same codes: spread each 2-bit field into a nibble
     N, K = w.shape
-    q = (m.q2.view(np.uint32)[:, :, None] >> (np.arange(16, dtype=np.uint32) * 2)) & 3
-    q = q.reshape(N, K)
+    fields = (m.q2.view(np.uint32)[:, :, None] >> (np.arange(16, dtype=np.uint32) * 2)) & 3
+    i16 = np.arange(16)
+    q = fields[:, :, 4 * (i16 % 4) + i16 // 4].reshape(N, K)   # K-index 4m+b in field 4b+m
     nib = np.bitwise_or.reduce(q.reshape(N, K // 8, 8) << (np.arange(8, dtype=np.uint32) * 4),
                                axis=2).astype(np.uint32).view(np.int32)
     assert np.array_equal(oracle.dequant_int4(nib, m.s2, m.z2), w2)
@@ -565,9 +591,11 @@ MUTANTS = [
      "    if (e >= 0) {\n      idx_out[a]"),
     ("mwq residual sign flipped", "        w = w + (bit ? m : -m);\n      }\n      if (bits == 4)",
      "        w = w + (bit ? -m : m);\n      }\n      if (bits == 4)"),
-    ("mwq second plane read from the first", "((uint32_t)p4[r * (K / 32) + kk / 32] >> (kk % 32))",
-     "((uint32_t)p3[r * (K / 32) + kk / 32] >> (kk % 32))"),
-    ("mwq 2-bit field order", "(w2 >> (2 * (kk % 16))) & 0x3u;", "(w2 >> (2 * (15 - kk % 16))) & 0x3u;"),
+    ("mwq second plane read from the first", "((uint32_t)p4[r * (K / 32) + kk / 32] >> mwq_bit(kk))",
+     "((uint32_t)p3[r * (K / 32) + kk / 32] >> mwq_bit(kk))"),
+    ("mwq 2-bit fields in natural order", "(w2 >> (2 * mwq_field(kk))) & 0x3u;",
+     "(w2 >> (2 * (kk % 16))) & 0x3u;"),
+    ("mwq residual bits in natural order", "  return 8 * (i % 4) + i / 4;", "  return i;"),
 ]
 
 

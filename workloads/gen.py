@@ -105,9 +105,10 @@ def quantize_mwq_rows(w_bits: np.ndarray):
     for b = 3, 4 the sign bit r_b of the remaining error (1 where it is >= 0) and
     a_b = fp16(mean |error|) -- the closed-form binary fit of the residual.  The
     errors are taken in float64 (this is the input quantiser, not the decode).
-    Returns q2 [N, K/16] int32 (2-bit field i of word j = K-index 16j+i), s2, z2,
-    a3, a4 fp16 bits [N, K/128], p3, p4 [N, K/32] int32 (bit i of word j =
-    K-index 32j+i)."""
+    Returns q2 [N, K/16] int32, s2, z2, a3, a4 fp16 bits [N, K/128], p3, p4
+    [N, K/32] int32, in the byte-transposed storage order of the nested format:
+    K-index 16j + 4m + b in 2-bit field 4b + m of q2 word j, K-index 32j + 4i + b
+    in bit 8b + i of plane word j."""
     N, K = w_bits.shape
     assert K % INT4_GROUP == 0
     G = K // INT4_GROUP
@@ -133,9 +134,11 @@ def quantize_mwq_rows(w_bits: np.ndarray):
         planes.append(r.reshape(N, K))
         mags.append(a16)
     qv = q.astype(np.uint32).reshape(N, K // 16, 16)
-    sh2 = (np.arange(16, dtype=np.uint32) * np.uint32(2))[None, None, :]
+    i16 = np.arange(16, dtype=np.uint32)
+    sh2 = (2 * (4 * (i16 % 4) + i16 // 4))[None, None, :]
     q2 = np.bitwise_or.reduce(qv << sh2, axis=2).astype(np.uint32).view(np.int32)
-    sh1 = np.arange(32, dtype=np.uint32)[None, None, :]
+    i32 = np.arange(32, dtype=np.uint32)
+    sh1 = (8 * (i32 % 4) + i32 // 4)[None, None, :]
 
     def pack_bits(r):
         return np.bitwise_or.reduce(r.reshape(N, K // 32, 32).astype(np.uint32) << sh1,
