@@ -211,6 +211,17 @@ def dequant_mwq(m, bits, group=INT4_GROUP):
     return out
 
 
+def mwq_groups(idx, bits, E):
+    """Rows grouped by (expert, bit width): group v = 3*e + (b - 2) for the width b
+    of each assignment (a width outside 2..4 is read as the nearest of them), then
+    the stable group-major permutation over 3E groups.  Returns (group ids [T][k],
+    counts [3E], offsets [3E+1], row_assign, assign_row)."""
+    b = np.clip(np.asarray(bits, np.int64), 2, 4)
+    vidx = (np.asarray(idx, np.int64) * 3 + (b - 2)).astype(np.int32)
+    counts, offsets, row_assign, assign_row, _ = permute(vidx, 3 * E)
+    return vidx, counts, offsets, row_assign, assign_row
+
+
 # --- the layer -----------------------------------------------------------
 
 def _h_round(wl):
@@ -287,9 +298,7 @@ def layer_forward(wl, logits=None, tokens=None, routing_only=False, replica=None
                    offsets=offsets2, row_assign=row_assign2, assign_row=assign_row2, lis=lis2)
         idx, row_assign, assign_row = idx2, row_assign2, assign_row2
     if cfg.mwq:
-        # rows grouped by (expert, bit width): virtual expert v = e*3 + (bits - 2)
-        vidx = (idx * 3 + (wl.bits - 2)).astype(np.int32)
-        vcounts, voffsets, vra, var_, _ = permute(vidx, 3 * E)
+        vidx, vcounts, voffsets, vra, var_ = mwq_groups(idx, wl.bits, E)
         out.update(mwq_idx=vidx, mwq_counts=vcounts, mwq_offsets=voffsets,
                    mwq_row_assign=vra, mwq_assign_row=var_)
         idx, row_assign, assign_row = vidx, vra, var_

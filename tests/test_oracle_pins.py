@@ -541,6 +541,34 @@ def test_mwq_nesting_and_reductions():
     assert errs[0] > errs[1] > errs[2]
 
 
+def test_mwq_groups_closed_forms():
+    """Grouping by (expert, width): an expert's groups add up to its count, rows of
+    one expert stay in flat order across its groups split by width, and widths
+    outside 2..4 read as the nearest of them."""
+    rng = np.random.default_rng(5)
+    T, E, k = 300, 7, 3
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    bits = rng.integers(2, 5, size=(T, k)).astype(np.int32)
+    vidx, c3, o3, ra3, ar3 = oracle.mwq_groups(idx, bits, E)
+    counts, offsets, ra, ar, _ = oracle.permute(idx, E)
+    assert np.array_equal(c3.reshape(E, 3).sum(axis=1), counts)
+    assert np.array_equal(o3[::3], offsets)
+    flat_idx, flat_b = idx.reshape(-1), bits.reshape(-1)
+    for e in range(E):
+        rows = ra3[o3[3 * e]:o3[3 * e + 3]]
+        assert np.all(flat_idx[rows] == e)
+        assert np.all(np.diff(flat_b[rows]) >= 0)              # widths ascending
+        for j in range(3):
+            grp = ra3[o3[3 * e + j]:o3[3 * e + j + 1]]
+            assert np.all(np.diff(grp) > 0) and np.all(flat_b[grp] == j + 2)
+    assert np.array_equal(ar3[ra3], np.arange(T * k))
+    wild = bits.copy()
+    wild[bits == 2] = rng.choice([-5, 0, 1, 2], size=int((bits == 2).sum()))
+    wild[bits == 4] = rng.choice([4, 5, 100], size=int((bits == 4).sum()))
+    for a, b in zip(oracle.mwq_groups(idx, wild, E), (vidx, c3, o3, ra3, ar3)):
+        assert np.array_equal(a, b)
+
+
 def test_mwq_layer_at_one_width_is_the_plain_layer():
     """All assignments at one width: rows group exactly as the plain routing and
     y equals the plain layer on the weights decoded at that width."""
