@@ -72,21 +72,57 @@ def work(cfg, counts):
                 gu_bytes=gu_bytes, dn_bytes=dn_bytes, active=active)
 
 
+def work_mwq(cfg, counts3):
+    """Algorithmic bytes of the nested-expert layer: per active expert, the 2-bit
+    codes with s2, z2, plus each residual plane (1 bit, fp16 magnitude per 128)
+    that one of its rows' widths needs; token rows and gate-scaled outputs as in
+    work()."""
+    T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F
+    c = np.asarray(counts3).reshape(E, 3)
+    gu_mats = 2 if cfg.act == "swiglu" else 1
+    per_w = np.zeros(E)
+    for e in range(E):
+        if c[e].sum() == 0:
+            continue
+        per_w[e] = 0.25 + 4.0 / 128                      # codes, s2, z2
+        if c[e, 1] + c[e, 2] > 0:
+            per_w[e] += 0.125 + 2.0 / 128                # plane 3, a3
+        if c[e, 2] > 0:
+            per_w[e] += 0.125 + 2.0 / 128                # plane 4, a4
+    wsum = float(per_w.sum())
+    gu_bytes = wsum * gu_mats * F * d + T * d * 2
+    dn_bytes = wsum * F * d + T * k * d * 4
+    widths = {str(b): int(c[:, b - 2].sum()) for b in (2, 3, 4)}
+    return dict(gu_bytes=gu_bytes, dn_bytes=dn_bytes, widths=widths,
+                active=int(np.count_nonzero(c.sum(axis=1))),
+                bytes=wsum * (gu_mats + 1) * F * d + E * d * 2 + T * d * 2 + T * d * 4)
+
+
 def run_gpu(name, steps, warmup):
     import torch
     import sparse_mixture_experts_wavefront_amd as moe
-    from sparse_mixture_experts_wavefront_amd.device_inputs import to_device
+    from sparse_mixture_experts_wavefront_amd.device_inputs import mwq_to_device, to_device
     from workloads import make_workload
     wl = make_workload(name)
     cfg = wl.cfg
     layer, x = to_device(wl)
-    runner = moe.LayerRunner(layer, cfg.T)
+    if cfg.mwq:
+        ex, widths = mwq_to_device(wl)
+        runner = moe.LayerRunner(layer, cfg.T, mwq=ex)
+
+        def call():
+            return runner(x, widths=widths)
+    else:
+        runner = moe.LayerRunner(layer, cfg.T)
+
+        def call():
+            return runner(x)
     for _ in range(warmup):
-        runner(x)
+        call()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        runner(x)
+        call()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1000.0 / steps
@@ -110,7 +146,7 @@ def run_gpu(name, steps, warmup):
     try:
         for evs in sets:
             B.moe_set_stage_events(C.cast(evs, C.POINTER(C.c_void_p)), 7)
-            runner(x)
+            call()
         B.moe_set_stage_events(None, 0)
         torch.cuda.synchronize()
         for n, evs in enumerate(sets):
@@ -129,6 +165,8 @@ def run_gpu(name, steps, warmup):
     st = per[:, :6].mean(axis=0)
     layer_ms = per[:, 6]
     w = work(cfg, counts)
+    if cfg.mwq:
+        w.update(work_mwq(cfg, runner.aux_t["mwq_counts"].cpu().numpy()))
     stages = dict(zip(["route_topk", "permute", "gate_up_gemm", "down_gemm", "shared_experts",
                        "combine"], [round(v * 1000.0, 2) for v in st]))
     timing = dict(event_ms_p10=round(float(np.percentile(layer_ms, 10)), 4),
@@ -208,6 +246,12 @@ def run_replica(name, steps, warmup):
 def roofline(cfg, r):
     w = r["work"]
     t = r["stages_us"]["gate_up_gemm"] * 1e-6
+    if cfg.mwq:
+        ach = w["gu_bytes"] / t / 1e9
+        return dict(kernel="mwq_stream gate/up (nested 2/3/4-bit table decode)", bound="hbm",
+                    achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                    per_launch=dict(bytes=w["gu_bytes"], us=round(t * 1e6, 2)))
     if cfg.T * cfg.k >= 1024:          # many rows per expert: the GEMM is MFMA-bound
         ach = w["gu_flops"] / t / 1e12
         return dict(kernel="grouped_gemm gate/up (SwiGLU epilogue)", bound="mfma",
@@ -259,6 +303,9 @@ def main():
     ap.add_argument("--replica", default="switch_bf16,deepseek_v2_lite_bf16",
                     help="comma-separated workloads also run with an INT4 replica of their "
                          "heaviest expert ('' for none)")
+    ap.add_argument("--mwq", default="mixtral_mwq_decode",
+                    help="comma-separated nested low-bit expert workloads reported in the "
+                         "same line ('' for none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (the known-size kernel "
                          "that scales the FETCH_SIZE/WRITE_SIZE counters)")
@@ -315,6 +362,19 @@ def main():
         del wl2
     if sec:
         out["secondary"] = sec
+    mw = []
+    for name in [s for s in args.mwq.split(",") if s]:
+        wl3, r3 = run_gpu(name, args.steps, args.warmup)
+        c3 = wl3.cfg
+        mw.append({"workload": name, "T": c3.T, "tokens_per_s": round(c3.T / (r3["ms"] / 1e3), 1),
+                   "ms_per_step": round(r3["ms"], 4), "lis": r3["lis"],
+                   "widths": r3["work"]["widths"], "active_experts": r3["work"]["active"],
+                   "layer_GBps": round(r3["work"]["bytes"] / (r3["ms"] * 1e-3) / 1e9, 1),
+                   "stages_us": r3["stages_us"], "timing": r3["timing"],
+                   "roofline": roofline(c3, r3)})
+        del wl3
+    if mw:
+        out["mwq"] = mw
     reps = [run_replica(n, args.steps, args.warmup) for n in args.replica.split(",") if n]
     if reps:
         out["replica"] = reps

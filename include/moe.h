@@ -240,6 +240,93 @@ moe_status moe_layer_forward_replica(const moe_layer_desc* L, const moe_replica*
                                      void* stream);
 moe_status moe_replica_workspace_size(const moe_layer_desc* L, int T, size_t* bytes);
 
+/* ---- Nested (matryoshka) low-bit experts ("D^2MoE: Dual Routing and Dynamic
+ * Scheduling for Efficient On-Device MoE-based LLM Serving" -- What carries the
+ * argument: one stored copy of each expert serves several bit widths, the
+ * lower-bit weights nested inside the higher-bit ones; Assumptions & free
+ * parameters: group size 128).  The pages fix the nesting, not the residual's
+ * form; this library's format: an asymmetric INT2 base per group of 128 along K,
+ * and for width 3 and 4 one binary residual plane each, a bit per weight and an
+ * fp16 magnitude per group.  At width b (2, 3 or 4) the weight is
+ *   w = fp32( fp32(q) - z2 ) * s2              (each fp32 operation rounded to
+ *   b >= 3: w = w + (r3 ? a3 : -a3)             nearest even, no fused
+ *   b == 4: w = w + (r4 ? a4 : -a4)             multiply-add)
+ *   W = bf16_RNE(w)
+ * Every (token, slot) assignment carries its own width, so an expert's rows are
+ * grouped by (expert, width): group v = 3*e + (width - 2), 3E groups. */
+
+/* One projection of all experts in the nested format, N output rows and K along
+ * the reduction (K a multiple of 128), every pointer non-NULL:
+ *   q2     int32 [E][N][K/16]: word j holds the 2-bit codes of K-indices
+ *          16j..16j+15, byte-transposed -- K-index 16j + 4m + b (m, b < 4) in
+ *          bits 8b+2m .. 8b+2m+1;
+ *   s2, z2 fp16 bits [E][N][K/128]: base scale and zero point;
+ *   p3, p4 int32 [E][N][K/32]: residual bits; word j covers K-indices
+ *          32j..32j+31, K-index 32j + 4i + b (i < 8, b < 4) in bit 8b + i;
+ *   a3, a4 fp16 bits [E][N][K/128]: residual magnitudes.
+ * The byte-transposed order puts, after one shift and mask, the codes of four
+ * consecutive weights in the four bytes of a word. */
+typedef struct {
+  const int32_t* q2;
+  const uint16_t* s2;
+  const uint16_t* z2;
+  const int32_t* p3;
+  const uint16_t* a3;
+  const int32_t* p4;
+  const uint16_t* a4;
+} moe_wmwq;
+
+/* Nested experts: gate and up with N = d_ff, K = d_model; down with N = d_model,
+ * K = d_ff.  ReLU experts use `up` as W_in and leave `gate` NULL. */
+typedef struct {
+  const moe_wmwq* gate;
+  const moe_wmwq* up;
+  const moe_wmwq* down;
+} moe_mwq_experts;
+
+/* Optional outputs of the (expert, width) grouping; every pointer may be NULL. */
+typedef struct {
+  int32_t* group_idx;  /* [T][k] 3*topk_idx + (width - 2) */
+  int32_t* counts;     /* [3E] rows per group */
+  int32_t* offsets;    /* [3E+1] exclusive prefix */
+  int32_t* row_assign; /* [T*k] row -> flat assignment, groups in order, a ascending */
+  int32_t* assign_row; /* [T*k] inverse */
+} moe_mwq_groups;
+
+/* Group the assignments by (expert, width): moe_permute of
+ * group_idx = 3*topk_idx + (clamp(widths, 2, 4) - 2) over 3E groups.
+ *   topk_idx, widths [T][k] int32 (a width outside 2..4 is clamped to it);
+ *   outputs as in moe_mwq_groups (counts and offsets required).
+ * 3E <= 64.  Workspace: moe_mwq_group_workspace_size(T, E, k) bytes. */
+moe_status moe_mwq_group(const int32_t* topk_idx, const int32_t* widths, int T, int E, int k,
+                         const moe_mwq_groups* out, void* ws, size_t ws_bytes, unsigned flags,
+                         void* stream);
+size_t moe_mwq_group_workspace_size(int T, int E, int k);
+
+/* Grouped expert FFN on nested weights, rows grouped by (expert, width) as
+ * moe_mwq_group leaves them: row r with offsets[3e+j] <= r < offsets[3e+j+1]
+ * runs expert e decoded at width 2 + j; otherwise as moe_grouped_ffn (bf16
+ * activations; y_rows [T*k][d] fp32, gate-scaled).  d_model and d_ff must be
+ * multiples of 512.  Workspace: moe_grouped_ffn_mwq_workspace_size(T, F, k). */
+moe_status moe_grouped_ffn_mwq(const void* x, int T, int d, int F, int E, int k, moe_act act,
+                               const moe_mwq_experts* w, const int32_t* offsets,
+                               const int32_t* row_assign, const float* topk_gate,
+                               float* y_rows, void* ws, size_t ws_bytes, unsigned flags,
+                               void* stream);
+size_t moe_grouped_ffn_mwq_workspace_size(int T, int F, int k);
+
+/* The layer with nested routed experts: route, permute (aux: the router's own
+ * routing over E experts, as moe_layer_forward), group by (expert, width)
+ * (groups, optional), nested FFN, shared experts (dense, from L->shared),
+ * combine.  L->routed is not read; bf16 activations only.  widths [T][k] int32
+ * gives the width of each assignment.
+ * Workspace: moe_mwq_workspace_size(L, T, &bytes). */
+moe_status moe_layer_forward_mwq(const moe_layer_desc* L, const moe_mwq_experts* W,
+                                 const int32_t* widths, const void* x, int T, void* y,
+                                 moe_dtype ydt, moe_aux* aux, const moe_mwq_groups* groups,
+                                 void* ws, size_t ws_bytes, unsigned flags, void* stream);
+moe_status moe_mwq_workspace_size(const moe_layer_desc* L, int T, size_t* bytes);
+
 /* Instrumentation (not part of the layer's arithmetic).  While set, every
  * moe_layer_forward call made on this thread records events[i] (hipEvent_t
  * handles created by the caller) on its stream at the stage boundaries:

@@ -23,7 +23,9 @@ MOE_F_LOGITS_GIVEN, MOE_F_VALIDATE_ONLY, MOE_F_NONDETERMINISTIC_COMBINE = 1, 2, 
 EXPORTED = ("moe_route_topk", "moe_permute", "moe_permute_workspace_size", "moe_grouped_ffn",
             "moe_grouped_ffn_workspace_size", "moe_combine", "moe_layer_forward",
             "moe_workspace_size", "moe_replica_split", "moe_layer_forward_replica",
-            "moe_replica_workspace_size", "moe_set_stage_events", "moe_status_string",
+            "moe_replica_workspace_size", "moe_mwq_group", "moe_mwq_group_workspace_size",
+            "moe_grouped_ffn_mwq", "moe_grouped_ffn_mwq_workspace_size", "moe_layer_forward_mwq",
+            "moe_mwq_workspace_size", "moe_set_stage_events", "moe_status_string",
             "moe_last_error")
 
 
@@ -57,6 +59,20 @@ class LayerDesc(C.Structure):
 class Replica(C.Structure):
     _fields_ = [("expert", C.c_int), ("q_gate", C.POINTER(W4)), ("q_up", C.POINTER(W4)),
                 ("q_down", C.POINTER(W4))]
+
+
+class WMwq(C.Structure):
+    _fields_ = [("q2", C.c_void_p), ("s2", C.c_void_p), ("z2", C.c_void_p), ("p3", C.c_void_p),
+                ("a3", C.c_void_p), ("p4", C.c_void_p), ("a4", C.c_void_p)]
+
+
+class MwqExperts(C.Structure):
+    _fields_ = [("gate", C.POINTER(WMwq)), ("up", C.POINTER(WMwq)), ("down", C.POINTER(WMwq))]
+
+
+class MwqGroups(C.Structure):
+    _fields_ = [("group_idx", C.c_void_p), ("counts", C.c_void_p), ("offsets", C.c_void_p),
+                ("row_assign", C.c_void_p), ("assign_row", C.c_void_p)]
 
 
 class Aux(C.Structure):
@@ -94,6 +110,17 @@ def lib():
             L.moe_layer_forward_replica.argtypes = [C.POINTER(LayerDesc), C.POINTER(Replica), p, i,
                                                     p, i, C.POINTER(Aux), p, p, sz, u, p]
             L.moe_replica_workspace_size.argtypes = [C.POINTER(LayerDesc), i, C.POINTER(sz)]
+            L.moe_mwq_group.argtypes = [p, p, i, i, i, C.POINTER(MwqGroups), p, sz, u, p]
+            L.moe_mwq_group_workspace_size.argtypes = [i, i, i]
+            L.moe_mwq_group_workspace_size.restype = sz
+            L.moe_grouped_ffn_mwq.argtypes = [p, i, i, i, i, i, i, C.POINTER(MwqExperts), p, p, p,
+                                              p, p, sz, u, p]
+            L.moe_grouped_ffn_mwq_workspace_size.argtypes = [i, i, i]
+            L.moe_grouped_ffn_mwq_workspace_size.restype = sz
+            L.moe_layer_forward_mwq.argtypes = [C.POINTER(LayerDesc), C.POINTER(MwqExperts), p, p,
+                                                i, p, i, C.POINTER(Aux), C.POINTER(MwqGroups), p,
+                                                sz, u, p]
+            L.moe_mwq_workspace_size.argtypes = [C.POINTER(LayerDesc), i, C.POINTER(sz)]
             L.moe_set_stage_events.argtypes = [C.POINTER(C.c_void_p), i]
             L.moe_set_stage_events.restype = C.c_int
             L.moe_status_string.argtypes = [i]
@@ -102,7 +129,9 @@ def lib():
             L.moe_last_error.restype = C.c_char_p
             for f in ("moe_route_topk", "moe_permute", "moe_grouped_ffn", "moe_combine",
                       "moe_layer_forward", "moe_workspace_size", "moe_replica_split",
-                      "moe_layer_forward_replica", "moe_replica_workspace_size"):
+                      "moe_layer_forward_replica", "moe_replica_workspace_size",
+                      "moe_mwq_group", "moe_grouped_ffn_mwq", "moe_layer_forward_mwq",
+                      "moe_mwq_workspace_size"):
                 getattr(L, f).restype = C.c_int
             _lib = L
     return _lib

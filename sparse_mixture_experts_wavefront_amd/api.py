@@ -136,6 +136,41 @@ class MoeReplica:
         return r
 
 
+@dataclass
+class MwqProj:
+    """One projection's nested 2/3/4-bit weights (all experts), storage order of moe.h."""
+    q2: torch.Tensor      # int32 [E][N][K/16]
+    s2: torch.Tensor      # fp16 [E][N][K/128]
+    z2: torch.Tensor
+    p3: torch.Tensor      # int32 [E][N][K/32]
+    a3: torch.Tensor      # fp16 [E][N][K/128]
+    p4: torch.Tensor
+    a4: torch.Tensor
+
+    def struct(self):
+        return B.WMwq(*[_p(getattr(self, n)) for n in ("q2", "s2", "z2", "p3", "a3", "p4", "a4")])
+
+
+@dataclass
+class MwqExperts:
+    """Nested experts: gate/up with N = d_ff, down with N = d_model (gate None for ReLU)."""
+    up: MwqProj
+    down: MwqProj
+    gate: Optional[MwqProj] = None
+    _keep: list = field(default_factory=list, repr=False)
+
+    def struct(self) -> B.MwqExperts:
+        m = B.MwqExperts()
+        self._keep = []
+        for name in ("gate", "up", "down"):
+            q = getattr(self, name)
+            if q is not None:
+                st = q.struct()
+                self._keep.append(st)
+                setattr(m, name, C.pointer(st))
+        return m
+
+
 # ---- the five calls -----------------------------------------------------------
 
 def route_topk(x, w_router, b_router, k, logits=None, logits_given=False, flags=0):
@@ -204,22 +239,27 @@ class LayerRunner:
     """Holds the descriptor, workspace and aux buffers for repeated layer calls.
 
     With ``replica`` the layer runs moe_layer_forward_replica: aux then holds
-    the split routing over E+1 slots and ``lis_base`` the router's own LIS."""
+    the split routing over E+1 slots and ``lis_base`` the router's own LIS.
+    With ``mwq`` (nested experts) it runs moe_layer_forward_mwq; each call then
+    takes the widths [T][k] and aux also holds the (expert, width) grouping
+    (mwq_idx, mwq_counts, mwq_offsets, mwq_row_assign, mwq_assign_row)."""
 
     def __init__(self, layer: MoeLayer, T: int, out_dtype=torch.float32, want_aux=True,
-                 replica: Optional[MoeReplica] = None):
+                 replica: Optional[MoeReplica] = None, mwq: Optional[MwqExperts] = None):
         self.layer = layer
         self.T = T
         dev = layer.w_router.device
         self.desc = layer.desc()
         self.replica = replica
         self.rep = None if replica is None else replica.struct()
-        if replica is None:
+        self.mwq = mwq
+        self.mwq_st = None if mwq is None else mwq.struct()
+        if replica is None and mwq is None:
             self.ws = _ws(layer.workspace_size(T), dev)
         else:
             n = C.c_size_t(0)
-            B.check(B.lib().moe_replica_workspace_size(C.byref(self.desc), T, C.byref(n)),
-                    "moe_replica_workspace_size")
+            fn = "moe_replica_workspace_size" if replica is not None else "moe_mwq_workspace_size"
+            B.check(getattr(B.lib(), fn)(C.byref(self.desc), T, C.byref(n)), fn)
             self.ws = _ws(n.value, dev)
         self.lis_base = torch.empty(1, dtype=torch.float64, device=dev)
         E, k = layer.n_experts, layer.top_k
@@ -238,10 +278,29 @@ class LayerRunner:
                 assign_row=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
                 lis=torch.empty(1, dtype=torch.float64, device=dev))
             self.aux = B.Aux(**{n: _p(t) for n, t in self.aux_t.items()})
+        self.groups = None
+        if want_aux and mwq is not None:
+            g = dict(mwq_idx=torch.empty(T, k, dtype=torch.int32, device=dev),
+                     mwq_counts=torch.empty(3 * E, dtype=torch.int32, device=dev),
+                     mwq_offsets=torch.empty(3 * E + 1, dtype=torch.int32, device=dev),
+                     mwq_row_assign=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
+                     mwq_assign_row=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev))
+            self.aux_t.update(g)
+            self.groups = B.MwqGroups(*[_p(g[n]) for n in ("mwq_idx", "mwq_counts", "mwq_offsets",
+                                                           "mwq_row_assign", "mwq_assign_row")])
 
-    def __call__(self, x, flags=0):
+    def __call__(self, x, flags=0, widths=None):
         aux = C.byref(self.aux) if self.aux is not None else None
-        if self.rep is None:
+        if self.mwq is not None:
+            if widths is None:
+                raise ValueError("a layer with nested experts needs the widths [T][k]")
+            groups = C.byref(self.groups) if self.groups is not None else None
+            B.check(B.lib().moe_layer_forward_mwq(C.byref(self.desc), C.byref(self.mwq_st),
+                                                  _p(widths), _p(x), self.T, _p(self.y),
+                                                  _dt(self.y), aux, groups, _p(self.ws),
+                                                  self.ws.numel(), flags, _stream()),
+                    "moe_layer_forward_mwq")
+        elif self.rep is None:
             B.check(B.lib().moe_layer_forward(C.byref(self.desc), _p(x), self.T, _p(self.y),
                                               _dt(self.y), aux, _p(self.ws), self.ws.numel(),
                                               flags, _stream()),
@@ -256,14 +315,17 @@ class LayerRunner:
 
 
 def layer_forward(layer: MoeLayer, x, out_dtype=torch.float32, flags=0, logits=None,
-                  replica: Optional[MoeReplica] = None):
+                  replica: Optional[MoeReplica] = None, mwq: Optional[MwqExperts] = None,
+                  widths=None):
     """One layer call; returns (y, aux dict of device tensors).  With ``replica``
-    aux describes the split routing and aux["lis_base"] the router's own LIS."""
-    r = LayerRunner(layer, x.shape[0], out_dtype, replica=replica)
+    aux describes the split routing and aux["lis_base"] the router's own LIS;
+    with ``mwq`` (and ``widths`` [T][k] int32) the routed experts are nested
+    low-bit ones and aux adds the (expert, width) grouping."""
+    r = LayerRunner(layer, x.shape[0], out_dtype, replica=replica, mwq=mwq)
     if logits is not None:
         r.aux_t["logits"].copy_(logits)
         flags |= B.MOE_F_LOGITS_GIVEN
-    y = r(x, flags)
+    y = r(x, flags, widths=widths)
     if replica is not None:
         r.aux_t["lis_base"] = r.lis_base
     return y, r.aux_t
@@ -285,3 +347,39 @@ def replica_split(idx, counts, offsets, assign_row, E, heavy, flags=0):
                                       _p(out["assign_row"]), _p(out["lis"]), flags, _stream()),
             "moe_replica_split")
     return out
+
+
+def mwq_group(idx, widths, E, flags=0):
+    """(expert, width) grouping of nested experts (see moe_mwq_group); returns a dict
+    with group_idx, counts [3E], offsets [3E+1], row_assign, assign_row."""
+    T, k = idx.shape
+    dev = idx.device
+    out = dict(group_idx=torch.empty_like(idx),
+               counts=torch.empty(3 * E, dtype=torch.int32, device=dev),
+               offsets=torch.empty(3 * E + 1, dtype=torch.int32, device=dev),
+               row_assign=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
+               assign_row=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev))
+    g = B.MwqGroups(*[_p(out[n]) for n in ("group_idx", "counts", "offsets", "row_assign",
+                                            "assign_row")])
+    ws = _ws(B.lib().moe_mwq_group_workspace_size(T, E, k), dev)
+    B.check(B.lib().moe_mwq_group(_p(idx), _p(widths), T, E, k, C.byref(g), _p(ws), ws.numel(),
+                                  flags, _stream()),
+            "moe_mwq_group")
+    return out
+
+
+def grouped_ffn_mwq(x, E, k, act, experts: MwqExperts, offsets, row_assign, topk_gate=None,
+                    flags=0):
+    """Gate-scaled rows y_rows [T*k][d] fp32 of nested experts, rows grouped by
+    (expert, width) as mwq_group leaves them."""
+    T, d = x.shape
+    F = experts.up.q2.shape[-2]
+    a = B.MOE_ACT_SWIGLU if act == "swiglu" else B.MOE_ACT_RELU
+    st = experts.struct()
+    y_rows = torch.empty(max(T * k, 1), d, dtype=torch.float32, device=x.device)
+    ws = _ws(B.lib().moe_grouped_ffn_mwq_workspace_size(T, F, k), x.device)
+    B.check(B.lib().moe_grouped_ffn_mwq(_p(x), T, d, F, E, k, a, C.byref(st), _p(offsets),
+                                        _p(row_assign), _p(topk_gate), _p(y_rows), _p(ws),
+                                        ws.numel(), flags, _stream()),
+            "moe_grouped_ffn_mwq")
+    return y_rows[:T * k]

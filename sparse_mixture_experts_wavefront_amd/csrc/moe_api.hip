@@ -172,13 +172,16 @@ LayerWs carve_layer(const moe_layer_desc* L, int T, void* ws, bool replica = fal
   return w;
 }
 
-moe_status check_layer(const moe_layer_desc* L, int T, unsigned flags) {
+// routed = false: the routed experts come from elsewhere (nested weights)
+moe_status check_layer(const moe_layer_desc* L, int T, unsigned flags, bool routed = true) {
   REQUIRE(L, "layer descriptor must not be NULL");
   moe_status s = check_common(T, L->n_experts, L->top_k, flags);
   if (s != MOE_OK) return s;
   REQUIRE(valid_dtype(L->act_dtype), "unknown activation dtype %d", (int)L->act_dtype);
-  s = check_experts(&L->routed, L->act_dtype, L->d_model, L->d_ff, L->act, "routed");
-  if (s != MOE_OK) return s;
+  if (routed) {
+    s = check_experts(&L->routed, L->act_dtype, L->d_model, L->d_ff, L->act, "routed");
+    if (s != MOE_OK) return s;
+  }
   if (!(flags & MOE_F_LOGITS_GIVEN)) REQUIRE_PTR(L->w_router, "w_router");
   OPT_PTR(L->b_router, "b_router");
   REQUIRE(L->n_shared >= 0, "n_shared must be >= 0");
@@ -516,6 +519,263 @@ moe_status moe_replica_split(const int32_t* topk_idx, const int32_t* counts,
                                          idx_out, counts_out, offsets_out, row_assign_out,
                                          assign_row_out, lis_out, (hipStream_t)stream),
                     "moe_replica_split launch");
+}
+
+}  // extern "C"
+
+// ---- nested (matryoshka) low-bit experts -----------------------------------
+
+namespace {
+
+moe_status check_mwq_experts(const moe_mwq_experts* w, int T, int d, int F, int k, moe_act act) {
+  REQUIRE(w, "nested experts must not be NULL");
+  REQUIRE(act == MOE_ACT_SWIGLU || act == MOE_ACT_RELU, "unknown activation %d", (int)act);
+  REQUIRE(d >= 128 && d % 128 == 0 && F >= 128 && F % 128 == 0,
+          "nested experts need d_model and d_ff positive multiples of 128 (got %d, %d)", d, F);
+  REQUIRE(w->up && w->down, "nested experts: up and down must not be NULL");
+  if (act == MOE_ACT_SWIGLU) REQUIRE(w->gate, "nested experts: gate must not be NULL for SwiGLU");
+  const moe_wmwq* ms[3] = {act == MOE_ACT_SWIGLU ? w->gate : nullptr, w->up, w->down};
+  for (int i = 0; i < 3; ++i) {
+    const moe_wmwq* m = ms[i];
+    if (!m) continue;
+    REQUIRE_PTR(m->q2, "nested q2");
+    REQUIRE_PTR(m->p3, "nested p3");
+    REQUIRE_PTR(m->p4, "nested p4");
+    REQUIRE(m->s2 && m->z2 && m->a3 && m->a4, "nested s2/z2/a3/a4 must not be NULL");
+    REQUIRE(aligned(m->s2, 2) && aligned(m->z2, 2) && aligned(m->a3, 2) && aligned(m->a4, 2),
+            "nested s2/z2/a3/a4 misaligned");
+  }
+  if (const char* why = mwq_ffn_unsupported(T, d, F, k)) return fail(MOE_ERR_UNSUPPORTED, "%s", why);
+  return MOE_OK;
+}
+
+size_t mwq_group_ws_bytes(int T, int E, int k) {
+  return align_up((size_t)T * k * 4) + align_up(permute_ws_bytes(T, 3 * E, k));
+}
+
+struct MwqLayerWs {
+  LayerWs base;
+  int32_t *gidx, *counts3, *offsets3, *row_assign3, *assign_row3;
+  void* gperm_ws;
+  size_t total;
+};
+
+MwqLayerWs carve_mwq_layer(const moe_layer_desc* L, int T, void* ws) {
+  // the router's own routing, H, y_rows and the shared experts as in the plain
+  // layer (one K slice), then the (expert, width) grouping
+  const int E = L->n_experts, k = L->top_k, d = L->d_model, F = L->d_ff;
+  const size_t n = (size_t)T * k;
+  Carver c(ws);
+  MwqLayerWs m;
+  LayerWs& w = m.base;
+  w.logits = (float*)c.take((size_t)T * E * 4);
+  w.idx = (int32_t*)c.take(n * 4);
+  w.gates = (float*)c.take(n * 4);
+  w.counts = (int32_t*)c.take((size_t)E * 4);
+  w.offsets = (int32_t*)c.take((size_t)(E + 1) * 4);
+  w.row_assign = (int32_t*)c.take(n * 4);
+  w.assign_row = (int32_t*)c.take(n * 4);
+  w.lis = (double*)c.take(8);
+  w.perm_ws = c.take(permute_ws_bytes(T, E, k));
+  w.H = c.take(n * F * 2);
+  w.down_splits = 1;
+  w.y_rows = (float*)c.take(n * d * 4);
+  const int Fs = L->n_shared * L->d_ff_shared;
+  w.Hs = L->n_shared ? c.take((size_t)T * Fs * 2) : nullptr;
+  w.y_shared = L->n_shared ? (float*)c.take((size_t)T * d * 4) : nullptr;
+  w.counts2 = w.offsets2 = w.row_assign2 = w.assign_row2 = nullptr;
+  w.lis2 = nullptr;
+  m.gidx = (int32_t*)c.take(n * 4);
+  m.counts3 = (int32_t*)c.take((size_t)3 * E * 4);
+  m.offsets3 = (int32_t*)c.take((size_t)(3 * E + 1) * 4);
+  m.row_assign3 = (int32_t*)c.take(n * 4);
+  m.assign_row3 = (int32_t*)c.take(n * 4);
+  m.gperm_ws = c.take(permute_ws_bytes(T, 3 * E, k));
+  m.total = w.total = c.off;
+  return m;
+}
+
+moe_status check_mwq_groups(const moe_mwq_groups* g) {
+  if (!g) return MOE_OK;
+  OPT_PTR(g->group_idx, "groups.group_idx");
+  OPT_PTR(g->counts, "groups.counts");
+  OPT_PTR(g->offsets, "groups.offsets");
+  OPT_PTR(g->row_assign, "groups.row_assign");
+  OPT_PTR(g->assign_row, "groups.assign_row");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_mwq_group_workspace_size(int T, int E, int k) {
+  if (T < 0 || E < 1 || k < 1) return 0;
+  return mwq_group_ws_bytes(T, E, k);
+}
+
+moe_status moe_mwq_group(const int32_t* topk_idx, const int32_t* widths, int T, int E, int k,
+                         const moe_mwq_groups* out, void* ws, size_t ws_bytes, unsigned flags,
+                         void* stream) {
+  moe_status s = check_common(T, E, k, flags);
+  if (s != MOE_OK) return s;
+  if (3 * E > kMaxExperts)
+    return fail(MOE_ERR_UNSUPPORTED, "(expert, width) groups need 3E <= %d (E = %d)", kMaxExperts, E);
+  REQUIRE(out, "out must not be NULL");
+  s = check_mwq_groups(out);
+  if (s != MOE_OK) return s;
+  REQUIRE(out->counts && out->offsets, "out->counts and out->offsets must not be NULL");
+  if (T > 0) {
+    REQUIRE_PTR(topk_idx, "topk_idx");
+    REQUIRE_PTR(widths, "widths");
+  }
+  const size_t need = mwq_group_ws_bytes(T, E, k);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_mwq_group needs %zu workspace bytes (got %zu)", need,
+                ws ? ws_bytes : (size_t)0);
+  REQUIRE(aligned(ws, 256), "ws must be 256-byte aligned");
+  if (flags & MOE_F_VALIDATE_ONLY) return ok();
+  hipStream_t st = (hipStream_t)stream;
+  const int n = T * k;
+  int32_t* gidx = out->group_idx ? out->group_idx : (int32_t*)ws;
+  void* pws = (char*)ws + align_up((size_t)n * 4);
+  hipError_t e = launch_mwq_group_ids(topk_idx, widths, n, gidx, st);
+  if (e != hipSuccess) return hip_status(e, "mwq group ids");
+  return hip_status(launch_permute(gidx, T, 3 * E, k, out->counts, out->offsets, out->row_assign,
+                                   out->assign_row, nullptr, pws, st),
+                    "mwq group permute");
+}
+
+size_t moe_grouped_ffn_mwq_workspace_size(int T, int F, int k) {
+  if (T < 0 || F < 0 || k < 1) return 0;
+  return (size_t)T * k * F * 2;
+}
+
+moe_status moe_grouped_ffn_mwq(const void* x, int T, int d, int F, int E, int k, moe_act act,
+                               const moe_mwq_experts* w, const int32_t* offsets,
+                               const int32_t* row_assign, const float* topk_gate,
+                               float* y_rows, void* ws, size_t ws_bytes, unsigned flags,
+                               void* stream) {
+  moe_status s = check_common(T, E, k, flags);
+  if (s != MOE_OK) return s;
+  if (3 * E > kMaxExperts)
+    return fail(MOE_ERR_UNSUPPORTED, "(expert, width) groups need 3E <= %d (E = %d)", kMaxExperts, E);
+  s = check_mwq_experts(w, T, d, F, k, act);
+  if (s != MOE_OK) return s;
+  REQUIRE_PTR(offsets, "offsets");
+  REQUIRE_PTR(row_assign, "row_assign");
+  if (T > 0) REQUIRE_PTR(x, "x");
+  REQUIRE_PTR(y_rows, "y_rows");
+  OPT_PTR(topk_gate, "topk_gate");
+  const size_t need = moe_grouped_ffn_mwq_workspace_size(T, F, k);
+  if (need && (!ws || ws_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "moe_grouped_ffn_mwq needs %zu workspace bytes (got %zu)",
+                need, ws ? ws_bytes : (size_t)0);
+  OPT_PTR(ws, "ws");
+  if (flags & MOE_F_VALIDATE_ONLY) return ok();
+  if (T == 0) return ok();
+  MwqProblem p{};
+  p.T = T; p.d = d; p.F = F; p.E = E; p.k = k; p.act = act; p.x = x; p.w = w;
+  p.offsets = offsets; p.row_assign = row_assign; p.gate = topk_gate; p.y_rows = y_rows;
+  p.H = ws; p.rows = T * k;
+  return hip_status(launch_mwq_ffn(p, (hipStream_t)stream), "moe_grouped_ffn_mwq launch");
+}
+
+moe_status moe_mwq_workspace_size(const moe_layer_desc* L, int T, size_t* bytes) {
+  REQUIRE(bytes, "bytes must not be NULL");
+  moe_status s = check_layer(L, T, 0, false);
+  if (s != MOE_OK) return s;
+  *bytes = carve_mwq_layer(L, T, nullptr).total;
+  return ok();
+}
+
+moe_status moe_layer_forward_mwq(const moe_layer_desc* L, const moe_mwq_experts* W,
+                                 const int32_t* widths, const void* x, int T, void* y,
+                                 moe_dtype ydt, moe_aux* aux, const moe_mwq_groups* groups,
+                                 void* ws, size_t ws_bytes, unsigned flags, void* stream) {
+  moe_status s = check_layer(L, T, flags, false);
+  if (s != MOE_OK) return s;
+  const int E = L->n_experts, k = L->top_k, d = L->d_model, F = L->d_ff;
+  if (L->act_dtype != MOE_DT_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "nested experts need bf16 activations");
+  if (3 * E > kMaxExperts)
+    return fail(MOE_ERR_UNSUPPORTED, "(expert, width) groups need 3E <= %d (E = %d)", kMaxExperts, E);
+  s = check_mwq_experts(W, T, d, F, k, L->act);
+  if (s != MOE_OK) return s;
+  s = check_mwq_groups(groups);
+  if (s != MOE_OK) return s;
+  REQUIRE(valid_dtype(ydt), "unknown output dtype %d", (int)ydt);
+  if (T > 0) {
+    REQUIRE_PTR(x, "x");
+    REQUIRE_PTR(y, "y");
+    REQUIRE_PTR(widths, "widths");
+  }
+  if (aux) {
+    OPT_PTR(aux->logits, "aux.logits"); OPT_PTR(aux->idx, "aux.idx");
+    OPT_PTR(aux->gates, "aux.gates"); OPT_PTR(aux->counts, "aux.counts");
+    OPT_PTR(aux->offsets, "aux.offsets"); OPT_PTR(aux->row_assign, "aux.row_assign");
+    OPT_PTR(aux->assign_row, "aux.assign_row"); OPT_PTR(aux->lis, "aux.lis");
+  }
+  if ((flags & MOE_F_LOGITS_GIVEN) && !(aux && aux->logits))
+    return fail(MOE_ERR_INVALID_ARG, "MOE_F_LOGITS_GIVEN needs aux->logits");
+  const size_t need = carve_mwq_layer(L, T, nullptr).total;
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "the layer needs %zu workspace bytes (got %zu)", need,
+                ws ? ws_bytes : (size_t)0);
+  REQUIRE(aligned(ws, 256), "ws must be 256-byte aligned");
+  if (flags & MOE_F_VALIDATE_ONLY) return ok();
+  if (T == 0) return ok();
+
+  hipStream_t st = (hipStream_t)stream;
+  MwqLayerWs m = carve_mwq_layer(L, T, ws);
+  LayerWs& w = m.base;
+  float* logits = (aux && aux->logits) ? aux->logits : w.logits;
+  int32_t* idx = (aux && aux->idx) ? aux->idx : w.idx;
+  float* gates = (aux && aux->gates) ? aux->gates : w.gates;
+  int32_t* counts = (aux && aux->counts) ? aux->counts : w.counts;
+  int32_t* offsets = (aux && aux->offsets) ? aux->offsets : w.offsets;
+  int32_t* row_assign = (aux && aux->row_assign) ? aux->row_assign : w.row_assign;
+  int32_t* assign_row = (aux && aux->assign_row) ? aux->assign_row : w.assign_row;
+  double* lis = (aux && aux->lis) ? aux->lis : w.lis;
+  int32_t* gidx = (groups && groups->group_idx) ? groups->group_idx : m.gidx;
+  int32_t* counts3 = (groups && groups->counts) ? groups->counts : m.counts3;
+  int32_t* offsets3 = (groups && groups->offsets) ? groups->offsets : m.offsets3;
+  int32_t* row_assign3 = (groups && groups->row_assign) ? groups->row_assign : m.row_assign3;
+  int32_t* assign_row3 = (groups && groups->assign_row) ? groups->assign_row : m.assign_row3;
+
+  stage(0, st);
+  hipError_t e = launch_route_topk(x, L->act_dtype, L->w_router, L->b_router, T, d, E, k, logits,
+                                   idx, gates, (flags & MOE_F_LOGITS_GIVEN) != 0, st);
+  if (e != hipSuccess) return hip_status(e, "route_topk");
+  stage(1, st);
+  e = launch_permute(idx, T, E, k, counts, offsets, row_assign, assign_row, lis, w.perm_ws, st);
+  if (e != hipSuccess) return hip_status(e, "permute");
+  e = launch_mwq_group_ids(idx, widths, T * k, gidx, st);
+  if (e != hipSuccess) return hip_status(e, "mwq group ids");
+  e = launch_permute(gidx, T, 3 * E, k, counts3, offsets3, row_assign3, assign_row3, nullptr,
+                     m.gperm_ws, st);
+  if (e != hipSuccess) return hip_status(e, "mwq group permute");
+  stage(2, st);
+  MwqProblem p{};
+  p.T = T; p.d = d; p.F = F; p.E = E; p.k = k; p.act = L->act; p.x = x; p.w = W;
+  p.offsets = offsets3; p.row_assign = row_assign3; p.gate = gates; p.y_rows = w.y_rows;
+  p.H = w.H; p.rows = T * k;
+  e = launch_mwq_ffn(p, st, g_stage_on ? g_stage_ev[3] : nullptr);
+  if (e != hipSuccess) return hip_status(e, "mwq ffn");
+  stage(4, st);
+  if (L->n_shared > 0) {
+    FfnProblem q{};
+    q.T = T; q.d = d; q.F = L->n_shared * L->d_ff_shared; q.E = 1; q.k = 1;
+    q.act = MOE_ACT_SWIGLU; q.dt = L->act_dtype; q.x = x; q.w = &L->shared;
+    q.offsets = nullptr; q.row_assign = nullptr; q.gate = nullptr;
+    q.y_rows = w.y_shared; q.H = w.Hs; q.rows = T;
+    e = launch_grouped_ffn(q, st);
+    if (e != hipSuccess) return hip_status(e, "shared experts");
+  }
+  stage(5, st);
+  e = launch_combine(w.y_rows, assign_row3, T, k, d, w.y_shared, y, ydt, st);
+  stage(6, st);
+  return hip_status(e, "combine");
 }
 
 }  // extern "C"

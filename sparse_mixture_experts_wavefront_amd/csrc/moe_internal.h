@@ -28,6 +28,15 @@ __device__ __forceinline__ u16 f32_to_bf16(float f) {  // RNE (v_cvt_pk_bf16_f32
   return __builtin_bit_cast(u16, (__bf16)f);
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ float h2f(u16 h) { return (float)__builtin_bit_cast(_Float16, h); }
+// two fp32 -> packed bf16 pair (a in the low half), round to nearest even
+// (one v_cvt_pk_bf16_f32)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -86,6 +95,28 @@ hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid
 // launch_grouped_ffn.
 bool stream_ffn_applies(const FfnProblem& p);
 hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid = nullptr);
+
+// (expert, width) group of each assignment: 3 * idx + clamp(width, 2, 4) - 2.
+hipError_t launch_mwq_group_ids(const int32_t* idx, const int32_t* widths, int n, int32_t* out,
+                                hipStream_t s);
+
+// Grouped FFN on nested 2/3/4-bit weights; rows grouped by (expert, width)
+// (offsets [3E+1]).  Requires bf16 activations and d, F multiples of 512.
+struct MwqProblem {
+  int T, d, F, E, k;
+  moe_act act;
+  const void* x;                 // [T][d] bf16
+  const moe_mwq_experts* w;
+  const int32_t* offsets;        // [3E+1]
+  const int32_t* row_assign;     // row -> flat assignment
+  const float* gate;             // gate per flat assignment, or NULL (1)
+  float* y_rows;                 // [rows][d]
+  void* H;                       // [rows][F] bf16 scratch
+  int rows;                      // T * k
+};
+// NULL if the shapes are supported, else the reason.
+const char* mwq_ffn_unsupported(int T, int d, int F, int k);
+hipError_t launch_mwq_ffn(const MwqProblem& p, hipStream_t s, hipEvent_t mid = nullptr);
 
 // y[t] = sum over slots j, then over K slices s, of y_rows[s * split_stride +
 // assign_row[t*k+j] * d], plus y_shared[t]; fixed order, so deterministic.

@@ -279,4 +279,25 @@ hipError_t launch_replica_remap(const int32_t* idx, const int32_t* counts, const
   return hipGetLastError();
 }
 
+// ---- (expert, width) groups of nested low-bit experts ----------------------
+// "D^2MoE: Dual Routing and Dynamic Scheduling for Efficient On-Device
+// MoE-based LLM Serving" -- What carries the argument: each assignment carries a
+// bit width, and the rows of one expert are run per width.  Group id
+// 3*e + (width - 2); the permutation over the 3E ids then orders rows by expert,
+// by width inside an expert, by flat assignment inside a group.
+__global__ __launch_bounds__(256) void mwq_group_ids_kernel(const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ widths,
+                                                            int n, int32_t* __restrict__ out) {
+  const int a = blockIdx.x * 256 + threadIdx.x;
+  if (a < n) out[a] = 3 * idx[a] + min(max(widths[a], 2), 4) - 2;
+}
+
+hipError_t launch_mwq_group_ids(const int32_t* idx, const int32_t* widths, int n, int32_t* out,
+                                hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(mwq_group_ids_kernel, dim3((n + 255) / 256), dim3(256), 0, s, idx, widths, n,
+                     out);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -70,8 +70,6 @@ struct StreamArgs {
   uint32_t xbytes;         // bytes of X (register-direct kernel: buffer size)
 };
 
-__device__ __forceinline__ float h2f(u16 h) { return (float)__builtin_bit_cast(_Float16, h); }
-
 // fp32(q) - z is exact for all q in 0..15 when z == 0 or |z| >= 2^-10 (finite).
 __device__ __forceinline__ bool zero_point_fma_exact(u16 z) {
   const unsigned ex = (z >> 10) & 0x1f;
@@ -83,13 +81,6 @@ __device__ __forceinline__ float ub0(uint32_t v) { float f; asm("v_cvt_f32_ubyte
 __device__ __forceinline__ float ub1(uint32_t v) { float f; asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(v)); return f; }
 __device__ __forceinline__ float ub2(uint32_t v) { float f; asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(v)); return f; }
 __device__ __forceinline__ float ub3(uint32_t v) { float f; asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(v)); return f; }
-// two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
-  const f32x2_t v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
 
 // 8 nibbles (low first) -> 8 bf16, fused form: fma(q, s, nzs), nzs = -(z*s) exact.
 __device__ __forceinline__ bf16x8 dq8_fma(uint32_t w, float s, float nzs) {

@@ -4,7 +4,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .api import ExpertWeights, Int4Proj, MoeLayer, MoeReplica
+from .api import ExpertWeights, Int4Proj, MoeLayer, MoeReplica, MwqExperts, MwqProj
 
 
 def _t(a: np.ndarray, dev, bf16: bool):
@@ -24,7 +24,9 @@ def to_device(wl, device="cuda"):
     """Returns (MoeLayer, x) for a ``workloads.Workload``."""
     cfg = wl.cfg
     bf = cfg.dtype == "bf16"
-    if cfg.int4:
+    if cfg.mwq:
+        routed = ExpertWeights()   # nested experts: see mwq_to_device
+    elif cfg.int4:
         routed = ExpertWeights(q_gate=None if wl.q_gate is None else _q(wl.q_gate, device),
                                q_up=_q(wl.q_up, device), q_down=_q(wl.q_down, device))
     else:
@@ -45,3 +47,18 @@ def replica_to_device(rep, device="cuda"):
     """MoeReplica for a ``workloads.Replica`` (INT4, one expert per projection)."""
     return MoeReplica(rep.heavy, _q(rep.q_up, device), _q(rep.q_down, device),
                       None if rep.q_gate is None else _q(rep.q_gate, device))
+
+
+def _m(mw, dev):
+    f16 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.float16).to(dev)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    return MwqProj(i32(mw.q2), f16(mw.s2), f16(mw.z2), i32(mw.p3), f16(mw.a3), i32(mw.p4),
+                   f16(mw.a4))
+
+
+def mwq_to_device(wl, device="cuda"):
+    """(MwqExperts, widths [T][k] int32) for a nested-expert ``workloads.Workload``."""
+    ex = MwqExperts(_m(wl.m_up, device), _m(wl.m_down, device),
+                    None if wl.m_gate is None else _m(wl.m_gate, device))
+    widths = torch.from_numpy(np.ascontiguousarray(wl.bits, dtype=np.int32)).to(device)
+    return ex, widths

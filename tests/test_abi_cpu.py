@@ -242,3 +242,85 @@ def test_replica_validation_and_workspace(L, B):
     assert split(8) == B.MOE_ERR_INVALID_ARG
     assert split(0, counts=False) == B.MOE_ERR_INVALID_ARG
     assert split(0, E=65) == B.MOE_ERR_UNSUPPORTED
+
+
+def _mwq_experts(B, gate=True, hole=None):
+    keep = []
+    ex = B.MwqExperts()
+    for j, name in enumerate(("gate", "up", "down")):
+        if name == "gate" and not gate:
+            continue
+        ptrs = [_addr(40 + 8 * j + i) for i in range(7)]
+        if hole is not None and name == hole[0]:
+            ptrs[hole[1]] = None
+        w = B.WMwq(*ptrs)
+        keep.append(w)
+        setattr(ex, name, C.pointer(w))
+    ex._keep = keep
+    return ex
+
+
+def test_mwq_validation_and_workspace(L, B):
+    VO = B.MOE_F_VALIDATE_ONLY
+    Ld = _desc(B)
+    Ld.d_model, Ld.d_ff = 512, 1024
+    Ld.routed = B.Experts()          # not read by the nested layer
+    n = C.c_size_t(0)
+    assert L.moe_mwq_workspace_size(C.byref(Ld), 100, C.byref(n)) == B.MOE_OK
+    assert n.value >= 100 * 2 * 1024 * 2 + 100 * 2 * 512 * 4     # H and the gate-scaled rows
+    ws = C.c_void_p(FAKE * 16)
+    groups = B.MwqGroups(_addr(60), _addr(61), _addr(62), _addr(63), _addr(64))
+
+    def fwd(ex, nbytes=None, Ldesc=None, widths=True, T=100, g=groups):
+        return L.moe_layer_forward_mwq(C.byref(Ldesc or Ld), None if ex is None else C.byref(ex),
+                                       _addr(5) if widths else None, _addr(1), T, _addr(2), 0,
+                                       None, None if g is None else C.byref(g), ws,
+                                       n.value if nbytes is None else nbytes, VO, None)
+    assert fwd(_mwq_experts(B)) == B.MOE_OK
+    assert fwd(_mwq_experts(B), g=None) == B.MOE_OK
+    assert fwd(_mwq_experts(B), n.value - 1) == B.MOE_ERR_WORKSPACE
+    assert fwd(None) == B.MOE_ERR_INVALID_ARG
+    assert fwd(_mwq_experts(B), widths=False) == B.MOE_ERR_INVALID_ARG
+    assert fwd(_mwq_experts(B, gate=False)) == B.MOE_ERR_INVALID_ARG      # SwiGLU needs gate
+    for hole in (("up", 0), ("down", 3), ("gate", 6), ("up", 1)):
+        assert fwd(_mwq_experts(B, hole=hole)) == B.MOE_ERR_INVALID_ARG, hole
+    Lr = _desc(B)
+    Lr.d_model, Lr.d_ff, Lr.act = 512, 1024, 1
+    Lr.routed = B.Experts()
+    assert fwd(_mwq_experts(B, gate=False), Ldesc=Lr) == B.MOE_OK         # ReLU: no gate
+    Lk = _desc(B)
+    Lk.d_model, Lk.d_ff = 512, 640                                         # d_ff % 512 != 0
+    Lk.routed = B.Experts()
+    assert fwd(_mwq_experts(B), Ldesc=Lk) == B.MOE_ERR_UNSUPPORTED
+    Le = _desc(B)
+    Le.d_model, Le.d_ff, Le.n_experts = 512, 1024, 22                     # 3E > 64
+    Le.routed = B.Experts()
+    assert fwd(_mwq_experts(B), Ldesc=Le) == B.MOE_ERR_UNSUPPORTED
+    Lf = _desc(B)
+    Lf.d_model, Lf.d_ff, Lf.act_dtype = 512, 1024, 0
+    Lf.routed = B.Experts()
+    assert fwd(_mwq_experts(B), Ldesc=Lf) == B.MOE_ERR_UNSUPPORTED       # bf16 activations only
+
+    def grp(T=16, E=8, k=2, nbytes=None, counts=True, widths=True):
+        g = B.MwqGroups(None, _addr(61) if counts else None, _addr(62), None, None)
+        need = L.moe_mwq_group_workspace_size(T, E, k)
+        return L.moe_mwq_group(_addr(1), _addr(2) if widths else None, T, E, k, C.byref(g), ws,
+                               need if nbytes is None else nbytes, VO, None)
+    assert grp() == B.MOE_OK
+    assert grp(E=21, k=8, T=333) == B.MOE_OK
+    assert grp(E=22) == B.MOE_ERR_UNSUPPORTED
+    assert grp(counts=False) == B.MOE_ERR_INVALID_ARG
+    assert grp(widths=False) == B.MOE_ERR_INVALID_ARG
+    assert grp(nbytes=16) == B.MOE_ERR_WORKSPACE
+    assert L.moe_mwq_group_workspace_size(9000, 8, 2) > L.moe_mwq_group_workspace_size(16, 8, 2)
+
+    def ffn(d=512, F=1024, act=0, nbytes=None, ex=None):
+        need = L.moe_grouped_ffn_mwq_workspace_size(16, F, 2)
+        return L.moe_grouped_ffn_mwq(_addr(1), 16, d, F, 8, 2, act,
+                                     C.byref(ex or _mwq_experts(B)), _addr(2), _addr(3), None,
+                                     _addr(4), ws, need if nbytes is None else nbytes, VO, None)
+    assert ffn() == B.MOE_OK
+    assert ffn(d=384) == B.MOE_ERR_UNSUPPORTED
+    assert ffn(d=200) == B.MOE_ERR_INVALID_ARG
+    assert ffn(nbytes=100) == B.MOE_ERR_WORKSPACE
+    assert ffn(act=1, ex=_mwq_experts(B, gate=False)) == B.MOE_OK
