@@ -256,7 +256,8 @@ moe_status moe_replica_workspace_size(const moe_layer_desc* L, int T, size_t* by
  * grouped by (expert, width): group v = 3*e + (width - 2), 3E groups. */
 
 /* One projection of all experts in the nested format, N output rows and K along
- * the reduction (K a multiple of 128), every pointer non-NULL:
+ * the reduction (K a multiple of 128), every pointer non-NULL (q2, p3, p4
+ * 16-byte aligned; s2, z2, a3, a4 8-byte aligned):
  *   q2     int32 [E][N][K/16]: word j holds the 2-bit codes of K-indices
  *          16j..16j+15, byte-transposed -- K-index 16j + 4m + b (m, b < 4) in
  *          bits 8b+2m .. 8b+2m+1;

@@ -542,8 +542,8 @@ moe_status check_mwq_experts(const moe_mwq_experts* w, int T, int d, int F, int 
     REQUIRE_PTR(m->p3, "nested p3");
     REQUIRE_PTR(m->p4, "nested p4");
     REQUIRE(m->s2 && m->z2 && m->a3 && m->a4, "nested s2/z2/a3/a4 must not be NULL");
-    REQUIRE(aligned(m->s2, 2) && aligned(m->z2, 2) && aligned(m->a3, 2) && aligned(m->a4, 2),
-            "nested s2/z2/a3/a4 misaligned");
+    REQUIRE(aligned(m->s2, 8) && aligned(m->z2, 8) && aligned(m->a3, 8) && aligned(m->a4, 8),
+            "nested s2/z2/a3/a4 must be 8-byte aligned");
   }
   if (const char* why = mwq_ffn_unsupported(T, d, F, k)) return fail(MOE_ERR_UNSUPPORTED, "%s", why);
   return MOE_OK;

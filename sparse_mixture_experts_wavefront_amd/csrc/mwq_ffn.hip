@@ -38,6 +38,16 @@
 
 #include "moe_internal.h"
 
+#ifndef MWQ_WAVES
+#define MWQ_WAVES 3
+#endif
+#ifndef MWQ_RM_GU
+#define MWQ_RM_GU 16
+#endif
+#ifndef MWQ_RM_DN
+#define MWQ_RM_DN 32
+#endif
+
 namespace moe {
 namespace {
 
@@ -127,11 +137,13 @@ __device__ __forceinline__ void build_tab(Tab& t, uint2 md) {
 __device__ __forceinline__ uint32_t pair01(uint32_t L, uint32_t H) { return perm(H, L, 0x05010400u); }
 __device__ __forceinline__ uint32_t pair23(uint32_t L, uint32_t H) { return perm(H, L, 0x07030602u); }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void mwq_stream_kernel(MwqArgs p) {
-  constexpr int R = (MODE == kMModeGateUp) ? 64 : 32;  // weight rows per block
+// RM: output columns per block (weight rows per matrix in a block)
+template <int MODE, int RM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MWQ_WAVES, 8)))
+void mwq_stream_kernel(MwqArgs p) {
+  constexpr int R = (MODE == kMModeGateUp) ? 2 * RM : RM;  // weight rows per block
   constexpr int RB = R / 16;
-  constexpr int NOUT = 32;
+  constexpr int NOUT = RM;
 
   extern __shared__ __align__(16) unsigned char smem[];
   float* red = (float*)smem;                           // [4][RB][64][4]
@@ -155,25 +167,32 @@ __global__ __launch_bounds__(256) void mwq_stream_kernel(MwqArgs p) {
   const int G = p.K >> 7, GP = G + 1;
   const uint32_t qrow = (uint32_t)p.K / 4, prow = (uint32_t)p.K / 8;  // bytes per row
 
-  // group metadata of the block's rows: block row r < 32 is row n0 + r of W0,
-  // r >= 32 (gate/up) row n0 + r - 32 of W1
-  for (int i = tid; i < R * G; i += 256) {
-    const int r = i / G, gi = i - r * G;
-    const bool second = (MODE == kMModeGateUp) && r >= 32;
-    const size_t o = ((size_t)e * p.N + n0 + (r & 31)) * G + gi;
-    const u16* s2 = second ? p.W1.s2 : p.W0.s2;
-    const u16* z2 = second ? p.W1.z2 : p.W0.z2;
-    const u16* a3 = second ? p.W1.a3 : p.W0.a3;
-    const u16* a4 = second ? p.W1.a4 : p.W0.a4;
-    md[r * GP + gi] = make_uint2((uint32_t)s2[o] | ((uint32_t)z2[o] << 16),
-                                 (uint32_t)a3[o] | ((uint32_t)a4[o] << 16));
-  }
-  __syncthreads();
+  // group metadata of the block's rows into LDS, md[r][g] = {s2 | z2 << 16,
+  // a3 | a4 << 16}: block row r < RM is row n0 + r of W0, r >= RM (gate/up) row
+  // n0 + r - RM of W1.  Four groups per 8-byte load (G is a multiple of 4).
+  auto stage_md = [&]() __attribute__((always_inline)) {
+    const int G4 = G >> 2;
+    for (int i = tid; i < R * G4; i += 256) {
+      const int r = i / G4, c = i - r * G4;
+      const bool second = (MODE == kMModeGateUp) && r >= RM;
+      const size_t o = ((size_t)e * p.N + n0 + (r % RM)) * G + 4 * c;
+      const uint2 vs = *(const uint2*)((second ? p.W1.s2 : p.W0.s2) + o);
+      const uint2 vz = *(const uint2*)((second ? p.W1.z2 : p.W0.z2) + o);
+      const uint2 v3 = *(const uint2*)((second ? p.W1.a3 : p.W0.a3) + o);
+      const uint2 v4 = *(const uint2*)((second ? p.W1.a4 : p.W0.a4) + o);
+      uint2* dst = md + r * GP + 4 * c;
+      // entry j: the low (j even) or high (j odd) halves of word j / 2
+      dst[0] = make_uint2(perm(vz.x, vs.x, 0x05040100u), perm(v4.x, v3.x, 0x05040100u));
+      dst[1] = make_uint2(perm(vz.x, vs.x, 0x07060302u), perm(v4.x, v3.x, 0x07060302u));
+      dst[2] = make_uint2(perm(vz.y, vs.y, 0x05040100u), perm(v4.y, v3.y, 0x05040100u));
+      dst[3] = make_uint2(perm(vz.y, vs.y, 0x07060302u), perm(v4.y, v3.y, 0x07060302u));
+    }
+  };
 
-  // buffer resources over the block's 32-row strips (sizes checked on the host
+  // buffer resources over the block's RM-row strips (sizes checked on the host
   // to fit 32-bit offsets)
   const size_t rbase = (size_t)e * p.N + n0;
-  const uint32_t qstrip = 32u * qrow, pstrip = 32u * prow;
+  const uint32_t qstrip = (uint32_t)RM * qrow, pstrip = (uint32_t)RM * prow;
   auto rsrc = [](const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
   };
@@ -185,11 +204,11 @@ __global__ __launch_bounds__(256) void mwq_stream_kernel(MwqArgs p) {
   const __amdgpu_buffer_rsrc_t r40 = rsrc((const char*)p.W0.p4 + rbase * prow, pstrip);
   const __amdgpu_buffer_rsrc_t r41 = rsrc((const char*)M1.p4 + rbase * prow, pstrip);
   const __amdgpu_buffer_rsrc_t xres = rsrc(p.X, p.xbytes);
-  // lane offsets inside the strips: row (rb*16 + r16) & 31, group g of the iteration
+  // lane offsets inside the strips: row (rb*16 + r16) % RM, group g of the iteration
   uint32_t qoff[RB], poff[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const uint32_t rr = (uint32_t)((rb * 16 + r16) & 31);
+    const uint32_t rr = (uint32_t)((rb * 16 + r16) % RM);
     qoff[rb] = rr * qrow + (uint32_t)g * 32u;
     poff[rb] = rr * prow + (uint32_t)g * 16u;
   }
@@ -221,7 +240,7 @@ __global__ __launch_bounds__(256) void mwq_stream_kernel(MwqArgs p) {
       const uint32_t kq = (uint32_t)(itg * 512 + u * 32);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const bool m0 = rb * 16 < 32;
+        const bool m0 = rb * 16 < RM;
         const uint32_t qo = live ? qoff[rb] + kq / 4 : qstrip;
         const auto qv = __builtin_amdgcn_raw_buffer_load_b64(m0 ? rq0 : rq1, (int)qo, 0, 0);
         S.q[rb][0] = qv[0];
@@ -254,50 +273,50 @@ __global__ __launch_bounds__(256) void mwq_stream_kernel(MwqArgs p) {
       for (int rb = 0; rb < RB; ++rb) build_tab<WM>(tab[rb], md[(rb * 16 + r16) * GP + grp]);
     };
 
+    // MFMA step s of a sub-step covers the lane's weights 8s..8s+7: the quartets
+    // (h, m) = (s / 2, 2 (s % 2)) and (s / 2, 2 (s % 2) + 1); each step's operands
+    // are built right before its MFMAs, which keeps few of them live
     auto compute = [&](const Set& S) __attribute__((always_inline)) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const Tab& T = tab[rb];
-        u32x4 A2[4], A3[4], A4[4];
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 xb = as_bf16x8(S.x[s]);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int rb = 0; rb < RB; ++rb) {
+          const Tab& T = tab[rb];
+          u32x4 A2, A3, A4;
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
+          for (int mm = 0; mm < 2; ++mm) {
+            const int h = s >> 1, m = 2 * (s & 1) + mm, d0 = 2 * mm;
             // bytes of t: 2-bit codes of the weights 16h + 4m + (0..3) of the sub-step
             const uint32_t t = (S.q[rb][h] >> (2 * m)) & 0x03030303u;
             const int i = 4 * h + m;           // their residual bits: bit 8b + i
-            const int sidx = 2 * h + (m >> 1), d0 = 2 * (m & 1);
             if constexpr ((WM & 1) != 0) {
               const uint32_t L = perm(0u, T.l2, t), H = perm(0u, T.h2, t);
-              A2[sidx][d0] = pair01(L, H);
-                A2[sidx][d0 + 1] = pair23(L, H);
+              A2[d0] = pair01(L, H);
+              A2[d0 + 1] = pair23(L, H);
             }
             if constexpr ((WM & 6) != 0) {
               const uint32_t c3 = t | (((S.p3[rb] >> i) & 0x01010101u) << 2);
               if constexpr ((WM & 2) != 0) {
                 const uint32_t L = perm(T.l3[1], T.l3[0], c3), H = perm(T.h3[1], T.h3[0], c3);
-                A3[sidx][d0] = pair01(L, H);
-                A3[sidx][d0 + 1] = pair23(L, H);
+                A3[d0] = pair01(L, H);
+                A3[d0 + 1] = pair23(L, H);
               }
               if constexpr ((WM & 4) != 0) {
-                const uint32_t r4 = (S.p4[rb] >> i) & 0x01010101u;
-                const uint32_t m4 = (r4 << 8) - r4;  // 0xff in the bytes whose r4 is set
+                // 0xff in the bytes whose r4 is set: byte 4 (of 0xffffffff) or byte 0 (of 0)
+                const uint32_t m4 = perm(0xffffffffu, 0u, ((S.p4[rb] >> i) & 0x01010101u) << 2);
                 const uint32_t L = (m4 & perm(T.l4[3], T.l4[2], c3)) |
                                    (~m4 & perm(T.l4[1], T.l4[0], c3));
                 const uint32_t H = (m4 & perm(T.h4[3], T.h4[2], c3)) |
                                    (~m4 & perm(T.h4[1], T.h4[0], c3));
-                A4[sidx][d0] = pair01(L, H);
-                A4[sidx][d0 + 1] = pair23(L, H);
+                A4[d0] = pair01(L, H);
+                A4[d0 + 1] = pair23(L, H);
               }
             }
           }
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 xb = as_bf16x8(S.x[s]);
-          if constexpr ((WM & 1) != 0) acc2[rb] = mfma16(as_bf16x8(A2[s]), xb, acc2[rb]);
-          if constexpr ((WM & 2) != 0) acc3[rb] = mfma16(as_bf16x8(A3[s]), xb, acc3[rb]);
-          if constexpr ((WM & 4) != 0) acc4[rb] = mfma16(as_bf16x8(A4[s]), xb, acc4[rb]);
+          if constexpr ((WM & 1) != 0) acc2[rb] = mfma16(as_bf16x8(A2), xb, acc2[rb]);
+          if constexpr ((WM & 2) != 0) acc3[rb] = mfma16(as_bf16x8(A3), xb, acc3[rb]);
+          if constexpr ((WM & 4) != 0) acc4[rb] = mfma16(as_bf16x8(A4), xb, acc4[rb]);
         }
       }
     };
@@ -305,6 +324,11 @@ __global__ __launch_bounds__(256) void mwq_stream_kernel(MwqArgs p) {
     Set st[2];
     load(st[0], 0);
     load(st[1], 1);
+    if (mbase == 0) {
+      // the first pass stages the metadata while its first operands are in flight
+      stage_md();
+      __syncthreads();
+    }
     for (int it = 0; it < ipw; ++it) {
       tables(it);
 #pragma unroll
@@ -344,7 +368,7 @@ __global__ __launch_bounds__(256) void mwq_stream_kernel(MwqArgs p) {
       };
       const size_t orow = (size_t)(row0 + row);
       if constexpr (MODE == kMModeGateUp) {
-        const float gv = part(col), uv = part(32 + col);
+        const float gv = part(col), uv = part(RM + col);
         p.H[orow * p.N + n0 + col] = f32_to_bf16(silu_f32(gv) * uv);
       } else if constexpr (MODE == kMModeRelu) {
         p.H[orow * p.N + n0 + col] = f32_to_bf16(fmaxf(part(col), 0.0f));
@@ -371,19 +395,21 @@ __global__ __launch_bounds__(256) void mwq_stream_kernel(MwqArgs p) {
   }
 }
 
-template <int MODE>
+template <int MODE, int RM>
 size_t mwq_lds_bytes(int K) {
-  constexpr int R = (MODE == kMModeGateUp) ? 64 : 32;
+  constexpr int R = (MODE == kMModeGateUp) ? 2 * RM : RM;
   return (size_t)4 * (R / 16) * 64 * 16 + (size_t)R * ((K >> 7) + 1) * 8;
 }
 
 constexpr size_t kMwqMaxLds = 64 * 1024;
+constexpr int kRmGateUp = MWQ_RM_GU, kRmDown = MWQ_RM_DN;
 
-template <int MODE>
-hipError_t launch_mwq_mode(const MwqArgs& a, int E, hipStream_t s) {
-  const size_t lds = mwq_lds_bytes<MODE>(a.K);
+template <int MODE, int RM>
+hipError_t launch_mwq_mode(MwqArgs a, int E, hipStream_t s) {
+  const size_t lds = mwq_lds_bytes<MODE, RM>(a.K);
   if (lds > kMwqMaxLds) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mwq_stream_kernel<MODE>), dim3((unsigned)(E * a.nblk_per_expert)),
+  a.nblk_per_expert = a.N / RM;
+  hipLaunchKernelGGL((mwq_stream_kernel<MODE, RM>), dim3((unsigned)(E * a.nblk_per_expert)),
                      dim3(256), lds, s, a);
   return hipGetLastError();
 }
@@ -394,7 +420,8 @@ const char* mwq_ffn_unsupported(int T, int d, int F, int k) {
   if (d % 512 != 0 || F % 512 != 0) return "nested experts need d_model and d_ff multiples of 512";
   if ((long long)T * d * 2 >= (1ll << 31) || (long long)T * k * F * 2 >= (1ll << 31))
     return "nested experts: token or hidden matrix too large for 32-bit offsets";
-  if (mwq_lds_bytes<kMModeGateUp>(d) > kMwqMaxLds || mwq_lds_bytes<kMModeDown>(F) > kMwqMaxLds)
+  if (mwq_lds_bytes<kMModeGateUp, kRmGateUp>(d) > kMwqMaxLds ||
+      mwq_lds_bytes<kMModeDown, kRmDown>(F) > kMwqMaxLds)
     return "nested experts: d_model or d_ff too large for the group metadata in LDS";
   return nullptr;
 }
@@ -413,10 +440,9 @@ hipError_t launch_mwq_ffn(const MwqProblem& p, hipStream_t s, hipEvent_t mid) {
   a.K = p.d;
   a.offsets = p.offsets;
   a.H = (u16*)p.H;
-  a.nblk_per_expert = p.F / 32;
   a.xbytes = (uint32_t)((size_t)p.T * p.d * 2);
-  hipError_t e = relu ? launch_mwq_mode<kMModeRelu>(a, p.E, s)
-                      : launch_mwq_mode<kMModeGateUp>(a, p.E, s);
+  hipError_t e = relu ? launch_mwq_mode<kMModeRelu, kRmGateUp>(a, p.E, s)
+                      : launch_mwq_mode<kMModeGateUp, kRmGateUp>(a, p.E, s);
   if (e != hipSuccess) return e;
   if (mid) {
     e = hipEventRecord(mid, s);
@@ -435,9 +461,8 @@ hipError_t launch_mwq_ffn(const MwqProblem& p, hipStream_t s, hipEvent_t mid) {
   b.Y = p.y_rows;
   b.gate_map = p.row_assign;
   b.gate = p.gate;
-  b.nblk_per_expert = p.d / 32;
   b.xbytes = (uint32_t)((size_t)p.rows * p.F * 2);
-  return launch_mwq_mode<kMModeDown>(b, p.E, s);
+  return launch_mwq_mode<kMModeDown, kRmDown>(b, p.E, s);
 }
 
 }  // namespace moe
