@@ -68,10 +68,12 @@ def lib():
             L.orc_dequant_int4.argtypes = [p, p, p, i64, i, i, p]
             L.orc_replica_split.argtypes = [p, i, i, i, i, p]
             L.orc_dequant_mwq.argtypes = [p, p, p, p, p, p, p, i64, i, i, i, p]
+            L.orc_floe_rows.argtypes = [p, i, i, p, p, p, p, p, p, i, p, p, p, p]
             L.orc_round_bf16.argtypes = [d]
             L.orc_round_bf16.restype = d
             for f in ("orc_router_logits", "orc_topk_gates", "orc_permute", "orc_expert_rows",
-                      "orc_combine", "orc_dequant_int4", "orc_replica_split", "orc_dequant_mwq"):
+                      "orc_combine", "orc_dequant_int4", "orc_replica_split", "orc_dequant_mwq",
+                      "orc_floe_rows"):
                 getattr(L, f).restype = C.c_int
             _lib = L
     return _lib
@@ -222,6 +224,52 @@ def mwq_groups(idx, bits, E):
     return vidx, counts, offsets, row_assign, assign_row
 
 
+def dequant_int2(q2, s2, z2, group=INT4_GROUP):
+    """INT2 weights (the base of the nested format) -> bf16 bits [.., N, K]:
+    bf16_RNE(fp32(fp32(q) - z) * s), the nested decode at width 2."""
+    q2 = np.ascontiguousarray(q2, np.int32)
+    K = q2.shape[-1] * 16
+    rows = int(np.prod(q2.shape[:-1]))
+    out = np.empty(q2.shape[:-1] + (K,), np.uint16)
+    s2 = np.ascontiguousarray(s2, np.uint16)
+    z2 = np.ascontiguousarray(z2, np.uint16)
+    _check(lib().orc_dequant_mwq(_ptr(q2), _ptr(s2), _ptr(z2), None, None, None, None, rows, K,
+                                 group, 2, _ptr(out)), "dequant_int2")
+    return out
+
+
+def floe_threshold(samples, sparsity):
+    """Threshold for a target sparsity from the empirical CDF of |activations|
+    ("FloE" -- Assumptions & free parameters: per-expert thresholds from the
+    empirical CDF; reading: its inverse at the target level), i.e. the smallest
+    sample value t with F_hat(t) >= sparsity, the ceil(sparsity * n)-th smallest
+    |sample|.  Channels with |u| <= t are then pruned."""
+    a = np.sort(np.abs(np.asarray(samples, np.float64)).ravel())
+    if a.size == 0:
+        raise OracleError("floe_threshold: no samples")
+    r = max(1, int(np.ceil(sparsity * a.size)))
+    return float(a[r - 1])
+
+
+def floe_rows(x, w_gate, w_up_dec, w_down, thr, tok, exp_id, u_given=None):
+    """Sparse-down expert rows (see orc_floe_rows).  Returns (Y [n][d] fp64,
+    u [n][F] fp64, keep [n][F] uint8)."""
+    x = np.ascontiguousarray(x, np.uint16)
+    tok = np.ascontiguousarray(tok, np.int32)
+    exp_id = np.ascontiguousarray(exp_id, np.int32)
+    n, d, F = tok.size, x.shape[1], w_up_dec.shape[1]
+    Y = np.empty((n, d), np.float64)
+    u = np.empty((n, F), np.float64)
+    keep = np.empty((n, F), np.uint8)
+    ug = None if u_given is None else np.ascontiguousarray(u_given, np.float32)
+    arrs = [np.ascontiguousarray(a, np.uint16) for a in (w_gate, w_up_dec, w_down)]
+    thr = np.ascontiguousarray(thr, np.float32)
+    _check(lib().orc_floe_rows(_ptr(x), d, F, _ptr(arrs[0]), _ptr(arrs[1]), _ptr(arrs[2]),
+                               _ptr(thr), _ptr(tok), _ptr(exp_id), n, _ptr(ug), _ptr(u),
+                               _ptr(keep), _ptr(Y)), "floe_rows")
+    return Y, u, keep
+
+
 # --- the layer -----------------------------------------------------------
 
 def _h_round(wl):
@@ -272,13 +320,16 @@ def replica_dense_weights(rep):
     return tuple(out)
 
 
-def layer_forward(wl, logits=None, tokens=None, routing_only=False, replica=None):
+def layer_forward(wl, logits=None, tokens=None, routing_only=False, replica=None, floe_u=None):
     """Run the whole layer on the CPU.
 
     ``logits``: if given (e.g. the GPU's fp32 logits), routing uses them instead
     of the oracle's own; that pins every integer output to one fp32 input.
     ``tokens``: optional subset of token ids whose y is computed (routing,
     counts, permutation and LIS always cover all T tokens).
+    ``floe_u``: sparse-down layers only -- up-projection outputs [T*k][F] fp32 in
+    expert-major row order (e.g. the GPU's) on which the keep/prune decisions
+    are taken, as ``logits`` is for routing.
     Returns a dict of every intermediate and output.
     """
     cfg = wl.cfg
@@ -316,6 +367,29 @@ def layer_forward(wl, logits=None, tokens=None, routing_only=False, replica=None
         pt = np.repeat(toks, k)
         pe = idx[toks].reshape(-1)
         ar = None
+    if cfg.floe:
+        ug = None
+        if floe_u is not None:
+            fu = np.asarray(floe_u, np.float32)
+            ug = fu if tokens is None else fu[assign_row[(toks[:, None] * k + np.arange(k)).ravel()]]
+        wu = dequant_int2(wl.u2_up.q2, wl.u2_up.s2, wl.u2_up.z2)
+        Y, u, keep = floe_rows(wl.x, wl.w_gate, wu, wl.w_down, wl.floe_thr, pt, pe, ug)
+        out.update(tokens=toks, Y=Y, Ys=None, floe_u=u, floe_keep=keep)
+        if tokens is None:
+            # channels a row of each expert keeps (rows are expert-major)
+            nnz = np.zeros(E, np.int64)
+            for e in range(E):
+                sel = pe == e
+                if sel.any():
+                    nnz[e] = int(keep[sel].any(axis=0).sum())
+            out["floe_nnz"] = nnz
+        Ys = None
+        if cfg.n_shared:
+            Ys = expert_rows(wl.x, wl.ws_gate[None], wl.ws_up[None], wl.ws_down[None], "swiglu",
+                             _h_round(wl), toks, np.zeros_like(toks))
+            out["Ys"] = Ys
+        out["y"] = combine(Y, ar, gate[toks], Ys)
+        return out
     needed = sorted(set(int(e) for e in pe if e < (3 * E if cfg.mwq else E)))
     wg, wu, wd = dense_expert_weights(wl, needed)
     if replica is not None:

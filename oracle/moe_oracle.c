@@ -386,3 +386,65 @@ int orc_dequant_mwq(const int32_t* q2, const uint16_t* s2, const uint16_t* z2, c
   }
   return ORC_OK;
 }
+
+/* ---- Contextual sparse down-projection ------------------------------------
+ * "FloE: On-the-Fly MoE Inference on Memory-constrained GPU" -- Core claim and
+ * What carries the argument: a channel of the expert's hidden layer whose
+ * up-projection output is small in magnitude is pruned, which removes its gate
+ * row and its down-projection column from the work; the up projection itself
+ * is kept (quantised to INT2).  Assumptions & free parameters: one threshold per
+ * expert, read off the empirical distribution of calibration activations.
+ * Per (token, expert) row p, all in fp64 unless stated:
+ *   u_f    = x_t . W_up[e][f]             (W_up: the decoded INT2 weights, bf16)
+ *   keep_f = |u_f| > thr[e]               (decided on u_given[p][f] when given)
+ *   h_f    = keep_f ? bf16_RNE( silu(x_t . W_gate[e][f]) * u_f ) : 0
+ *   Y[p]   = W_down[e] . h
+ * x [T][d], w_gate / w_up [E][F][d], w_down [E][d][F]: bf16 bits.  u_out
+ * [n][F] and keep_out [n][F] may be NULL. */
+int orc_floe_rows(const uint16_t* x, int d, int F, const uint16_t* w_gate, const uint16_t* w_up,
+                  const uint16_t* w_down, const float* thr, const int32_t* tok,
+                  const int32_t* exp_id, int n, const float* u_given, double* u_out,
+                  uint8_t* keep_out, double* Y) {
+  if (d < 1 || F < 1 || n < 0 || !x || !w_gate || !w_up || !w_down || !thr || !Y)
+    return ORC_ERR_ARG;
+  int err = 0;
+#pragma omp parallel
+  {
+    double* h = (double*)malloc(sizeof(double) * (size_t)F);
+    if (!h) {
+#pragma omp atomic write
+      err = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int p = 0; p < n; ++p) {
+      if (!h) continue;
+      size_t t = (size_t)tok[p], e = (size_t)exp_id[p];
+      size_t xo = t * (size_t)d;
+      for (int f = 0; f < F; ++f) {
+        size_t wo = (e * (size_t)F + (size_t)f) * (size_t)d;
+        double u = 0.0;
+        for (int i = 0; i < d; ++i) u += bf16_to_double(x[xo + i]) * bf16_to_double(w_up[wo + i]);
+        double mag = u_given ? fabs((double)u_given[(size_t)p * F + f]) : fabs(u);
+        int keep = mag > (double)thr[e];
+        if (u_out) u_out[(size_t)p * F + f] = u;
+        if (keep_out) keep_out[(size_t)p * F + f] = (uint8_t)keep;
+        if (keep) {
+          double g = 0.0;
+          for (int i = 0; i < d; ++i)
+            g += bf16_to_double(x[xo + i]) * bf16_to_double(w_gate[wo + i]);
+          h[f] = orc_round_bf16((g / (1.0 + exp(-g))) * u);
+        } else {
+          h[f] = 0.0;
+        }
+      }
+      for (int i = 0; i < d; ++i) {
+        size_t wo = (e * (size_t)d + (size_t)i) * (size_t)F;
+        double s = 0.0;
+        for (int f = 0; f < F; ++f) s += h[f] * bf16_to_double(w_down[wo + f]);
+        Y[(size_t)p * d + i] = s;
+      }
+    }
+    free(h);
+  }
+  return err ? ORC_ERR_ARG : ORC_OK;
+}

@@ -590,6 +590,98 @@ def test_mwq_layer_at_one_width_is_the_plain_layer():
         assert np.array_equal(mw["y"], ref["y"])
 
 
+# ---------------------------------------------------------------- sparse down (FloE)
+
+def _floe_small(T=6, d=256, F=384, E=3, seed=3):
+    rng = np.random.default_rng(seed)
+    b = lambda *sh: f32_to_bf16_bits((rng.standard_normal(sh) * 0.05).astype(np.float32))
+    x = f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    return x, b(E, F, d), b(E, F, d), b(E, d, F)
+
+
+def test_floe_keep_all_is_the_dense_expert():
+    """A threshold below zero keeps every channel: the rows equal the pinned dense
+    SwiGLU expert (same fp64 arithmetic, bit for bit)."""
+    x, wg, wu, wd = _floe_small()
+    tok = np.array([0, 1, 2, 3, 4, 5, 0, 2], np.int32)
+    ex = np.array([0, 0, 1, 1, 2, 2, 2, 0], np.int32)
+    Y, u, keep = oracle.floe_rows(x, wg, wu, wd, np.full(3, -1.0, np.float32), tok, ex)
+    ref = oracle.expert_rows(x, wg, wu, wd, "swiglu", oracle.ROUND_BF16, tok, ex)
+    assert keep.all() and np.array_equal(Y, ref)
+    # u is the fp64 up projection (numpy matmul)
+    xf = bf16_bits_to_f32(x).astype(np.float64)
+    for p_, (t, e) in enumerate(zip(tok, ex)):
+        ref_u = bf16_bits_to_f32(wu[e]).astype(np.float64) @ xf[t]
+        assert np.allclose(u[p_], ref_u, rtol=1e-12, atol=1e-12)
+
+
+def test_floe_prune_all_and_given_decisions():
+    x, wg, wu, wd = _floe_small(seed=4)
+    tok = np.arange(6, dtype=np.int32)
+    ex = np.array([0, 1, 2, 0, 1, 2], np.int32)
+    Y, _, keep = oracle.floe_rows(x, wg, wu, wd, np.full(3, np.inf, np.float32), tok, ex)
+    assert not keep.any() and np.all(Y == 0.0)
+    # decisions follow the given values, not the oracle's own u
+    Y0, u, _ = oracle.floe_rows(x, wg, wu, wd, np.zeros(3, np.float32), tok, ex)
+    Yz, _, kz = oracle.floe_rows(x, wg, wu, wd, np.zeros(3, np.float32), tok, ex,
+                                 u_given=np.zeros((6, 384), np.float32))
+    assert not kz.any() and np.all(Yz == 0.0)
+    Ys, _, ks = oracle.floe_rows(x, wg, wu, wd, np.zeros(3, np.float32), tok, ex,
+                                 u_given=u.astype(np.float32))
+    assert np.array_equal(ks, (np.abs(u.astype(np.float32)) > 0).astype(np.uint8))
+
+
+def test_floe_single_row_equals_dense_with_pruned_columns_zeroed():
+    """For one row, pruning channel f is the dense expert with column f of W_down
+    zeroed (an independent route through the pinned dense routine)."""
+    x, wg, wu, wd = _floe_small(seed=5)
+    for t, e in ((0, 0), (3, 2), (5, 1)):
+        tok, ex = np.array([t], np.int32), np.array([e], np.int32)
+        _, u, _ = oracle.floe_rows(x, wg, wu, wd, np.full(3, -1.0, np.float32), tok, ex)
+        thr = np.full(3, np.float32(np.quantile(np.abs(u[0]), 0.8)), np.float32)
+        Y, _, keep = oracle.floe_rows(x, wg, wu, wd, thr, tok, ex)
+        assert 0.1 < keep.mean() < 0.3
+        wd2 = wd.copy()
+        wd2[e][:, keep[0] == 0] = 0
+        ref = oracle.expert_rows(x, wg, wu, wd2, "swiglu", oracle.ROUND_BF16, tok, ex)
+        assert np.array_equal(Y, ref)
+
+
+def test_floe_threshold_is_the_empirical_quantile():
+    """The inverse empirical CDF at the target level: numpy's inverted-CDF
+    quantile, and the fraction of samples at or below it is ceil(k n)/n."""
+    rng = np.random.default_rng(9)
+    for n, k in ((1000, 0.9), (917, 0.8), (5, 0.5), (64, 1.0)):
+        a = rng.standard_normal(n)
+        t = oracle.floe_threshold(a, k)
+        assert t == float(np.quantile(np.abs(a), k, method="inverted_cdf"))
+        assert (np.abs(a) <= t).sum() == max(1, math.ceil(k * n))
+    # the workload's calibrated thresholds are the same reading
+    from workloads.gen import FLOE_CAL_TOKENS, TID_XCAL, _normal
+    wl = make_workload(get_config("mixtral_floe_decode", d=256, F=512, x_rows_of=None,
+                                  weights_of=None))
+    xc = bf16_bits_to_f32(_normal(wl.cfg.cfg_id, TID_XCAL, 0, (FLOE_CAL_TOKENS, 256), 1.0,
+                                  True)).astype(np.float64)
+    for e in range(wl.cfg.E):
+        samples = xc @ bf16_bits_to_f32(wl.w_up[e]).astype(np.float64).T
+        assert np.float32(oracle.floe_threshold(samples, 0.9)) == wl.floe_thr[e]
+
+
+def test_floe_layer_keep_all_is_the_plain_layer():
+    """Thresholds below zero: the sparse-down layer is the plain layer on the
+    decoded INT2 up weights."""
+    import dataclasses
+    wl = make_workload(get_config("mixtral_floe_decode", T=20, d=256, F=512, x_rows_of=None,
+                                  weights_of=None))
+    wl.floe_thr = np.full(wl.cfg.E, -1.0, np.float32)
+    fl = oracle.layer_forward(wl)
+    plain = dataclasses.replace(wl, cfg=dataclasses.replace(wl.cfg, floe=False))
+    plain.w_up = oracle.dequant_int2(wl.u2_up.q2, wl.u2_up.s2, wl.u2_up.z2)
+    ref = oracle.layer_forward(plain)
+    assert np.array_equal(fl["y"], ref["y"]) and fl["floe_keep"].all()
+    assert np.array_equal(fl["floe_nnz"], np.where(ref["counts"] > 0, 512, 0))
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 MUTANTS = [
@@ -619,6 +711,13 @@ MUTANTS = [
      "    if (e >= 0) {\n      idx_out[a]"),
     ("mwq residual sign flipped", "        w = w + (bit ? m : -m);\n      }\n      if (bits == 4)",
      "        w = w + (bit ? -m : m);\n      }\n      if (bits == 4)"),
+    ("floe mask inverted", "int keep = mag > (double)thr[e];", "int keep = mag < (double)thr[e];"),
+    ("floe silu on the up output", "h[f] = orc_round_bf16((g / (1.0 + exp(-g))) * u);",
+     "h[f] = orc_round_bf16((u / (1.0 + exp(-u))) * g);"),
+    ("floe h not rounded", "h[f] = orc_round_bf16((g / (1.0 + exp(-g))) * u);",
+     "h[f] = (g / (1.0 + exp(-g))) * u;"),
+    ("floe given values ignored", "double mag = u_given ? fabs((double)u_given[(size_t)p * F + f]) : fabs(u);",
+     "double mag = fabs(u);"),
     ("mwq second plane read from the first", "((uint32_t)p4[r * (K / 32) + kk / 32] >> mwq_bit(kk))",
      "((uint32_t)p3[r * (K / 32) + kk / 32] >> mwq_bit(kk))"),
     ("mwq 2-bit fields in natural order", "(w2 >> (2 * mwq_field(kk))) & 0x3u;",

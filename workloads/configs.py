@@ -36,6 +36,8 @@ class WorkloadConfig:
     beta: float = 0.0    # bias strength for "neg_log" / "zipf"
     int4: bool = False   # expert weights as asymmetric INT4, group 128 along K
     mwq: bool = False    # nested INT2 + binary residual planes, per-assignment bit width
+    floe: bool = False   # INT2 up projection, gate/down channels kept where |up| > threshold
+    sparsity: float = 0.0  # target fraction of pruned channels (floe thresholds)
     x_rows_of: Optional[str] = None   # take the first T rows of this workload's x
     weights_of: Optional[str] = None  # reuse this workload's router/expert weights
     notes: str = field(default="", compare=False)
@@ -71,6 +73,16 @@ CONFIGS = {
         weights_of="mixtral_prefill_bf16",
         notes="nested INT2 base + binary residual planes, bit width per assignment "
               "uniform over {2, 3, 4}"),
+    "mixtral_floe_decode": WorkloadConfig(
+        "mixtral_floe_decode", 6, T=16, d=4096, E=8, k=2, F=14336, act="swiglu",
+        dtype="bf16", floe=True, sparsity=0.9, x_rows_of="mixtral_prefill_bf16",
+        weights_of="mixtral_prefill_bf16",
+        notes="INT2 up projection; per-expert thresholds for 90% pruned up outputs, "
+              "calibrated on 64 seeded tokens"),
+    "mixtral_floe_decode_t1": WorkloadConfig(
+        "mixtral_floe_decode_t1", 6, T=1, d=4096, E=8, k=2, F=14336, act="swiglu",
+        dtype="bf16", floe=True, sparsity=0.9, x_rows_of="mixtral_prefill_bf16",
+        weights_of="mixtral_prefill_bf16", notes="one-token decode step"),
 }
 
 

@@ -26,6 +26,8 @@ from .configs import CONFIGS, WorkloadConfig
 TID_X, TID_WR, TID_WGATE, TID_WUP, TID_WDOWN = 0, 1, 2, 3, 4
 TID_SGATE, TID_SUP, TID_SDOWN, TID_ZIPF = 5, 6, 7, 8
 TID_BITS = 9   # per-assignment bit widths of the nested-quantisation workload
+TID_XCAL = 10  # calibration activations (sparsity thresholds)
+FLOE_CAL_TOKENS = 64
 
 W_STD = 0.02
 INT4_GROUP = 128
@@ -96,6 +98,39 @@ def quantize_int4_rows(w_bits: np.ndarray, fractional_zero: bool = False):
     return words.view(np.int32), s16.view(np.uint16), z16.view(np.uint16)
 
 
+def _int2_base(w, N, K):
+    """INT2 base of the nested format on float64 groups w [N, G, 128]."""
+    lo = w.min(axis=2)
+    hi = w.max(axis=2)
+    const = hi == lo
+    s16 = ((hi - lo) / 3.0).astype(np.float16)
+    s16[const] = np.float16(1.0)
+    s = s16.astype(np.float64)
+    z16 = np.clip(np.rint(-lo / s), 0.0, 3.0).astype(np.float16)
+    z16[const] = np.float16(0.0)
+    z = z16.astype(np.float64)
+    q = np.clip(np.rint(w / s[..., None]) + z[..., None], 0, 3)
+    return q, s16, z16, s, z
+
+
+def _pack_q2(q, N, K):
+    qv = q.astype(np.uint32).reshape(N, K // 16, 16)
+    i16 = np.arange(16, dtype=np.uint32)
+    sh2 = (2 * (4 * (i16 % 4) + i16 // 4))[None, None, :]
+    return np.bitwise_or.reduce(qv << sh2, axis=2).astype(np.uint32).view(np.int32)
+
+
+def quantize_int2_rows(w_bits: np.ndarray):
+    """Asymmetric INT2 (group 128 along K) of bf16 rows: the base of the nested
+    format alone (see quantize_mwq_rows).  Returns q2 [N, K/16] int32 in the
+    byte-transposed order, s2, z2 fp16 bits [N, K/128]."""
+    N, K = w_bits.shape
+    assert K % INT4_GROUP == 0
+    w = bf16_bits_to_f32(w_bits).astype(np.float64).reshape(N, K // INT4_GROUP, INT4_GROUP)
+    q, s16, z16, _, _ = _int2_base(w, N, K)
+    return _pack_q2(q, N, K), s16.view(np.uint16), z16.view(np.uint16)
+
+
 def quantize_mwq_rows(w_bits: np.ndarray):
     """Nested INT2 + two binary residual planes (group 128 along K) of bf16 rows.
 
@@ -113,16 +148,7 @@ def quantize_mwq_rows(w_bits: np.ndarray):
     assert K % INT4_GROUP == 0
     G = K // INT4_GROUP
     w = bf16_bits_to_f32(w_bits).astype(np.float64).reshape(N, G, INT4_GROUP)
-    lo = w.min(axis=2)
-    hi = w.max(axis=2)
-    const = hi == lo
-    s16 = ((hi - lo) / 3.0).astype(np.float16)
-    s16[const] = np.float16(1.0)
-    s = s16.astype(np.float64)
-    z16 = np.clip(np.rint(-lo / s), 0.0, 3.0).astype(np.float16)
-    z16[const] = np.float16(0.0)
-    z = z16.astype(np.float64)
-    q = np.clip(np.rint(w / s[..., None]) + z[..., None], 0, 3)
+    q, s16, z16, s, z = _int2_base(w, N, K)
     approx = (q - z[..., None]) * s[..., None]
     planes, mags = [], []
     for _ in range(2):
@@ -133,10 +159,7 @@ def quantize_mwq_rows(w_bits: np.ndarray):
         approx = approx + np.where(r, a, -a)
         planes.append(r.reshape(N, K))
         mags.append(a16)
-    qv = q.astype(np.uint32).reshape(N, K // 16, 16)
-    i16 = np.arange(16, dtype=np.uint32)
-    sh2 = (2 * (4 * (i16 % 4) + i16 // 4))[None, None, :]
-    q2 = np.bitwise_or.reduce(qv << sh2, axis=2).astype(np.uint32).view(np.int32)
+    q2 = _pack_q2(q, N, K)
     i32 = np.arange(32, dtype=np.uint32)
     sh1 = (8 * (i32 % 4) + i32 // 4)[None, None, :]
 
@@ -157,6 +180,29 @@ class MwqWeights:
     a3: np.ndarray      # [E, N, K/128] fp16 bits
     p4: np.ndarray
     a4: np.ndarray
+
+
+@dataclass
+class Int2Weights:
+    """INT2 weights of one projection, all experts (see quantize_int2_rows)."""
+    q2: np.ndarray      # [E, N, K/16] int32
+    s2: np.ndarray      # [E, N, K/128] fp16 bits
+    z2: np.ndarray
+
+
+def sparsity_thresholds(x_cal_bits: np.ndarray, w_up_bits: np.ndarray, sparsity: float):
+    """Per-expert magnitude thresholds of the up-projection output for a target
+    sparsity: for expert e, the ceil(sparsity * n)-th smallest of the n values
+    |x_cal . W_up[e]^T| over a calibration batch (float64, unquantised weights).
+    These are layer parameters produced offline; the layer only compares against
+    them."""
+    xc = bf16_bits_to_f32(x_cal_bits).astype(np.float64)
+    out = np.empty(w_up_bits.shape[0], np.float32)
+    for e in range(w_up_bits.shape[0]):
+        a = np.abs(xc @ bf16_bits_to_f32(w_up_bits[e]).astype(np.float64).T).ravel()
+        r = max(1, int(math.ceil(sparsity * a.size)))
+        out[e] = np.float32(np.partition(a, r - 1)[r - 1])
+    return out
 
 
 @dataclass
@@ -185,6 +231,8 @@ class Workload:
     m_up: Optional[MwqWeights] = None
     m_down: Optional[MwqWeights] = None
     bits: Optional[np.ndarray] = None      # [T, k] int32 bit width of each assignment
+    u2_up: Optional[Int2Weights] = None    # INT2 up projection (floe configs)
+    floe_thr: Optional[np.ndarray] = None  # [E] fp32 |up output| threshold per expert
 
     @property
     def bf16(self) -> bool:
@@ -272,6 +320,17 @@ def make_workload(cfg, beta: Optional[float] = None, fractional_zero: bool = Fal
         # per-assignment bit widths, uniform over {2, 3, 4} (the pages' learned
         # bit-width router is not part of this workload)
         wl.bits = (_rng(cfg.cfg_id, TID_BITS).integers(0, 3, size=(T, cfg.k)) + 2).astype(np.int32)
+    if cfg.floe:
+        assert bf16 and cfg.act == "swiglu", "the sparse-down layer is a bf16 SwiGLU layer"
+        parts = [None] * E
+
+        def one(e):
+            parts[e] = quantize_int2_rows(w_up[e])
+        with ThreadPoolExecutor(max(1, min(threads, E))) as ex:
+            list(ex.map(one, range(E)))
+        wl.u2_up = Int2Weights(*[np.stack([p[i] for p in parts]) for i in range(3)])
+        x_cal = _normal(cfg.cfg_id, TID_XCAL, 0, (FLOE_CAL_TOKENS, d), 1.0, True)
+        wl.floe_thr = sparsity_thresholds(x_cal, w_up, cfg.sparsity)
     return wl
 
 
