@@ -98,10 +98,27 @@ def work_mwq(cfg, counts3):
                 bytes=wsum * (gu_mats + 1) * F * d + E * d * 2 + T * d * 2 + T * d * 4)
 
 
+def work_floe(cfg, counts, nnz):
+    """Algorithmic bytes of the sparse-down layer: per active expert the INT2 up
+    projection (2 bits + fp16 s2, z2 per 128) and, for the channels some row
+    keeps, the gate rows and down columns in bf16."""
+    T, d, E, k, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.F
+    active = np.asarray(counts) > 0
+    nz = np.asarray(nnz, np.float64) * active
+    up = float(active.sum()) * F * d * (0.25 + 4.0 / 128)
+    gate = float(nz.sum()) * d * 2
+    down = float(nz.sum()) * d * 2
+    return dict(gu_bytes=up + gate + T * d * 2, dn_bytes=down + T * k * d * 4,
+                bytes=up + gate + down + E * d * 2 + T * d * 2 + T * d * 4,
+                kept_channels=[int(v) for v in np.asarray(nnz)],
+                dense_bf16_bytes=float(active.sum()) * 3 * F * d * 2)
+
+
 def run_gpu(name, steps, warmup):
     import torch
     import sparse_mixture_experts_wavefront_amd as moe
-    from sparse_mixture_experts_wavefront_amd.device_inputs import mwq_to_device, to_device
+    from sparse_mixture_experts_wavefront_amd.device_inputs import (floe_to_device, mwq_to_device,
+                                                                    to_device)
     from workloads import make_workload
     wl = make_workload(name)
     cfg = wl.cfg
@@ -112,6 +129,11 @@ def run_gpu(name, steps, warmup):
 
         def call():
             return runner(x, widths=widths)
+    elif cfg.floe:
+        runner = moe.LayerRunner(layer, cfg.T, floe=floe_to_device(wl))
+
+        def call():
+            return runner(x)
     else:
         runner = moe.LayerRunner(layer, cfg.T)
 
@@ -167,6 +189,8 @@ def run_gpu(name, steps, warmup):
     w = work(cfg, counts)
     if cfg.mwq:
         w.update(work_mwq(cfg, runner.aux_t["mwq_counts"].cpu().numpy()))
+    if cfg.floe:
+        w.update(work_floe(cfg, counts, runner.aux_t["floe_nnz"].cpu().numpy()))
     stages = dict(zip(["route_topk", "permute", "gate_up_gemm", "down_gemm", "shared_experts",
                        "combine"], [round(v * 1000.0, 2) for v in st]))
     timing = dict(event_ms_p10=round(float(np.percentile(layer_ms, 10)), 4),
@@ -246,6 +270,12 @@ def run_replica(name, steps, warmup):
 def roofline(cfg, r):
     w = r["work"]
     t = r["stages_us"]["gate_up_gemm"] * 1e-6
+    if cfg.floe:
+        ach = w["gu_bytes"] / t / 1e9
+        return dict(kernel="sparse-down up+gate (INT2 up, kept gate rows)", bound="hbm",
+                    achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                    per_launch=dict(bytes=w["gu_bytes"], us=round(t * 1e6, 2)))
     if cfg.mwq:
         ach = w["gu_bytes"] / t / 1e9
         return dict(kernel="mwq_stream gate/up (nested 2/3/4-bit table decode)", bound="hbm",
@@ -306,6 +336,9 @@ def main():
     ap.add_argument("--mwq", default="mixtral_mwq_decode",
                     help="comma-separated nested low-bit expert workloads reported in the "
                          "same line ('' for none)")
+    ap.add_argument("--floe", default="mixtral_floe_decode,mixtral_floe_decode_t1",
+                    help="comma-separated sparse-down workloads reported in the same line "
+                         "('' for none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (the known-size kernel "
                          "that scales the FETCH_SIZE/WRITE_SIZE counters)")
@@ -375,6 +408,21 @@ def main():
         del wl3
     if mw:
         out["mwq"] = mw
+    fl = []
+    for name in [s for s in args.floe.split(",") if s]:
+        wl4, r4 = run_gpu(name, args.steps, args.warmup)
+        c4 = wl4.cfg
+        w4 = r4["work"]
+        fl.append({"workload": name, "T": c4.T, "tokens_per_s": round(c4.T / (r4["ms"] / 1e3), 1),
+                   "ms_per_step": round(r4["ms"], 4), "lis": r4["lis"],
+                   "kept_channels": w4["kept_channels"],
+                   "bytes_vs_dense_bf16": round(w4["bytes"] / w4["dense_bf16_bytes"], 4),
+                   "layer_GBps": round(w4["bytes"] / (r4["ms"] * 1e-3) / 1e9, 1),
+                   "stages_us": r4["stages_us"], "timing": r4["timing"],
+                   "roofline": roofline(c4, r4)})
+        del wl4
+    if fl:
+        out["floe"] = fl
     reps = [run_replica(n, args.steps, args.warmup) for n in args.replica.split(",") if n]
     if reps:
         out["replica"] = reps

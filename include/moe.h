@@ -328,6 +328,46 @@ moe_status moe_layer_forward_mwq(const moe_layer_desc* L, const moe_mwq_experts*
                                  void* ws, size_t ws_bytes, unsigned flags, void* stream);
 moe_status moe_mwq_workspace_size(const moe_layer_desc* L, int T, size_t* bytes);
 
+/* ---- Contextual sparse down-projection ("FloE: On-the-Fly MoE Inference on
+ * Memory-constrained GPU" -- Core claim, What carries the argument; Assumptions
+ * & free parameters: one threshold per expert from the empirical distribution
+ * of activations).  Per (token, expert) row, with u = W_up x (INT2 up weights,
+ * fp32 accumulate), channel f is kept when |u_f| > threshold[e]; then
+ *   h_f = kept ? bf16_RNE( silu(W_gate[f] . x) * u_f ) : 0,   y_row = W_down h,
+ * so gate rows and down columns of pruned channels are never read. */
+
+/* Sparse-down experts (bf16 activations, SwiGLU):
+ *   up        INT2 up projection: q2, s2, z2 of moe_wmwq (N = d_ff, K = d_model,
+ *             decoded as the nested format at width 2); p3, a3, p4, a4 unused
+ *   w_gate    bf16 [E][d_ff][d_model]
+ *   w_down_t  bf16 [E][d_ff][d_model]: W_down transposed, row f holds the
+ *             down-projection column of channel f
+ *   threshold fp32 [E] */
+typedef struct {
+  const moe_wmwq* up;
+  const void* w_gate;
+  const void* w_down_t;
+  const float* threshold;
+} moe_floe_experts;
+
+/* Optional outputs of moe_layer_forward_floe; every pointer may be NULL. */
+typedef struct {
+  float* up_out;      /* [T*k][d_ff] fp32 u of each row, rows expert-major */
+  int32_t* kept;      /* [E] channels some row of the expert keeps */
+  int32_t* channels;  /* [E][d_ff] those channels ascending (first kept[e]) */
+} moe_floe_aux;
+
+/* The layer with sparse-down routed experts: route, permute (aux as in
+ * moe_layer_forward), INT2 up projection, per-expert kept channels, gate rows
+ * and down columns of kept channels only, shared experts (dense, L->shared),
+ * combine.  L->routed is not read.  Requires bf16 activations, SwiGLU, d_model
+ * and d_ff multiples of 512.  Workspace: moe_floe_workspace_size(L, T, &bytes). */
+moe_status moe_layer_forward_floe(const moe_layer_desc* L, const moe_floe_experts* W,
+                                  const void* x, int T, void* y, moe_dtype ydt, moe_aux* aux,
+                                  const moe_floe_aux* floe_out, void* ws, size_t ws_bytes,
+                                  unsigned flags, void* stream);
+moe_status moe_floe_workspace_size(const moe_layer_desc* L, int T, size_t* bytes);
+
 /* Instrumentation (not part of the layer's arithmetic).  While set, every
  * moe_layer_forward call made on this thread records events[i] (hipEvent_t
  * handles created by the caller) on its stream at the stage boundaries:

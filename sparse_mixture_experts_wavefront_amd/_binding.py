@@ -25,8 +25,8 @@ EXPORTED = ("moe_route_topk", "moe_permute", "moe_permute_workspace_size", "moe_
             "moe_workspace_size", "moe_replica_split", "moe_layer_forward_replica",
             "moe_replica_workspace_size", "moe_mwq_group", "moe_mwq_group_workspace_size",
             "moe_grouped_ffn_mwq", "moe_grouped_ffn_mwq_workspace_size", "moe_layer_forward_mwq",
-            "moe_mwq_workspace_size", "moe_set_stage_events", "moe_status_string",
-            "moe_last_error")
+            "moe_mwq_workspace_size", "moe_layer_forward_floe", "moe_floe_workspace_size",
+            "moe_set_stage_events", "moe_status_string", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -75,6 +75,15 @@ class MwqGroups(C.Structure):
                 ("row_assign", C.c_void_p), ("assign_row", C.c_void_p)]
 
 
+class FloeExperts(C.Structure):
+    _fields_ = [("up", C.POINTER(WMwq)), ("w_gate", C.c_void_p), ("w_down_t", C.c_void_p),
+                ("threshold", C.c_void_p)]
+
+
+class FloeAux(C.Structure):
+    _fields_ = [("up_out", C.c_void_p), ("kept", C.c_void_p), ("channels", C.c_void_p)]
+
+
 class Aux(C.Structure):
     _fields_ = [("logits", C.c_void_p), ("idx", C.c_void_p), ("gates", C.c_void_p),
                 ("counts", C.c_void_p), ("offsets", C.c_void_p), ("row_assign", C.c_void_p),
@@ -121,6 +130,10 @@ def lib():
                                                 i, p, i, C.POINTER(Aux), C.POINTER(MwqGroups), p,
                                                 sz, u, p]
             L.moe_mwq_workspace_size.argtypes = [C.POINTER(LayerDesc), i, C.POINTER(sz)]
+            L.moe_layer_forward_floe.argtypes = [C.POINTER(LayerDesc), C.POINTER(FloeExperts),
+                                                 p, i, p, i, C.POINTER(Aux), C.POINTER(FloeAux),
+                                                 p, sz, u, p]
+            L.moe_floe_workspace_size.argtypes = [C.POINTER(LayerDesc), i, C.POINTER(sz)]
             L.moe_set_stage_events.argtypes = [C.POINTER(C.c_void_p), i]
             L.moe_set_stage_events.restype = C.c_int
             L.moe_status_string.argtypes = [i]
@@ -131,7 +144,8 @@ def lib():
                       "moe_layer_forward", "moe_workspace_size", "moe_replica_split",
                       "moe_layer_forward_replica", "moe_replica_workspace_size",
                       "moe_mwq_group", "moe_grouped_ffn_mwq", "moe_layer_forward_mwq",
-                      "moe_mwq_workspace_size"):
+                      "moe_mwq_workspace_size", "moe_layer_forward_floe",
+                      "moe_floe_workspace_size"):
                 getattr(L, f).restype = C.c_int
             _lib = L
     return _lib

@@ -171,6 +171,25 @@ class MwqExperts:
         return m
 
 
+@dataclass
+class FloeExperts:
+    """Sparse-down experts: INT2 up (q2, s2, z2 as in MwqProj), bf16 gate [E][F][d],
+    bf16 W_down transposed [E][F][d], fp32 thresholds [E]."""
+    q2: torch.Tensor
+    s2: torch.Tensor
+    z2: torch.Tensor
+    w_gate: torch.Tensor
+    w_down_t: torch.Tensor
+    threshold: torch.Tensor
+    _keep: list = field(default_factory=list, repr=False)
+
+    def struct(self) -> B.FloeExperts:
+        up = B.WMwq(_p(self.q2), _p(self.s2), _p(self.z2), None, None, None, None)
+        self._keep = [up]
+        return B.FloeExperts(C.pointer(up), _p(self.w_gate), _p(self.w_down_t),
+                             _p(self.threshold))
+
+
 # ---- the five calls -----------------------------------------------------------
 
 def route_topk(x, w_router, b_router, k, logits=None, logits_given=False, flags=0):
@@ -245,7 +264,8 @@ class LayerRunner:
     (mwq_idx, mwq_counts, mwq_offsets, mwq_row_assign, mwq_assign_row)."""
 
     def __init__(self, layer: MoeLayer, T: int, out_dtype=torch.float32, want_aux=True,
-                 replica: Optional[MoeReplica] = None, mwq: Optional[MwqExperts] = None):
+                 replica: Optional[MoeReplica] = None, mwq: Optional[MwqExperts] = None,
+                 floe: Optional[FloeExperts] = None):
         self.layer = layer
         self.T = T
         dev = layer.w_router.device
@@ -254,11 +274,14 @@ class LayerRunner:
         self.rep = None if replica is None else replica.struct()
         self.mwq = mwq
         self.mwq_st = None if mwq is None else mwq.struct()
-        if replica is None and mwq is None:
+        self.floe = floe
+        self.floe_st = None if floe is None else floe.struct()
+        if replica is None and mwq is None and floe is None:
             self.ws = _ws(layer.workspace_size(T), dev)
         else:
             n = C.c_size_t(0)
-            fn = "moe_replica_workspace_size" if replica is not None else "moe_mwq_workspace_size"
+            fn = ("moe_replica_workspace_size" if replica is not None else
+                  "moe_mwq_workspace_size" if mwq is not None else "moe_floe_workspace_size")
             B.check(getattr(B.lib(), fn)(C.byref(self.desc), T, C.byref(n)), fn)
             self.ws = _ws(n.value, dev)
         self.lis_base = torch.empty(1, dtype=torch.float64, device=dev)
@@ -289,9 +312,25 @@ class LayerRunner:
             self.groups = B.MwqGroups(*[_p(g[n]) for n in ("mwq_idx", "mwq_counts", "mwq_offsets",
                                                            "mwq_row_assign", "mwq_assign_row")])
 
+        self.floe_aux = None
+        if want_aux and floe is not None:
+            F = layer.d_ff
+            g = dict(floe_u=torch.empty(max(T * k, 1), F, dtype=torch.float32, device=dev),
+                     floe_nnz=torch.empty(E, dtype=torch.int32, device=dev),
+                     floe_channels=torch.empty(E, F, dtype=torch.int32, device=dev))
+            self.aux_t.update(g)
+            self.floe_aux = B.FloeAux(_p(g["floe_u"]), _p(g["floe_nnz"]), _p(g["floe_channels"]))
+
     def __call__(self, x, flags=0, widths=None):
         aux = C.byref(self.aux) if self.aux is not None else None
-        if self.mwq is not None:
+        if self.floe is not None:
+            fa = C.byref(self.floe_aux) if self.floe_aux is not None else None
+            B.check(B.lib().moe_layer_forward_floe(C.byref(self.desc), C.byref(self.floe_st),
+                                                   _p(x), self.T, _p(self.y), _dt(self.y), aux,
+                                                   fa, _p(self.ws), self.ws.numel(), flags,
+                                                   _stream()),
+                    "moe_layer_forward_floe")
+        elif self.mwq is not None:
             if widths is None:
                 raise ValueError("a layer with nested experts needs the widths [T][k]")
             groups = C.byref(self.groups) if self.groups is not None else None
@@ -316,12 +355,14 @@ class LayerRunner:
 
 def layer_forward(layer: MoeLayer, x, out_dtype=torch.float32, flags=0, logits=None,
                   replica: Optional[MoeReplica] = None, mwq: Optional[MwqExperts] = None,
-                  widths=None):
+                  widths=None, floe: Optional[FloeExperts] = None):
     """One layer call; returns (y, aux dict of device tensors).  With ``replica``
     aux describes the split routing and aux["lis_base"] the router's own LIS;
     with ``mwq`` (and ``widths`` [T][k] int32) the routed experts are nested
-    low-bit ones and aux adds the (expert, width) grouping."""
-    r = LayerRunner(layer, x.shape[0], out_dtype, replica=replica, mwq=mwq)
+    low-bit ones and aux adds the (expert, width) grouping; with ``floe`` the
+    routed experts are sparse-down ones and aux adds floe_u (up outputs, rows
+    expert-major), floe_nnz and floe_channels (kept channels per expert)."""
+    r = LayerRunner(layer, x.shape[0], out_dtype, replica=replica, mwq=mwq, floe=floe)
     if logits is not None:
         r.aux_t["logits"].copy_(logits)
         flags |= B.MOE_F_LOGITS_GIVEN

@@ -779,3 +779,164 @@ moe_status moe_layer_forward_mwq(const moe_layer_desc* L, const moe_mwq_experts*
 }
 
 }  // extern "C"
+
+// ---- contextual sparse down-projection --------------------------------------
+
+namespace {
+
+moe_status check_floe_experts(const moe_floe_experts* w, int T, int d, int F, int k) {
+  REQUIRE(w, "sparse-down experts must not be NULL");
+  REQUIRE(w->up, "sparse-down experts: up must not be NULL");
+  REQUIRE_PTR(w->up->q2, "up q2");
+  REQUIRE(w->up->s2 && w->up->z2, "up s2/z2 must not be NULL");
+  REQUIRE(aligned(w->up->s2, 8) && aligned(w->up->z2, 8), "up s2/z2 must be 8-byte aligned");
+  REQUIRE_PTR(w->w_gate, "w_gate");
+  REQUIRE_PTR(w->w_down_t, "w_down_t");
+  REQUIRE_PTR(w->threshold, "threshold");
+  if (const char* why = floe_unsupported(T, d, F, k)) return fail(MOE_ERR_UNSUPPORTED, "%s", why);
+  return MOE_OK;
+}
+
+struct FloeLayerWs {
+  LayerWs base;
+  float* U;
+  uint8_t* flags;
+  int32_t *list, *nnz;
+  void* Hc;
+  size_t total;
+};
+
+FloeLayerWs carve_floe_layer(const moe_layer_desc* L, int T, void* ws) {
+  const int E = L->n_experts, k = L->top_k, d = L->d_model, F = L->d_ff;
+  const size_t n = (size_t)T * k;
+  Carver c(ws);
+  FloeLayerWs m;
+  LayerWs& w = m.base;
+  w.logits = (float*)c.take((size_t)T * E * 4);
+  w.idx = (int32_t*)c.take(n * 4);
+  w.gates = (float*)c.take(n * 4);
+  w.counts = (int32_t*)c.take((size_t)E * 4);
+  w.offsets = (int32_t*)c.take((size_t)(E + 1) * 4);
+  w.row_assign = (int32_t*)c.take(n * 4);
+  w.assign_row = (int32_t*)c.take(n * 4);
+  w.lis = (double*)c.take(8);
+  w.perm_ws = c.take(permute_ws_bytes(T, E, k));
+  w.H = nullptr;
+  w.down_splits = floe_down_splits(d, E);
+  w.y_rows = (float*)c.take(n * d * 4 * w.down_splits);
+  const int Fs = L->n_shared * L->d_ff_shared;
+  w.Hs = L->n_shared ? c.take((size_t)T * Fs * 2) : nullptr;
+  w.y_shared = L->n_shared ? (float*)c.take((size_t)T * d * 4) : nullptr;
+  w.counts2 = w.offsets2 = w.row_assign2 = w.assign_row2 = nullptr;
+  w.lis2 = nullptr;
+  m.U = (float*)c.take(n * F * 4);
+  m.flags = (uint8_t*)c.take((size_t)E * F);
+  m.list = (int32_t*)c.take((size_t)E * F * 4);
+  m.nnz = (int32_t*)c.take((size_t)E * 4);
+  m.Hc = c.take(n * F * 2);
+  m.total = w.total = c.off;
+  return m;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_floe_workspace_size(const moe_layer_desc* L, int T, size_t* bytes) {
+  REQUIRE(bytes, "bytes must not be NULL");
+  moe_status s = check_layer(L, T, 0, false);
+  if (s != MOE_OK) return s;
+  *bytes = carve_floe_layer(L, T, nullptr).total;
+  return ok();
+}
+
+moe_status moe_layer_forward_floe(const moe_layer_desc* L, const moe_floe_experts* W,
+                                  const void* x, int T, void* y, moe_dtype ydt, moe_aux* aux,
+                                  const moe_floe_aux* floe_out, void* ws, size_t ws_bytes,
+                                  unsigned flags, void* stream) {
+  moe_status s = check_layer(L, T, flags, false);
+  if (s != MOE_OK) return s;
+  const int E = L->n_experts, k = L->top_k, d = L->d_model, F = L->d_ff;
+  if (L->act_dtype != MOE_DT_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "sparse-down experts need bf16 activations");
+  if (L->act != MOE_ACT_SWIGLU)
+    return fail(MOE_ERR_UNSUPPORTED, "sparse-down experts are SwiGLU experts");
+  s = check_floe_experts(W, T, d, F, k);
+  if (s != MOE_OK) return s;
+  REQUIRE(valid_dtype(ydt), "unknown output dtype %d", (int)ydt);
+  if (T > 0) {
+    REQUIRE_PTR(x, "x");
+    REQUIRE_PTR(y, "y");
+  }
+  if (aux) {
+    OPT_PTR(aux->logits, "aux.logits"); OPT_PTR(aux->idx, "aux.idx");
+    OPT_PTR(aux->gates, "aux.gates"); OPT_PTR(aux->counts, "aux.counts");
+    OPT_PTR(aux->offsets, "aux.offsets"); OPT_PTR(aux->row_assign, "aux.row_assign");
+    OPT_PTR(aux->assign_row, "aux.assign_row"); OPT_PTR(aux->lis, "aux.lis");
+  }
+  if (floe_out) {
+    OPT_PTR(floe_out->up_out, "floe_out.up_out");
+    OPT_PTR(floe_out->kept, "floe_out.kept");
+    OPT_PTR(floe_out->channels, "floe_out.channels");
+  }
+  if ((flags & MOE_F_LOGITS_GIVEN) && !(aux && aux->logits))
+    return fail(MOE_ERR_INVALID_ARG, "MOE_F_LOGITS_GIVEN needs aux->logits");
+  const size_t need = carve_floe_layer(L, T, nullptr).total;
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "the layer needs %zu workspace bytes (got %zu)", need,
+                ws ? ws_bytes : (size_t)0);
+  REQUIRE(aligned(ws, 256), "ws must be 256-byte aligned");
+  if (flags & MOE_F_VALIDATE_ONLY) return ok();
+  if (T == 0) return ok();
+
+  hipStream_t st = (hipStream_t)stream;
+  FloeLayerWs m = carve_floe_layer(L, T, ws);
+  LayerWs& w = m.base;
+  float* logits = (aux && aux->logits) ? aux->logits : w.logits;
+  int32_t* idx = (aux && aux->idx) ? aux->idx : w.idx;
+  float* gates = (aux && aux->gates) ? aux->gates : w.gates;
+  int32_t* counts = (aux && aux->counts) ? aux->counts : w.counts;
+  int32_t* offsets = (aux && aux->offsets) ? aux->offsets : w.offsets;
+  int32_t* row_assign = (aux && aux->row_assign) ? aux->row_assign : w.row_assign;
+  int32_t* assign_row = (aux && aux->assign_row) ? aux->assign_row : w.assign_row;
+  double* lis = (aux && aux->lis) ? aux->lis : w.lis;
+
+  stage(0, st);
+  hipError_t e = launch_route_topk(x, L->act_dtype, L->w_router, L->b_router, T, d, E, k, logits,
+                                   idx, gates, (flags & MOE_F_LOGITS_GIVEN) != 0, st);
+  if (e != hipSuccess) return hip_status(e, "route_topk");
+  stage(1, st);
+  e = launch_permute(idx, T, E, k, counts, offsets, row_assign, assign_row, lis, w.perm_ws, st);
+  if (e != hipSuccess) return hip_status(e, "permute");
+  stage(2, st);
+  FloeProblem p{};
+  p.T = T; p.d = d; p.F = F; p.E = E; p.k = k; p.x = x; p.w = W; p.offsets = offsets;
+  p.row_assign = row_assign; p.gate = gates;
+  p.U = (floe_out && floe_out->up_out) ? floe_out->up_out : m.U;
+  p.flags = m.flags;
+  p.list = (floe_out && floe_out->channels) ? floe_out->channels : m.list;
+  p.nnz = (floe_out && floe_out->kept) ? floe_out->kept : m.nnz;
+  p.Hc = (u16*)m.Hc;
+  p.y_rows = w.y_rows;
+  p.rows = T * k;
+  p.splits = w.down_splits;
+  e = launch_floe_ffn(p, st, g_stage_on ? g_stage_ev[3] : nullptr);
+  if (e != hipSuccess) return hip_status(e, "sparse-down ffn");
+  stage(4, st);
+  if (L->n_shared > 0) {
+    FfnProblem q{};
+    q.T = T; q.d = d; q.F = L->n_shared * L->d_ff_shared; q.E = 1; q.k = 1;
+    q.act = MOE_ACT_SWIGLU; q.dt = L->act_dtype; q.x = x; q.w = &L->shared;
+    q.offsets = nullptr; q.row_assign = nullptr; q.gate = nullptr;
+    q.y_rows = w.y_shared; q.H = w.Hs; q.rows = T;
+    e = launch_grouped_ffn(q, st);
+    if (e != hipSuccess) return hip_status(e, "shared experts");
+  }
+  stage(5, st);
+  e = launch_combine(w.y_rows, assign_row, T, k, d, w.y_shared, y, ydt, st, w.down_splits,
+                     (size_t)T * k * d);
+  stage(6, st);
+  return hip_status(e, "combine");
+}
+
+}  // extern "C"

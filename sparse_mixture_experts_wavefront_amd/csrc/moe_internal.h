@@ -118,6 +118,35 @@ struct MwqProblem {
 const char* mwq_ffn_unsupported(int T, int d, int F, int k);
 hipError_t launch_mwq_ffn(const MwqProblem& p, hipStream_t s, hipEvent_t mid = nullptr);
 
+// INT2 up projection of the contextual sparse down-projection: U [rows][F] fp32
+// for every row of every expert (offsets [E+1]) and flags [E][F] = 1 where some
+// row of the expert has |U| > thr[e].  Experts without rows leave their flags.
+hipError_t launch_int2_up(const void* x, int T, int d, int F, int E, int k, const moe_wmwq* w,
+                          const int32_t* offsets, const int32_t* row_assign, const float* thr,
+                          float* U, uint8_t* flags, hipStream_t s);
+
+// Contextual sparse down-projection (rows grouped by expert, offsets [E+1]).
+struct FloeProblem {
+  int T, d, F, E, k;
+  const void* x;                 // [T][d] bf16
+  const moe_floe_experts* w;
+  const int32_t* offsets;        // [E+1]
+  const int32_t* row_assign;     // row -> flat assignment
+  const float* gate;             // gate per flat assignment, or NULL (1)
+  float* U;                      // [rows][F] fp32 up outputs
+  uint8_t* flags;                // [E][F]
+  int32_t* list;                 // [E][F] kept channels of each expert, ascending
+  int32_t* nnz;                  // [E]
+  u16* Hc;                       // [rows][F] bf16 hidden values of the kept channels
+  float* y_rows;                 // splits x [rows][d] gate-scaled partial sums
+  int rows;
+  int splits;
+};
+// Channel-list slices of the sparse down pass (pure function of the shapes).
+int floe_down_splits(int d, int E);
+const char* floe_unsupported(int T, int d, int F, int k);
+hipError_t launch_floe_ffn(const FloeProblem& p, hipStream_t s, hipEvent_t mid = nullptr);
+
 // y[t] = sum over slots j, then over K slices s, of y_rows[s * split_stride +
 // assign_row[t*k+j] * d], plus y_shared[t]; fixed order, so deterministic.
 hipError_t launch_combine(const float* y_rows, const int32_t* assign_row, int T, int k, int d,

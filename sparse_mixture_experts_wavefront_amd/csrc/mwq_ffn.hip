@@ -51,7 +51,10 @@
 namespace moe {
 namespace {
 
-constexpr int kMModeGateUp = 0, kMModeRelu = 1, kMModeDown = 2;
+// kMModeUp: one INT2 matrix (the width-2 base alone), fp32 outputs U and, per
+// output column, whether any row of the expert exceeds the expert's threshold in
+// magnitude (the channel flags of the contextual sparse down-projection)
+constexpr int kMModeGateUp = 0, kMModeRelu = 1, kMModeDown = 2, kMModeUp = 3;
 
 struct MwqArgs {
   const u16* X;            // gate/up: x [T][ldx]; down: H [rows][ldx]
@@ -60,7 +63,11 @@ struct MwqArgs {
   int k;
   moe_wmwq W0, W1;         // gate/up: gate, up (ReLU: W_in in W0); down: W_down in W0
   int N, K;
-  const int32_t* offsets;  // [3E+1], group 3e + j = expert e at width 2 + j
+  const int32_t* offsets;  // [gpe*E+1], group gpe*e + j = expert e at width 2 + j
+  int gpe;                 // groups per expert: 3 (nested widths) or 1 (INT2 only)
+  float* U;                // up mode: output [rows][N] fp32
+  const float* thr;        // up mode: [E] magnitude thresholds
+  uint8_t* flags;          // up mode: [E][N] 1 where a row of the expert keeps the channel
   u16* H;                  // gate/up output [rows][N]
   float* Y;                // down output [rows][N]
   const int32_t* gate_map; // down: row -> flat assignment (gate index)
@@ -153,12 +160,17 @@ void mwq_stream_kernel(MwqArgs p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int e = blockIdx.x / p.nblk_per_expert;
   const int nb = blockIdx.x - e * p.nblk_per_expert;
-  const int* off = p.offsets + 3 * e;
+  const int* off = p.offsets + p.gpe * e;
   const int row0 = __builtin_amdgcn_readfirstlane(off[0]);
-  const int b3 = __builtin_amdgcn_readfirstlane(off[1]) - row0;  // first width-3 row
-  const int b4 = __builtin_amdgcn_readfirstlane(off[2]) - row0;  // first width-4 row
-  const int cnt = __builtin_amdgcn_readfirstlane(off[3]) - row0;
+  const int cnt = __builtin_amdgcn_readfirstlane(off[p.gpe]) - row0;
+  // first width-3 and width-4 rows (one group per expert: every row at width 2)
+  const int b3 = p.gpe == 3 ? __builtin_amdgcn_readfirstlane(off[1]) - row0 : cnt;
+  const int b4 = p.gpe == 3 ? __builtin_amdgcn_readfirstlane(off[2]) - row0 : cnt;
   if (cnt <= 0) return;
+  __shared__ int uflag[RM];  // up mode: per output column, some row kept it
+  if constexpr (MODE == kMModeUp) {
+    if (tid < RM) uflag[tid] = 0;
+  }
   const int n0 = nb * NOUT;
   const int r16 = lane & 15, g = lane >> 4;
   const int NI = p.K >> 9;              // 512-wide K iterations
@@ -178,8 +190,11 @@ void mwq_stream_kernel(MwqArgs p) {
       const size_t o = ((size_t)e * p.N + n0 + (r % RM)) * G + 4 * c;
       const uint2 vs = *(const uint2*)((second ? p.W1.s2 : p.W0.s2) + o);
       const uint2 vz = *(const uint2*)((second ? p.W1.z2 : p.W0.z2) + o);
-      const uint2 v3 = *(const uint2*)((second ? p.W1.a3 : p.W0.a3) + o);
-      const uint2 v4 = *(const uint2*)((second ? p.W1.a4 : p.W0.a4) + o);
+      // INT2-only weights have no residual magnitudes
+      const u16* a3 = second ? p.W1.a3 : p.W0.a3;
+      const u16* a4 = second ? p.W1.a4 : p.W0.a4;
+      const uint2 v3 = a3 ? *(const uint2*)(a3 + o) : make_uint2(0u, 0u);
+      const uint2 v4 = a4 ? *(const uint2*)(a4 + o) : make_uint2(0u, 0u);
       uint2* dst = md + r * GP + 4 * c;
       // entry j: the low (j even) or high (j odd) halves of word j / 2
       dst[0] = make_uint2(perm(vz.x, vs.x, 0x05040100u), perm(v4.x, v3.x, 0x05040100u));
@@ -372,6 +387,10 @@ void mwq_stream_kernel(MwqArgs p) {
         p.H[orow * p.N + n0 + col] = f32_to_bf16(silu_f32(gv) * uv);
       } else if constexpr (MODE == kMModeRelu) {
         p.H[orow * p.N + n0 + col] = f32_to_bf16(fmaxf(part(col), 0.0f));
+      } else if constexpr (MODE == kMModeUp) {
+        const float u = part(col);
+        p.U[orow * p.N + n0 + col] = u;
+        if (fabsf(u) > p.thr[e]) uflag[col] = 1;
       } else {
         const float gs = p.gate ? p.gate[p.gate_map[orow]] : 1.0f;
         p.Y[orow * p.N + n0 + col] = gs * part(col);
@@ -380,6 +399,12 @@ void mwq_stream_kernel(MwqArgs p) {
     __syncthreads();
   };
 
+  if constexpr (MODE == kMModeUp) {
+    for (int mbase = 0; mbase < cnt; mbase += 16) pass(std::integral_constant<int, 1>{}, mbase);
+    __syncthreads();
+    if (tid < RM) p.flags[(size_t)e * p.N + n0 + tid] = (uint8_t)uflag[tid];
+    return;
+  }
   for (int mbase = 0; mbase < cnt; mbase += 16) {
     const int hi = min(mbase + 16, cnt);
     const int wm = (mbase < b3 ? 1 : 0) | ((mbase < b4 && hi > b3) ? 2 : 0) | (hi > b4 ? 4 : 0);
@@ -439,6 +464,7 @@ hipError_t launch_mwq_ffn(const MwqProblem& p, hipStream_t s, hipEvent_t mid) {
   a.N = p.F;
   a.K = p.d;
   a.offsets = p.offsets;
+  a.gpe = 3;
   a.H = (u16*)p.H;
   a.xbytes = (uint32_t)((size_t)p.T * p.d * 2);
   hipError_t e = relu ? launch_mwq_mode<kMModeRelu, kRmGateUp>(a, p.E, s)
@@ -458,11 +484,34 @@ hipError_t launch_mwq_ffn(const MwqProblem& p, hipStream_t s, hipEvent_t mid) {
   b.N = p.d;
   b.K = p.F;
   b.offsets = p.offsets;
+  b.gpe = 3;
   b.Y = p.y_rows;
   b.gate_map = p.row_assign;
   b.gate = p.gate;
   b.xbytes = (uint32_t)((size_t)p.rows * p.F * 2);
   return launch_mwq_mode<kMModeDown, kRmDown>(b, p.E, s);
+}
+
+hipError_t launch_int2_up(const void* x, int T, int d, int F, int E, int k, const moe_wmwq* w,
+                          const int32_t* offsets, const int32_t* row_assign, const float* thr,
+                          float* U, uint8_t* flags, hipStream_t s) {
+  if (mwq_ffn_unsupported(T, d, F, k)) return hipErrorInvalidValue;
+  MwqArgs a{};
+  a.X = (const u16*)x;
+  a.ldx = d;
+  a.gather = row_assign;
+  a.k = k;
+  a.W0 = *w;
+  a.W1 = *w;
+  a.N = F;
+  a.K = d;
+  a.offsets = offsets;
+  a.gpe = 1;
+  a.U = U;
+  a.thr = thr;
+  a.flags = flags;
+  a.xbytes = (uint32_t)((size_t)T * d * 2);
+  return launch_mwq_mode<kMModeUp, kRmDown>(a, E, s);
 }
 
 }  // namespace moe

@@ -4,7 +4,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .api import ExpertWeights, Int4Proj, MoeLayer, MoeReplica, MwqExperts, MwqProj
+from .api import (ExpertWeights, FloeExperts, Int4Proj, MoeLayer, MoeReplica, MwqExperts,
+                  MwqProj)
 
 
 def _t(a: np.ndarray, dev, bf16: bool):
@@ -24,8 +25,8 @@ def to_device(wl, device="cuda"):
     """Returns (MoeLayer, x) for a ``workloads.Workload``."""
     cfg = wl.cfg
     bf = cfg.dtype == "bf16"
-    if cfg.mwq:
-        routed = ExpertWeights()   # nested experts: see mwq_to_device
+    if cfg.mwq or cfg.floe:
+        routed = ExpertWeights()   # nested or sparse-down experts: see mwq_to_device, floe_to_device
     elif cfg.int4:
         routed = ExpertWeights(q_gate=None if wl.q_gate is None else _q(wl.q_gate, device),
                                q_up=_q(wl.q_up, device), q_down=_q(wl.q_down, device))
@@ -62,3 +63,14 @@ def mwq_to_device(wl, device="cuda"):
                     None if wl.m_gate is None else _m(wl.m_gate, device))
     widths = torch.from_numpy(np.ascontiguousarray(wl.bits, dtype=np.int32)).to(device)
     return ex, widths
+
+
+def floe_to_device(wl, device="cuda"):
+    """FloeExperts for a sparse-down ``workloads.Workload`` (W_down transposed on
+    the device to channel-major [E][F][d])."""
+    f16 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.float16).to(device)
+    wd = _t(wl.w_down, device, True)
+    return FloeExperts(torch.from_numpy(np.ascontiguousarray(wl.u2_up.q2)).to(device),
+                       f16(wl.u2_up.s2), f16(wl.u2_up.z2), _t(wl.w_gate, device, True),
+                       wd.transpose(1, 2).contiguous(),
+                       torch.from_numpy(np.ascontiguousarray(wl.floe_thr)).to(device))

@@ -324,3 +324,39 @@ def test_mwq_validation_and_workspace(L, B):
     assert ffn(d=200) == B.MOE_ERR_INVALID_ARG
     assert ffn(nbytes=100) == B.MOE_ERR_WORKSPACE
     assert ffn(act=1, ex=_mwq_experts(B, gate=False)) == B.MOE_OK
+
+
+def test_floe_validation_and_workspace(L, B):
+    VO = B.MOE_F_VALIDATE_ONLY
+    Ld = _desc(B)
+    Ld.d_model, Ld.d_ff = 512, 1024
+    Ld.routed = B.Experts()
+    n = C.c_size_t(0)
+    assert L.moe_floe_workspace_size(C.byref(Ld), 16, C.byref(n)) == B.MOE_OK
+    assert n.value >= 16 * 2 * 1024 * (4 + 2) + 8 * 1024 * 5   # U, Hc, flags, lists
+    ws = C.c_void_p(FAKE * 16)
+
+    def experts(up=True, gate=True, down=True, thr=True, s2=True):
+        w = B.WMwq(_addr(40), _addr(41) if s2 else None, _addr(42), None, None, None, None)
+        ex = B.FloeExperts(C.pointer(w) if up else None, _addr(43) if gate else None,
+                           _addr(44) if down else None, _addr(45) if thr else None)
+        ex._keep = [w]
+        return ex
+
+    def fwd(ex, Ldesc=None, nbytes=None, T=16):
+        return L.moe_layer_forward_floe(C.byref(Ldesc or Ld), None if ex is None else C.byref(ex),
+                                        _addr(1), T, _addr(2), 0, None, None, ws,
+                                        n.value if nbytes is None else nbytes, VO, None)
+    assert fwd(experts()) == B.MOE_OK
+    assert fwd(experts(), nbytes=n.value - 1) == B.MOE_ERR_WORKSPACE
+    assert fwd(None) == B.MOE_ERR_INVALID_ARG
+    for kw in ("up", "gate", "down", "thr", "s2"):
+        assert fwd(experts(**{kw: False})) == B.MOE_ERR_INVALID_ARG, kw
+    Lr = _desc(B)
+    Lr.d_model, Lr.d_ff, Lr.act = 512, 1024, 1
+    Lr.routed = B.Experts()
+    assert fwd(experts(), Ldesc=Lr) == B.MOE_ERR_UNSUPPORTED            # SwiGLU only
+    Lk = _desc(B)
+    Lk.d_model, Lk.d_ff = 640, 1024
+    Lk.routed = B.Experts()
+    assert fwd(experts(), Ldesc=Lk) == B.MOE_ERR_UNSUPPORTED            # d_model % 512
