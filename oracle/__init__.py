@@ -69,11 +69,15 @@ def lib():
             L.orc_replica_split.argtypes = [p, i, i, i, i, p]
             L.orc_dequant_mwq.argtypes = [p, p, p, p, p, p, p, i64, i, i, i, p]
             L.orc_floe_rows.argtypes = [p, i, i, p, p, p, p, p, p, i, p, p, p, p]
+            L.orc_log_softmax_rows.argtypes = [p, i, i, p]
+            L.orc_grid_topk.argtypes = [p, p, i, i, i, i, p, p]
+            L.orc_atomic_rows.argtypes = [p, i, p, p, i, p, p, i, i, p, i, p]
             L.orc_round_bf16.argtypes = [d]
             L.orc_round_bf16.restype = d
             for f in ("orc_router_logits", "orc_topk_gates", "orc_permute", "orc_expert_rows",
                       "orc_combine", "orc_dequant_int4", "orc_replica_split", "orc_dequant_mwq",
-                      "orc_floe_rows"):
+                      "orc_floe_rows", "orc_log_softmax_rows", "orc_grid_topk",
+                      "orc_atomic_rows"):
                 getattr(L, f).restype = C.c_int
             _lib = L
     return _lib
@@ -268,6 +272,72 @@ def floe_rows(x, w_gate, w_up_dec, w_down, thr, tok, exp_id, u_given=None):
                                _ptr(thr), _ptr(tok), _ptr(exp_id), n, _ptr(ug), _ptr(u),
                                _ptr(keep), _ptr(Y)), "floe_rows")
     return Y, u, keep
+
+
+def log_softmax_rows(l):
+    l = np.ascontiguousarray(l, np.float32)
+    T, n = l.shape
+    out = np.empty_like(l)
+    _check(lib().orc_log_softmax_rows(_ptr(l), T, n, _ptr(out)), "log_softmax_rows")
+    return out
+
+
+def grid_topk(pr, pc, K):
+    """Exact top-K of S_ij = fp32(pr[i] + pc[j]) per token (ties to the lower id
+    i*Nc + j), ids in ascending order, gates = softmax over the chosen S."""
+    pr = np.ascontiguousarray(pr, np.float32)
+    pc = np.ascontiguousarray(pc, np.float32)
+    T, Nr = pr.shape
+    Nc = pc.shape[1]
+    idx = np.empty((T, K), np.int32)
+    gate = np.empty((T, K), np.float32)
+    _check(lib().orc_grid_topk(_ptr(pr), _ptr(pc), T, Nr, Nc, K, _ptr(idx), _ptr(gate)),
+           "grid_topk")
+    return idx, gate
+
+
+def atomic_rows(x, w_in, w_out_t, idx, gate, act, tok):
+    """fp64 outputs of the atomic experts of tokens ``tok`` (see orc_atomic_rows)."""
+    x = np.ascontiguousarray(x, np.uint16)
+    w_in = np.ascontiguousarray(w_in, np.uint16)
+    w_out_t = np.ascontiguousarray(w_out_t, np.uint16)
+    idx = np.ascontiguousarray(idx, np.int32)
+    gate = np.ascontiguousarray(gate, np.float32)
+    tok = np.ascontiguousarray(tok, np.int32)
+    d, N = w_out_t.shape
+    Y = np.empty((tok.size, d), np.float64)
+    _check(lib().orc_atomic_rows(_ptr(x), d, _ptr(w_in), _ptr(w_out_t), N, _ptr(idx), _ptr(gate),
+                                 idx.shape[1], 0 if act == "silu" else 1, _ptr(tok), tok.size,
+                                 _ptr(Y)), "atomic_rows")
+    return Y
+
+
+def atomic_layer_forward(wl, pr=None, pc=None, tokens=None):
+    """The atomic-expert layer on the CPU: router logits of the grid's rows and
+    columns, their log-softmax, exact top-K over the grid with gates, the
+    expert-major permutation over N = nr*nc experts with LIS, the atomic expert
+    outputs and the shared MLP.  ``pr``/``pc``: given row / column
+    log-probabilities (e.g. the GPU's), on which the selection is taken."""
+    cfg = wl.cfg
+    T, K, N = cfg.T, cfg.k, cfg.nr * cfg.nc
+    lr = router_logits(wl.x, wl.w_router, None)
+    lc = router_logits(wl.x, wl.w_col, None)
+    own_pr, own_pc = log_softmax_rows(lr), log_softmax_rows(lc)
+    PR = own_pr if pr is None else np.ascontiguousarray(pr, np.float32)
+    PC = own_pc if pc is None else np.ascontiguousarray(pc, np.float32)
+    idx, gate = grid_topk(PR, PC, K)
+    counts, offsets, row_assign, assign_row, lis = permute(idx, N)
+    out = dict(logits_r=lr, logits_c=lc, pr=own_pr, pc=own_pc, idx=idx, gate=gate, counts=counts,
+               offsets=offsets, row_assign=row_assign, assign_row=assign_row, lis=lis)
+    toks = np.arange(T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
+    Y = atomic_rows(wl.x, wl.w_in, wl.w_out_t, idx, gate, cfg.act, toks)
+    Ys = None
+    if cfg.n_shared:
+        Ys = expert_rows(wl.x, wl.ws_gate[None], wl.ws_up[None], wl.ws_down[None], "swiglu",
+                         ROUND_BF16, toks, np.zeros_like(toks))
+    out["tokens"] = toks
+    out["y"] = combine(Y, None, np.ones((toks.size, 1), np.float32), Ys)
+    return out
 
 
 # --- the layer -----------------------------------------------------------

@@ -448,3 +448,119 @@ int orc_floe_rows(const uint16_t* x, int d, int F, const uint16_t* w_gate, const
   }
   return err ? ORC_ERR_ARG : ORC_OK;
 }
+
+/* ---- Atomic experts on a Cartesian router grid ------------------------------
+ * "OmniMoE: An Efficient MoE by Orchestrating Atomic Experts at Scale" -- What
+ * carries the argument and Core claim: an atomic expert is one vector pair
+ * (w_in, w_out) with output act(x . w_in) w_out (Eq. 4); the router treats an
+ * expert id as a cell (i, j) of an Nr x Nc grid and scores it as the sum of a
+ * row and a column log-probability (Eq. 8); each token assembles its top-K
+ * atomic experts (Dynamic Expert Assembly). */
+
+/* Row-wise log-softmax of an [T][n] fp32 matrix: fp64 inside, rounded once. */
+int orc_log_softmax_rows(const float* l, int T, int n, float* out) {
+  if (T < 0 || n < 1 || (T > 0 && (!l || !out))) return ORC_ERR_ARG;
+  for (int t = 0; t < T; ++t) {
+    const float* r = l + (size_t)t * n;
+    double m = r[0];
+    for (int i = 1; i < n; ++i) if (r[i] > m) m = r[i];
+    double s = 0.0;
+    for (int i = 0; i < n; ++i) s += exp((double)r[i] - m);
+    double lse = m + log(s);
+    for (int i = 0; i < n; ++i) out[(size_t)t * n + i] = (float)((double)r[i] - lse);
+  }
+  return ORC_OK;
+}
+
+typedef struct {
+  float s;
+  int32_t id;
+} orc_scored;
+
+static int cmp_scored(const void* a, const void* b) {
+  const orc_scored* x = (const orc_scored*)a;
+  const orc_scored* y = (const orc_scored*)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return (x->id < y->id) ? -1 : (x->id > y->id);
+}
+
+static int cmp_int32(const void* a, const void* b) {
+  int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+/* Exact top-K over the grid S_ij = fp32(pr[t][i] + pc[t][j]), expert id
+ * n = i*Nc + j: (i,j) precedes (i',j') iff S > S', or S == S' and n < n'.  The
+ * K chosen ids of a token are written in ascending id order (the slot order);
+ * gates are the softmax over their S, fp64 inside (sum in slot order), rounded
+ * once. */
+int orc_grid_topk(const float* pr, const float* pc, int T, int Nr, int Nc, int K, int32_t* idx,
+                  float* gate) {
+  if (T < 0 || Nr < 1 || Nc < 1 || K < 1 || (int64_t)K > (int64_t)Nr * Nc || !idx || !gate)
+    return ORC_ERR_ARG;
+  const int N = Nr * Nc;
+  int err = 0;
+#pragma omp parallel
+  {
+    orc_scored* sc = (orc_scored*)malloc(sizeof(orc_scored) * (size_t)N);
+    double* w = (double*)malloc(sizeof(double) * (size_t)K);
+    if (!sc || !w) {
+#pragma omp atomic write
+      err = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int t = 0; t < T; ++t) {
+      if (!sc || !w) continue;
+      for (int i = 0; i < Nr; ++i)
+        for (int j = 0; j < Nc; ++j) {
+          float s = pr[(size_t)t * Nr + i] + pc[(size_t)t * Nc + j];
+          sc[i * Nc + j].s = s;
+          sc[i * Nc + j].id = i * Nc + j;
+        }
+      qsort(sc, (size_t)N, sizeof(orc_scored), cmp_scored);
+      int32_t* out = idx + (size_t)t * K;
+      double m = (double)sc[0].s;
+      for (int s = 0; s < K; ++s) out[s] = sc[s].id;
+      qsort(out, (size_t)K, sizeof(int32_t), cmp_int32);
+      double sum = 0.0;
+      for (int s = 0; s < K; ++s) {
+        int n = out[s];
+        float sv = pr[(size_t)t * Nr + n / Nc] + pc[(size_t)t * Nc + n % Nc];
+        w[s] = exp((double)sv - m);
+        sum += w[s];
+      }
+      for (int s = 0; s < K; ++s) gate[(size_t)t * K + s] = (float)(w[s] / sum);
+    }
+    free(sc);
+    free(w);
+  }
+  return err ? ORC_ERR_ARG : ORC_OK;
+}
+
+/* Atomic-expert rows, per token p of the list (t = tok[p]):
+ *   Y[p] = sum over slots s (ascending) of w_out[:, n_s] * bf16_RNE(g_s * act(x_t . w_in[n_s]))
+ * fp64 accumulation; act 0 = SiLU, 1 = ReLU.  x [T][d], w_in [N][d], w_out
+ * [d][N] (bf16 bits), idx/gate [T][K]. */
+int orc_atomic_rows(const uint16_t* x, int d, const uint16_t* w_in, const uint16_t* w_out, int N,
+                    const int32_t* idx, const float* gate, int K, int act, const int32_t* tok,
+                    int n, double* Y) {
+  if (d < 1 || N < 1 || K < 1 || n < 0 || !x || !w_in || !w_out || !idx || !gate || !Y)
+    return ORC_ERR_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int p = 0; p < n; ++p) {
+    size_t t = (size_t)tok[p];
+    double* y = Y + (size_t)p * d;
+    for (int i = 0; i < d; ++i) y[i] = 0.0;
+    for (int s = 0; s < K; ++s) {
+      size_t e = (size_t)idx[t * K + s];
+      double u = 0.0;
+      for (int i = 0; i < d; ++i)
+        u += bf16_to_double(x[t * d + i]) * bf16_to_double(w_in[e * d + i]);
+      double h = act == 0 ? u / (1.0 + exp(-u)) : (u > 0.0 ? u : 0.0);
+      double a = orc_round_bf16((double)gate[t * K + s] * h);
+      for (int i = 0; i < d; ++i) y[i] += a * bf16_to_double(w_out[(size_t)i * N + e]);
+    }
+  }
+  return ORC_OK;
+}

@@ -682,6 +682,148 @@ def test_floe_layer_keep_all_is_the_plain_layer():
     assert np.array_equal(fl["floe_nnz"], np.where(ref["counts"] > 0, 512, 0))
 
 
+# ---------------------------------------------------------------- atomic experts (OmniMoE)
+
+def _grid_brute(pr, pc, K):
+    """Full sort of every cell by (S descending, id ascending); S in fp32."""
+    T, Nr = pr.shape
+    Nc = pc.shape[1]
+    out = np.empty((T, K), np.int64)
+    for t in range(T):
+        S = (pr[t][:, None] + pc[t][None, :]).astype(np.float32).ravel()
+        ids = np.arange(Nr * Nc)
+        order = np.lexsort((ids, -S.astype(np.float64)))
+        out[t] = np.sort(order[:K])
+    return out
+
+
+@pytest.mark.parametrize("Nr,Nc,K,quant", [(4, 8, 5, True), (7, 3, 21, False), (16, 32, 64, True),
+                                           (9, 9, 1, True), (5, 12, 17, False)])
+def test_grid_topk_matches_brute_force(Nr, Nc, K, quant):
+    rng = np.random.default_rng(Nr * 100 + Nc + K)
+    T = 12
+    pr = rng.standard_normal((T, Nr)).astype(np.float32)
+    pc = rng.standard_normal((T, Nc)).astype(np.float32)
+    if quant:   # a small alphabet: many exact ties in the sums
+        pr = np.round(pr * 2) / 2
+        pc = np.round(pc * 2) / 2
+    idx, gate = oracle.grid_topk(pr, pc, K)
+    assert np.array_equal(idx, _grid_brute(pr, pc, K))
+    assert np.allclose(gate.astype(np.float64).sum(1), 1.0, atol=1e-6)
+
+
+def test_grid_all_cells_gates_are_the_product_distribution():
+    """K = N: the gates are softmax(l_r)_i * softmax(l_c)_j (the row and column
+    log-probabilities add)."""
+    rng = np.random.default_rng(2)
+    lr = rng.standard_normal((6, 5)).astype(np.float32)
+    lc = rng.standard_normal((6, 7)).astype(np.float32)
+    pr, pc = oracle.log_softmax_rows(lr), oracle.log_softmax_rows(lc)
+    idx, gate = oracle.grid_topk(pr, pc, 35)
+    sr = np.exp(lr - lr.max(1, keepdims=True)); sr /= sr.sum(1, keepdims=True)
+    sc = np.exp(lc - lc.max(1, keepdims=True)); sc /= sc.sum(1, keepdims=True)
+    assert np.array_equal(idx, np.tile(np.arange(35), (6, 1)))
+    ref = (sr[:, :, None] * sc[:, None, :]).reshape(6, 35)
+    assert np.allclose(gate, ref, rtol=2e-6, atol=1e-8)
+
+
+def test_grid_one_column_is_the_coarse_router():
+    """Nc = 1: the column log-probability is 0, so the grid's top-K is the coarse
+    top-k of the row logits (same set; gates equal)."""
+    rng = np.random.default_rng(8)
+    lr = rng.standard_normal((20, 12)).astype(np.float32)
+    pr = oracle.log_softmax_rows(lr)
+    pc = oracle.log_softmax_rows(np.zeros((20, 1), np.float32))
+    assert np.all(pc == 0.0)
+    for K in (1, 3, 12):
+        idx, gate = oracle.grid_topk(pr, pc, K)
+        cidx, cgate = oracle.topk_gates(lr, K)
+        for t in range(20):
+            o = np.argsort(cidx[t])
+            assert np.array_equal(idx[t], cidx[t][o])
+            assert np.allclose(gate[t], cgate[t][o], rtol=1e-6, atol=1e-7)
+
+
+def _atomic_small(**over):
+    kw = dict(T=24, d=256, nr=8, nc=16, E=128, k=16, F_shared=128)
+    kw.update(over)
+    return make_workload(get_config("omni_atomic", **kw))
+
+
+def test_atomic_top1_relu_one_column_is_the_coarse_relu_layer():
+    """K = 1, Nc = 1, ReLU: each token runs one width-1 ReLU expert with gate 1,
+    which is the coarse ReLU layer with d_ff = 1 and top-1, bit for bit."""
+    import dataclasses
+    wl = _atomic_small(nr=12, nc=1, E=12, k=1, n_shared=0)
+    wl.cfg = dataclasses.replace(wl.cfg, act="relu")
+    at = oracle.atomic_layer_forward(wl)
+    E, d = 12, wl.cfg.d
+    lr = oracle.router_logits(wl.x, wl.w_router, None)
+    cidx, cgate = oracle.topk_gates(lr, 1)
+    assert np.array_equal(at["idx"], cidx) and np.all(cgate == 1.0)
+    Y = oracle.expert_rows(wl.x, None, wl.w_in.reshape(E, 1, d),
+                           np.ascontiguousarray(wl.w_out_t.T.reshape(E, d, 1)), "relu",
+                           oracle.ROUND_BF16, np.arange(wl.cfg.T, dtype=np.int32), cidx[:, 0])
+    assert np.array_equal(at["y"], oracle.combine(Y, None, cgate))
+
+
+def test_atomic_silu_single_unit_closed_form():
+    """One token, one unit: y = w_out * bf16(silu(x . w_in)), gate 1."""
+    x = f32_to_bf16_bits(np.array([[1.0, 0.5]], np.float32))
+    w_in = f32_to_bf16_bits(np.array([[1.5, 1.0]], np.float32))
+    w_out_t = f32_to_bf16_bits(np.array([[2.0], [-0.25]], np.float32))
+    idx = np.zeros((1, 1), np.int32)
+    Y = oracle.atomic_rows(x, w_in, w_out_t, idx, np.ones((1, 1), np.float32), "silu",
+                           np.zeros(1, np.int32))
+    h = 2.0 / (1.0 + math.exp(-2.0))           # silu(2)
+    a = float(bf16_bits_to_f32(f32_to_bf16_bits(np.array([h], np.float32)))[0])
+    assert np.array_equal(Y, np.array([[2.0 * a, -0.25 * a]]))
+
+
+def test_atomic_gate_scaled_value_rounded_once():
+    """Two units with gates g and 1 - g: each contributes w_out * bf16(g * silu(u)),
+    the gate inside the one bf16 rounding."""
+    x = f32_to_bf16_bits(np.array([[1.0, 0.5]], np.float32))
+    w_in = f32_to_bf16_bits(np.array([[1.5, 1.0], [0.5, -1.0]], np.float32))   # u = 2, 0
+    w_out_t = f32_to_bf16_bits(np.array([[1.0, 3.0], [-2.0, 1.0]], np.float32))  # [d][N]
+    idx = np.array([[0, 1]], np.int32)
+    g = np.array([[0.75, 0.25]], np.float32)
+    Y = oracle.atomic_rows(x, w_in, w_out_t, idx, g, "silu", np.zeros(1, np.int32))
+    rb = lambda v: float(bf16_bits_to_f32(f32_to_bf16_bits(np.array([v], np.float32)))[0])
+    a0 = rb(0.75 * (2.0 / (1.0 + math.exp(-2.0))))   # 1.3212 -> 1.3203125
+    assert a0 != 0.75 * rb(2.0 / (1.0 + math.exp(-2.0)))
+    assert Y[0, 0] == 1.0 * a0 + 3.0 * 0.0 and Y[0, 1] == -2.0 * a0   # silu(0) = 0
+
+
+def test_atomic_layer_grid_relabelling_equivariance():
+    """Swapping grid rows (and the atomic experts of those rows) or transposing the
+    grid (rows <-> columns) relabels experts and leaves y unchanged."""
+    wl = _atomic_small()
+    ref = oracle.atomic_layer_forward(wl)
+    nr, nc, d = 8, 16, wl.cfg.d
+    perm = np.random.default_rng(3).permutation(nr)
+    w2 = make_workload(get_config("omni_atomic", T=24, d=256, nr=8, nc=16, E=128, k=16,
+                                  F_shared=128))
+    w2.w_router = wl.w_router[perm]
+    cell = (perm[:, None] * nc + np.arange(nc)[None, :]).ravel()   # new id -> old id
+    w2.w_in = wl.w_in[cell]
+    w2.w_out_t = np.ascontiguousarray(wl.w_out_t[:, cell])
+    out = oracle.atomic_layer_forward(w2)
+    assert np.allclose(out["y"], ref["y"], rtol=0, atol=1e-9)
+    assert np.array_equal(np.sort(cell[out["idx"]], axis=1), ref["idx"])
+    # transpose: rows and columns swap roles, id i*nc + j becomes j*nr + i
+    import dataclasses
+    w3 = make_workload(get_config("omni_atomic", T=24, d=256, nr=16, nc=8, E=128, k=16,
+                                  F_shared=128))
+    w3.w_router, w3.w_col = wl.w_col, wl.w_router
+    tcell = (np.arange(nr)[None, :] * nc + np.arange(nc)[:, None]).ravel()   # (j, i) -> i*nc+j
+    w3.w_in = wl.w_in[tcell]
+    w3.w_out_t = np.ascontiguousarray(wl.w_out_t[:, tcell])
+    out3 = oracle.atomic_layer_forward(w3)
+    assert np.allclose(out3["y"], ref["y"], rtol=0, atol=1e-9)
+    assert np.array_equal(out3["counts"].sum(), ref["counts"].sum())
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 MUTANTS = [
@@ -718,6 +860,16 @@ MUTANTS = [
      "h[f] = (g / (1.0 + exp(-g))) * u;"),
     ("floe given values ignored", "double mag = u_given ? fabs((double)u_given[(size_t)p * F + f]) : fabs(u);",
      "double mag = fabs(u);"),
+    ("grid ties to the higher id", "return (x->id < y->id) ? -1 : (x->id > y->id);",
+     "return (x->id > y->id) ? -1 : (x->id < y->id);"),
+    ("grid slots left in score order", "qsort(out, (size_t)K, sizeof(int32_t), cmp_int32);",
+     "(void)cmp_int32;"),
+    ("atomic activation swapped", "double h = act == 0 ? u / (1.0 + exp(-u)) : (u > 0.0 ? u : 0.0);",
+     "double h = act == 1 ? u / (1.0 + exp(-u)) : (u > 0.0 ? u : 0.0);"),
+    ("atomic output vectors read as rows", "y[i] += a * bf16_to_double(w_out[(size_t)i * N + e]);",
+     "y[i] += a * bf16_to_double(w_out[e * (size_t)d + i]);"),
+    ("atomic gate outside the rounding", "double a = orc_round_bf16((double)gate[t * K + s] * h);",
+     "double a = (double)gate[t * K + s] * orc_round_bf16(h);"),
     ("mwq second plane read from the first", "((uint32_t)p4[r * (K / 32) + kk / 32] >> mwq_bit(kk))",
      "((uint32_t)p3[r * (K / 32) + kk / 32] >> mwq_bit(kk))"),
     ("mwq 2-bit fields in natural order", "(w2 >> (2 * mwq_field(kk))) & 0x3u;",

@@ -38,6 +38,9 @@ class WorkloadConfig:
     mwq: bool = False    # nested INT2 + binary residual planes, per-assignment bit width
     floe: bool = False   # INT2 up projection, gate/down channels kept where |up| > threshold
     sparsity: float = 0.0  # target fraction of pruned channels (floe thresholds)
+    atomic: bool = False   # atomic experts on an nr x nc router grid: E = nr*nc, k = K
+    nr: int = 0
+    nc: int = 0
     x_rows_of: Optional[str] = None   # take the first T rows of this workload's x
     weights_of: Optional[str] = None  # reuse this workload's router/expert weights
     notes: str = field(default="", compare=False)
@@ -73,6 +76,11 @@ CONFIGS = {
         weights_of="mixtral_prefill_bf16",
         notes="nested INT2 base + binary residual planes, bit width per assignment "
               "uniform over {2, 3, 4}"),
+    "omni_atomic": WorkloadConfig(
+        "omni_atomic", 7, T=4096, d=2048, E=320 * 320, k=4096, F=1, act="silu", dtype="bf16",
+        atomic=True, nr=320, nc=320, n_shared=1, F_shared=1536,
+        notes="102,400 atomic experts on a 320 x 320 router grid, top-4096 per token, "
+              "SiLU units, one shared SwiGLU MLP (d_ff 1536)"),
     "mixtral_floe_decode": WorkloadConfig(
         "mixtral_floe_decode", 6, T=16, d=4096, E=8, k=2, F=14336, act="swiglu",
         dtype="bf16", floe=True, sparsity=0.9, x_rows_of="mixtral_prefill_bf16",

@@ -27,6 +27,8 @@ TID_X, TID_WR, TID_WGATE, TID_WUP, TID_WDOWN = 0, 1, 2, 3, 4
 TID_SGATE, TID_SUP, TID_SDOWN, TID_ZIPF = 5, 6, 7, 8
 TID_BITS = 9   # per-assignment bit widths of the nested-quantisation workload
 TID_XCAL = 10  # calibration activations (sparsity thresholds)
+TID_WRCOL = 11 # column router of the atomic-expert grid (the row router uses TID_WR)
+ATOMIC_CHUNK = 1024  # atomic experts per seeded chunk
 FLOE_CAL_TOKENS = 64
 
 W_STD = 0.02
@@ -231,6 +233,9 @@ class Workload:
     m_up: Optional[MwqWeights] = None
     m_down: Optional[MwqWeights] = None
     bits: Optional[np.ndarray] = None      # [T, k] int32 bit width of each assignment
+    w_col: Optional[np.ndarray] = None     # [nc, d] column router (atomic configs; w_router = rows)
+    w_in: Optional[np.ndarray] = None      # [N, d] atomic input vectors
+    w_out_t: Optional[np.ndarray] = None   # [d, N] atomic output vectors as columns
     u2_up: Optional[Int2Weights] = None    # INT2 up projection (floe configs)
     floe_thr: Optional[np.ndarray] = None  # [E] fp32 |up output| threshold per expert
 
@@ -258,11 +263,42 @@ def router_bias(cfg: WorkloadConfig, beta: Optional[float] = None) -> np.ndarray
     return b.astype(np.float32)
 
 
+def _make_atomic(cfg, threads):
+    """Atomic-expert workload: row / column routers and the two atomic matrices,
+    drawn in seeded chunks of ATOMIC_CHUNK experts."""
+    T, d, N = cfg.T, cfg.d, cfg.nr * cfg.nc
+    wid = CONFIGS[cfg.weights_of].cfg_id if cfg.weights_of else cfg.cfg_id
+    x = _normal(cfg.cfg_id, TID_X, 0, (T, d), 1.0, True)
+    w_row = _normal(wid, TID_WR, 0, (cfg.nr, d), W_STD, True)
+    w_col = _normal(wid, TID_WRCOL, 0, (cfg.nc, d), W_STD, True)
+    nch = (N + ATOMIC_CHUNK - 1) // ATOMIC_CHUNK
+
+    def chunks(tid):
+        def one(c):
+            n = min(ATOMIC_CHUNK, N - c * ATOMIC_CHUNK)
+            return _normal(wid, tid, c, (n, d), W_STD, True)
+        with ThreadPoolExecutor(max(1, min(threads, nch))) as ex:
+            return np.concatenate(list(ex.map(one, range(nch))), axis=0)
+    w_in = chunks(TID_WUP)
+    w_out_t = np.ascontiguousarray(chunks(TID_WDOWN).T)
+    wl = Workload(cfg, x, w_row, np.zeros(cfg.nr, np.float32), None, w_in, w_out_t)
+    wl.w_col, wl.w_in, wl.w_out_t = w_col, w_in, w_out_t
+    if cfg.n_shared:
+        Fs = cfg.n_shared * cfg.F_shared
+        wl.ws_gate = _normal(wid, TID_SGATE, 0, (Fs, d), W_STD, True)
+        wl.ws_up = _normal(wid, TID_SUP, 0, (Fs, d), W_STD, True)
+        wl.ws_down = _normal(wid, TID_SDOWN, 0, (d, Fs), W_STD, True)
+    return wl
+
+
 def make_workload(cfg, beta: Optional[float] = None, fractional_zero: bool = False,
                   threads: int = 8) -> Workload:
     """Draw every tensor of a workload.  ``cfg`` is a WorkloadConfig or a name."""
     if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
+    if cfg.atomic:
+        assert cfg.dtype == "bf16" and cfg.E == cfg.nr * cfg.nc
+        return _make_atomic(cfg, threads)
     bf16 = cfg.dtype == "bf16"
     T, d, E, F = cfg.T, cfg.d, cfg.E, cfg.F
     wid = CONFIGS[cfg.weights_of].cfg_id if cfg.weights_of else cfg.cfg_id
