@@ -230,6 +230,75 @@ def measured_traffic(workload, kernel):
     return None
 
 
+def run_atomic(name, steps, warmup):
+    """The atomic-expert layer (router grid, exact top-K, expert grouping, masked
+    input GEMM, output GEMM, shared MLP), per-stage HIP events as in run_gpu."""
+    import torch
+    import sparse_mixture_experts_wavefront_amd as moe
+    from sparse_mixture_experts_wavefront_amd.device_inputs import atomic_to_device
+    from workloads import make_workload
+    wl = make_workload(name)
+    cfg = wl.cfg
+    layer, x = atomic_to_device(wl)
+    runner = moe.AtomicRunner(layer, cfg.T)
+    for _ in range(warmup):
+        runner(x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        runner(x)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / steps
+    hip = _hip()
+    B = moe.lib()
+    per = np.zeros((steps, 7))
+    sets = []
+    try:
+        for _ in range(steps):
+            hs = []
+            for i in range(7):
+                h = C.c_void_p()
+                assert hip.hipEventCreate(C.byref(h)) == 0
+                hs.append(h.value)
+            sets.append((C.c_void_p * 7)(*hs))
+        for evs in sets:
+            B.moe_set_stage_events(C.cast(evs, C.POINTER(C.c_void_p)), 7)
+            runner(x)
+        B.moe_set_stage_events(None, 0)
+        torch.cuda.synchronize()
+        for n, evs in enumerate(sets):
+            for i in range(6):
+                f = C.c_float(0)
+                assert hip.hipEventElapsedTime(C.byref(f), evs[i], evs[i + 1]) == 0
+                per[n, i] = f.value
+            f = C.c_float(0)
+            assert hip.hipEventElapsedTime(C.byref(f), evs[0], evs[6]) == 0
+            per[n, 6] = f.value
+    finally:
+        B.moe_set_stage_events(None, 0)
+        for evs in sets:
+            for i in range(7):
+                hip.hipEventDestroy(evs[i])
+    st = per[:, :6].mean(axis=0)
+    stages = dict(zip(["route_grid_topk", "permute", "input_gemm_masked", "output_gemm",
+                       "shared_mlp", "combine"], [round(v * 1000.0, 2) for v in st]))
+    T, d, N, K = cfg.T, cfg.d, cfg.nr * cfg.nc, cfg.k
+    dense_flops = 2.0 * T * N * d
+    t_in = st[2] * 1e-3
+    ach = dense_flops / t_in / 1e12
+    return {"workload": name, "T": T, "d_model": d, "experts": N, "top_k": K,
+            "tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+            "lis": float(runner.aux_t["lis"].cpu().numpy()[0]),
+            "useful_fraction_of_dense_gemm": round(K / N, 4),
+            "stages_us": stages,
+            "timing": dict(event_ms_p50=round(float(np.percentile(per[:, 6], 50)), 4)),
+            "roofline": dict(kernel="grouped_gemm_tile<kAtomIn> (dense x . W_in^T, masked epilogue)",
+                             bound="mfma", achieved=round(ach, 1), peak=MFMA_BF16_PEAK_TFLOPS,
+                             unit="TFLOP/s", frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                             traffic=None,
+                             per_launch=dict(flops=dense_flops, us=round(t_in * 1e6, 2)))}
+
+
 def run_replica(name, steps, warmup):
     """The layer with an INT4 replica of its heaviest expert (chosen by a
     calibration call on the same batch) against the plain layer."""
@@ -339,6 +408,9 @@ def main():
     ap.add_argument("--floe", default="mixtral_floe_decode,mixtral_floe_decode_t1",
                     help="comma-separated sparse-down workloads reported in the same line "
                          "('' for none)")
+    ap.add_argument("--atomic", default="omni_atomic",
+                    help="comma-separated atomic-expert workloads reported in the same line "
+                         "('' for none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (the known-size kernel "
                          "that scales the FETCH_SIZE/WRITE_SIZE counters)")
@@ -423,6 +495,9 @@ def main():
         del wl4
     if fl:
         out["floe"] = fl
+    atoms = [run_atomic(n, args.steps, args.warmup) for n in args.atomic.split(",") if n]
+    if atoms:
+        out["atomic"] = atoms
     reps = [run_replica(n, args.steps, args.warmup) for n in args.replica.split(",") if n]
     if reps:
         out["replica"] = reps

@@ -368,6 +368,54 @@ moe_status moe_layer_forward_floe(const moe_layer_desc* L, const moe_floe_expert
                                   unsigned flags, void* stream);
 moe_status moe_floe_workspace_size(const moe_layer_desc* L, int T, size_t* bytes);
 
+/* ---- Atomic experts on a Cartesian router grid ("OmniMoE: An Efficient MoE by
+ * Orchestrating Atomic Experts at Scale" -- What carries the argument, Core
+ * claim; Axiom ledger: the selection is the exact global top-K).  Expert
+ * n = i*nc + j is cell (i, j) of an nr x nc grid and one vector pair
+ * (w_in[n], w_out[:, n]).  Per token:
+ *   lr = x W_row^T, lc = x W_col^T (fp32), pr = log_softmax(lr), pc = log_softmax(lc)
+ *   S_n = fp32(pr[i] + pc[j]); the K cells with the largest S (equal S: lower n)
+ *   are kept, slots in ascending n; gates g = softmax over the kept S
+ *   y = sum over kept n of w_out[:, n] * bf16_RNE(g_n * silu(x . w_in[n]))
+ *       + the shared SwiGLU MLP (n_shared > 0)
+ * The kept (token, expert) pairs are grouped by expert (counts, offsets,
+ * token-ordered rows, LIS = N * max_n count_n / (T * K)). */
+typedef struct {
+  int d_model;
+  int grid_rows, grid_cols;  /* nr, nc: N = nr * nc atomic experts */
+  int top_k;                 /* K */
+  const void* w_row;         /* bf16 [nr][d_model] */
+  const void* w_col;         /* bf16 [nc][d_model] */
+  const void* w_in;          /* bf16 [N][d_model] */
+  const void* w_out;         /* bf16 [d_model][N]: column n is w_out of expert n */
+  int n_shared, d_ff_shared;
+  moe_experts shared;        /* as in moe_layer_desc */
+} moe_atomic_layer_desc;
+
+/* Optional outputs of moe_atomic_layer_forward; every pointer may be NULL. */
+typedef struct {
+  float* logp_row;      /* [T][nr] */
+  float* logp_col;      /* [T][nc] */
+  int32_t* idx;         /* [T][K] kept experts, ascending */
+  float* gates;         /* [T][K] */
+  int32_t* counts;      /* [N] */
+  int32_t* offsets;     /* [N+1] */
+  int32_t* row_assign;  /* [T*K] row -> flat pair t*K + slot, experts in order */
+  int32_t* assign_row;  /* [T*K] */
+  double* lis;          /* [1] */
+} moe_atomic_aux;
+
+/* The atomic-expert layer.  x [T][d_model] bf16, y [T][d_model] in ydt.
+ * Requires d_model % 128 == 0, nc % 32 == 0, nr, nc <= 1024, N % 128 == 0,
+ * 1 <= K <= N.  The input side is one dense GEMM of x against all N input
+ * vectors whose epilogue keeps only the selected cells (gate and SiLU applied,
+ * rounded to bf16, zeros elsewhere); the output side is one dense GEMM of that
+ * [T][N] matrix against w_out.  Workspace: moe_atomic_workspace_size. */
+moe_status moe_atomic_layer_forward(const moe_atomic_layer_desc* L, const void* x, int T, void* y,
+                                    moe_dtype ydt, moe_atomic_aux* aux, void* ws, size_t ws_bytes,
+                                    unsigned flags, void* stream);
+moe_status moe_atomic_workspace_size(const moe_atomic_layer_desc* L, int T, size_t* bytes);
+
 /* Instrumentation (not part of the layer's arithmetic).  While set, every
  * moe_layer_forward call made on this thread records events[i] (hipEvent_t
  * handles created by the caller) on its stream at the stage boundaries:

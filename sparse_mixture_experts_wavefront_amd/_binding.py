@@ -26,6 +26,7 @@ EXPORTED = ("moe_route_topk", "moe_permute", "moe_permute_workspace_size", "moe_
             "moe_replica_workspace_size", "moe_mwq_group", "moe_mwq_group_workspace_size",
             "moe_grouped_ffn_mwq", "moe_grouped_ffn_mwq_workspace_size", "moe_layer_forward_mwq",
             "moe_mwq_workspace_size", "moe_layer_forward_floe", "moe_floe_workspace_size",
+            "moe_atomic_layer_forward", "moe_atomic_workspace_size",
             "moe_set_stage_events", "moe_status_string", "moe_last_error")
 
 
@@ -84,6 +85,19 @@ class FloeAux(C.Structure):
     _fields_ = [("up_out", C.c_void_p), ("kept", C.c_void_p), ("channels", C.c_void_p)]
 
 
+class AtomicLayerDesc(C.Structure):
+    _fields_ = [("d_model", C.c_int), ("grid_rows", C.c_int), ("grid_cols", C.c_int),
+                ("top_k", C.c_int), ("w_row", C.c_void_p), ("w_col", C.c_void_p),
+                ("w_in", C.c_void_p), ("w_out", C.c_void_p), ("n_shared", C.c_int),
+                ("d_ff_shared", C.c_int), ("shared", Experts)]
+
+
+class AtomicAux(C.Structure):
+    _fields_ = [("logp_row", C.c_void_p), ("logp_col", C.c_void_p), ("idx", C.c_void_p),
+                ("gates", C.c_void_p), ("counts", C.c_void_p), ("offsets", C.c_void_p),
+                ("row_assign", C.c_void_p), ("assign_row", C.c_void_p), ("lis", C.c_void_p)]
+
+
 class Aux(C.Structure):
     _fields_ = [("logits", C.c_void_p), ("idx", C.c_void_p), ("gates", C.c_void_p),
                 ("counts", C.c_void_p), ("offsets", C.c_void_p), ("row_assign", C.c_void_p),
@@ -134,6 +148,10 @@ def lib():
                                                  p, i, p, i, C.POINTER(Aux), C.POINTER(FloeAux),
                                                  p, sz, u, p]
             L.moe_floe_workspace_size.argtypes = [C.POINTER(LayerDesc), i, C.POINTER(sz)]
+            L.moe_atomic_layer_forward.argtypes = [C.POINTER(AtomicLayerDesc), p, i, p, i,
+                                                   C.POINTER(AtomicAux), p, sz, u, p]
+            L.moe_atomic_workspace_size.argtypes = [C.POINTER(AtomicLayerDesc), i,
+                                                    C.POINTER(sz)]
             L.moe_set_stage_events.argtypes = [C.POINTER(C.c_void_p), i]
             L.moe_set_stage_events.restype = C.c_int
             L.moe_status_string.argtypes = [i]
@@ -145,7 +163,8 @@ def lib():
                       "moe_layer_forward_replica", "moe_replica_workspace_size",
                       "moe_mwq_group", "moe_grouped_ffn_mwq", "moe_layer_forward_mwq",
                       "moe_mwq_workspace_size", "moe_layer_forward_floe",
-                      "moe_floe_workspace_size"):
+                      "moe_floe_workspace_size", "moe_atomic_layer_forward",
+                      "moe_atomic_workspace_size"):
                 getattr(L, f).restype = C.c_int
             _lib = L
     return _lib

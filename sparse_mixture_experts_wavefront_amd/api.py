@@ -424,3 +424,76 @@ def grouped_ffn_mwq(x, E, k, act, experts: MwqExperts, offsets, row_assign, topk
                                         ws.numel(), flags, _stream()),
             "moe_grouped_ffn_mwq")
     return y_rows[:T * k]
+
+
+@dataclass
+class AtomicLayer:
+    """Atomic experts on an nr x nc router grid (see moe_atomic_layer_forward):
+    w_row [nr][d], w_col [nc][d], w_in [N][d], w_out [d][N] bf16; optional
+    shared SwiGLU MLP."""
+    d_model: int
+    grid_rows: int
+    grid_cols: int
+    top_k: int
+    w_row: torch.Tensor
+    w_col: torch.Tensor
+    w_in: torch.Tensor
+    w_out: torch.Tensor
+    n_shared: int = 0
+    d_ff_shared: int = 0
+    shared: Optional[ExpertWeights] = None
+
+    def desc(self) -> B.AtomicLayerDesc:
+        L = B.AtomicLayerDesc()
+        L.d_model, L.grid_rows, L.grid_cols, L.top_k = (self.d_model, self.grid_rows,
+                                                        self.grid_cols, self.top_k)
+        L.w_row, L.w_col, L.w_in, L.w_out = (_p(self.w_row), _p(self.w_col), _p(self.w_in),
+                                             _p(self.w_out))
+        L.n_shared, L.d_ff_shared = self.n_shared, self.d_ff_shared
+        if self.shared is not None:
+            L.shared = self.shared.struct(B.MOE_DT_BF16)
+        return L
+
+
+class AtomicRunner:
+    """Descriptor, workspace and aux buffers for repeated atomic-layer calls."""
+
+    def __init__(self, layer: AtomicLayer, T: int, out_dtype=torch.float32, want_aux=True):
+        self.layer, self.T = layer, T
+        dev = layer.w_row.device
+        self.desc = layer.desc()
+        n = C.c_size_t(0)
+        B.check(B.lib().moe_atomic_workspace_size(C.byref(self.desc), T, C.byref(n)),
+                "moe_atomic_workspace_size")
+        self.ws = _ws(n.value, dev)
+        self.y = torch.empty(T, layer.d_model, dtype=out_dtype, device=dev)
+        nr, nc, K = layer.grid_rows, layer.grid_cols, layer.top_k
+        N = nr * nc
+        self.aux_t, self.aux = None, None
+        if want_aux:
+            self.aux_t = dict(
+                logp_row=torch.empty(T, nr, dtype=torch.float32, device=dev),
+                logp_col=torch.empty(T, nc, dtype=torch.float32, device=dev),
+                idx=torch.empty(T, K, dtype=torch.int32, device=dev),
+                gates=torch.empty(T, K, dtype=torch.float32, device=dev),
+                counts=torch.empty(N, dtype=torch.int32, device=dev),
+                offsets=torch.empty(N + 1, dtype=torch.int32, device=dev),
+                row_assign=torch.empty(max(T * K, 1), dtype=torch.int32, device=dev),
+                assign_row=torch.empty(max(T * K, 1), dtype=torch.int32, device=dev),
+                lis=torch.empty(1, dtype=torch.float64, device=dev))
+            self.aux = B.AtomicAux(**{k: _p(v) for k, v in self.aux_t.items()})
+
+    def __call__(self, x, flags=0):
+        aux = C.byref(self.aux) if self.aux is not None else None
+        B.check(B.lib().moe_atomic_layer_forward(C.byref(self.desc), _p(x), self.T, _p(self.y),
+                                                 _dt(self.y), aux, _p(self.ws), self.ws.numel(),
+                                                 flags, _stream()),
+                "moe_atomic_layer_forward")
+        return self.y
+
+
+def atomic_layer_forward(layer: AtomicLayer, x, out_dtype=torch.float32, flags=0):
+    """One atomic-layer call; returns (y, aux dict of device tensors)."""
+    r = AtomicRunner(layer, x.shape[0], out_dtype)
+    y = r(x, flags)
+    return y, r.aux_t

@@ -32,7 +32,9 @@ namespace {
 constexpr int kBK = 64;
 constexpr int kThreads = 256;
 
-enum Mode { kGateUpSwiglu = 0, kUpRelu = 1, kDown = 2 };
+// kAtomIn: one matrix, output bf16(gate * silu(acc)) at the cells a per-row
+// bitmap keeps and 0 elsewhere (the input side of the atomic experts)
+enum Mode { kGateUpSwiglu = 0, kUpRelu = 1, kDown = 2, kAtomIn = 3 };
 
 struct TileArgs {
   const u16* A;            // gate/up: x [T][lda]; down: H [rows][lda]
@@ -57,6 +59,10 @@ struct TileArgs {
   int m_tiles_max, n_tiles;
   int ksplit;              // K slices (down only): slice s covers K [s*K/ksplit, +K/ksplit)
   size_t ystride;          // elements between the partial outputs of two slices
+  const uint32_t* bits;    // kAtomIn: [rows][wpr] kept cells, bit c%32 of word c/32
+  const int32_t* bitpre;   // kAtomIn: [rows][wpr] kept cells of the row before the word
+  int wpr;                 // kAtomIn: words per row (N / 32)
+  int ksel;                // kAtomIn: gates per row (gate [rows][ksel], kept cells in order)
 };
 
 // LDS rows of 64 bf16 (128 B).  The LDS has 64 banks of 4 bytes and serves a
@@ -493,6 +499,23 @@ void grouped_gemm_tile_kernel(TileArgs p) {
           if (col < p.N)
             p.H[(size_t)grow * p.N + col] = f32_to_bf16(silu_f32(acc[i][j][r]) * acc[i][j + 2][r]);
         }
+      } else if constexpr (MODE == kAtomIn) {
+        const uint32_t* brw = p.bits + (size_t)grow * p.wpr;
+        const int32_t* prw = p.bitpre + (size_t)grow * p.wpr;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = n_tile * 256 + wn * 128 + j * 32 + fr;
+          if (col < p.N) {
+            const uint32_t w = brw[col >> 5];
+            const uint32_t b = (uint32_t)col & 31u;
+            u16 v = 0;
+            if ((w >> b) & 1u) {
+              const int rank = prw[col >> 5] + __popc(w & ((1u << b) - 1u));
+              v = f32_to_bf16(p.gate[(size_t)grow * p.ksel + rank] * silu_f32(acc[i][j][r]));
+            }
+            p.H[(size_t)grow * p.N + col] = v;
+          }
+        }
       } else if constexpr (MODE == kUpRelu) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -712,6 +735,47 @@ hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid
   if (p.F % 128 == 0) return run_tiles_v2<kDown>(b, s);
   if (b.ksplit > 1) return hipErrorInvalidValue;  // slices exist only on the 256x256 path
   return run_tiles<128, 128, kDown, false>(b, s);
+}
+
+hipError_t launch_gemm_bt(const u16* A, int lda, int M, const u16* B, int N, int K, float* Y,
+                          int ksplit, size_t ystride, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (K % (128 * (ksplit < 1 ? 1 : ksplit)) != 0) return hipErrorInvalidValue;
+  TileArgs a = {};
+  a.A = A;
+  a.lda = lda;
+  a.B0 = B;
+  a.N = N;
+  a.K = K;
+  a.E = 1;
+  a.rows = M;
+  a.Y = Y;
+  a.ksplit = ksplit < 1 ? 1 : ksplit;
+  a.ystride = ystride;
+  return run_tiles_v2<kDown>(a, s);
+}
+
+hipError_t launch_atomic_in(const u16* A, int M, const u16* B, int N, int K, const uint32_t* bits,
+                            const int32_t* bitpre, const float* gates, int ksel, u16* H,
+                            hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (K % 128 != 0 || N % 32 != 0) return hipErrorInvalidValue;
+  TileArgs a = {};
+  a.A = A;
+  a.lda = K;
+  a.B0 = B;
+  a.N = N;
+  a.K = K;
+  a.E = 1;
+  a.rows = M;
+  a.H = H;
+  a.gate = gates;
+  a.bits = bits;
+  a.bitpre = bitpre;
+  a.wpr = N / 32;
+  a.ksel = ksel;
+  a.ksplit = 1;
+  return run_tiles_v2<kAtomIn>(a, s);
 }
 
 }  // namespace moe

@@ -940,3 +940,176 @@ moe_status moe_layer_forward_floe(const moe_layer_desc* L, const moe_floe_expert
 }
 
 }  // extern "C"
+
+// ---- atomic experts on a Cartesian router grid ------------------------------
+
+namespace {
+
+moe_status check_atomic(const moe_atomic_layer_desc* L, int T, unsigned flags) {
+  REQUIRE(L, "layer descriptor must not be NULL");
+  REQUIRE((flags & ~kKnownFlags) == 0, "unknown flag bits 0x%x", flags & ~kKnownFlags);
+  REQUIRE(!(flags & MOE_F_LOGITS_GIVEN), "MOE_F_LOGITS_GIVEN is not defined for the atomic layer");
+  REQUIRE(T >= 0, "T must be >= 0 (got %d)", T);
+  const int d = L->d_model, nr = L->grid_rows, nc = L->grid_cols, K = L->top_k;
+  REQUIRE(d >= 128 && d % 128 == 0, "atomic layer: d_model must be a positive multiple of 128");
+  REQUIRE(nr >= 1 && nc >= 1, "atomic layer: grid must be at least 1 x 1");
+  const long long N = (long long)nr * nc;
+  REQUIRE(K >= 1 && K <= N, "atomic layer: top_k must be in [1, N] (got %d)", K);
+  if (nr > 1024 || nc > 1024 || nc % 32 != 0 || N % 128 != 0)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "atomic layer needs nr, nc <= 1024, nc %% 32 == 0 and N %% 128 == 0 (nr=%d, nc=%d)",
+                nr, nc);
+  REQUIRE((long long)T * K < (1ll << 31) && (long long)T * N < (1ll << 40), "T too large");
+  REQUIRE_PTR(L->w_row, "w_row");
+  REQUIRE_PTR(L->w_col, "w_col");
+  REQUIRE_PTR(L->w_in, "w_in");
+  REQUIRE_PTR(L->w_out, "w_out");
+  REQUIRE(L->n_shared >= 0, "n_shared must be >= 0");
+  if (L->n_shared > 0) {
+    REQUIRE(L->d_ff_shared >= 8 && L->d_ff_shared % 8 == 0,
+            "d_ff_shared must be a positive multiple of 8");
+    moe_status s = check_experts(&L->shared, MOE_DT_BF16, d, L->n_shared * L->d_ff_shared,
+                                 MOE_ACT_SWIGLU, "shared");
+    if (s != MOE_OK) return s;
+  }
+  return MOE_OK;
+}
+
+int atomic_out_splits(int T, int d, int N) {
+  const long long tiles = (long long)((T + 255) / 256) * ((d + 255) / 256);
+  int S = 1;
+  while (tiles * S < 512 && S < 8 && N % (128 * 2 * S) == 0) S *= 2;
+  return S;
+}
+
+struct AtomicWs {
+  float *lr, *lc, *pr, *pc, *gates, *y_rows, *y_shared;
+  int32_t *idx, *counts, *offsets, *row_assign, *assign_row, *iota, *bitpre;
+  uint32_t* bits;
+  double* lis;
+  void *perm_ws, *H, *Hs;
+  int splits;
+  size_t total;
+};
+
+AtomicWs carve_atomic(const moe_atomic_layer_desc* L, int T, void* ws) {
+  const int d = L->d_model, nr = L->grid_rows, nc = L->grid_cols, K = L->top_k;
+  const size_t N = (size_t)nr * nc, n = (size_t)T * K, W = N / 32;
+  Carver c(ws);
+  AtomicWs w;
+  w.lr = (float*)c.take((size_t)T * nr * 4);
+  w.lc = (float*)c.take((size_t)T * nc * 4);
+  w.pr = (float*)c.take((size_t)T * nr * 4);
+  w.pc = (float*)c.take((size_t)T * nc * 4);
+  w.idx = (int32_t*)c.take(n * 4);
+  w.gates = (float*)c.take(n * 4);
+  w.bits = (uint32_t*)c.take((size_t)T * W * 4);
+  w.bitpre = (int32_t*)c.take((size_t)T * W * 4);
+  w.counts = (int32_t*)c.take(N * 4);
+  w.offsets = (int32_t*)c.take((N + 1) * 4);
+  w.row_assign = (int32_t*)c.take(n * 4);
+  w.assign_row = (int32_t*)c.take(n * 4);
+  w.lis = (double*)c.take(8);
+  w.perm_ws = c.take(grid_permute_ws_bytes(T, (int)N));
+  w.H = c.take((size_t)T * N * 2);
+  w.splits = atomic_out_splits(T, d, (int)N);
+  w.y_rows = (float*)c.take((size_t)w.splits * T * d * 4);
+  w.iota = (int32_t*)c.take((size_t)T * 4);
+  const int Fs = L->n_shared * L->d_ff_shared;
+  w.Hs = L->n_shared ? c.take((size_t)T * Fs * 2) : nullptr;
+  w.y_shared = L->n_shared ? (float*)c.take((size_t)T * d * 4) : nullptr;
+  w.total = c.off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_atomic_workspace_size(const moe_atomic_layer_desc* L, int T, size_t* bytes) {
+  REQUIRE(bytes, "bytes must not be NULL");
+  moe_status s = check_atomic(L, T, 0);
+  if (s != MOE_OK) return s;
+  *bytes = carve_atomic(L, T, nullptr).total;
+  return ok();
+}
+
+moe_status moe_atomic_layer_forward(const moe_atomic_layer_desc* L, const void* x, int T, void* y,
+                                    moe_dtype ydt, moe_atomic_aux* aux, void* ws, size_t ws_bytes,
+                                    unsigned flags, void* stream) {
+  moe_status s = check_atomic(L, T, flags);
+  if (s != MOE_OK) return s;
+  REQUIRE(valid_dtype(ydt), "unknown output dtype %d", (int)ydt);
+  if (T > 0) {
+    REQUIRE_PTR(x, "x");
+    REQUIRE_PTR(y, "y");
+  }
+  if (aux) {
+    OPT_PTR(aux->logp_row, "aux.logp_row"); OPT_PTR(aux->logp_col, "aux.logp_col");
+    OPT_PTR(aux->idx, "aux.idx"); OPT_PTR(aux->gates, "aux.gates");
+    OPT_PTR(aux->counts, "aux.counts"); OPT_PTR(aux->offsets, "aux.offsets");
+    OPT_PTR(aux->row_assign, "aux.row_assign"); OPT_PTR(aux->assign_row, "aux.assign_row");
+    OPT_PTR(aux->lis, "aux.lis");
+  }
+  const size_t need = carve_atomic(L, T, nullptr).total;
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "the atomic layer needs %zu workspace bytes (got %zu)", need,
+                ws ? ws_bytes : (size_t)0);
+  REQUIRE(aligned(ws, 256), "ws must be 256-byte aligned");
+  if (flags & MOE_F_VALIDATE_ONLY) return ok();
+  if (T == 0) return ok();
+
+  hipStream_t st = (hipStream_t)stream;
+  AtomicWs w = carve_atomic(L, T, ws);
+  const int d = L->d_model, nr = L->grid_rows, nc = L->grid_cols, K = L->top_k;
+  const int N = nr * nc;
+  float* pr = (aux && aux->logp_row) ? aux->logp_row : w.pr;
+  float* pc = (aux && aux->logp_col) ? aux->logp_col : w.pc;
+  int32_t* idx = (aux && aux->idx) ? aux->idx : w.idx;
+  float* gates = (aux && aux->gates) ? aux->gates : w.gates;
+  int32_t* counts = (aux && aux->counts) ? aux->counts : w.counts;
+  int32_t* offsets = (aux && aux->offsets) ? aux->offsets : w.offsets;
+  int32_t* row_assign = (aux && aux->row_assign) ? aux->row_assign : w.row_assign;
+  int32_t* assign_row = (aux && aux->assign_row) ? aux->assign_row : w.assign_row;
+  double* lis = (aux && aux->lis) ? aux->lis : w.lis;
+  const u16* X = (const u16*)x;
+
+  stage(0, st);
+  hipError_t e = launch_gemm_bt(X, d, T, (const u16*)L->w_row, nr, d, w.lr, 1, 0, st);
+  if (e == hipSuccess) e = launch_gemm_bt(X, d, T, (const u16*)L->w_col, nc, d, w.lc, 1, 0, st);
+  if (e == hipSuccess) e = launch_log_softmax_rows(w.lr, T, nr, pr, st);
+  if (e == hipSuccess) e = launch_log_softmax_rows(w.lc, T, nc, pc, st);
+  if (e == hipSuccess)
+    e = launch_grid_topk(pr, pc, T, nr, nc, K, idx, gates, w.bits, w.bitpre, st);
+  if (e != hipSuccess) return hip_status(e, "grid routing");
+  stage(1, st);
+  e = launch_grid_permute(w.bits, w.bitpre, T, N, K, counts, offsets, row_assign, assign_row, lis,
+                          w.perm_ws, st);
+  if (e != hipSuccess) return hip_status(e, "grid permutation");
+  stage(2, st);
+  e = launch_atomic_in(X, T, (const u16*)L->w_in, N, d, w.bits, w.bitpre, gates, K, (u16*)w.H, st);
+  if (e != hipSuccess) return hip_status(e, "atomic input GEMM");
+  stage(3, st);
+  e = launch_gemm_bt((const u16*)w.H, N, T, (const u16*)L->w_out, d, N, w.y_rows, w.splits,
+                     (size_t)T * d, st);
+  if (e != hipSuccess) return hip_status(e, "atomic output GEMM");
+  stage(4, st);
+  if (L->n_shared > 0) {
+    FfnProblem q{};
+    q.T = T; q.d = d; q.F = L->n_shared * L->d_ff_shared; q.E = 1; q.k = 1;
+    q.act = MOE_ACT_SWIGLU; q.dt = MOE_DT_BF16; q.x = x; q.w = &L->shared;
+    q.offsets = nullptr; q.row_assign = nullptr; q.gate = nullptr;
+    q.y_rows = w.y_shared; q.H = w.Hs; q.rows = T;
+    e = launch_grouped_ffn(q, st);
+    if (e != hipSuccess) return hip_status(e, "shared experts");
+  }
+  stage(5, st);
+  e = launch_iota(w.iota, T, st);
+  if (e == hipSuccess)
+    e = launch_combine(w.y_rows, w.iota, T, 1, d, w.y_shared, y, ydt, st, w.splits,
+                       (size_t)T * d);
+  stage(6, st);
+  return hip_status(e, "combine");
+}
+
+}  // extern "C"

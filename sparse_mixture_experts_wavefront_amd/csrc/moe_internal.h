@@ -147,6 +147,33 @@ int floe_down_splits(int d, int E);
 const char* floe_unsupported(int T, int d, int F, int k);
 hipError_t launch_floe_ffn(const FloeProblem& p, hipStream_t s, hipEvent_t mid = nullptr);
 
+// Dense tiled GEMMs on the grouped-GEMM kernel (one group):
+// Y[M][N] fp32 = A[M][K] . B[N][K]^T, K in ksplit slices (slice s adds nothing
+// to the others: its partial sums go to Y + s * ystride); K % (128*ksplit) == 0.
+hipError_t launch_gemm_bt(const u16* A, int lda, int M, const u16* B, int N, int K, float* Y,
+                          int ksplit, size_t ystride, hipStream_t s);
+// H[M][N] bf16 = bf16(gate * silu(A . B^T)) at cells whose bit is set in
+// bits [M][N/32] (rank among the row's set bits = bitpre + popcount before it,
+// gate [M][ksel] by rank), 0 elsewhere.  K % 128 == 0, N % 32 == 0.
+hipError_t launch_atomic_in(const u16* A, int M, const u16* B, int N, int K, const uint32_t* bits,
+                            const int32_t* bitpre, const float* gates, int ksel, u16* H,
+                            hipStream_t s);
+
+// Atomic experts on an nr x nc router grid (atomic.hip).
+hipError_t launch_log_softmax_rows(const float* l, int T, int n, float* out, hipStream_t s);
+// exact top-K of fp32(pr[i] + pc[j]) per token (ties to the lower id i*nc + j),
+// ids ascending, softmax gates, and the kept-cell bitmap with per-word prefixes
+hipError_t launch_grid_topk(const float* pr, const float* pc, int T, int nr, int nc, int K,
+                            int32_t* idx, float* gate, uint32_t* bits, int32_t* bitpre,
+                            hipStream_t s);
+size_t grid_permute_ws_bytes(int T, int N);
+// expert-major permutation over N experts from the bitmap (token order inside
+// an expert), counts, offsets, LIS
+hipError_t launch_grid_permute(const uint32_t* bits, const int32_t* bitpre, int T, int N, int K,
+                               int32_t* counts, int32_t* offsets, int32_t* row_assign,
+                               int32_t* assign_row, double* lis, void* ws, hipStream_t s);
+hipError_t launch_iota(int32_t* out, int n, hipStream_t s);
+
 // y[t] = sum over slots j, then over K slices s, of y_rows[s * split_stride +
 // assign_row[t*k+j] * d], plus y_shared[t]; fixed order, so deterministic.
 hipError_t launch_combine(const float* y_rows, const int32_t* assign_row, int T, int k, int d,

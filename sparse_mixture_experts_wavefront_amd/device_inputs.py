@@ -4,7 +4,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .api import (ExpertWeights, FloeExperts, Int4Proj, MoeLayer, MoeReplica, MwqExperts,
+from .api import (AtomicLayer, ExpertWeights, FloeExperts, Int4Proj, MoeLayer, MoeReplica, MwqExperts,
                   MwqProj)
 
 
@@ -74,3 +74,16 @@ def floe_to_device(wl, device="cuda"):
                        f16(wl.u2_up.s2), f16(wl.u2_up.z2), _t(wl.w_gate, device, True),
                        wd.transpose(1, 2).contiguous(),
                        torch.from_numpy(np.ascontiguousarray(wl.floe_thr)).to(device))
+
+
+def atomic_to_device(wl, device="cuda"):
+    """(AtomicLayer, x) for an atomic-expert ``workloads.Workload``."""
+    cfg = wl.cfg
+    shared = None
+    if cfg.n_shared:
+        shared = ExpertWeights(w_gate=_t(wl.ws_gate, device, True), w_up=_t(wl.ws_up, device, True),
+                               w_down=_t(wl.ws_down, device, True))
+    layer = AtomicLayer(cfg.d, cfg.nr, cfg.nc, cfg.k, _t(wl.w_router, device, True),
+                        _t(wl.w_col, device, True), _t(wl.w_in, device, True),
+                        _t(wl.w_out_t, device, True), cfg.n_shared, cfg.F_shared, shared)
+    return layer, _t(wl.x, device, True)

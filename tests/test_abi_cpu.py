@@ -360,3 +360,40 @@ def test_floe_validation_and_workspace(L, B):
     Lk.d_model, Lk.d_ff = 640, 1024
     Lk.routed = B.Experts()
     assert fwd(experts(), Ldesc=Lk) == B.MOE_ERR_UNSUPPORTED            # d_model % 512
+
+
+def test_atomic_validation_and_workspace(L, B):
+    VO = B.MOE_F_VALIDATE_ONLY
+
+    def desc(d=256, nr=8, nc=32, K=16, shared=False):
+        Ld = B.AtomicLayerDesc()
+        Ld.d_model, Ld.grid_rows, Ld.grid_cols, Ld.top_k = d, nr, nc, K
+        Ld.w_row, Ld.w_col, Ld.w_in, Ld.w_out = _addr(50), _addr(51), _addr(52), _addr(53)
+        if shared:
+            Ld.n_shared, Ld.d_ff_shared = 1, 128
+            Ld.shared = _experts(B)
+        return Ld
+    Ld = desc()
+    n = C.c_size_t(0)
+    assert L.moe_atomic_workspace_size(C.byref(Ld), 48, C.byref(n)) == B.MOE_OK
+    assert n.value >= 48 * 256 * 2 + 48 * 16 * 8     # the [T][N] hidden matrix, ids and gates
+    ws = C.c_void_p(FAKE * 16)
+
+    def fwd(Ldesc, nbytes=None, T=48, flags=VO):
+        need = C.c_size_t(0)
+        L.moe_atomic_workspace_size(C.byref(Ldesc), T, C.byref(need))
+        return L.moe_atomic_layer_forward(C.byref(Ldesc), _addr(1), T, _addr(2), 0, None, ws,
+                                          need.value if nbytes is None else nbytes, flags, None)
+    assert fwd(Ld) == B.MOE_OK
+    assert fwd(desc(shared=True)) == B.MOE_OK
+    assert fwd(Ld, nbytes=n.value - 1) == B.MOE_ERR_WORKSPACE
+    assert fwd(desc(K=0)) == B.MOE_ERR_INVALID_ARG
+    assert fwd(desc(K=257)) == B.MOE_ERR_INVALID_ARG          # K > N
+    assert fwd(desc(d=200)) == B.MOE_ERR_INVALID_ARG
+    assert fwd(desc(nc=40)) == B.MOE_ERR_UNSUPPORTED          # nc % 32
+    assert fwd(desc(nr=2000)) == B.MOE_ERR_UNSUPPORTED        # nr > 1024
+    assert fwd(desc(nr=3, nc=32)) == B.MOE_ERR_UNSUPPORTED    # N % 128
+    assert fwd(Ld, flags=VO | B.MOE_F_LOGITS_GIVEN) == B.MOE_ERR_INVALID_ARG
+    bad = desc()
+    bad.w_in = None
+    assert fwd(bad) == B.MOE_ERR_INVALID_ARG
