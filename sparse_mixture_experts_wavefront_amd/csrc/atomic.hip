@@ -14,7 +14,7 @@
 //                        one binary search per row in the sorted columns), then
 //                        one pass over the grid in id order writes the kept ids
 //                        (ascending), their softmax gates and a kept-cell bitmap
-//   grid_count/scan/write_kernel
+//   grid_count/.../write_kernel
 //                        counting sort of the kept pairs by expert from the
 //                        bitmap: per (32-expert word, 256-token chunk) counts,
 //                        per-expert offsets, then rows in token order inside
@@ -26,7 +26,7 @@ namespace moe {
 namespace {
 
 constexpr int kGridMax = 1024;   // nr, nc limit
-constexpr int kPermChunkT = 256; // tokens per counting chunk
+constexpr int kPermChunkT = 64;  // tokens per counting chunk
 
 __device__ __forceinline__ uint32_t fkey(float f) {
   uint32_t u = __float_as_uint(f);
@@ -70,27 +70,46 @@ __device__ __forceinline__ int block_exscan(int v, int* red) {
 }
 
 // ---- log-probabilities ---------------------------------------------------------
+// one wave per token; the logits may arrive as nsplit partial sums (K slices of
+// the router GEMM, split_stride floats apart) that are added here in slice order
 __global__ __launch_bounds__(64) void log_softmax_kernel(const float* __restrict__ l, int n,
+                                                         int nsplit, size_t split_stride,
                                                          float* __restrict__ out) {
+  __shared__ float row[kGridMax];
   const float* r = l + (size_t)blockIdx.x * n;
   float m = -INFINITY;
-  for (int i = threadIdx.x; i < n; i += 64) m = fmaxf(m, r[i]);
+  for (int i = threadIdx.x; i < n; i += 64) {
+    float v = r[i];
+    for (int q = 1; q < nsplit; ++q) v += r[(size_t)q * split_stride + i];
+    row[i] = v;
+    m = fmaxf(m, v);
+  }
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   float s = 0.0f;
-  for (int i = threadIdx.x; i < n; i += 64) s += expf(r[i] - m);
+  for (int i = threadIdx.x; i < n; i += 64) s += expf(row[i] - m);
   s = wave_sum_f(s);
   const float lse = m + logf(s);
-  for (int i = threadIdx.x; i < n; i += 64) out[(size_t)blockIdx.x * n + i] = r[i] - lse;
+  for (int i = threadIdx.x; i < n; i += 64) out[(size_t)blockIdx.x * n + i] = row[i] - lse;
 }
 
 // ---- exact top-K over the grid -----------------------------------------------
+// The column scores are sorted once (descending, ties by column id); for a row i
+// the cells at or above any key form a prefix of that order, found by binary
+// search, so theta (the K-th largest key) comes from a binary search over the
+// 32-bit keys with one such count per row.  Emission then walks the grid in
+// rounds of 256 consecutive 32-cell words (one word per thread): a cell is kept
+// if its key is above theta, or equal to it while the ties before it (in id
+// order, a block scan per round) are fewer than the ties needed; positions come
+// from a block scan of the kept counts, so ids and gates leave in ascending id
+// order and the bitmap words and their prefixes in coalesced stores.
 __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict__ pr,
                                                         const float* __restrict__ pc, int nr,
                                                         int nc, int K, int32_t* __restrict__ idx,
                                                         float* __restrict__ gate,
                                                         uint32_t* __restrict__ bits,
                                                         int32_t* __restrict__ bitpre) {
-  __shared__ float a[kGridMax], b[kGridMax], bs[kGridMax];
+  __shared__ float a[kGridMax], b[kGridMax], bv[kGridMax];
+  __shared__ unsigned long long bk[kGridMax];  // sort keys: fkey(b) << 32 | ~column
   __shared__ int red[4];
   __shared__ float redf[4];
   const int t = blockIdx.x, tid = threadIdx.x;
@@ -98,35 +117,41 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
   while (ncp < nc) ncp <<= 1;
   for (int i = tid; i < nr; i += 256) a[i] = pr[(size_t)t * nr + i];
   for (int j = tid; j < ncp; j += 256) {
-    const float v = j < nc ? pc[(size_t)t * nc + j] : -INFINITY;
-    if (j < nc) b[j] = v;
-    bs[j] = v;
+    unsigned long long key = 0ull;  // padding sorts last
+    if (j < nc) {
+      const float v = pc[(size_t)t * nc + j];
+      b[j] = v;
+      key = ((unsigned long long)fkey(v) << 32) | (uint32_t)(~(uint32_t)j);
+    }
+    bk[j] = key;
   }
   __syncthreads();
-  // bitonic sort of bs, descending
+  // bitonic sort of bk, descending
   for (int size = 2; size <= ncp; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int q = tid; q < ncp / 2; q += 256) {
         const int lo = 2 * q - (q & (stride - 1));
         const int hi = lo + stride;
         const bool desc = (lo & size) == 0;
-        const float x = bs[lo], y = bs[hi];
+        const unsigned long long x = bk[lo], y = bk[hi];
         if (desc ? (x < y) : (x > y)) {
-          bs[lo] = y;
-          bs[hi] = x;
+          bk[lo] = y;
+          bk[hi] = x;
         }
       }
       __syncthreads();
     }
   }
-  // cells with key >= kt: per row, the columns form a prefix of bs
+  for (int j = tid; j < nc; j += 256) bv[j] = b[~(uint32_t)bk[j]];
+  __syncthreads();
   auto count_ge = [&](uint32_t kt) {
     int c = 0;
     for (int i = tid; i < nr; i += 256) {
+      const float ai = a[i];
       int lo = 0, hi = nc;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (fkey(a[i] + bs[mid]) >= kt)
+        if (fkey(ai + bv[mid]) >= kt)
           lo = mid + 1;
         else
           hi = mid;
@@ -135,8 +160,26 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
     }
     return block_sum(c, red);
   };
+  // the largest and smallest cell scores: row extreme plus column extreme
+  float am = -INFINITY, an = INFINITY;
+  for (int i = tid; i < nr; i += 256) {
+    am = fmaxf(am, a[i]);
+    an = fminf(an, a[i]);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    am = fmaxf(am, __shfl_xor(am, o, 64));
+    an = fminf(an, __shfl_xor(an, o, 64));
+  }
+  __shared__ float redn[4];
+  if ((tid & 63) == 0) {
+    redf[tid >> 6] = am;
+    redn[tid >> 6] = an;
+  }
+  __syncthreads();
+  const float smax = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3])) + bv[0];
+  const float smin = fminf(fminf(redn[0], redn[1]), fminf(redn[2], redn[3])) + bv[nc - 1];
   // theta: the largest key with at least K cells at or above it
-  uint32_t lo = 0u, hi = 0xffffffffu;
+  uint32_t lo = fkey(smin), hi = fkey(smax);
   while (lo < hi) {
     const uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
     if (count_ge(mid) >= K)
@@ -145,62 +188,58 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
       hi = mid - 1;
   }
   const uint32_t theta = lo;
-  const int c_gt = theta == 0xffffffffu ? 0 : count_ge(theta + 1);
+  const int c_gt = theta == 0xffffffffu ? 0 : count_ge(theta + 1u);
   const int m_tie = K - c_gt;  // cells at theta to keep, lowest ids first
 
-  // rows in id order: thread tid owns rows [r0, r1)
-  const int rpt = (nr + 255) / 256;
-  const int r0 = min(tid * rpt, nr), r1 = min(r0 + rpt, nr);
-  int gt_sum = 0, eq_sum = 0;
-  for (int i = r0; i < r1; ++i)
-    for (int j = 0; j < nc; ++j) {
-      const uint32_t kk = fkey(a[i] + b[j]);
-      gt_sum += kk > theta;
-      eq_sum += kk == theta;
-    }
-  const int eq_before = block_exscan(eq_sum, red);
-  int take = min(max(m_tie - eq_before, 0), eq_sum);  // ties this thread keeps
-  const int pos0 = block_exscan(gt_sum + take, red);
-  // max score (the row max plus the column max) for the softmax
-  float am = -INFINITY;
-  for (int i = tid; i < nr; i += 256) am = fmaxf(am, a[i]);
-  for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-  __syncthreads();
-  if ((tid & 63) == 0) redf[tid >> 6] = am;
-  __syncthreads();
-  const float smax = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3])) + bs[0];
-
-  const int W = nr * nc / 32;
-  int pos = pos0;
+  const int W = nr * nc / 32, nw = nc / 32;
+  int base = 0, ties = 0;
   float wsum = 0.0f;
   int32_t* out = idx + (size_t)t * K;
   float* gout = gate + (size_t)t * K;
-  for (int i = r0; i < r1; ++i) {
-    for (int w0 = 0; w0 < nc; w0 += 32) {
-      uint32_t word = 0u;
-      const int wpre = pos;  // kept cells of the token before this word
-      for (int jj = 0; jj < 32; ++jj) {
-        const int j = w0 + jj;
-        const float sv = a[i] + b[j];
-        const uint32_t kk = fkey(sv);
-        bool keep = kk > theta;
-        if (!keep && kk == theta && take > 0) {
-          keep = true;
-          --take;
-        }
-        if (keep) {
-          word |= 1u << jj;
-          const float wv = expf(sv - smax);
-          out[pos] = i * nc + j;
-          gout[pos] = wv;
-          wsum += wv;
-          ++pos;
-        }
+  for (int w0 = 0; w0 < W; w0 += 256) {
+    const int w = w0 + tid;
+    uint32_t word = 0u, tiew = 0u;
+    int i = 0, j0 = 0;
+    if (w < W) {
+      i = w / nw;
+      j0 = (w - i * nw) * 32;
+      const float ai = a[i];
+      for (int q = 0; q < 32; ++q) {
+        const uint32_t kk = fkey(ai + b[j0 + q]);
+        word |= (uint32_t)(kk > theta) << q;
+        tiew |= (uint32_t)(kk == theta) << q;
       }
-      const size_t wi = (size_t)t * W + (size_t)(i * nc + w0) / 32;
-      bits[wi] = word;
-      bitpre[wi] = wpre;
     }
+    // ties before this word in id order, then keep as many as are still needed
+    const int nt = __popc(tiew);
+    const int tb = ties + block_exscan(nt, red);
+    int room = min(max(m_tie - tb, 0), nt);
+    while (room > 0) {  // lowest tie columns first
+      const uint32_t low = tiew & (0u - tiew);
+      word |= low;
+      tiew ^= low;
+      --room;
+    }
+    const int nk = __popc(word);
+    const int pos = base + block_exscan(nk, red);
+    if (w < W) {
+      bits[(size_t)t * W + w] = word;
+      bitpre[(size_t)t * W + w] = pos;
+      int p = pos;
+      uint32_t ww = word;
+      const float ai = a[i];
+      while (ww && p < K) {  // p < K always holds for finite scores
+        const int q = __ffs(ww) - 1;
+        ww &= ww - 1u;
+        const float wv = expf((ai + b[j0 + q]) - smax);
+        out[p] = i * nc + j0 + q;
+        gout[p] = wv;
+        wsum += wv;
+        ++p;
+      }
+    }
+    ties += block_sum(nt, red);
+    base += block_sum(nk, red);
   }
   // normalise: total over the block in a fixed order
   wsum = wave_sum_f(wsum);
@@ -208,7 +247,7 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
   if ((tid & 63) == 0) redf[tid >> 6] = wsum;
   __syncthreads();
   const float total = (redf[0] + redf[1]) + (redf[2] + redf[3]);
-  for (int p = pos0; p < pos; ++p) gout[p] = gout[p] / total;
+  for (int p = tid; p < K; p += 256) gout[p] = gout[p] / total;
 }
 
 // ---- counting sort of the kept pairs by expert ---------------------------------
@@ -250,25 +289,46 @@ __global__ __launch_bounds__(256) void grid_chunkprefix_kernel(int32_t* __restri
   counts[n] = run;
 }
 
-// one block of 1024 threads: exclusive offsets over the experts and LIS
-__global__ __launch_bounds__(1024) void grid_scan_kernel(const int32_t* __restrict__ counts, int N,
-                                                         int T, int K,
-                                                         int32_t* __restrict__ offsets,
-                                                         double* __restrict__ lis) {
+// exclusive offsets over the experts and LIS, in three launches: per-block
+// (256 experts) sums and maxima, one block scanning those, then each expert's
+// offset = its block's prefix + its rank inside the block
+__global__ __launch_bounds__(256) void grid_blocksum_kernel(const int32_t* __restrict__ counts,
+                                                            int N, int32_t* __restrict__ bsum,
+                                                            int32_t* __restrict__ bmax) {
+  __shared__ int red[4];
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int v = n < N ? counts[n] : 0;
+  int m = v;
+  for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
+  const int tot = block_sum(v, red);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    bsum[blockIdx.x] = tot;
+    bmax[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+  }
+}
+
+__global__ __launch_bounds__(1024) void grid_blockscan_kernel(int32_t* __restrict__ bsum,
+                                                              const int32_t* __restrict__ bmax,
+                                                              int nb, int N, int T, int K,
+                                                              int32_t* __restrict__ offsets,
+                                                              double* __restrict__ lis) {
   __shared__ int part[1024];
   __shared__ int mx[1024];
   const int tid = threadIdx.x;
-  const int per = (N + 1023) / 1024;
-  const int n0 = min(tid * per, N), n1 = min(n0 + per, N);
+  const int per = (nb + 1023) / 1024;
+  const int b0 = min(tid * per, nb), b1 = min(b0 + per, nb);
   int sum = 0, best = 0;
-  for (int n = n0; n < n1; ++n) {
-    sum += counts[n];
-    best = max(best, counts[n]);
+  for (int b = b0; b < b1; ++b) {
+    sum += bsum[b];
+    best = max(best, bmax[b]);
   }
   part[tid] = sum;
   mx[tid] = best;
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan of segment sums
+  for (int o = 1; o < 1024; o <<= 1) {
     const int v = tid >= o ? part[tid - o] : 0;
     __syncthreads();
     part[tid] += v;
@@ -279,12 +339,23 @@ __global__ __launch_bounds__(1024) void grid_scan_kernel(const int32_t* __restri
     __syncthreads();
   }
   int run = part[tid] - sum;
-  for (int n = n0; n < n1; ++n) {
-    offsets[n] = run;
-    run += counts[n];
+  for (int b = b0; b < b1; ++b) {  // in place: block sums become block prefixes
+    const int v = bsum[b];
+    bsum[b] = run;
+    run += v;
   }
   if (tid == 1023) offsets[N] = part[1023];
   if (tid == 0) *lis = T == 0 ? NAN : (double)((int64_t)N * mx[0]) / (double)((int64_t)T * K);
+}
+
+__global__ __launch_bounds__(256) void grid_offsets_kernel(const int32_t* __restrict__ counts,
+                                                           const int32_t* __restrict__ bpre, int N,
+                                                           int32_t* __restrict__ offsets) {
+  __shared__ int red[4];
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  const int v = n < N ? counts[n] : 0;
+  const int r = block_exscan(v, red);
+  if (n < N) offsets[n] = bpre[blockIdx.x] + r;
 }
 
 __global__ __launch_bounds__(256) void grid_write_kernel(const uint32_t* __restrict__ bits,
@@ -294,29 +365,41 @@ __global__ __launch_bounds__(256) void grid_write_kernel(const uint32_t* __restr
                                                          const int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ row_assign,
                                                          int32_t* __restrict__ assign_row) {
+  __shared__ int base_s[256][33];
   const int wc = blockIdx.x * 256 + threadIdx.x;
   const int c = blockIdx.y;
   if (wc >= W) return;
   const int N = W * 32;
-  int base[32];
-#pragma unroll
+  int* base = base_s[threadIdx.x];
   for (int q = 0; q < 32; ++q)
     base[q] = offsets[wc * 32 + q] + ccount[(size_t)c * N + wc * 32 + q];
   const int t1 = min((c + 1) * kPermChunkT, T);
   for (int t = c * kPermChunkT; t < t1; ++t) {
-    const uint32_t w = bits[(size_t)t * W + wc];
+    uint32_t w = bits[(size_t)t * W + wc];
     if (!w) continue;
-    const int pre = bitpre[(size_t)t * W + wc];
-#pragma unroll
-    for (int q = 0; q < 32; ++q) {
-      if ((w >> q) & 1u) {
-        const int row = base[q]++;
-        const int a = t * K + pre + __popc(w & ((1u << q) - 1u));
-        if (row_assign) row_assign[row] = a;
-        if (assign_row) assign_row[a] = row;
-      }
+    int slot = bitpre[(size_t)t * W + wc];
+    while (w) {
+      const int q = __ffs(w) - 1;
+      w &= w - 1u;
+      const int row = base[q]++;
+      const int a = t * K + slot++;
+      if (row_assign) row_assign[row] = a;
+      if (assign_row) assign_row[a] = row;
     }
   }
+}
+
+// the input side's activations at the kept cells: thread per (token, slot),
+// bf16(gate * silu(u)) written into the token's row of H (zero elsewhere)
+__global__ __launch_bounds__(256) void atomic_assemble_kernel(const int32_t* __restrict__ idx,
+                                                              const float* __restrict__ gate,
+                                                              const float* __restrict__ ukept,
+                                                              int K, int N, size_t n,
+                                                              u16* __restrict__ H) {
+  const size_t a = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (a >= n) return;
+  const size_t t = a / (size_t)K;
+  H[t * N + idx[a]] = f32_to_bf16(gate[a] * silu_f32(ukept[a]));
 }
 
 __global__ void iota_kernel(int32_t* out, int n) {
@@ -331,9 +414,20 @@ __global__ void iota_kernel_zero(int32_t* out, int n) {
 
 }  // namespace
 
-hipError_t launch_log_softmax_rows(const float* l, int T, int n, float* out, hipStream_t s) {
+hipError_t launch_log_softmax_rows(const float* l, int T, int n, float* out, hipStream_t s,
+                                   int nsplit, size_t split_stride) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(log_softmax_kernel, dim3(T), dim3(64), 0, s, l, n, out);
+  if (n > kGridMax || nsplit < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(log_softmax_kernel, dim3(T), dim3(64), 0, s, l, n, nsplit, split_stride, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_atomic_assemble(const int32_t* idx, const float* gate, const float* ukept, int T,
+                                  int K, int N, u16* H, hipStream_t s) {
+  const size_t n = (size_t)T * K;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(atomic_assemble_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     idx, gate, ukept, K, N, n, H);
   return hipGetLastError();
 }
 
@@ -349,7 +443,8 @@ hipError_t launch_grid_topk(const float* pr, const float* pc, int T, int nr, int
 
 size_t grid_permute_ws_bytes(int T, int N) {
   const size_t nchunk = (size_t)(T + kPermChunkT - 1) / kPermChunkT;
-  return nchunk * (size_t)N * sizeof(int32_t);
+  const size_t nb = (size_t)(N + 255) / 256;
+  return (nchunk * (size_t)N + 2 * nb) * sizeof(int32_t);
 }
 
 hipError_t launch_grid_permute(const uint32_t* bits, const int32_t* bitpre, int T, int N, int K,
@@ -369,7 +464,15 @@ hipError_t launch_grid_permute(const uint32_t* bits, const int32_t* bitpre, int 
   else
     hipLaunchKernelGGL(iota_kernel_zero, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s,
                        counts, N);
-  hipLaunchKernelGGL(grid_scan_kernel, dim3(1), dim3(1024), 0, s, counts, N, T, K, offsets, lis);
+  const int nb = (N + 255) / 256;
+  int32_t* bsum = ccount + (size_t)nchunk * N;
+  int32_t* bmax = bsum + nb;
+  hipLaunchKernelGGL(grid_blocksum_kernel, dim3((unsigned)nb), dim3(256), 0, s, counts, N, bsum,
+                     bmax);
+  hipLaunchKernelGGL(grid_blockscan_kernel, dim3(1), dim3(1024), 0, s, bsum, bmax, nb, N, T, K,
+                     offsets, lis);
+  hipLaunchKernelGGL(grid_offsets_kernel, dim3((unsigned)nb), dim3(256), 0, s, counts, bsum, N,
+                     offsets);
   if (T > 0) {
     const dim3 grid((unsigned)((W + 255) / 256), (unsigned)nchunk);
     hipLaunchKernelGGL(grid_write_kernel, grid, dim3(256), 0, s, bits, bitpre, T, W, K, ccount,

@@ -32,8 +32,10 @@ namespace {
 constexpr int kBK = 64;
 constexpr int kThreads = 256;
 
-// kAtomIn: one matrix, output bf16(gate * silu(acc)) at the cells a per-row
-// bitmap keeps and 0 elsewhere (the input side of the atomic experts)
+// kAtomIn: one matrix; the cells a per-row bitmap keeps go, as fp32, to a
+// compact [rows][ksel] array (position = rank of the cell in its row), and the
+// bf16 output gets 0 everywhere (the input side of the atomic experts: another
+// kernel writes the kept cells' values into it)
 enum Mode { kGateUpSwiglu = 0, kUpRelu = 1, kDown = 2, kAtomIn = 3 };
 
 struct TileArgs {
@@ -62,7 +64,8 @@ struct TileArgs {
   const uint32_t* bits;    // kAtomIn: [rows][wpr] kept cells, bit c%32 of word c/32
   const int32_t* bitpre;   // kAtomIn: [rows][wpr] kept cells of the row before the word
   int wpr;                 // kAtomIn: words per row (N / 32)
-  int ksel;                // kAtomIn: gates per row (gate [rows][ksel], kept cells in order)
+  int ksel;                // kAtomIn: kept cells per row
+  float* ukept;            // kAtomIn: [rows][ksel] fp32 values of the kept cells
 };
 
 // LDS rows of 64 bf16 (128 B).  The LDS has 64 banks of 4 bytes and serves a
@@ -485,6 +488,21 @@ void grouped_gemm_tile_kernel(TileArgs p) {
   }
   wait_vm_lgkm0<0>();
 
+  // kAtomIn: the tile's kept-cell words and their prefixes, staged once in the
+  // (now free) operand buffer: [256 rows][8 words] each
+  uint32_t* tbits = (uint32_t*)sA0;
+  int32_t* tpre = (int32_t*)sA0 + 2048;
+  if constexpr (MODE == kAtomIn) {
+    __syncthreads();
+    for (int q = tid; q < 2048; q += 256) {
+      const int rr = q >> 3, wcol = n_tile * 8 + (q & 7);
+      const size_t gi = (size_t)(row0 + min(rr, rvalid - 1)) * p.wpr + wcol;
+      tbits[q] = wcol < p.wpr ? p.bits[gi] : 0u;
+      tpre[q] = wcol < p.wpr ? p.bitpre[gi] : 0;
+    }
+    __syncthreads();
+  }
+
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -500,20 +518,16 @@ void grouped_gemm_tile_kernel(TileArgs p) {
             p.H[(size_t)grow * p.N + col] = f32_to_bf16(silu_f32(acc[i][j][r]) * acc[i][j + 2][r]);
         }
       } else if constexpr (MODE == kAtomIn) {
-        const uint32_t* brw = p.bits + (size_t)grow * p.wpr;
-        const int32_t* prw = p.bitpre + (size_t)grow * p.wpr;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int col = n_tile * 256 + wn * 128 + j * 32 + fr;
           if (col < p.N) {
-            const uint32_t w = brw[col >> 5];
-            const uint32_t b = (uint32_t)col & 31u;
-            u16 v = 0;
-            if ((w >> b) & 1u) {
-              const int rank = prw[col >> 5] + __popc(w & ((1u << b) - 1u));
-              v = f32_to_bf16(p.gate[(size_t)grow * p.ksel + rank] * silu_f32(acc[i][j][r]));
-            }
-            p.H[(size_t)grow * p.N + col] = v;
+            const int tw = row * 8 + wn * 4 + j;  // word of (row, col) in the staged tile
+            const uint32_t w = tbits[tw];
+            if ((w >> fr) & 1u)
+              p.ukept[(size_t)grow * p.ksel + tpre[tw] + __popc(w & ((1u << fr) - 1u))] =
+                  acc[i][j][r];
+            p.H[(size_t)grow * p.N + col] = 0;
           }
         }
       } else if constexpr (MODE == kUpRelu) {
@@ -756,8 +770,7 @@ hipError_t launch_gemm_bt(const u16* A, int lda, int M, const u16* B, int N, int
 }
 
 hipError_t launch_atomic_in(const u16* A, int M, const u16* B, int N, int K, const uint32_t* bits,
-                            const int32_t* bitpre, const float* gates, int ksel, u16* H,
-                            hipStream_t s) {
+                            const int32_t* bitpre, int ksel, float* ukept, u16* H, hipStream_t s) {
   if (M == 0) return hipSuccess;
   if (K % 128 != 0 || N % 32 != 0) return hipErrorInvalidValue;
   TileArgs a = {};
@@ -769,7 +782,7 @@ hipError_t launch_atomic_in(const u16* A, int M, const u16* B, int N, int K, con
   a.E = 1;
   a.rows = M;
   a.H = H;
-  a.gate = gates;
+  a.ukept = ukept;
   a.bits = bits;
   a.bitpre = bitpre;
   a.wpr = N / 32;

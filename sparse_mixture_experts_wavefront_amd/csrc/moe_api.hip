@@ -982,13 +982,21 @@ int atomic_out_splits(int T, int d, int N) {
   return S;
 }
 
+// K slices of the router GEMMs (T x n x d): enough tiles to fill the chip
+int atomic_router_splits(int T, int n, int d) {
+  const long long tiles = (long long)((T + 255) / 256) * ((n + 255) / 256);
+  int S = 1;
+  while (tiles * S < 256 && S < 16 && d % (128 * 2 * S) == 0) S *= 2;
+  return S;
+}
+
 struct AtomicWs {
-  float *lr, *lc, *pr, *pc, *gates, *y_rows, *y_shared;
+  float *lr, *lc, *pr, *pc, *gates, *ukept, *y_rows, *y_shared;
   int32_t *idx, *counts, *offsets, *row_assign, *assign_row, *iota, *bitpre;
   uint32_t* bits;
   double* lis;
   void *perm_ws, *H, *Hs;
-  int splits;
+  int splits, rsplit, csplit;
   size_t total;
 };
 
@@ -997,12 +1005,15 @@ AtomicWs carve_atomic(const moe_atomic_layer_desc* L, int T, void* ws) {
   const size_t N = (size_t)nr * nc, n = (size_t)T * K, W = N / 32;
   Carver c(ws);
   AtomicWs w;
-  w.lr = (float*)c.take((size_t)T * nr * 4);
-  w.lc = (float*)c.take((size_t)T * nc * 4);
+  w.rsplit = atomic_router_splits(T, nr, d);
+  w.csplit = atomic_router_splits(T, nc, d);
+  w.lr = (float*)c.take((size_t)w.rsplit * T * nr * 4);
+  w.lc = (float*)c.take((size_t)w.csplit * T * nc * 4);
   w.pr = (float*)c.take((size_t)T * nr * 4);
   w.pc = (float*)c.take((size_t)T * nc * 4);
   w.idx = (int32_t*)c.take(n * 4);
   w.gates = (float*)c.take(n * 4);
+  w.ukept = (float*)c.take(n * 4);
   w.bits = (uint32_t*)c.take((size_t)T * W * 4);
   w.bitpre = (int32_t*)c.take((size_t)T * W * 4);
   w.counts = (int32_t*)c.take(N * 4);
@@ -1075,10 +1086,12 @@ moe_status moe_atomic_layer_forward(const moe_atomic_layer_desc* L, const void* 
   const u16* X = (const u16*)x;
 
   stage(0, st);
-  hipError_t e = launch_gemm_bt(X, d, T, (const u16*)L->w_row, nr, d, w.lr, 1, 0, st);
-  if (e == hipSuccess) e = launch_gemm_bt(X, d, T, (const u16*)L->w_col, nc, d, w.lc, 1, 0, st);
-  if (e == hipSuccess) e = launch_log_softmax_rows(w.lr, T, nr, pr, st);
-  if (e == hipSuccess) e = launch_log_softmax_rows(w.lc, T, nc, pc, st);
+  const size_t sr = (size_t)T * nr, sc = (size_t)T * nc;
+  hipError_t e = launch_gemm_bt(X, d, T, (const u16*)L->w_row, nr, d, w.lr, w.rsplit, sr, st);
+  if (e == hipSuccess)
+    e = launch_gemm_bt(X, d, T, (const u16*)L->w_col, nc, d, w.lc, w.csplit, sc, st);
+  if (e == hipSuccess) e = launch_log_softmax_rows(w.lr, T, nr, pr, st, w.rsplit, sr);
+  if (e == hipSuccess) e = launch_log_softmax_rows(w.lc, T, nc, pc, st, w.csplit, sc);
   if (e == hipSuccess)
     e = launch_grid_topk(pr, pc, T, nr, nc, K, idx, gates, w.bits, w.bitpre, st);
   if (e != hipSuccess) return hip_status(e, "grid routing");
@@ -1087,7 +1100,9 @@ moe_status moe_atomic_layer_forward(const moe_atomic_layer_desc* L, const void* 
                           w.perm_ws, st);
   if (e != hipSuccess) return hip_status(e, "grid permutation");
   stage(2, st);
-  e = launch_atomic_in(X, T, (const u16*)L->w_in, N, d, w.bits, w.bitpre, gates, K, (u16*)w.H, st);
+  e = launch_atomic_in(X, T, (const u16*)L->w_in, N, d, w.bits, w.bitpre, K, w.ukept, (u16*)w.H,
+                       st);
+  if (e == hipSuccess) e = launch_atomic_assemble(idx, gates, w.ukept, T, K, N, (u16*)w.H, st);
   if (e != hipSuccess) return hip_status(e, "atomic input GEMM");
   stage(3, st);
   e = launch_gemm_bt((const u16*)w.H, N, T, (const u16*)L->w_out, d, N, w.y_rows, w.splits,

@@ -152,15 +152,19 @@ hipError_t launch_floe_ffn(const FloeProblem& p, hipStream_t s, hipEvent_t mid =
 // to the others: its partial sums go to Y + s * ystride); K % (128*ksplit) == 0.
 hipError_t launch_gemm_bt(const u16* A, int lda, int M, const u16* B, int N, int K, float* Y,
                           int ksplit, size_t ystride, hipStream_t s);
-// H[M][N] bf16 = bf16(gate * silu(A . B^T)) at cells whose bit is set in
-// bits [M][N/32] (rank among the row's set bits = bitpre + popcount before it,
-// gate [M][ksel] by rank), 0 elsewhere.  K % 128 == 0, N % 32 == 0.
+// U = A . B^T [M][N]: the cells whose bit is set in bits [M][N/32] go, fp32, to
+// ukept [M][ksel] at their rank in the row (bitpre + popcount before them);
+// H [M][N] bf16 is set to 0.  K % 128 == 0, N % 32 == 0.
 hipError_t launch_atomic_in(const u16* A, int M, const u16* B, int N, int K, const uint32_t* bits,
-                            const int32_t* bitpre, const float* gates, int ksel, u16* H,
-                            hipStream_t s);
+                            const int32_t* bitpre, int ksel, float* ukept, u16* H, hipStream_t s);
+// H[t][idx[t][s]] = bf16(gate[t][s] * silu(ukept[t][s])) for every kept slot
+hipError_t launch_atomic_assemble(const int32_t* idx, const float* gate, const float* ukept,
+                                  int T, int K, int N, u16* H, hipStream_t s);
 
 // Atomic experts on an nr x nc router grid (atomic.hip).
-hipError_t launch_log_softmax_rows(const float* l, int T, int n, float* out, hipStream_t s);
+// out = log_softmax over each row of the sum of nsplit partial [T][n] slices
+hipError_t launch_log_softmax_rows(const float* l, int T, int n, float* out, hipStream_t s,
+                                   int nsplit = 1, size_t split_stride = 0);
 // exact top-K of fp32(pr[i] + pc[j]) per token (ties to the lower id i*nc + j),
 // ids ascending, softmax gates, and the kept-cell bitmap with per-word prefixes
 hipError_t launch_grid_topk(const float* pr, const float* pc, int T, int nr, int nc, int K,
