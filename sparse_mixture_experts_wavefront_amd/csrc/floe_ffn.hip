@@ -18,7 +18,7 @@
 //   4. floe_down_kernel: the down projection over the listed channels only,
 //      W_down stored transposed so a channel is one contiguous row of d_model
 //      values.  With a few token rows per expert this is a sparse GEMV: each
-//      lane owns two output columns and runs fp32 FMAs over the channels, the
+//      lane owns four output columns and runs fp32 FMAs over the channels, the
 //      hidden values broadcast from LDS; the channel list is split into slices
 //      whose partial sums the combine adds in a fixed order.
 // A row keeps exactly its own channels: a channel that only another row of the
