@@ -50,8 +50,8 @@ def build(verbose: bool = False) -> str:
             if m.strip():
                 print(m)
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + \
-        [o for o, _ in results]
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-Wl,--no-undefined", "-o",
+           tmp] + [o for o, _ in results]
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
     return LIB

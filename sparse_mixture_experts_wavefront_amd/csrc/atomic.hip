@@ -389,19 +389,6 @@ __global__ __launch_bounds__(256) void grid_write_kernel(const uint32_t* __restr
   }
 }
 
-// the input side's activations at the kept cells: thread per (token, slot),
-// bf16(gate * silu(u)) written into the token's row of H (zero elsewhere)
-__global__ __launch_bounds__(256) void atomic_assemble_kernel(const int32_t* __restrict__ idx,
-                                                              const float* __restrict__ gate,
-                                                              const float* __restrict__ ukept,
-                                                              int K, int N, size_t n,
-                                                              u16* __restrict__ H) {
-  const size_t a = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (a >= n) return;
-  const size_t t = a / (size_t)K;
-  H[t * N + idx[a]] = f32_to_bf16(gate[a] * silu_f32(ukept[a]));
-}
-
 __global__ void iota_kernel(int32_t* out, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) out[i] = i;
@@ -419,15 +406,6 @@ hipError_t launch_log_softmax_rows(const float* l, int T, int n, float* out, hip
   if (T == 0) return hipSuccess;
   if (n > kGridMax || nsplit < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(log_softmax_kernel, dim3(T), dim3(64), 0, s, l, n, nsplit, split_stride, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_atomic_assemble(const int32_t* idx, const float* gate, const float* ukept, int T,
-                                  int K, int N, u16* H, hipStream_t s) {
-  const size_t n = (size_t)T * K;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(atomic_assemble_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     idx, gate, ukept, K, N, n, H);
   return hipGetLastError();
 }
 

@@ -24,6 +24,8 @@
 // Two tiled kernels: the 256x256x64 DMA-staged kernel (bf16, K % 128 == 0: the
 // layer path) and a 128x128x64 register-staged kernel (INT4 weights decoded
 // while staged, and any other shape).
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -32,11 +34,14 @@ namespace {
 constexpr int kBK = 64;
 constexpr int kThreads = 256;
 
-// kAtomIn: one matrix; the cells a per-row bitmap keeps go, as fp32, to a
-// compact [rows][ksel] array (position = rank of the cell in its row), and the
-// bf16 output gets 0 everywhere (the input side of the atomic experts: another
-// kernel writes the kept cells' values into it)
+// kAtomIn: one matrix (the input side of the atomic experts); at the cells a
+// per-row bitmap keeps the output is bf16(gate * silu(acc)), elsewhere 0.  The
+// kept cells' fp32 values pass through a compact [rows][ksel] array (position =
+// rank of the cell in its row, where the gates and ids of the row also sit).
 enum Mode { kGateUpSwiglu = 0, kUpRelu = 1, kDown = 2, kAtomIn = 3 };
+// kAtomIn: kept cells of a tile listed in LDS (the operand buffer holds 8192
+// entries; the last 64 take the writes of lanes whose cell is not kept)
+constexpr int kAtomTileCap = 8192 - 64;
 
 struct TileArgs {
   const u16* A;            // gate/up: x [T][lda]; down: H [rows][lda]
@@ -66,6 +71,7 @@ struct TileArgs {
   int wpr;                 // kAtomIn: words per row (N / 32)
   int ksel;                // kAtomIn: kept cells per row
   float* ukept;            // kAtomIn: [rows][ksel] fp32 values of the kept cells
+  const int32_t* kidx;     // kAtomIn: [rows][ksel] column of each kept cell (ascending)
 };
 
 // LDS rows of 64 bf16 (128 B).  The LDS has 64 banks of 4 bytes and serves a
@@ -489,22 +495,107 @@ void grouped_gemm_tile_kernel(TileArgs p) {
   wait_vm_lgkm0<0>();
 
   // kAtomIn: the tile's kept-cell words and their prefixes, staged once in the
-  // (now free) operand buffer: [256 rows][8 words] each
+  // (now free) operand buffers, [256 rows][8 words] each (a word past the row's
+  // end is empty with prefix ksel); per row the first rank in the tile (rlo)
+  // and the tile-local start of its kept cells (rbase, a block scan of the
+  // counts); then each word's prefix is turned into the tile-local position of
+  // its first kept cell.  Up to kAtomTileCap kept cells of the tile are listed
+  // in LDS (fp32 value and row << 8 | column in the tile); a denser tile goes
+  // through ukept in global memory instead.
   uint32_t* tbits = (uint32_t*)sA0;
-  int32_t* tpre = (int32_t*)sA0 + 2048;
+  int32_t* tpos = (int32_t*)sA0 + 2048;
+  int32_t* rlo = (int32_t*)sB0;
+  int32_t* rbase = (int32_t*)sB0 + 256;  // 257 entries
+  float* lu = (float*)sA1;
+  int32_t* lrc = (int32_t*)sB1;
+  bool small_tile = true;
   if constexpr (MODE == kAtomIn) {
     __syncthreads();
     for (int q = tid; q < 2048; q += 256) {
       const int rr = q >> 3, wcol = n_tile * 8 + (q & 7);
       const size_t gi = (size_t)(row0 + min(rr, rvalid - 1)) * p.wpr + wcol;
-      tbits[q] = wcol < p.wpr ? p.bits[gi] : 0u;
-      tpre[q] = wcol < p.wpr ? p.bitpre[gi] : 0;
+      const bool in = wcol < p.wpr && rr < rvalid;
+      tbits[q] = in ? p.bits[gi] : 0u;
+      tpos[q] = in ? p.bitpre[gi] : p.ksel;
     }
     __syncthreads();
+    {
+      const int r = tid;
+      const int lo = r < rvalid ? tpos[r * 8] : 0;
+      const int cnt = r < rvalid ? tpos[r * 8 + 7] + __popc(tbits[r * 8 + 7]) - lo : 0;
+      int incl = cnt;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      __shared__ int wtot[4];
+      if (lane == 63) wtot[wid] = incl;
+      __syncthreads();
+      int base = 0;
+      for (int w = 0; w < wid; ++w) base += wtot[w];
+      rlo[r] = lo;
+      rbase[r] = base + incl - cnt;
+      if (r == 255) rbase[256] = base + incl;
+    }
+    __syncthreads();
+    small_tile = rbase[256] <= kAtomTileCap;
+    if (small_tile) {
+      for (int q = tid; q < 2048; q += 256) tpos[q] += rbase[q >> 3] - rlo[q >> 3];
+      __syncthreads();
+    }
+  }
+
+  if constexpr (MODE == kAtomIn) {
+    // H = 0 at every cell of the tile (the kept cells are rewritten below, after
+    // a barrier); the kept cells' values go to the LDS list (a lane whose cell
+    // is not kept writes to its own spare entry, so no branch per cell), or,
+    // for a dense tile, to ukept at their rank in the row
+    // zeros go through a buffer resource over the tile's rows: a row past them
+    // is dropped by the bounds check, and a column past N lands in the next
+    // row's first columns, which are zeroed too or rewritten after the barrier
+    const __amdgpu_buffer_rsrc_t hres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.H + (size_t)row0 * p.N), (short)0, rvalid * p.N * 2, 0x00020000);
+    const uint32_t below = (1u << fr) - 1u;
+    const int spare = kAtomTileCap + lane;
+    auto cells = [&](auto listed) __attribute__((always_inline)) {
+      constexpr bool LISTED = decltype(listed)::value;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          // (a row past the tile's rows has empty words: nothing is listed)
+          const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
+          const int grow = row0 + row;
+          const uint4 wv = *(const uint4*)(tbits + row * 8 + wn * 4);
+          const int4 pv = *(const int4*)(tpos + row * 8 + wn * 4);
+          const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
+          const int ps[4] = {pv.x, pv.y, pv.z, pv.w};
+          const int hoff = (row * p.N + n_tile * 256 + wn * 128 + fr) * 2;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            __builtin_amdgcn_raw_buffer_store_b16((u16)0, hres, hoff + j * 64, 0, 0);
+            const bool kept = (ws[j] >> fr) & 1u;
+            const int pos = ps[j] + __popc(ws[j] & below);
+            if constexpr (LISTED) {
+              const int at = kept ? pos : spare;
+              lu[at] = acc[i][j][r];
+              lrc[at] = (row << 8) | (wn * 128 + j * 32 + fr);
+            } else if (kept) {  // kept implies row < rvalid
+              p.ukept[(size_t)grow * p.ksel + pos] = acc[i][j][r];
+            }
+          }
+        }
+    };
+    if (small_tile)
+      cells(std::true_type{});
+    else
+      cells(std::false_type{});
+    // the zeros are written before any kept value is (same addresses)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4 && MODE != kAtomIn; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
@@ -516,19 +607,6 @@ void grouped_gemm_tile_kernel(TileArgs p) {
           const int col = n_tile * 128 + wn * 64 + j * 32 + fr;
           if (col < p.N)
             p.H[(size_t)grow * p.N + col] = f32_to_bf16(silu_f32(acc[i][j][r]) * acc[i][j + 2][r]);
-        }
-      } else if constexpr (MODE == kAtomIn) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n_tile * 256 + wn * 128 + j * 32 + fr;
-          if (col < p.N) {
-            const int tw = row * 8 + wn * 4 + j;  // word of (row, col) in the staged tile
-            const uint32_t w = tbits[tw];
-            if ((w >> fr) & 1u)
-              p.ukept[(size_t)grow * p.ksel + tpre[tw] + __popc(w & ((1u << fr) - 1u))] =
-                  acc[i][j][r];
-            p.H[(size_t)grow * p.N + col] = 0;
-          }
         }
       } else if constexpr (MODE == kUpRelu) {
 #pragma unroll
@@ -546,6 +624,47 @@ void grouped_gemm_tile_kernel(TileArgs p) {
         }
       }
     }
+
+  if constexpr (MODE == kAtomIn) {
+    // the tile's kept cells, spread over the block: list entry e of row r has
+    // rank rlo[r] + e - rbase[r] in its row, where its gate (and, for a dense
+    // tile, its value and column) sit
+    __syncthreads();  // the list (or this block's ukept stores) is complete
+    const int total = rbase[256];
+    if (small_tile) {
+      for (int e0 = tid; e0 < total; e0 += 1024) {
+        float u[4], g[4];
+        int rc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int e = min(e0 + 256 * q, total - 1);
+          rc[q] = lrc[e];
+          u[q] = lu[e];
+          const int r = rc[q] >> 8;
+          g[q] = p.gate[(size_t)(row0 + r) * p.ksel + rlo[r] + e - rbase[r]];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (e0 + 256 * q < total)
+            p.H[(size_t)(row0 + (rc[q] >> 8)) * p.N + n_tile * 256 + (rc[q] & 255)] =
+                f32_to_bf16(g[q] * silu_f32(u[q]));
+      }
+    } else {
+      for (int e = tid; e < total; e += 256) {
+        int lo = 0, hi = 255;  // the last row whose list starts at or before e
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (rbase[mid] <= e)
+            lo = mid;
+          else
+            hi = mid - 1;
+        }
+        const size_t a = (size_t)(row0 + lo) * p.ksel + rlo[lo] + (e - rbase[lo]);
+        p.H[(size_t)(row0 + lo) * p.N + p.kidx[a]] =
+            f32_to_bf16(p.gate[a] * silu_f32(p.ukept[a]));
+      }
+    }
+  }
 }
 
 template <int MODE>
@@ -770,7 +889,8 @@ hipError_t launch_gemm_bt(const u16* A, int lda, int M, const u16* B, int N, int
 }
 
 hipError_t launch_atomic_in(const u16* A, int M, const u16* B, int N, int K, const uint32_t* bits,
-                            const int32_t* bitpre, int ksel, float* ukept, u16* H, hipStream_t s) {
+                            const int32_t* bitpre, const int32_t* kidx, const float* gates,
+                            int ksel, float* ukept, u16* H, hipStream_t s) {
   if (M == 0) return hipSuccess;
   if (K % 128 != 0 || N % 32 != 0) return hipErrorInvalidValue;
   TileArgs a = {};
@@ -783,6 +903,8 @@ hipError_t launch_atomic_in(const u16* A, int M, const u16* B, int N, int K, con
   a.rows = M;
   a.H = H;
   a.ukept = ukept;
+  a.kidx = kidx;
+  a.gate = gates;
   a.bits = bits;
   a.bitpre = bitpre;
   a.wpr = N / 32;

@@ -1100,9 +1100,8 @@ moe_status moe_atomic_layer_forward(const moe_atomic_layer_desc* L, const void* 
                           w.perm_ws, st);
   if (e != hipSuccess) return hip_status(e, "grid permutation");
   stage(2, st);
-  e = launch_atomic_in(X, T, (const u16*)L->w_in, N, d, w.bits, w.bitpre, K, w.ukept, (u16*)w.H,
-                       st);
-  if (e == hipSuccess) e = launch_atomic_assemble(idx, gates, w.ukept, T, K, N, (u16*)w.H, st);
+  e = launch_atomic_in(X, T, (const u16*)L->w_in, N, d, w.bits, w.bitpre, idx, gates, K, w.ukept,
+                       (u16*)w.H, st);
   if (e != hipSuccess) return hip_status(e, "atomic input GEMM");
   stage(3, st);
   e = launch_gemm_bt((const u16*)w.H, N, T, (const u16*)L->w_out, d, N, w.y_rows, w.splits,

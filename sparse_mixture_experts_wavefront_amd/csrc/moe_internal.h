@@ -152,14 +152,13 @@ hipError_t launch_floe_ffn(const FloeProblem& p, hipStream_t s, hipEvent_t mid =
 // to the others: its partial sums go to Y + s * ystride); K % (128*ksplit) == 0.
 hipError_t launch_gemm_bt(const u16* A, int lda, int M, const u16* B, int N, int K, float* Y,
                           int ksplit, size_t ystride, hipStream_t s);
-// U = A . B^T [M][N]: the cells whose bit is set in bits [M][N/32] go, fp32, to
-// ukept [M][ksel] at their rank in the row (bitpre + popcount before them);
-// H [M][N] bf16 is set to 0.  K % 128 == 0, N % 32 == 0.
+// U = A . B^T [M][N]; H [M][N] bf16 = bf16(gates * silu(U)) at the cells whose
+// bit is set in bits [M][N/32] and 0 elsewhere.  A kept cell's rank in its row
+// (bitpre + popcount before it) indexes gates, kidx (its column) and ukept
+// ([M][ksel] fp32 scratch for U).  K % 128 == 0, N % 32 == 0.
 hipError_t launch_atomic_in(const u16* A, int M, const u16* B, int N, int K, const uint32_t* bits,
-                            const int32_t* bitpre, int ksel, float* ukept, u16* H, hipStream_t s);
-// H[t][idx[t][s]] = bf16(gate[t][s] * silu(ukept[t][s])) for every kept slot
-hipError_t launch_atomic_assemble(const int32_t* idx, const float* gate, const float* ukept,
-                                  int T, int K, int N, u16* H, hipStream_t s);
+                            const int32_t* bitpre, const int32_t* kidx, const float* gates,
+                            int ksel, float* ukept, u16* H, hipStream_t s);
 
 // Atomic experts on an nr x nc router grid (atomic.hip).
 // out = log_softmax over each row of the sum of nsplit partial [T][n] slices

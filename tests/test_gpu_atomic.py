@@ -76,6 +76,9 @@ SMALL = {
     "top1": dict(T=40, d=256, nr=8, nc=32, E=256, k=1, n_shared=0),
     "all_cells": dict(T=20, d=256, nr=4, nc=32, E=128, k=128, F_shared=128),
     "ragged": dict(T=300, d=384, nr=20, nc=64, E=1280, k=100, F_shared=256),
+    # 96 x 256 cells per tile, 3/4 kept: more kept cells than a tile lists in
+    # LDS, so the input GEMM takes its dense-tile path
+    "dense_tiles": dict(T=96, d=256, nr=8, nc=32, E=256, k=192, F_shared=128),
 }
 
 
