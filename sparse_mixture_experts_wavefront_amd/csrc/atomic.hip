@@ -34,6 +34,12 @@ __device__ __forceinline__ uint32_t fkey(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// the float whose key is k (for keys of non-NaN floats: s >= kf(k) <=> fkey(s) >= k,
+// with -0.0 and +0.0 equal on both sides)
+__device__ __forceinline__ float kf(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 __device__ __forceinline__ int wave_sum(int v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
@@ -145,13 +151,14 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
   for (int j = tid; j < nc; j += 256) bv[j] = b[~(uint32_t)bk[j]];
   __syncthreads();
   auto count_ge = [&](uint32_t kt) {
+    const float th = kf(kt);
     int c = 0;
     for (int i = tid; i < nr; i += 256) {
       const float ai = a[i];
       int lo = 0, hi = nc;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (fkey(ai + bv[mid]) >= kt)
+        if (ai + bv[mid] >= th)
           lo = mid + 1;
         else
           hi = mid;
@@ -178,18 +185,28 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
   __syncthreads();
   const float smax = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3])) + bv[0];
   const float smin = fminf(fminf(redn[0], redn[1]), fminf(redn[2], redn[3])) + bv[nc - 1];
-  // theta: the largest key with at least K cells at or above it
+  // theta: the largest key with at least K cells at or above it.  A probe with
+  // exactly K cells at or above it ends the search early: those cells are the
+  // selection (kept: key >= probe, no ties to break).
   uint32_t lo = fkey(smin), hi = fkey(smax);
+  bool exact = false;
   while (lo < hi) {
     const uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
-    if (count_ge(mid) >= K)
+    const int c = count_ge(mid);
+    if (c == K) {
+      lo = mid;
+      exact = true;
+      break;
+    }
+    if (c > K)
       lo = mid;
     else
       hi = mid - 1;
   }
   const uint32_t theta = lo;
-  const int c_gt = theta == 0xffffffffu ? 0 : count_ge(theta + 1u);
+  const int c_gt = exact ? K : (theta == 0xffffffffu ? 0 : count_ge(theta + 1u));
   const int m_tie = K - c_gt;  // cells at theta to keep, lowest ids first
+  const float thf = kf(theta);
 
   const int W = nr * nc / 32, nw = nc / 32;
   int base = 0, ties = 0;
@@ -204,10 +221,15 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
       i = w / nw;
       j0 = (w - i * nw) * 32;
       const float ai = a[i];
-      for (int q = 0; q < 32; ++q) {
-        const uint32_t kk = fkey(ai + b[j0 + q]);
-        word |= (uint32_t)(kk > theta) << q;
-        tiew |= (uint32_t)(kk == theta) << q;
+      for (int q0 = 0; q0 < 32; ++q0) {
+        const int q = (q0 + tid) & 31;  // rotated per lane: no LDS bank conflicts
+        const float sv = ai + b[j0 + q];
+        word |= (uint32_t)(sv > thf) << q;
+        tiew |= (uint32_t)(sv == thf) << q;
+      }
+      if (exact) {  // the cells at theta are kept outright
+        word |= tiew;
+        tiew = 0u;
       }
     }
     // ties before this word in id order, then keep as many as are still needed
@@ -373,18 +395,31 @@ __global__ __launch_bounds__(256) void grid_write_kernel(const uint32_t* __restr
   int* base = base_s[threadIdx.x];
   for (int q = 0; q < 32; ++q)
     base[q] = offsets[wc * 32 + q] + ccount[(size_t)c * N + wc * 32 + q];
-  const int t1 = min((c + 1) * kPermChunkT, T);
-  for (int t = c * kPermChunkT; t < t1; ++t) {
-    uint32_t w = bits[(size_t)t * W + wc];
-    if (!w) continue;
-    int slot = bitpre[(size_t)t * W + wc];
-    while (w) {
-      const int q = __ffs(w) - 1;
-      w &= w - 1u;
-      const int row = base[q]++;
-      const int a = t * K + slot++;
-      if (row_assign) row_assign[row] = a;
-      if (assign_row) assign_row[a] = row;
+  // tokens in batches of 16 whose words and prefixes are loaded before any
+  // store, so the loads of a batch overlap
+  const int t0 = c * kPermChunkT, t1 = min(t0 + kPermChunkT, T);
+  for (int tb = t0; tb < t1; tb += 16) {
+    uint32_t wv[16];
+    int pv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int t = min(tb + u, t1 - 1);
+      wv[u] = tb + u < t1 ? bits[(size_t)t * W + wc] : 0u;
+      pv[u] = bitpre[(size_t)t * W + wc];
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      uint32_t w = wv[u];
+      int slot = pv[u];
+      const int t = tb + u;
+      while (w) {
+        const int q = __ffs(w) - 1;
+        w &= w - 1u;
+        const int row = base[q]++;
+        const int a = t * K + slot++;
+        if (row_assign) row_assign[row] = a;
+        if (assign_row) assign_row[a] = row;
+      }
     }
   }
 }
