@@ -343,29 +343,19 @@ void grouped_gemm_tile_kernel(TileArgs p) {
   constexpr int STAGE = BM * BK;
   __shared__ __align__(16) u16 sA0[STAGE], sA1[STAGE];
   __shared__ __align__(16) u16 sB0[STAGE], sB1[STAGE];
-  __shared__ int s_tile[3];
+  __shared__ int s_tile[5];  // expert, first row, valid rows, column tile, K slice
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
 
-  const int nb = gridDim.x;
-  const int bid = blockIdx.x;
-  int t = (bid & 7) * (nb >> 3) + (bid >> 3);
-  // K slice outermost: slice ks covers K [ks*K/ksplit, +K/ksplit) and writes
-  // its partial sums to Y + ks*ystride (the combine adds the slices)
-  const int slice_tiles = p.m_tiles_max * p.n_tiles;
-  const int ks = t / slice_tiles;
-  if (ks >= p.ksplit) return;
-  t -= ks * slice_tiles;
-  const int kslice = p.K / p.ksplit;
-  const int per_group = kV2GroupM * p.n_tiles;
-  const int g = t / per_group;
-  const int first_m = g * kV2GroupM;
-  const int gm = min(p.m_tiles_max - first_m, kV2GroupM);
-  const int in_g = t - g * per_group;
-  const int m_tile = first_m + in_g % gm;
-  const int n_tile = in_g / gm;
-
+  // Tile map.  Wave 0 scans the experts' row-tile counts; the real tiles are
+  // numbered K slice first (slice ks covers K [ks*K/ksplit, +K/ksplit) and
+  // writes its partial sums to Y + ks*ystride, which the combine adds), then in
+  // groups of kV2GroupM row tiles per column strip.  Block bid runs on XCD
+  // bid % 8 and takes tile (bid % 8) * ceil(R/8) + bid / 8 of the R real tiles:
+  // every XCD gets a contiguous eighth of the real tiles (equal work, and
+  // neighbouring tiles share A and B slices in that XCD's L2); blocks past them
+  // exit at once.
   if (wid == 0) {
     int cnt = 0, first = 0;
     if (p.offsets) {
@@ -383,11 +373,32 @@ void grouped_gemm_tile_kernel(TileArgs p) {
       if (lane >= o) incl += v;
     }
     const int excl = incl - tiles;
+    const int m_real = __shfl(incl, 63, 64);
+    const int slice_tiles = m_real * p.n_tiles;
+    const int total = slice_tiles * p.ksplit;
+    const int per_xcd = (total + 7) >> 3;
+    const int loc = blockIdx.x >> 3;
+    int t = (blockIdx.x & 7) * per_xcd + loc;
     if (lane == 0) s_tile[0] = -1;
-    if (m_tile >= excl && m_tile < incl) {
-      s_tile[0] = lane;
-      s_tile[1] = first + (m_tile - excl) * BM;
-      s_tile[2] = min(BM, cnt - (m_tile - excl) * BM);
+    if (loc < per_xcd && t < total) {
+      const int ksl = t / slice_tiles;
+      t -= ksl * slice_tiles;
+      const int per_group = kV2GroupM * p.n_tiles;
+      const int g = t / per_group;
+      const int first_m = g * kV2GroupM;
+      const int gm = min(m_real - first_m, kV2GroupM);
+      const int in_g = t - g * per_group;
+      const int m_tile = first_m + in_g % gm;
+      if (lane == 0) {
+        s_tile[3] = in_g / gm;
+        s_tile[4] = ksl;
+      }
+      // (one lane matches; a wave executes its LDS writes in program order)
+      if (m_tile >= excl && m_tile < incl) {
+        s_tile[0] = lane;
+        s_tile[1] = first + (m_tile - excl) * BM;
+        s_tile[2] = min(BM, cnt - (m_tile - excl) * BM);
+      }
     }
   }
   __syncthreads();
@@ -395,6 +406,9 @@ void grouped_gemm_tile_kernel(TileArgs p) {
   if (expert < 0) return;
   const int row0 = __builtin_amdgcn_readfirstlane(s_tile[1]);
   const int rvalid = __builtin_amdgcn_readfirstlane(s_tile[2]);
+  const int n_tile = __builtin_amdgcn_readfirstlane(s_tile[3]);
+  const int ks = __builtin_amdgcn_readfirstlane(s_tile[4]);
+  const int kslice = p.K / p.ksplit;
 
   // DMA: instruction j (0..7 A, 8..15 B) of wave w fills LDS rows (w*8+j%8)*8 ..
   // +8 (1 KB); lane L feeds row (w*8+j%8)*8 + L/8 at 16-byte position L%8.
@@ -669,7 +683,9 @@ void grouped_gemm_tile_kernel(TileArgs p) {
 
 template <int MODE>
 hipError_t run_tiles_v2(TileArgs a, hipStream_t s) {
-  const int m_tiles_max = (a.rows + kV2BM - 1) / kV2BM + min(a.E, a.rows);
+  // bound on the real row tiles: sum over experts of ceil(rows_e / 256)
+  const int m_tiles_max =
+      (a.rows + kV2BM - 1) / kV2BM + (a.E > 1 ? min(a.E, a.rows) : 0);
   a.m_tiles_max = m_tiles_max;
   const int ncols = (MODE == kGateUpSwiglu) ? 128 : 256;
   a.n_tiles = (a.N + ncols - 1) / ncols;
