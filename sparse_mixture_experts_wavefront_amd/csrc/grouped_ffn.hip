@@ -564,15 +564,17 @@ void grouped_gemm_tile_kernel(TileArgs p) {
     // a barrier); the kept cells' values go to the LDS list (a lane whose cell
     // is not kept writes to its own spare entry, so no branch per cell), or,
     // for a dense tile, to ukept at their rank in the row
-    // zeros go through a buffer resource over the tile's rows: a row past them
-    // is dropped by the bounds check, and a column past N lands in the next
-    // row's first columns, which are zeroed too or rewritten after the barrier
+    // zeros go through a buffer resource over the tile's rows, so a row past
+    // them is dropped by the bounds check; a 32-column group past N (N is a
+    // multiple of 32) is skipped by a branch that is uniform over the wave
     const __amdgpu_buffer_rsrc_t hres = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.H + (size_t)row0 * p.N), (short)0, rvalid * p.N * 2, 0x00020000);
+    const int wcol0 = n_tile * 256 + __builtin_amdgcn_readfirstlane(wn) * 128;
     const uint32_t below = (1u << fr) - 1u;
     const int spare = kAtomTileCap + lane;
-    auto cells = [&](auto listed) __attribute__((always_inline)) {
+    auto cells = [&](auto listed, auto whole) __attribute__((always_inline)) {
       constexpr bool LISTED = decltype(listed)::value;
+      constexpr bool WHOLE = decltype(whole)::value;  // all of the wave's 128 columns < N
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -587,7 +589,8 @@ void grouped_gemm_tile_kernel(TileArgs p) {
           const int hoff = (row * p.N + n_tile * 256 + wn * 128 + fr) * 2;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            __builtin_amdgcn_raw_buffer_store_b16((u16)0, hres, hoff + j * 64, 0, 0);
+            if (WHOLE || wcol0 + j * 32 < p.N)
+              __builtin_amdgcn_raw_buffer_store_b16((u16)0, hres, hoff + j * 64, 0, 0);
             const bool kept = (ws[j] >> fr) & 1u;
             const int pos = ps[j] + __popc(ws[j] & below);
             if constexpr (LISTED) {
@@ -600,10 +603,12 @@ void grouped_gemm_tile_kernel(TileArgs p) {
           }
         }
     };
-    if (small_tile)
-      cells(std::true_type{});
+    if (small_tile && wcol0 + 128 <= p.N)
+      cells(std::true_type{}, std::true_type{});
+    else if (small_tile)
+      cells(std::true_type{}, std::false_type{});
     else
-      cells(std::false_type{});
+      cells(std::false_type{}, std::false_type{});
     // the zeros are written before any kept value is (same addresses)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }

@@ -79,6 +79,8 @@ SMALL = {
     # 96 x 256 cells per tile, 3/4 kept: more kept cells than a tile lists in
     # LDS, so the input GEMM takes its dense-tile path
     "dense_tiles": dict(T=96, d=256, nr=8, nc=32, E=256, k=192, F_shared=128),
+    # N = 384: the last column tile of the input GEMM is half outside the grid
+    "odd_width": dict(T=300, d=256, nr=12, nc=32, E=384, k=40, F_shared=128),
 }
 
 
