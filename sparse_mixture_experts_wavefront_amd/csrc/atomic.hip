@@ -14,11 +14,11 @@
 //                        one binary search per row in the sorted columns), then
 //                        one pass over the grid in id order writes the kept ids
 //                        (ascending), their softmax gates and a kept-cell bitmap
-//   grid_count/.../write_kernel
+//   grid_count/.../rows_kernel
 //                        counting sort of the kept pairs by expert from the
-//                        bitmap: per (32-expert word, 256-token chunk) counts,
-//                        per-expert offsets, then rows in token order inside
-//                        each expert -- deterministic, no atomics
+//                        bitmap: per (32-expert word, 64-token chunk) counts,
+//                        per-expert offsets, then each expert's rows in token
+//                        order -- deterministic, no atomics
 // Cells with equal fp32 scores are ordered by id, so the selection is unique.
 #include "moe_internal.h"
 
@@ -27,6 +27,8 @@ namespace {
 
 constexpr int kGridMax = 1024;   // nr, nc limit
 constexpr int kPermChunkT = 64;  // tokens per counting chunk
+constexpr int kRowsTok = 256;    // tokens staged per round of grid_rows_kernel
+constexpr int kRowsSpan = 1024;  // tokens per grid_rows_kernel block (a multiple of both)
 
 __device__ __forceinline__ uint32_t fkey(float f) {
   uint32_t u = __float_as_uint(f);
@@ -380,45 +382,67 @@ __global__ __launch_bounds__(256) void grid_offsets_kernel(const int32_t* __rest
   if (n < N) offsets[n] = bpre[blockIdx.x] + r;
 }
 
-__global__ __launch_bounds__(256) void grid_write_kernel(const uint32_t* __restrict__ bits,
-                                                         const int32_t* __restrict__ bitpre, int T,
-                                                         int W, int K,
-                                                         const int32_t* __restrict__ ccount,
-                                                         const int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ row_assign,
-                                                         int32_t* __restrict__ assign_row) {
-  __shared__ int base_s[256][33];
-  const int wc = blockIdx.x * 256 + threadIdx.x;
-  const int c = blockIdx.y;
-  if (wc >= W) return;
+// Block: 256 experts (8 bitmap words) x one range of kRowsSpan tokens; thread:
+// one expert, which writes its rows of row_assign for those tokens in token
+// order, from its offset plus the chunk prefix at the range's start on.
+// Tokens are staged kRowsTok at a time (words and prefixes of the block's 8
+// words; the next round's loads are issued before this round is processed);
+// per 32 tokens the thread gathers its bit of each into a mask and walks the
+// set bits.  The slots of one token that the 64 experts of a wave keep are
+// consecutive, so assign_row stores from a wave land together too.
+__global__ __launch_bounds__(256) void grid_rows_kernel(const uint32_t* __restrict__ bits,
+                                                        const int32_t* __restrict__ bitpre, int T,
+                                                        int W, int K,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ cpre,
+                                                        int32_t* __restrict__ row_assign,
+                                                        int32_t* __restrict__ assign_row) {
+  __shared__ uint32_t sw[kRowsTok][8];
+  __shared__ int32_t sp[kRowsTok][8];
+  const int tid = threadIdx.x;
+  const int wc0 = blockIdx.x * 8;
   const int N = W * 32;
-  int* base = base_s[threadIdx.x];
-  for (int q = 0; q < 32; ++q)
-    base[q] = offsets[wc * 32 + q] + ccount[(size_t)c * N + wc * 32 + q];
-  // tokens in batches of 16 whose words and prefixes are loaded before any
-  // store, so the loads of a batch overlap
-  const int t0 = c * kPermChunkT, t1 = min(t0 + kPermChunkT, T);
-  for (int tb = t0; tb < t1; tb += 16) {
-    uint32_t wv[16];
-    int pv[16];
+  const int n = blockIdx.x * 256 + tid;
+  const int myw = tid >> 5, b = tid & 31;
+  const uint32_t below = (1u << b) - 1u;
+  const int tbeg = blockIdx.y * kRowsSpan, tend = min(tbeg + kRowsSpan, T);
+  int row = n < N ? offsets[n] + cpre[(size_t)(tbeg / kPermChunkT) * N + n] : 0;
+  uint32_t rw[8];
+  int rp[8];
+  auto load = [&](int t0) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int t = min(tb + u, t1 - 1);
-      wv[u] = tb + u < t1 ? bits[(size_t)t * W + wc] : 0u;
-      pv[u] = bitpre[(size_t)t * W + wc];
+    for (int i = 0; i < 8; ++i) {
+      const int q = tid + 256 * i;
+      const int t = t0 + (q >> 3), w = wc0 + (q & 7);
+      const bool in = t < tend && w < W;
+      rw[i] = in ? bits[(size_t)t * W + w] : 0u;
+      rp[i] = in ? bitpre[(size_t)t * W + w] : 0;
     }
+  };
+  load(tbeg);
+  for (int t0 = tbeg; t0 < tend; t0 += kRowsTok) {
+    __syncthreads();  // the previous round's reads are done
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      uint32_t w = wv[u];
-      int slot = pv[u];
-      const int t = tb + u;
-      while (w) {
-        const int q = __ffs(w) - 1;
-        w &= w - 1u;
-        const int row = base[q]++;
-        const int a = t * K + slot++;
+    for (int i = 0; i < 8; ++i) {
+      const int q = tid + 256 * i;
+      sw[q >> 3][q & 7] = rw[i];
+      sp[q >> 3][q & 7] = rp[i];
+    }
+    __syncthreads();
+    if (t0 + kRowsTok < tend) load(t0 + kRowsTok);
+    if (n >= N) continue;
+    for (int u0 = 0; u0 < kRowsTok; u0 += 32) {
+      uint32_t m = 0u;  // bit u: token t0 + u0 + u keeps expert n
+#pragma unroll
+      for (int u = 0; u < 32; ++u) m |= ((sw[u0 + u][myw] >> b) & 1u) << u;
+      while (m) {
+        const int u = u0 + __ffs(m) - 1;
+        m &= m - 1u;
+        const uint32_t w = sw[u][myw];
+        const int a = (t0 + u) * K + sp[u][myw] + __popc(w & below);
         if (row_assign) row_assign[row] = a;
         if (assign_row) assign_row[a] = row;
+        ++row;
       }
     }
   }
@@ -486,11 +510,11 @@ hipError_t launch_grid_permute(const uint32_t* bits, const int32_t* bitpre, int 
                      offsets, lis);
   hipLaunchKernelGGL(grid_offsets_kernel, dim3((unsigned)nb), dim3(256), 0, s, counts, bsum, N,
                      offsets);
-  if (T > 0) {
-    const dim3 grid((unsigned)((W + 255) / 256), (unsigned)nchunk);
-    hipLaunchKernelGGL(grid_write_kernel, grid, dim3(256), 0, s, bits, bitpre, T, W, K, ccount,
-                       offsets, row_assign, assign_row);
-  }
+  if (T > 0 && (row_assign || assign_row))
+    hipLaunchKernelGGL(grid_rows_kernel,
+                       dim3((unsigned)((W + 7) / 8), (unsigned)((T + kRowsSpan - 1) / kRowsSpan)),
+                       dim3(256), 0, s, bits, bitpre, T, W, K, offsets, ccount, row_assign,
+                       assign_row);
   return hipGetLastError();
 }
 
