@@ -61,8 +61,9 @@ __device__ __forceinline__ int block_sum(int v, int* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
-// exclusive scan of one value per thread over the block (256 threads)
-__device__ __forceinline__ int block_exscan(int v, int* red) {
+// exclusive scan of one value per thread over the block (256 threads); the
+// block total goes to *total
+__device__ __forceinline__ int block_exscan(int v, int* red, int* total = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int incl = v;
   for (int o = 1; o < 64; o <<= 1) {
@@ -74,6 +75,7 @@ __device__ __forceinline__ int block_exscan(int v, int* red) {
   __syncthreads();
   int base = 0;
   for (int i = 0; i < w; ++i) base += red[i];
+  if (total) *total = red[0] + red[1] + red[2] + red[3];
   return base + incl - v;
 }
 
@@ -191,21 +193,22 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
   // exactly K cells at or above it ends the search early: those cells are the
   // selection (kept: key >= probe, no ties to break).
   uint32_t lo = fkey(smin), hi = fkey(smax);
-  bool exact = false;
+  int c_lo = nr * nc;  // cells at or above key lo
   while (lo < hi) {
     const uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
     const int c = count_ge(mid);
-    if (c == K) {
+    if (c >= K) {
       lo = mid;
-      exact = true;
-      break;
-    }
-    if (c > K)
-      lo = mid;
-    else
+      c_lo = c;
+      if (c == K) break;
+    } else {
       hi = mid - 1;
+    }
   }
   const uint32_t theta = lo;
+  // exactly K cells at or above theta (the usual case): they are the selection;
+  // otherwise theta is the K-th largest key and ties at it are broken by id
+  const bool exact = c_lo == K;
   const int c_gt = exact ? K : (theta == 0xffffffffu ? 0 : count_ge(theta + 1u));
   const int m_tie = K - c_gt;  // cells at theta to keep, lowest ids first
   const float thf = kf(theta);
@@ -217,35 +220,47 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
   float* gout = gate + (size_t)t * K;
   for (int w0 = 0; w0 < W; w0 += 256) {
     const int w = w0 + tid;
-    uint32_t word = 0u, tiew = 0u;
+    uint32_t word = 0u;
     int i = 0, j0 = 0;
-    if (w < W) {
-      i = w / nw;
-      j0 = (w - i * nw) * 32;
-      const float ai = a[i];
-      for (int q0 = 0; q0 < 32; ++q0) {
-        const int q = (q0 + tid) & 31;  // rotated per lane: no LDS bank conflicts
-        const float sv = ai + b[j0 + q];
-        word |= (uint32_t)(sv > thf) << q;
-        tiew |= (uint32_t)(sv == thf) << q;
+    if (exact) {  // block-uniform: keep every cell at or above theta
+      if (w < W) {
+        i = w / nw;
+        j0 = (w - i * nw) * 32;
+        const float ai = a[i];
+        for (int q0 = 0; q0 < 32; ++q0) {
+          const int q = (q0 + tid) & 31;  // rotated per lane: no LDS bank conflicts
+          word |= (uint32_t)(ai + b[j0 + q] >= thf) << q;
+        }
       }
-      if (exact) {  // the cells at theta are kept outright
-        word |= tiew;
-        tiew = 0u;
+    } else {
+      uint32_t tiew = 0u;
+      if (w < W) {
+        i = w / nw;
+        j0 = (w - i * nw) * 32;
+        const float ai = a[i];
+        for (int q0 = 0; q0 < 32; ++q0) {
+          const int q = (q0 + tid) & 31;
+          const float sv = ai + b[j0 + q];
+          word |= (uint32_t)(sv > thf) << q;
+          tiew |= (uint32_t)(sv == thf) << q;
+        }
       }
-    }
-    // ties before this word in id order, then keep as many as are still needed
-    const int nt = __popc(tiew);
-    const int tb = ties + block_exscan(nt, red);
-    int room = min(max(m_tie - tb, 0), nt);
-    while (room > 0) {  // lowest tie columns first
-      const uint32_t low = tiew & (0u - tiew);
-      word |= low;
-      tiew ^= low;
-      --room;
+      // ties before this word in id order, then keep as many as are still needed
+      const int nt = __popc(tiew);
+      int tsum;
+      const int tb = ties + block_exscan(nt, red, &tsum);
+      int room = min(max(m_tie - tb, 0), nt);
+      while (room > 0) {  // lowest tie columns first
+        const uint32_t low = tiew & (0u - tiew);
+        word |= low;
+        tiew ^= low;
+        --room;
+      }
+      ties += tsum;
     }
     const int nk = __popc(word);
-    const int pos = base + block_exscan(nk, red);
+    int ksum;
+    const int pos = base + block_exscan(nk, red, &ksum);
     if (w < W) {
       bits[(size_t)t * W + w] = word;
       bitpre[(size_t)t * W + w] = pos;
@@ -262,8 +277,7 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
         ++p;
       }
     }
-    ties += block_sum(nt, red);
-    base += block_sum(nk, red);
+    base += ksum;
   }
   // normalise: total over the block in a fixed order
   wsum = wave_sum_f(wsum);
