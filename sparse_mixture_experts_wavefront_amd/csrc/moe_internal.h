@@ -19,7 +19,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kMaxExperts = 64;
 constexpr int kMaxTopK = 8;
 constexpr int kPermChunk = 2048;      // assignments per block in the multi-block permutation
-constexpr int kPermFusedMax = 16384;  // up to this many assignments: one fused block
+constexpr int kPermFusedMax = 2048;  // up to this many assignments: one fused block
 
 __device__ __forceinline__ float bf16_to_f32(u16 b) {
   return __uint_as_float((uint32_t)b << 16);

@@ -178,9 +178,9 @@ hipError_t launch_route_topk(const void* x, moe_dtype xdt, const void* w_router,
                        b_router, T, d, E, k, seg, logits, idx, gate, lg);
     return hipGetLastError();
   }
-  // few token groups (decode): 16 waves share each group's reduction over d;
-  // many groups: 4 waves per group already fill the chip
-  const bool wide = groups <= 64;
+  // up to 256 token groups (decode, 4096-token prefill): 16 waves share each
+  // group's reduction over d; more groups: 4 waves per group fill the chip
+  const bool wide = groups <= 256;
   const int eb = (E + 15) / 16;
 #define MOE_ROUTE_LAUNCH(EBV, NWV)                                                       \
   hipLaunchKernelGGL((route_topk_kernel<EBV, NWV, false>), grid, dim3(64 * NWV), 0, s, x, \
