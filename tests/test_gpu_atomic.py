@@ -81,6 +81,9 @@ SMALL = {
     "dense_tiles": dict(T=96, d=256, nr=8, nc=32, E=256, k=192, F_shared=128),
     # N = 384: the last column tile of the input GEMM is half outside the grid
     "odd_width": dict(T=300, d=256, nr=12, nc=32, E=384, k=40, F_shared=128),
+    # the largest grid (1024 x 1024 = 1,048,576 experts): sort of 1024 column
+    # scores, 4 rows per thread, 32768 bitmap words per token
+    "max_grid": dict(T=3, d=128, nr=1024, nc=1024, E=1024 * 1024, k=4096, F_shared=128),
 }
 
 
