@@ -613,21 +613,43 @@ void grouped_gemm_tile_kernel(TileArgs p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
+  if constexpr (MODE == kGateUpSwiglu) {
+    // the tile's 256 x 128 bf16 outputs are assembled in LDS (rows 0..127 in
+    // sA0, 128..255 in sA1; 16-byte chunk c of row r at position c ^ (r & 7), so
+    // rows 4 apart, written by the two lane halves, use different banks) and
+    // leave in 16-byte stores, 16 lanes per 256-byte row
+    __syncthreads();  // every wave is done with the operand buffers
+    auto hp = [&](int row, int col) -> u16* {
+      return (row < 128 ? sA0 : sA1) + (row & 127) * 128 + (((col >> 3) ^ (row & 7)) << 3) + (col & 7);
+    };
 #pragma unroll
-  for (int i = 0; i < 4 && MODE != kAtomIn; ++i)
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          *hp(row, wn * 64 + j * 32 + fr) = f32_to_bf16(silu_f32(acc[i][j][r]) * acc[i][j + 2][r]);
+      }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int l = q * 256 + tid;
+      const int row = l >> 4, c = l & 15;
+      const int col = n_tile * 128 + c * 8;
+      if (row < rvalid && col < p.N)
+        *(u32x4*)(p.H + (size_t)(row0 + row) * p.N + col) = *(const u32x4*)hp(row, c * 8);
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4 && MODE != kAtomIn && MODE != kGateUpSwiglu; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
       if (row >= rvalid) continue;
       const int grow = row0 + row;
-      if constexpr (MODE == kGateUpSwiglu) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n_tile * 128 + wn * 64 + j * 32 + fr;
-          if (col < p.N)
-            p.H[(size_t)grow * p.N + col] = f32_to_bf16(silu_f32(acc[i][j][r]) * acc[i][j + 2][r]);
-        }
-      } else if constexpr (MODE == kUpRelu) {
+      if constexpr (MODE == kUpRelu) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int col = n_tile * 256 + wn * 128 + j * 32 + fr;

@@ -45,7 +45,11 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+// g / (1 + e^-g) with the hardware reciprocal (about 1 ulp of fp32): every
+// caller rounds the product with the up value to bf16, 2^14 times coarser
+__device__ __forceinline__ float silu_f32(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
 
 // ---- launchers (each returns the launch status) -----------------------------
 
