@@ -409,6 +409,15 @@ void grouped_gemm_tile_kernel(TileArgs p) {
   const int n_tile = __builtin_amdgcn_readfirstlane(s_tile[3]);
   const int ks = __builtin_amdgcn_readfirstlane(s_tile[4]);
   const int kslice = p.K / p.ksplit;
+  // down: the gate of this thread's row of the tile, loaded now so that its
+  // latency passes under the main loop (staged in LDS for the epilogue)
+  float gpre = 1.0f;
+  if constexpr (MODE == kDown) {
+    if (p.gate) {
+      const int gr = row0 + min(tid, rvalid - 1);
+      gpre = p.gate[p.gate_map ? p.gate_map[gr] : gr];
+    }
+  }
 
   // DMA: instruction j (0..7 A, 8..15 B) of wave w fills LDS rows (w*8+j%8)*8 ..
   // +8 (1 KB); lane L feeds row (w*8+j%8)*8 + L/8 at 16-byte position L%8.
@@ -642,27 +651,52 @@ void grouped_gemm_tile_kernel(TileArgs p) {
     }
     return;
   }
+  if constexpr (MODE == kDown) {
+    // gate-scaled fp32 rows through a buffer resource over the tile's rows of
+    // this K slice's output (a row past them is dropped by the bounds check);
+    // the row gates come from LDS; in a wave whose 128 columns are not all
+    // below N, each lane tests its own column
+    __syncthreads();  // every wave is done with the operand buffers
+    float* gsc = (float*)sA0;
+    gsc[tid] = gpre;
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t yres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.Y + (size_t)ks * p.ystride + (size_t)row0 * p.N), (short)0, rvalid * p.N * 4,
+        0x00020000);
+    const int wcol0 = n_tile * 256 + __builtin_amdgcn_readfirstlane(wn) * 128;
+    auto rows = [&](auto whole) __attribute__((always_inline)) {
+      constexpr bool WHOLE = decltype(whole)::value;  // all of the wave's 128 columns < N
 #pragma unroll
-  for (int i = 0; i < 4 && MODE != kAtomIn && MODE != kGateUpSwiglu; ++i)
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
+          const float g = gsc[row];
+          const int off = (row * p.N + wcol0 + fr) * 4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (WHOLE || wcol0 + j * 32 + fr < p.N)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g * acc[i][j][r]), yres,
+                                                    off + j * 128, 0, 0);
+        }
+    };
+    if (wcol0 + 128 <= p.N)
+      rows(std::true_type{});
+    else
+      rows(std::false_type{});
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 4 && MODE == kUpRelu; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
       if (row >= rvalid) continue;
       const int grow = row0 + row;
-      if constexpr (MODE == kUpRelu) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n_tile * 256 + wn * 128 + j * 32 + fr;
-          if (col < p.N) p.H[(size_t)grow * p.N + col] = f32_to_bf16(fmaxf(acc[i][j][r], 0.0f));
-        }
-      } else {
-        const float gscale = p.gate ? p.gate[p.gate_map ? p.gate_map[grow] : grow] : 1.0f;
-        float* Y = p.Y + (size_t)ks * p.ystride;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n_tile * 256 + wn * 128 + j * 32 + fr;
-          if (col < p.N) Y[(size_t)grow * p.N + col] = gscale * acc[i][j][r];
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int col = n_tile * 256 + wn * 128 + j * 32 + fr;
+        if (col < p.N) p.H[(size_t)grow * p.N + col] = f32_to_bf16(fmaxf(acc[i][j][r], 0.0f));
       }
     }
 
