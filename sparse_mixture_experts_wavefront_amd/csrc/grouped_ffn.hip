@@ -686,19 +686,34 @@ void grouped_gemm_tile_kernel(TileArgs p) {
       rows(std::false_type{});
     return;
   }
+  if constexpr (MODE == kUpRelu) {
+    // as the SwiGLU epilogue: the 256 x 256 bf16 tile assembled in LDS (64 rows
+    // per 32 KB region; chunk c of row r at position c ^ (r & 7)), then 16-byte
+    // stores, 32 lanes per 512-byte row
+    __syncthreads();  // every wave is done with the operand buffers
+    auto hp = [&](int row, int col) -> u16* {
+      u16* const reg = row < 128 ? (row < 64 ? sA0 : sA1) : (row < 192 ? sB0 : sB1);
+      return reg + (row & 63) * 256 + (((col >> 3) ^ (row & 7)) << 3) + (col & 7);
+    };
 #pragma unroll
-  for (int i = 0; i < 4 && MODE == kUpRelu; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
-      if (row >= rvalid) continue;
-      const int grow = row0 + row;
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n_tile * 256 + wn * 128 + j * 32 + fr;
-        if (col < p.N) p.H[(size_t)grow * p.N + col] = f32_to_bf16(fmaxf(acc[i][j][r], 0.0f));
+        for (int j = 0; j < 4; ++j)
+          *hp(row, wn * 128 + j * 32 + fr) = f32_to_bf16(fmaxf(acc[i][j][r], 0.0f));
       }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      const int l = q * 256 + tid;
+      const int row = l >> 5, c = l & 31;
+      const int col = n_tile * 256 + c * 8;
+      if (row < rvalid && col < p.N)
+        *(u32x4*)(p.H + (size_t)(row0 + row) * p.N + col) = *(const u32x4*)hp(row, c * 8);
     }
+  }
 
   if constexpr (MODE == kAtomIn) {
     // the tile's kept cells, spread over the block: list entry e of row r has
