@@ -152,6 +152,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(TileArgs p) {
   if (expert < 0) return;
   const int row0 = s_tile[1], rvalid = s_tile[2];
   const int n0 = n_tile * BN;
+  // down: the gate of tile row tid, loaded now (its latency passes under the
+  // main loop) and staged in LDS for the epilogue
+  float gpre = 1.0f;
+  if constexpr (MODE == kDown) {
+    if (p.gate && tid < BM) {
+      const int gr = row0 + min(tid, rvalid - 1);
+      gpre = p.gate[p.gate_map ? p.gate_map[gr] : gr];
+    }
+  }
 
   // ---- per-thread global pointers ----
   const int kc = tid & 7;               // this thread's 16-byte chunk inside a 64-wide K slice
@@ -268,6 +277,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(TileArgs p) {
   }
 
   // ---- epilogue; 32x32 C layout: reg r -> row 8*(r/4) + 4*(lane/32) + r%4, col lane%32 ----
+  float* gsc = (float*)smem;  // the operand buffers are free (barrier above)
+  if constexpr (MODE == kDown) {
+    if (tid < BM) gsc[tid] = gpre;
+    __syncthreads();
+  }
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -276,9 +290,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(TileArgs p) {
       if (row >= rvalid) continue;
       const int grow = row0 + row;
       float gscale = 1.0f;
-      if constexpr (MODE == kDown) {
-        if (p.gate) gscale = p.gate[p.gate_map ? p.gate_map[grow] : grow];
-      }
+      if constexpr (MODE == kDown) gscale = gsc[row];
 #pragma unroll
       for (int j = 0; j < NI; ++j) {
         const int col = n0 + wn * WN + j * 32 + fr;
