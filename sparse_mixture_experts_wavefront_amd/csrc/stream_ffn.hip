@@ -207,9 +207,18 @@ __global__ __launch_bounds__(256) void stream_ffn_kernel(StreamArgs p) {
     }
   }
 
+  __shared__ float gsm[MB * 16];  // down: gates of this pass's token rows
   for (int mbase = 0; mbase < cnt; mbase += MB * 16) {
     const int mrows = min(MB * 16, cnt - mbase);
     const int mb_act = (mrows + 15) >> 4;
+    // down: the gate of row tid of this pass, loaded before the weight stream
+    float gpre = 1.0f;
+    if constexpr (MODE == kSModeDown) {
+      if (p.gate && tid < MB * 16) {
+        const int rr = row0 + mbase + min(tid, mrows - 1);
+        gpre = p.gate[p.gate_map ? p.gate_map[rr] : rr];
+      }
+    }
     const u16* xrow[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -339,6 +348,7 @@ __global__ __launch_bounds__(256) void stream_ffn_kernel(StreamArgs p) {
     // ---- cross-wave reduction and epilogue, one 16-row token block at a time ----
     float* red = (float*)sW0;  // [4 waves][RBLK][64 lanes][4]
     static_assert(4 * RBLK * 64 * 16 <= CBYTES, "reduction buffer");
+    if (tid < MB * 16) gsm[tid] = gpre;  // published by the barrier below
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       if (mb >= mb_act) break;
@@ -367,8 +377,7 @@ __global__ __launch_bounds__(256) void stream_ffn_kernel(StreamArgs p) {
         } else if constexpr (MODE == kSModeRelu) {
           p.H[orow * p.N + n0 + col] = f32_to_bf16(fmaxf(part(col), 0.0f));
         } else {
-          const float gs = p.gate ? p.gate[p.gate_map ? p.gate_map[orow] : orow] : 1.0f;
-          p.Y[orow * p.N + n0 + col] = gs * part(col);
+          p.Y[orow * p.N + n0 + col] = gsm[mb * 16 + m] * part(col);
         }
       }
     }
@@ -472,10 +481,19 @@ __global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
     fused_ok = __syncthreads_and(ok) != 0;
   }
 
+  __shared__ float gsm[MB * 16];  // down: gates of this pass's token rows
   auto body = [&](auto fused) {
     for (int mbase = 0; mbase < cnt; mbase += MB * 16) {
       const int mrows = min(MB * 16, cnt - mbase);
       const int mb_act = (mrows + 15) >> 4;
+      // down: the gate of row tid of this pass, loaded before the weight stream
+      float gpre = 1.0f;
+      if constexpr (MODE == kSModeDown) {
+        if (p.gate && tid < MB * 16) {
+          const int rr = row0 + mbase + min(tid, mrows - 1);
+          gpre = p.gate[p.gate_map ? p.gate_map[rr] : rr];
+        }
+      }
       uint32_t xvoff[MB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -567,6 +585,7 @@ __global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
       }
 
       // cross-wave K reduction and epilogue, one 16-row token block at a time
+      if (tid < MB * 16) gsm[tid] = gpre;  // published by the barrier below
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         if (mb >= mb_act) break;
@@ -595,8 +614,7 @@ __global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
           } else if constexpr (MODE == kSModeRelu) {
             p.H[orow * p.N + n0 + col] = f32_to_bf16(fmaxf(part(col), 0.0f));
           } else {
-            const float gs = p.gate ? p.gate[p.gate_map ? p.gate_map[orow] : orow] : 1.0f;
-            p.Y[orow * p.N + n0 + col] = gs * part(col);
+            p.Y[orow * p.N + n0 + col] = gsm[mb * 16 + m] * part(col);
           }
         }
       }
