@@ -596,15 +596,22 @@ void grouped_gemm_tile_kernel(TileArgs p) {
     auto cells = [&](auto listed, auto whole) __attribute__((always_inline)) {
       constexpr bool LISTED = decltype(listed)::value;
       constexpr bool WHOLE = decltype(whole)::value;  // all of the wave's 128 columns < N
+      // (a row past the tile's rows has empty words: nothing is listed); the
+      // next row's words are read one row ahead, before this row's writes
+      auto row_of = [&](int t) { return wm * 128 + (t >> 4) * 32 + 8 * ((t & 15) >> 2) + 4 * fk + (t & 3); };
+      uint4 wv_n = *(const uint4*)(tbits + row_of(0) * 8 + wn * 4);
+      int4 pv_n = *(const int4*)(tpos + row_of(0) * 8 + wn * 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          // (a row past the tile's rows has empty words: nothing is listed)
-          const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
+      for (int t = 0; t < 64; ++t) {
+          const int i = t >> 4, r = t & 15;
+          const int row = row_of(t);
           const int grow = row0 + row;
-          const uint4 wv = *(const uint4*)(tbits + row * 8 + wn * 4);
-          const int4 pv = *(const int4*)(tpos + row * 8 + wn * 4);
+          const uint4 wv = wv_n;
+          const int4 pv = pv_n;
+          if (t + 1 < 64) {
+            wv_n = *(const uint4*)(tbits + row_of(t + 1) * 8 + wn * 4);
+            pv_n = *(const int4*)(tpos + row_of(t + 1) * 8 + wn * 4);
+          }
           const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
           const int ps[4] = {pv.x, pv.y, pv.z, pv.w};
           const int hoff = (row * p.N + n_tile * 256 + wn * 128 + fr) * 2;
