@@ -19,8 +19,8 @@
 // The tile map is ragged and lives on the device: every block reads offsets[],
 // forms the per-expert tile prefix with one wave scan, and finds its own
 // (expert, row tile); blocks past the last tile exit.  Block ids are remapped
-// so that consecutive ids on one XCD (ids that differ by 8) take the row tiles
-// of one weight panel, which then stays in that XCD's L2.
+// so that each XCD (block id % 8) takes a contiguous share of the tiles, whose
+// row tiles of one weight panel then meet in that XCD's L2.
 // Two tiled kernels: the 256x256x64 DMA-staged kernel (bf16, K % 128 == 0: the
 // layer path) and a 128x128x64 register-staged kernel (INT4 weights decoded
 // while staged, and any other shape).
@@ -36,8 +36,9 @@ constexpr int kThreads = 256;
 
 // kAtomIn: one matrix (the input side of the atomic experts); at the cells a
 // per-row bitmap keeps the output is bf16(gate * silu(acc)), elsewhere 0.  The
-// kept cells' fp32 values pass through a compact [rows][ksel] array (position =
-// rank of the cell in its row, where the gates and ids of the row also sit).
+// kept cells' fp32 values are listed in LDS (or, for a dense tile, in a compact
+// [rows][ksel] array at the cell's rank in its row, where the gates and ids of
+// the row also sit).
 enum Mode { kGateUpSwiglu = 0, kUpRelu = 1, kDown = 2, kAtomIn = 3 };
 // kAtomIn: kept cells of a tile listed in LDS (the operand buffer holds 8192
 // entries; the last 64 take the writes of lanes whose cell is not kept)
@@ -345,9 +346,13 @@ __device__ __forceinline__ int v3_off(int row, int chunk) { return row * 64 + (v
 // quarters ahead (four register sets), and one barrier per stage, after its
 // second quarter, publishes the next stage and frees the current buffer for the
 // DMA of the stage two ahead, issued during the third and fourth quarters.
-// Blocks are ordered in groups of 8 row tiles per column strip and remapped so
-// consecutive ids on one XCD share A and B slices in its L2.  The down pass may
-// split K into slices (partial rows reduced by the combine).
+// Real tiles are numbered in groups of 8 row tiles per column strip and each
+// XCD takes a contiguous eighth of them, so its concurrent tiles share A and B
+// slices in its L2.  The down pass may split K into slices (partial rows
+// reduced by the combine).  Epilogues avoid per-element waits: the SwiGLU and
+// ReLU tiles are assembled in the free LDS and leave in 16-byte stores; the
+// down rows take their gates from LDS (loaded before the main loop) and leave
+// through a bounds-checked buffer resource.
 template <int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_tile_kernel(TileArgs p) {
