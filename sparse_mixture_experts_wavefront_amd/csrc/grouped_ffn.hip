@@ -468,6 +468,148 @@ void grouped_gemm_tile_kernel(TileArgs p) {
     dma16(src[j] + k0, (j < 8 ? sa : sb) + wbase + (j & 7) * 512);
   };
 
+  const int fr = lane & 31, fk = lane >> 5;
+  if constexpr (MODE != kAtomIn) {
+    if (rvalid <= 128) {
+      // ---- half tile: at most 128 valid rows (an expert's remainder).  All four
+      // waves take rows 0..127 and wave w a quarter of the columns (gate/up: the
+      // gate and up columns w*32..+32 of the strip), so each wave runs 8 MFMAs
+      // per K quarter instead of 16 and the tile costs about half a full one.
+      // Staging, swizzle and pipeline are those of the full tile below.
+      f32x16 hacc[4][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) hacc[i][j][r] = 0.0f;
+      const int wq = __builtin_amdgcn_readfirstlane(wid);
+      auto hbrow = [&](int j) {
+        if constexpr (MODE == kGateUpSwiglu) return j == 0 ? wq * 32 : 128 + wq * 32;
+        else return wq * 64 + j * 32;
+      };
+      // fragment f (0..3 A rows f*32.., 4..5 B columns) of K quarter kk
+      auto hread = [&](const u16* sa, const u16* sb, int kk, int f, bf16x8 (&af)[4],
+                       bf16x8 (&bfr)[4]) {
+        const int c = kk * 2 + fk;
+        if (f < 4)
+          af[f] = as_bf16x8(*(const u32x4*)(sa + v3_off(f * 32 + fr, c)));
+        else
+          bfr[f - 4] = as_bf16x8(*(const u32x4*)(sb + v3_off(hbrow(f - 4) + fr, c)));
+      };
+      constexpr int kReadH[6] = {0, 4, 5, 1, 2, 3};
+      bf16x8 ha[4][4], hb[4][4];  // [quarter set][fragment]
+      auto hquarter = [&](int q, const u16* sa_r, const u16* sb_r, int kk_r, int r, u16* sa_d,
+                          u16* sb_d, int kt_dma, int j0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          hacc[m >> 1][m & 1] = mfma32(ha[q][m >> 1], hb[q][m & 1], hacc[m >> 1][m & 1]);
+          if (m < 6) hread(sa_r, sb_r, kk_r, kReadH[m], ha[r], hb[r]);
+          if (j0 >= 0) dma(sa_d, sb_d, kt_dma, j0 + m);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      auto hstage = [&](u16* sa, u16* sb, u16* na, u16* nb_, int kt) __attribute__((always_inline)) {
+        hquarter(0, sa, sb, 2, 2, sa, sb, 0, -1);
+        hquarter(1, sa, sb, 3, 3, sa, sb, 0, -1);
+        wait_vm_lgkm0<0>();
+        block_barrier();
+        hquarter(2, na, nb_, 0, 0, sa, sb, kt + 2, 0);
+        hquarter(3, na, nb_, 1, 1, sa, sb, kt + 2, 8);
+      };
+#pragma unroll
+      for (int j = 0; j < 16; ++j) dma(sA0, sB0, 0, j);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) dma(sA1, sB1, 1, j);
+      wait_vm_lgkm0<16>();
+      block_barrier();
+#pragma unroll
+      for (int f = 0; f < 6; ++f) hread(sA0, sB0, 0, kReadH[f], ha[0], hb[0]);
+#pragma unroll
+      for (int f = 0; f < 6; ++f) hread(sA0, sB0, 1, kReadH[f], ha[1], hb[1]);
+      for (int kt = 0; kt < nk; kt += 2) {
+        hstage(sA0, sB0, sA1, sB1, kt);
+        hstage(sA1, sB1, sA0, sB0, kt + 1);
+      }
+      wait_vm_lgkm0<0>();
+      __syncthreads();  // every wave is done with the operand buffers
+      // output element (i, j, r): tile row i*32 + 8*(r/4) + 4*fk + r%4
+      if constexpr (MODE == kGateUpSwiglu) {
+        auto hp = [&](int row, int col) -> u16* {
+          return sA0 + row * 128 + (((col >> 3) ^ (row & 7)) << 3) + (col & 7);
+        };
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
+            *hp(row, wq * 32 + fr) = f32_to_bf16(silu_f32(hacc[i][0][r]) * hacc[i][1][r]);
+          }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int l = q * 256 + tid;
+          const int row = l >> 4, c = l & 15;
+          const int col = n_tile * 128 + c * 8;
+          if (row < rvalid && col < p.N)
+            *(u32x4*)(p.H + (size_t)(row0 + row) * p.N + col) = *(const u32x4*)hp(row, c * 8);
+        }
+      } else if constexpr (MODE == kUpRelu) {
+        auto hp = [&](int row, int col) -> u16* {
+          return (row < 64 ? sA0 : sA1) + (row & 63) * 256 + (((col >> 3) ^ (row & 7)) << 3) +
+                 (col & 7);
+        };
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              *hp(row, wq * 64 + j * 32 + fr) = f32_to_bf16(fmaxf(hacc[i][j][r], 0.0f));
+          }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int l = q * 256 + tid;
+          const int row = l >> 5, c = l & 31;
+          const int col = n_tile * 256 + c * 8;
+          if (row < rvalid && col < p.N)
+            *(u32x4*)(p.H + (size_t)(row0 + row) * p.N + col) = *(const u32x4*)hp(row, c * 8);
+        }
+      } else {  // kDown
+        float* gsc = (float*)sA0;
+        gsc[tid] = gpre;
+        __syncthreads();
+        const __amdgpu_buffer_rsrc_t yres = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.Y + (size_t)ks * p.ystride + (size_t)row0 * p.N), (short)0, rvalid * p.N * 4,
+            0x00020000);
+        const int wcol0 = n_tile * 256 + wq * 64;
+        auto rows = [&](auto whole) __attribute__((always_inline)) {
+          constexpr bool WHOLE = decltype(whole)::value;  // the wave's 64 columns all < N
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
+              const float g = gsc[row];
+              const int off = (row * p.N + wcol0 + fr) * 4;
+#pragma unroll
+              for (int j = 0; j < 2; ++j)
+                if (WHOLE || wcol0 + j * 32 + fr < p.N)
+                  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g * hacc[i][j][r]), yres,
+                                                        off + j * 128, 0, 0);
+            }
+        };
+        if (wcol0 + 64 <= p.N)
+          rows(std::true_type{});
+        else
+          rows(std::false_type{});
+      }
+      return;
+    }
+  }
+
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -476,7 +618,6 @@ void grouped_gemm_tile_kernel(TileArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int fr = lane & 31, fk = lane >> 5;
   auto brow = [&](int j) {
     if constexpr (MODE == kGateUpSwiglu) return (j < 2 ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32);
     else return wn * 128 + j * 32;
