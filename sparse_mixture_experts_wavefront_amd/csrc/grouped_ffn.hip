@@ -346,9 +346,9 @@ __device__ __forceinline__ int v3_off(int row, int chunk) { return row * 64 + (v
 // quarters ahead (four register sets), and one barrier per stage, after its
 // second quarter, publishes the next stage and frees the current buffer for the
 // DMA of the stage two ahead, issued during the third and fourth quarters.
-// Real tiles are numbered in groups of 8 row tiles per column strip and each
-// XCD takes a contiguous eighth of them, so its concurrent tiles share A and B
-// slices in its L2.  The down pass may split K into slices (partial rows
+// Real tiles are numbered expert by expert, in groups of up to 8 of the
+// expert's row tiles per column strip, and each XCD takes a contiguous eighth
+// of them, so its concurrent tiles share A and B slices in its L2.  The down pass may split K into slices (partial rows
 // reduced by the combine).  Epilogues avoid per-element waits: the SwiGLU and
 // ReLU tiles are assembled in the free LDS and leave in 16-byte stores; the
 // down rows take their gates from LDS (loaded before the main loop) and leave
@@ -367,12 +367,13 @@ void grouped_gemm_tile_kernel(TileArgs p) {
 
   // Tile map.  Wave 0 scans the experts' row-tile counts; the real tiles are
   // numbered K slice first (slice ks covers K [ks*K/ksplit, +K/ksplit) and
-  // writes its partial sums to Y + ks*ystride, which the combine adds), then in
-  // groups of kV2GroupM row tiles per column strip.  Block bid runs on XCD
-  // bid % 8 and takes tile (bid % 8) * ceil(R/8) + bid / 8 of the R real tiles:
-  // every XCD gets a contiguous eighth of the real tiles (equal work, and
-  // neighbouring tiles share A and B slices in that XCD's L2); blocks past them
-  // exit at once.
+  // writes its partial sums to Y + ks*ystride, which the combine adds), then
+  // expert by expert, and inside an expert in groups of up to kV2GroupM of its
+  // row tiles per column strip (a group never mixes experts, so its tiles share
+  // one weight strip).  Block bid runs on XCD bid % 8 and takes tile
+  // (bid % 8) * ceil(R/8) + bid / 8 of the R real tiles: every XCD gets a
+  // contiguous eighth of the real tiles (equal work, and neighbouring tiles
+  // share A and B slices in that XCD's L2); blocks past them exit at once.
   if (wid == 0) {
     int cnt = 0, first = 0;
     if (p.offsets) {
@@ -400,21 +401,19 @@ void grouped_gemm_tile_kernel(TileArgs p) {
     if (loc < per_xcd && t < total) {
       const int ksl = t / slice_tiles;
       t -= ksl * slice_tiles;
-      const int per_group = kV2GroupM * p.n_tiles;
-      const int g = t / per_group;
-      const int first_m = g * kV2GroupM;
-      const int gm = min(m_real - first_m, kV2GroupM);
-      const int in_g = t - g * per_group;
-      const int m_tile = first_m + in_g % gm;
-      if (lane == 0) {
+      const int u = t - excl * p.n_tiles;  // tile index inside this lane's expert
+      if (u >= 0 && u < tiles * p.n_tiles) {  // exactly one lane
+        const int per_group = kV2GroupM * p.n_tiles;
+        const int g = u / per_group;
+        const int first_m = g * kV2GroupM;
+        const int gm = min(tiles - first_m, kV2GroupM);
+        const int in_g = u - g * per_group;
+        const int m_loc = first_m + in_g % gm;
+        s_tile[0] = lane;
+        s_tile[1] = first + m_loc * BM;
+        s_tile[2] = min(BM, cnt - m_loc * BM);
         s_tile[3] = in_g / gm;
         s_tile[4] = ksl;
-      }
-      // (one lane matches; a wave executes its LDS writes in program order)
-      if (m_tile >= excl && m_tile < incl) {
-        s_tile[0] = lane;
-        s_tile[1] = first + (m_tile - excl) * BM;
-        s_tile[2] = min(BM, cnt - (m_tile - excl) * BM);
       }
     }
   }
