@@ -350,8 +350,10 @@ __device__ __forceinline__ int v3_off(int row, int chunk) { return row * 64 + (v
 // expert's row tiles per column strip, and each XCD takes a contiguous eighth
 // of them, so its concurrent tiles share A and B slices in its L2.  The down pass may split K into slices (partial rows
 // reduced by the combine).  Epilogues avoid per-element waits: the SwiGLU and
-// ReLU tiles are assembled in the free LDS and leave in 16-byte stores; the
-// down rows take their gates from LDS (loaded before the main loop) and leave
+// ReLU modes feed the MFMA weights-first, so each lane ends with four
+// consecutive output columns per register quad; their tiles are assembled in
+// the free LDS with 8-byte writes and leave in 16-byte buffer stores; the down
+// rows take their gates from LDS (loaded before the main loop) and leave
 // through a bounds-checked buffer resource.
 template <int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
@@ -632,9 +634,16 @@ void grouped_gemm_tile_kernel(TileArgs p) {
   // read order A0 B0 B1 B2 B3 A1 A2 A3: MFMAs 0..3 (A0 x B0..B3) need only the
   // first five reads
   constexpr int kRead[8] = {0, 4, 5, 6, 7, 1, 2, 3};
-  // MFMA m (0..15) of a quarter: A fragment m/4, B fragment m%4
+  // MFMA m (0..15) of a quarter: A fragment m/4, B fragment m%4.  Gate/up
+  // passes the weight fragment as the MFMA's first operand, so acc holds the
+  // transposed 32x32 block: register r of lane (fr, fk) is output column
+  // brow(j) + 8*(r/4) + 4*fk + r%4 of tile row wm*128 + i*32 + fr, four
+  // consecutive columns of one row per lane and register quad
   auto mfma1 = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4], int m) {
-    acc[m >> 2][m & 3] = mfma32(af[m >> 2], bfr[m & 3], acc[m >> 2][m & 3]);
+    if constexpr (MODE == kGateUpSwiglu || MODE == kUpRelu)
+      acc[m >> 2][m & 3] = mfma32(bfr[m & 3], af[m >> 2], acc[m >> 2][m & 3]);
+    else
+      acc[m >> 2][m & 3] = mfma32(af[m >> 2], bfr[m & 3], acc[m >> 2][m & 3]);
   };
   bf16x8 fa[4][4], fb[4][4];  // [quarter set][fragment]
   // quarter q: MFMAs on set q; reads for (sa_r, sb_r, kk_r) into set r after
@@ -788,30 +797,40 @@ void grouped_gemm_tile_kernel(TileArgs p) {
 
   if constexpr (MODE == kGateUpSwiglu) {
     // the tile's 256 x 128 bf16 outputs are assembled in LDS (rows 0..127 in
-    // sA0, 128..255 in sA1; 16-byte chunk c of row r at position c ^ (r & 7), so
-    // rows 4 apart, written by the two lane halves, use different banks) and
-    // leave in 16-byte stores, 16 lanes per 256-byte row
+    // sA0, 128..255 in sA1; 16-byte chunk c of row r at position c ^ (r & 15)),
+    // each lane writing its four consecutive columns as one 8-byte word, and
+    // leave in 16-byte stores, 16 lanes per 256-byte row, through a buffer
+    // resource that drops rows past the tile's valid ones
     __syncthreads();  // every wave is done with the operand buffers
-    auto hp = [&](int row, int col) -> u16* {
-      return (row < 128 ? sA0 : sA1) + (row & 127) * 128 + (((col >> 3) ^ (row & 7)) << 3) + (col & 7);
+    auto hq = [&](int row, int chunk) -> u16* {
+      return (row < 128 ? sA0 : sA1) + (row & 127) * 128 + ((chunk ^ (row & 15)) << 3);
     };
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + i * 32 + fr;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          *hp(row, wn * 64 + j * 32 + fr) = f32_to_bf16(silu_f32(acc[i][j][r]) * acc[i][j + 2][r]);
-      }
+        for (int q = 0; q < 4; ++q) {
+          const int col = wn * 64 + j * 32 + 8 * q + 4 * fk;
+          float h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = silu_f32(acc[i][j][4 * q + e]) * acc[i][j + 2][4 * q + e];
+          *(uint2*)(hq(row, col >> 3) + (col & 7)) = make_uint2(pk_bf16(h[0], h[1]), pk_bf16(h[2], h[3]));
+        }
+    }
     __syncthreads();
+    const __amdgpu_buffer_rsrc_t hres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.H + (size_t)row0 * p.N), (short)0, rvalid * p.N * 2, 0x00020000);
+    const int c = tid & 15;
+    const int col = n_tile * 128 + c * 8;
+    u32x4 v[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int l = q * 256 + tid;
-      const int row = l >> 4, c = l & 15;
-      const int col = n_tile * 128 + c * 8;
-      if (row < rvalid && col < p.N)
-        *(u32x4*)(p.H + (size_t)(row0 + row) * p.N + col) = *(const u32x4*)hp(row, c * 8);
+    for (int q = 0; q < 16; ++q) v[q] = *(const u32x4*)hq(q * 16 + (tid >> 4), c);
+    if (col < p.N) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        __builtin_amdgcn_raw_buffer_store_b128(v[q], hres, ((q * 16 + (tid >> 4)) * p.N + col) * 2, 0, 0);
     }
     return;
   }
@@ -851,31 +870,45 @@ void grouped_gemm_tile_kernel(TileArgs p) {
     return;
   }
   if constexpr (MODE == kUpRelu) {
-    // as the SwiGLU epilogue: the 256 x 256 bf16 tile assembled in LDS (64 rows
-    // per 32 KB region; chunk c of row r at position c ^ (r & 7)), then 16-byte
-    // stores, 32 lanes per 512-byte row
+    // as the SwiGLU epilogue (transposed accumulators, four consecutive
+    // columns per 8-byte LDS write): the 256 x 256 bf16 tile assembled in LDS
+    // (64 rows per 32 KB region; chunk c of row r at position c ^ (r & 31)),
+    // then 16-byte buffer stores, 32 lanes per 512-byte row
     __syncthreads();  // every wave is done with the operand buffers
-    auto hp = [&](int row, int col) -> u16* {
+    auto hq = [&](int row, int chunk) -> u16* {
       u16* const reg = row < 128 ? (row < 64 ? sA0 : sA1) : (row < 192 ? sB0 : sB1);
-      return reg + (row & 63) * 256 + (((col >> 3) ^ (row & 7)) << 3) + (col & 7);
+      return reg + (row & 63) * 256 + ((chunk ^ (row & 31)) << 3);
     };
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + i * 32 + fr;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *hp(row, wn * 128 + j * 32 + fr) = f32_to_bf16(fmaxf(acc[i][j][r], 0.0f));
-      }
+        for (int q = 0; q < 4; ++q) {
+          const int col = wn * 128 + j * 32 + 8 * q + 4 * fk;
+          const f32x16& a = acc[i][j];
+          *(uint2*)(hq(row, col >> 3) + (col & 7)) =
+              make_uint2(pk_bf16(fmaxf(a[4 * q], 0.0f), fmaxf(a[4 * q + 1], 0.0f)),
+                         pk_bf16(fmaxf(a[4 * q + 2], 0.0f), fmaxf(a[4 * q + 3], 0.0f)));
+        }
+    }
     __syncthreads();
+    const __amdgpu_buffer_rsrc_t hres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.H + (size_t)row0 * p.N), (short)0, rvalid * p.N * 2, 0x00020000);
+    const int c = tid & 31;
+    const int col = n_tile * 256 + c * 8;
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
-      const int l = q * 256 + tid;
-      const int row = l >> 5, c = l & 31;
-      const int col = n_tile * 256 + c * 8;
-      if (row < rvalid && col < p.N)
-        *(u32x4*)(p.H + (size_t)(row0 + row) * p.N + col) = *(const u32x4*)hp(row, c * 8);
+    for (int b = 0; b < 2; ++b) {
+      u32x4 v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = *(const u32x4*)hq((b * 16 + q) * 8 + (tid >> 5), c);
+      if (col < p.N) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          __builtin_amdgcn_raw_buffer_store_b128(v[q], hres,
+                                                 (((b * 16 + q) * 8 + (tid >> 5)) * p.N + col) * 2, 0, 0);
+      }
     }
   }
 
