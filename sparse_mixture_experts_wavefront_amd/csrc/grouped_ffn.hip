@@ -671,7 +671,24 @@ void grouped_gemm_tile_kernel(TileArgs p) {
   for (int j = 0; j < 16; ++j) dma(sA0, sB0, 0, j);
 #pragma unroll
   for (int j = 0; j < 16; ++j) dma(sA1, sB1, 1, j);
-  wait_vm_lgkm0<16>();
+  // kAtomIn: the tile's kept-cell words and their prefixes ([256 rows][8]
+  // each) come in by DMA now, behind the first two stages, so they are in
+  // LDS long before the epilogue (entries past the rows or words are masked
+  // there); instruction k of wave w fills rows (w*8+k)*8 .. +8
+  __shared__ __align__(16) uint32_t s_cells[MODE == kAtomIn ? 4096 : 4];
+  if constexpr (MODE == kAtomIn) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int g = wid * 8 + k;
+      const int r = g * 8 + (lane >> 3);
+      const size_t gi = (size_t)(row0 + min(r, rvalid - 1)) * p.wpr + min(n_tile * 8 + (lane & 7), p.wpr - 1);
+      __builtin_amdgcn_global_load_lds(p.bits + gi, (lds_void_t*)(s_cells + g * 64), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(p.bitpre + gi, (lds_void_t*)(s_cells + 2048 + g * 64), 4, 0, 0);
+    }
+    wait_vm_lgkm0<32>();  // the first stage (16 of them per wave) landed
+  } else {
+    wait_vm_lgkm0<16>();
+  }
   block_barrier();
 #pragma unroll
   for (int f = 0; f < 8; ++f) read1(sA0, sB0, 0, f, fa[0], fb[0]);
@@ -683,16 +700,17 @@ void grouped_gemm_tile_kernel(TileArgs p) {
   }
   wait_vm_lgkm0<0>();
 
-  // kAtomIn: the tile's kept-cell words and their prefixes, staged once in the
-  // (now free) operand buffers, [256 rows][8 words] each (a word past the row's
-  // end is empty with prefix ksel); per row the first rank in the tile (rlo)
+  // kAtomIn: the tile's kept-cell words and their prefixes, [256 rows][8
+  // words] each, already in LDS (s_cells, loaded with the first stages); a word
+  // past the row's end, or of a row past the tile's rows, is set empty with
+  // prefix ksel here; per row the first rank in the tile (rlo)
   // and the tile-local start of its kept cells (rbase, a block scan of the
   // counts); then each word's prefix is turned into the tile-local position of
   // its first kept cell.  Up to kAtomTileCap kept cells of the tile are listed
   // in LDS (fp32 value and row << 8 | column in the tile); a denser tile goes
   // through ukept in global memory instead.
-  uint32_t* tbits = (uint32_t*)sA0;
-  int32_t* tpos = (int32_t*)sA0 + 2048;
+  uint32_t* tbits = s_cells;
+  int32_t* tpos = (int32_t*)s_cells + 2048;
   int32_t* rlo = (int32_t*)sB0;
   int32_t* rbase = (int32_t*)sB0 + 256;  // 257 entries
   float* lu = (float*)sA1;
@@ -702,10 +720,10 @@ void grouped_gemm_tile_kernel(TileArgs p) {
     __syncthreads();
     for (int q = tid; q < 2048; q += 256) {
       const int rr = q >> 3, wcol = n_tile * 8 + (q & 7);
-      const size_t gi = (size_t)(row0 + min(rr, rvalid - 1)) * p.wpr + wcol;
-      const bool in = wcol < p.wpr && rr < rvalid;
-      tbits[q] = in ? p.bits[gi] : 0u;
-      tpos[q] = in ? p.bitpre[gi] : p.ksel;
+      if (!(wcol < p.wpr && rr < rvalid)) {
+        tbits[q] = 0u;
+        tpos[q] = p.ksel;
+      }
     }
     __syncthreads();
     {
