@@ -438,16 +438,28 @@ void grouped_gemm_tile_kernel(TileArgs p) {
   }
 
   // DMA: instruction j (0..7 A, 8..15 B) of wave w fills LDS rows (w*8+j%8)*8 ..
-  // +8 (1 KB); lane L feeds row (w*8+j%8)*8 + L/8 at 16-byte position L%8.
+  // +8 (1 KB); lane L feeds row (w*8+j%8)*8 + L/8 at 16-byte position L%8.  The
+  // first two stages issue their B (weight) instructions before the A ones,
+  // whose addresses may wait for the gather map.
   const u16* src[16];
   const size_t wstride = (size_t)p.N * p.K;
+  // source rows of the 8 A rows this lane feeds; with a gather map, its 8
+  // entries are loaded together (one memory round trip, not eight)
+  int srow[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) srow[j] = row0 + min((wid * 8 + j) * 8 + (lane >> 3), rvalid - 1);
+  if (p.gather) {
+    int gv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gv[j] = p.gather[srow[j]];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) srow[j] = gv[j] / p.k;
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = (wid * 8 + j) * 8 + (lane >> 3);
     const int c = v3_pos(r, lane & 7);
-    const int gr = row0 + min(r, rvalid - 1);
-    const int sr = p.gather ? (p.gather[gr] / p.k) : gr;
-    src[j] = p.A + (size_t)sr * p.lda + c * 8;
+    src[j] = p.A + (size_t)srow[j] * p.lda + c * 8;
     const u16* Bm;
     int n;
     if constexpr (MODE == kGateUpSwiglu) {
@@ -519,10 +531,14 @@ void grouped_gemm_tile_kernel(TileArgs p) {
         hquarter(3, na, nb_, 1, 1, sa, sb, kt + 2, 8);
       };
 #pragma unroll
-      for (int j = 0; j < 16; ++j) dma(sA0, sB0, 0, j);
+      for (int j = 8; j < 16; ++j) dma(sA0, sB0, 0, j);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) dma(sA1, sB1, 1, j);
-      wait_vm_lgkm0<16>();
+      for (int j = 8; j < 16; ++j) dma(sA1, sB1, 1, j);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dma(sA0, sB0, 0, j);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dma(sA1, sB1, 1, j);
+      wait_vm_lgkm0<8>();
       block_barrier();
 #pragma unroll
       for (int f = 0; f < 6; ++f) hread(sA0, sB0, 0, kReadH[f], ha[0], hb[0]);
@@ -668,9 +684,13 @@ void grouped_gemm_tile_kernel(TileArgs p) {
     quarter(3, na, nb_, 1, 1, sa, sb, kt + 2, 8);
   };
 #pragma unroll
-  for (int j = 0; j < 16; ++j) dma(sA0, sB0, 0, j);
+  for (int j = 8; j < 16; ++j) dma(sA0, sB0, 0, j);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) dma(sA1, sB1, 1, j);
+  for (int j = 8; j < 16; ++j) dma(sA1, sB1, 1, j);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dma(sA0, sB0, 0, j);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dma(sA1, sB1, 1, j);
   // kAtomIn: the tile's kept-cell words and their prefixes ([256 rows][8]
   // each) come in by DMA now, behind the first two stages, so they are in
   // LDS long before the epilogue (entries past the rows or words are masked
@@ -685,9 +705,9 @@ void grouped_gemm_tile_kernel(TileArgs p) {
       __builtin_amdgcn_global_load_lds(p.bits + gi, (lds_void_t*)(s_cells + g * 64), 4, 0, 0);
       __builtin_amdgcn_global_load_lds(p.bitpre + gi, (lds_void_t*)(s_cells + 2048 + g * 64), 4, 0, 0);
     }
-    wait_vm_lgkm0<32>();  // the first stage (16 of them per wave) landed
+    wait_vm_lgkm0<24>();  // the first stage landed
   } else {
-    wait_vm_lgkm0<16>();
+    wait_vm_lgkm0<8>();
   }
   block_barrier();
 #pragma unroll
