@@ -8,9 +8,9 @@
 // MoE-based LLM Serving" -- What carries the argument and Figure 8: low-bit
 // expert weights are decoded inside the GEMM kernel).
 //
-// One block = one expert x one strip of 32 output columns (64 weight rows for
-// gate/up: 32 gate + 32 up, the same f-values; 32 rows for ReLU W_in and for
-// down); its 4 waves split K and their partial sums meet in LDS at the end,
+// One block = one expert x one strip of output columns (64 weight rows for
+// gate/up: 32 gate + 32 up, the same f-values; for ReLU W_in and for down 32
+// rows, or 64 in the register-direct INT4 kernel); its 4 waves split K and their partial sums meet in LDS at the end,
 // where the epilogue applies SiLU(gate)*up (to bf16 H) or the gate scale (fp32
 // rows).  Two ways to feed the 16x16x32 MFMA from the weight stream:
 //   register-direct (gate/up, ReLU W_in, INT4 down): each wave loads its MFMA
@@ -403,11 +403,16 @@ __global__ __launch_bounds__(256) void stream_ffn_kernel(StreamArgs p) {
 // add zeros.  A straight-line loop lets the compiler wait for exactly the
 // oldest register set (vmcnt = loads of the D-1 younger sets) instead of all.
 
+constexpr int stream_reg_rows(int mode, bool int4) { return (mode == kSModeGateUp || int4) ? 64 : 32; }
+
 template <int MODE, bool INT4, int MB, int D>
 __global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
-  constexpr int R = (MODE == kSModeGateUp) ? 64 : 32;  // weight rows per block
+  // weight rows per block: gate/up 32 gate + 32 up rows; INT4 down and ReLU
+  // W_in 64 rows (each token fragment then feeds four MFMAs, which halves the
+  // token-operand loads per weight byte); bf16 down and ReLU W_in 32 rows
+  constexpr int R = stream_reg_rows(MODE, INT4);
   constexpr int RB = R / 16;
-  constexpr int NOUT = 32;
+  constexpr int NOUT = (MODE == kSModeGateUp) ? 32 : R;
   constexpr int KI = 128, NS = 4;
   constexpr int WL = INT4 ? 1 : NS;                  // 16-byte weight loads per row block
   constexpr int IT_BYTES = INT4 ? KI / 2 : KI * 2;    // weight bytes per row per iteration
@@ -442,9 +447,11 @@ __global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
   const uint32_t strip_bytes = 32u * row_bytes;
   const __amdgpu_buffer_rsrc_t wres0 = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.W0 + ((size_t)e * p.N + n0) * row_bytes), (short)0, (int)strip_bytes, 0x00020000);
+  // (gate/up: the up matrix's strip; 64-row blocks: rows 32..63 of the block)
   const __amdgpu_buffer_rsrc_t wres1 = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((MODE == kSModeGateUp ? p.W1 : p.W0) + ((size_t)e * p.N + n0) * row_bytes), (short)0,
-      (int)strip_bytes, 0x00020000);
+      (void*)(MODE == kSModeGateUp ? p.W1 + ((size_t)e * p.N + n0) * row_bytes
+                                   : p.W0 + ((size_t)e * p.N + n0 + (R == 64 ? 32 : 0)) * row_bytes),
+      (short)0, (int)strip_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t xres =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.X, (short)0, (int)p.xbytes, 0x00020000);
   // row block rb covers block rows rb*16..+15: matrix 0 for rows < 32, 1 above
@@ -633,16 +640,18 @@ __global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
 
 template <int MODE, bool INT4>
 size_t stream_reg_lds_bytes(int K) {
-  constexpr int R = (MODE == kSModeGateUp) ? 64 : 32;
+  constexpr int R = stream_reg_rows(MODE, INT4);
   return (size_t)4 * (R / 16) * 64 * 16 + (INT4 ? (size_t)R * ((K >> 7) + 1) * 4 : 0);
 }
 
 template <int MODE, bool INT4>
-hipError_t launch_reg_mode(const StreamArgs& a, int E, int mb, hipStream_t s) {
+hipError_t launch_reg_mode(const StreamArgs& a0, int E, int mb, hipStream_t s) {
+  constexpr int NOUT = MODE == kSModeGateUp ? 32 : stream_reg_rows(MODE, INT4);
+  StreamArgs a = a0;
+  a.nblk_per_expert = (a.N + NOUT - 1) / NOUT;
   const dim3 grid((unsigned)(E * a.nblk_per_expert)), block(256);
   const size_t lds = stream_reg_lds_bytes<MODE, INT4>(a.K);
-  // two register sets in flight: deeper prefetch measured no faster here (the
-  // INT4 decode is bound by its VALU work, bf16 by the access pattern)
+  // two register sets in flight: deeper prefetch measured no faster here
   if (mb <= 1)
     hipLaunchKernelGGL((stream_reg_kernel<MODE, INT4, 1, 2>), grid, block, lds, s, a);
   else
