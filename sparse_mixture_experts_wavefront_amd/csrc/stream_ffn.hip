@@ -10,7 +10,7 @@
 //
 // One block = one expert x one strip of output columns (64 weight rows for
 // gate/up: 32 gate + 32 up, the same f-values; for ReLU W_in and for down 32
-// rows, or 64 in the register-direct INT4 kernel); its 4 waves split K and their partial sums meet in LDS at the end,
+// rows; twice those in the register-direct INT4 kernel); its 4 waves split K and their partial sums meet in LDS at the end,
 // where the epilogue applies SiLU(gate)*up (to bf16 H) or the gate scale (fp32
 // rows).  Two ways to feed the 16x16x32 MFMA from the weight stream:
 //   register-direct (gate/up, ReLU W_in, INT4 down): each wave loads its MFMA
@@ -403,16 +403,20 @@ __global__ __launch_bounds__(256) void stream_ffn_kernel(StreamArgs p) {
 // add zeros.  A straight-line loop lets the compiler wait for exactly the
 // oldest register set (vmcnt = loads of the D-1 younger sets) instead of all.
 
-constexpr int stream_reg_rows(int mode, bool int4) { return (mode == kSModeGateUp || int4) ? 64 : 32; }
+constexpr int stream_reg_rows(int mode, bool int4) {
+  return mode == kSModeGateUp ? (int4 ? 128 : 64) : (int4 ? 64 : 32);
+}
 
 template <int MODE, bool INT4, int MB, int D>
 __global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
-  // weight rows per block: gate/up 32 gate + 32 up rows; INT4 down and ReLU
-  // W_in 64 rows (each token fragment then feeds four MFMAs, which halves the
-  // token-operand loads per weight byte); bf16 down and ReLU W_in 32 rows
+  // weight rows per block: gate/up 32 gate + 32 up rows (INT4: 64 + 64); down
+  // and ReLU W_in 32 rows (INT4: 64).  More rows let each token fragment feed
+  // more MFMAs, fewer token-operand loads per weight byte; the INT4 weight
+  // registers leave room for that
   constexpr int R = stream_reg_rows(MODE, INT4);
   constexpr int RB = R / 16;
-  constexpr int NOUT = (MODE == kSModeGateUp) ? 32 : R;
+  constexpr int NOUT = (MODE == kSModeGateUp) ? R / 2 : R;
+  constexpr int SR = (MODE == kSModeGateUp) ? R / 2 : 32;  // weight rows per buffer resource
   constexpr int KI = 128, NS = 4;
   constexpr int WL = INT4 ? 1 : NS;                  // 16-byte weight loads per row block
   constexpr int IT_BYTES = INT4 ? KI / 2 : KI * 2;    // weight bytes per row per iteration
@@ -444,7 +448,7 @@ __global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
 
   // weight resources: the block's strip of 32 rows in each matrix (the launcher
   // checks that 32 rows and the token matrix fit 32-bit offsets)
-  const uint32_t strip_bytes = 32u * row_bytes;
+  const uint32_t strip_bytes = (uint32_t)SR * row_bytes;
   const __amdgpu_buffer_rsrc_t wres0 = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.W0 + ((size_t)e * p.N + n0) * row_bytes), (short)0, (int)strip_bytes, 0x00020000);
   // (gate/up: the up matrix's strip; 64-row blocks: rows 32..63 of the block)
@@ -458,13 +462,13 @@ __global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
   uint32_t wvoff[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
-    wvoff[rb] = (uint32_t)((rb * 16 + r16) & 31) * row_bytes +
+    wvoff[rb] = (uint32_t)((rb * 16 + r16) & (SR - 1)) * row_bytes +
                 (INT4 ? (uint32_t)(kw0 + g * 32) / 2 : (uint32_t)(kw0 + g * 8) * 2);
 
   auto wsel = [&](int r, int& n, bool& second) {
     if constexpr (MODE == kSModeGateUp) {
-      second = r >= 32;
-      n = n0 + (r & 31);
+      second = r >= SR;
+      n = n0 + (r & (SR - 1));
     } else {
       second = false;
       n = n0 + r;
@@ -528,7 +532,7 @@ __global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
 #pragma unroll
           for (int q = 0; q < WL; ++q)
             S.wv[rb][q] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128((rb * 16 < 32) ? wres0 : wres1,
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128((rb * 16 < SR) ? wres0 : wres1,
                                                              (int)(wvoff[rb] + wo + q * 64), 0, 0));
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -616,7 +620,7 @@ __global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
           };
           const size_t orow = (size_t)(row0 + row);
           if constexpr (MODE == kSModeGateUp) {
-            const float gv = part(col), uv = part(32 + col);
+            const float gv = part(col), uv = part(SR + col);
             p.H[orow * p.N + n0 + col] = f32_to_bf16(silu_f32(gv) * uv);
           } else if constexpr (MODE == kSModeRelu) {
             p.H[orow * p.N + n0 + col] = f32_to_bf16(fmaxf(part(col), 0.0f));
@@ -646,7 +650,7 @@ size_t stream_reg_lds_bytes(int K) {
 
 template <int MODE, bool INT4>
 hipError_t launch_reg_mode(const StreamArgs& a0, int E, int mb, hipStream_t s) {
-  constexpr int NOUT = MODE == kSModeGateUp ? 32 : stream_reg_rows(MODE, INT4);
+  constexpr int NOUT = MODE == kSModeGateUp ? stream_reg_rows(MODE, INT4) / 2 : stream_reg_rows(MODE, INT4);
   StreamArgs a = a0;
   a.nblk_per_expert = (a.N + NOUT - 1) / NOUT;
   const dim3 grid((unsigned)(E * a.nblk_per_expert)), block(256);
@@ -701,9 +705,9 @@ hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid)
   a.H = (u16*)p.H;
   a.nblk_per_expert = (p.F + 31) / 32;
   // the register-direct kernel addresses the token matrix (x, then H) and a
-  // 32-row weight strip with 32-bit buffer offsets
+  // weight strip of up to 64 rows with 32-bit buffer offsets
   const size_t xb = (size_t)p.T * p.d * 2, hb = (size_t)p.rows * p.F * 2;
-  const size_t strip = 32 * (size_t)(p.d > p.F ? p.d : p.F) * (int4 ? 1 : 4) / 2;
+  const size_t strip = 64 * (size_t)(p.d > p.F ? p.d : p.F) * (int4 ? 1 : 4) / 2;
   const bool reg = xb < (1u << 31) && hb < (1u << 31) && strip < (1u << 31);
   a.xbytes = (uint32_t)xb;
   if (int4) {
