@@ -446,8 +446,8 @@ __global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
   const int G = p.K >> 7, GP = G + 1;
   const uint32_t row_bytes = INT4 ? (uint32_t)p.K / 2 : (uint32_t)p.K * 2;
 
-  // weight resources: the block's strip of 32 rows in each matrix (the launcher
-  // checks that 32 rows and the token matrix fit 32-bit offsets)
+  // weight resources: SR rows of the block's strip each (the launcher checks
+  // that 64 rows and the token matrix fit 32-bit offsets)
   const uint32_t strip_bytes = (uint32_t)SR * row_bytes;
   const __amdgpu_buffer_rsrc_t wres0 = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.W0 + ((size_t)e * p.N + n0) * row_bytes), (short)0, (int)strip_bytes, 0x00020000);
