@@ -192,17 +192,52 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
   // theta: the largest key with at least K cells at or above it.  A probe with
   // exactly K cells at or above it ends the search early: those cells are the
   // selection (kept: key >= probe, no ties to break).
+  // Per row i of this thread (i = tid + 256*s), the count of its cells at or
+  // above a key is a prefix length of the sorted column order; the search keeps
+  // that length at lo (rub) and at the last probe that fell short (rlb) and
+  // looks for the next probe's length only between them.
   uint32_t lo = fkey(smin), hi = fkey(smax);
   int c_lo = nr * nc;  // cells at or above key lo
+  constexpr int kRowsPer = kGridMax / 256;
+  int rlb[kRowsPer], rub[kRowsPer], rl[kRowsPer];
+#pragma unroll
+  for (int s = 0; s < kRowsPer; ++s) {
+    rlb[s] = 0;
+    rub[s] = nc;
+  }
   while (lo < hi) {
     const uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
-    const int c = count_ge(mid);
+    const float th = kf(mid);
+    int cpart = 0;
+#pragma unroll
+    for (int s = 0; s < kRowsPer; ++s) {
+      const int i = tid + 256 * s;
+      rl[s] = 0;
+      if (i < nr) {
+        const float ai = a[i];
+        int l = rlb[s], h = rub[s];
+        while (l < h) {
+          const int m = (l + h) >> 1;
+          if (ai + bv[m] >= th)
+            l = m + 1;
+          else
+            h = m;
+        }
+        rl[s] = l;
+        cpart += l;
+      }
+    }
+    const int c = block_sum(cpart, red);
     if (c >= K) {
       lo = mid;
       c_lo = c;
+#pragma unroll
+      for (int s = 0; s < kRowsPer; ++s) rub[s] = rl[s];
       if (c == K) break;
     } else {
       hi = mid - 1;
+#pragma unroll
+      for (int s = 0; s < kRowsPer; ++s) rlb[s] = rl[s];
     }
   }
   const uint32_t theta = lo;
