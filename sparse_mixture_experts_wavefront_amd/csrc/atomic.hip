@@ -324,26 +324,36 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
 }
 
 // ---- counting sort of the kept pairs by expert ---------------------------------
-// thread = (32-expert word wc, token chunk c): per-bit counts of the chunk
+// thread = (32-expert word wc, token chunk c): per-bit counts of the chunk,
+// kept bit-sliced while the chunk's words are added (plane p holds bit p of
+// all 32 counts; a count never exceeds kPermChunkT = 64, so 7 planes), then
+// unpacked once; the chunk's loads are unrolled so many are in flight
 __global__ __launch_bounds__(256) void grid_count_kernel(const uint32_t* __restrict__ bits, int T,
                                                          int W, int32_t* __restrict__ ccount) {
+  static_assert(kPermChunkT <= 127, "7 count planes");
   const int wc = blockIdx.x * 256 + threadIdx.x;
   const int c = blockIdx.y;
   if (wc >= W) return;
-  int cnt[32];
-#pragma unroll
-  for (int q = 0; q < 32; ++q) cnt[q] = 0;
+  uint32_t plane[7] = {0u, 0u, 0u, 0u, 0u, 0u, 0u};
   const int t1 = min((c + 1) * kPermChunkT, T);
+#pragma unroll 16
   for (int t = c * kPermChunkT; t < t1; ++t) {
-    const uint32_t w = bits[(size_t)t * W + wc];
-    if (w) {
+    uint32_t carry = bits[(size_t)t * W + wc];
 #pragma unroll
-      for (int q = 0; q < 32; ++q) cnt[q] += (w >> q) & 1u;
+    for (int p = 0; p < 7; ++p) {
+      const uint32_t nc = plane[p] & carry;
+      plane[p] ^= carry;
+      carry = nc;
     }
   }
   int32_t* o = ccount + (size_t)c * W * 32 + (size_t)wc * 32;
 #pragma unroll
-  for (int q = 0; q < 32; ++q) o[q] = cnt[q];
+  for (int q = 0; q < 32; ++q) {
+    int v = 0;
+#pragma unroll
+    for (int p = 0; p < 7; ++p) v |= (int)((plane[p] >> q) & 1u) << p;
+    o[q] = v;
+  }
 }
 
 // thread per expert: counts (sum over chunks) and the chunk prefixes, in place
