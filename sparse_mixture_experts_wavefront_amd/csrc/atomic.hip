@@ -362,8 +362,20 @@ __global__ __launch_bounds__(256) void grid_chunkprefix_kernel(int32_t* __restri
                                                                int32_t* __restrict__ counts) {
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= N) return;
+  // loads of 16 chunks are issued before their prefixes are written
   int run = 0;
-  for (int c = 0; c < nchunk; ++c) {
+  int c0 = 0;
+  for (; c0 + 16 <= nchunk; c0 += 16) {
+    int v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = ccount[(size_t)(c0 + u) * N + n];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      ccount[(size_t)(c0 + u) * N + n] = run;
+      run += v[u];
+    }
+  }
+  for (int c = c0; c < nchunk; ++c) {
     int32_t* p = ccount + (size_t)c * N + n;
     const int v = *p;
     *p = run;
