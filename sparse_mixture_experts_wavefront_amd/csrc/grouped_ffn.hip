@@ -24,6 +24,7 @@
 // Two tiled kernels: the 256x256x64 DMA-staged kernel (bf16, K % 128 == 0: the
 // layer path) and a 128x128x64 register-staged kernel (INT4 weights decoded
 // while staged, and any other shape).
+#include <mutex>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -33,6 +34,7 @@ namespace {
 
 constexpr int kBK = 64;
 constexpr int kThreads = 256;
+constexpr int kAttrDevices = 64;  // devices whose kernel attributes are cached
 
 // kAtomIn: one matrix (the input side of the atomic experts); at the cells a
 // per-row bitmap keeps the output is bf16(gate * silu(acc)), elsewhere 0.  The
@@ -1071,12 +1073,22 @@ hipError_t run_tiles(TileArgs a, hipStream_t s) {
   nblk = (nblk + 7) / 8 * 8;
   const size_t lds = (size_t)2 * (BM + NMAT * BN) * kBK * sizeof(u16);
   auto kern = grouped_gemm_kernel<BM, BN, MODE, INT4>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+  // the dynamic-LDS limit is raised once per device for this instantiation,
+  // under a lock, so concurrent first calls from several threads are safe
+  static std::mutex attr_mu;
+  static bool attr_set[kAttrDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lk(attr_mu);
+    const bool cached = dev >= 0 && dev < kAttrDevices;
+    if (!cached || !attr_set[dev]) {
+      e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+      if (e != hipSuccess) return e;
+      if (cached) attr_set[dev] = true;
+    }
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(kThreads), lds, s, a);
   return hipGetLastError();

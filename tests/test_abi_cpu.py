@@ -75,7 +75,10 @@ def test_route_validation(L, B):
     # logits given: x and w may be absent
     assert route(L, B, x=False, w=False,
                  flags=B.MOE_F_VALIDATE_ONLY | B.MOE_F_LOGITS_GIVEN) == B.MOE_OK
-    assert b"x must not be NULL" in L.moe_last_error() or True
+    # a successful validation clears the thread's error string
+    assert L.moe_last_error() == b""
+    assert route(L, B, x=False) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_last_error() == b"x must not be NULL"
     r = L.moe_route_topk(C.c_void_p(FAKE + 8), 1, _addr(2), None, 4, 64, 8, 2, _addr(3),
                          _addr(4), None, B.MOE_F_VALIDATE_ONLY, None)
     assert r == B.MOE_ERR_INVALID_ARG and b"aligned" in L.moe_last_error()
