@@ -195,6 +195,25 @@ moe_status moe_layer_forward(const moe_layer_desc* L, const void* x, int T, void
 /* Workspace bytes moe_layer_forward needs for T tokens (host only, pure). */
 moe_status moe_workspace_size(const moe_layer_desc* L, int T, size_t* bytes);
 
+/* moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, arithmetic and results as
+ * moe_layer_forward.  The workspace is a static device array of
+ * moe_noalloc_scratch_bytes() bytes (64 MiB) that every GPU the library runs
+ * on holds until the process ends; its address is looked up once per device
+ * on the first call there.  The call allocates nothing.
+ *   - A call whose workspace (moe_workspace_size) exceeds the array returns
+ *     MOE_ERR_WORKSPACE and enqueues nothing (decode-sized calls fit: at the
+ *     Mixtral shape, T up to a few hundred tokens).
+ *   - Every call on one GPU uses that GPU's one array, which keeps the last
+ *     call's contents; nothing in it has to start at zero (each call writes
+ *     what it reads).  Calls whose work overlaps on one GPU (other streams,
+ *     other threads) race on it: the caller serialises them. */
+moe_status moe_layer_forward_noalloc(const moe_layer_desc* L, const void* x, int T, void* y,
+                                     moe_dtype ydt, moe_aux* aux, unsigned flags, void* stream);
+/* Bytes of the static array behind moe_layer_forward_noalloc (host only). */
+size_t moe_noalloc_scratch_bytes(void);
+
 /* ---- Replica of the heaviest-loaded expert ("A Replicate-and-Quantize
  * Strategy for Plug-and-Play Load Balancing of Sparse Mixture-of-Experts
  * LLMs" -- What carries the argument: a quantized copy of the heavy-hitter

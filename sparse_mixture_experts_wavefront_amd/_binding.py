@@ -27,6 +27,7 @@ EXPORTED = ("moe_route_topk", "moe_permute", "moe_permute_workspace_size", "moe_
             "moe_grouped_ffn_mwq", "moe_grouped_ffn_mwq_workspace_size", "moe_layer_forward_mwq",
             "moe_mwq_workspace_size", "moe_layer_forward_floe", "moe_floe_workspace_size",
             "moe_atomic_layer_forward", "moe_atomic_workspace_size",
+            "moe_layer_forward_noalloc", "moe_noalloc_scratch_bytes",
             "moe_set_stage_events", "moe_status_string", "moe_last_error")
 
 
@@ -129,6 +130,10 @@ def lib():
             L.moe_layer_forward.argtypes = [C.POINTER(LayerDesc), p, i, p, i, C.POINTER(Aux), p,
                                             sz, u, p]
             L.moe_workspace_size.argtypes = [C.POINTER(LayerDesc), i, C.POINTER(sz)]
+            L.moe_layer_forward_noalloc.argtypes = [C.POINTER(LayerDesc), p, i, p, i,
+                                                    C.POINTER(Aux), u, p]
+            L.moe_noalloc_scratch_bytes.argtypes = []
+            L.moe_noalloc_scratch_bytes.restype = sz
             L.moe_replica_split.argtypes = [p, p, p, p, i, i, i, i, p, p, p, p, p, p, u, p]
             L.moe_layer_forward_replica.argtypes = [C.POINTER(LayerDesc), C.POINTER(Replica), p, i,
                                                     p, i, C.POINTER(Aux), p, p, sz, u, p]
@@ -160,6 +165,7 @@ def lib():
             L.moe_last_error.restype = C.c_char_p
             for f in ("moe_route_topk", "moe_permute", "moe_grouped_ffn", "moe_combine",
                       "moe_layer_forward", "moe_workspace_size", "moe_replica_split",
+                      "moe_layer_forward_noalloc",
                       "moe_layer_forward_replica", "moe_replica_workspace_size",
                       "moe_mwq_group", "moe_grouped_ffn_mwq", "moe_layer_forward_mwq",
                       "moe_mwq_workspace_size", "moe_layer_forward_floe",

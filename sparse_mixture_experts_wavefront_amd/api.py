@@ -372,6 +372,28 @@ def layer_forward(layer: MoeLayer, x, out_dtype=torch.float32, flags=0, logits=N
     return y, r.aux_t
 
 
+def noalloc_scratch_bytes() -> int:
+    """Size of the static device array behind layer_forward_noalloc."""
+    return int(B.lib().moe_noalloc_scratch_bytes())
+
+
+def layer_forward_noalloc(layer: MoeLayer, x, y, aux=None, flags=0):
+    """moe_layer_forward_noalloc: the layer with the library's static device
+    array as workspace (the call allocates nothing).  y [T][d] (fp32 or bf16)
+    is written; aux, if given, is a dict of caller tensors named as the fields
+    of moe_aux (any subset).  Returns y."""
+    T = x.shape[0]
+    desc = layer.desc()
+    a = None
+    if aux:
+        a = B.Aux(**{n: _p(t) for n, t in aux.items()})
+    B.check(B.lib().moe_layer_forward_noalloc(C.byref(desc), _p(x), T, _p(y), _dt(y),
+                                              C.byref(a) if a is not None else None, flags,
+                                              _stream()),
+            "moe_layer_forward_noalloc")
+    return y
+
+
 def replica_split(idx, counts, offsets, assign_row, E, heavy, flags=0):
     """Split routing of expert ``heavy`` (see moe_replica_split); returns a dict."""
     T, k = idx.shape

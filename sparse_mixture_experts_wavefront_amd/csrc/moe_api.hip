@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
 #include <string>
 
 #include "moe_internal.h"
@@ -478,6 +480,76 @@ moe_status moe_layer_forward(const moe_layer_desc* L, const void* x, int T, void
                              moe_dtype ydt, moe_aux* aux, void* ws, size_t ws_bytes,
                              unsigned flags, void* stream) {
   return layer_forward_impl(L, nullptr, x, T, y, ydt, aux, nullptr, ws, ws_bytes, flags, stream);
+}
+
+}  // extern "C"
+
+// ---- the layer without a caller workspace -----------------------------------
+// The workspace of moe_layer_forward lives in one file-scope device array.
+// Each device holds its own copy; host code never passes the array's name to a
+// kernel (on the host it is only a stand-in), it passes the address that
+// hipGetSymbolAddress returned for the current device.
+
+namespace {
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kScratchDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_addr[kScratchDevices];
+
+// Device address of this device's scratch array, looked up once per device.
+moe_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d: scratch addresses are kept for devices 0..%d",
+                dev, kScratchDevices - 1);
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+      if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+moe_status moe_layer_forward_noalloc(const moe_layer_desc* L, const void* x, int T, void* y,
+                                     moe_dtype ydt, moe_aux* aux, unsigned flags, void* stream) {
+  moe_status s = check_layer(L, T, flags);
+  if (s != MOE_OK) return s;
+  const size_t need = carve_layer(L, T, nullptr).total;
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_layer_forward_noalloc: T = %d needs %zu bytes of scratch, above the "
+                "static %zu bytes; call moe_layer_forward with a workspace instead",
+                T, need, kScratchBytes);
+  // no device is touched for a validation-only or empty call: any 256-byte
+  // aligned address stands in for the scratch (it is never dereferenced)
+  void* ws = (void*)(uintptr_t)256;
+  if (!(flags & MOE_F_VALIDATE_ONLY) && T > 0) {
+    s = scratch_address(&ws);
+    if (s != MOE_OK) return s;
+  }
+  return layer_forward_impl(L, nullptr, x, T, y, ydt, aux, nullptr, ws, kScratchBytes, flags,
+                            stream);
 }
 
 moe_status moe_layer_forward_replica(const moe_layer_desc* L, const moe_replica* R,

@@ -193,6 +193,38 @@ def test_layer_workspace_and_validation(L, B):
     assert L.moe_workspace_size(C.byref(Li), 64, C.byref(n)) == B.MOE_OK
 
 
+def test_noalloc_validation(L, B):
+    """The allocation-free layer call checks its arguments and the size of its
+    static scratch on the host; nothing here touches a device."""
+    VO = B.MOE_F_VALIDATE_ONLY
+    cap = L.moe_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    Ld = _desc(B)
+    n = C.c_size_t(0)
+
+    def ws(T):
+        assert L.moe_workspace_size(C.byref(Ld), T, C.byref(n)) == B.MOE_OK
+        return n.value
+    T = 100
+    assert ws(T) <= cap
+    assert L.moe_layer_forward_noalloc(C.byref(Ld), _addr(1), T, _addr(2), 0, None, VO,
+                                       None) == B.MOE_OK
+    assert L.moe_last_error() == b""
+    big = T
+    while ws(big) <= cap:
+        big *= 2
+    assert L.moe_layer_forward_noalloc(C.byref(Ld), _addr(1), big, _addr(2), 0, None, VO,
+                                       None) == B.MOE_ERR_WORKSPACE
+    assert b"static" in L.moe_last_error()
+    assert L.moe_layer_forward_noalloc(C.byref(Ld), None, T, _addr(2), 0, None, VO,
+                                       None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_forward_noalloc(C.byref(Ld), _addr(1), 0, None, 0, None, VO,
+                                       None) == B.MOE_OK
+    Ld.top_k = 0
+    assert L.moe_layer_forward_noalloc(C.byref(Ld), _addr(1), T, _addr(2), 0, None, VO,
+                                       None) == B.MOE_ERR_INVALID_ARG
+
+
 def test_status_strings(L, B):
     for s in range(5):
         assert L.moe_status_string(s).decode().startswith("MOE_")
