@@ -271,14 +271,11 @@ FULL = ["tiny_fp32", "switch_bf16", "mixtral_decode_bf16", "mixtral_prefill_bf16
 
 @pytest.mark.parametrize("name", FULL)
 def test_layer_parity_full_size(name):
-    """Full configs in the benchmark's launch configuration; y on sampled tokens."""
+    """Full configs in the benchmark's launch configuration; y on every token,
+    so every row tile, half tile and K slice of the launch is compared."""
     _say("full-size %s" % name)
     wl = _workload(name)
     g = run_layer(wl)
     ref = check_routing(wl, g)
-    T = wl.cfg.T
-    rng = np.random.default_rng(15)
-    n = min(T, 12 if wl.cfg.d >= 4096 else 24)
-    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=n, replace=False)]))
-    check_y(wl, g, tokens=toks)
+    check_y(wl, g)
     print("  LIS %.6f counts %s" % (ref["lis"], ref["counts"][:16]), flush=True)
