@@ -114,7 +114,14 @@ def work_floe(cfg, counts, nnz):
                 dense_bf16_bytes=float(active.sum()) * 3 * F * d * 2)
 
 
-def run_gpu(name, steps, warmup):
+FLUSH_BYTES = 512 << 20   # written before each cold step: more than the 256 MB MALL
+
+
+def run_gpu(name, steps, warmup, cold=False):
+    """Warm wall-clock timing of `steps` back-to-back layer calls, then one
+    event-timed pass per step (per-stage HIP events).  With cold=True a 512 MB
+    buffer is written before each event-timed step, outside its events, so the
+    weights start from HBM rather than the MALL."""
     import torch
     import sparse_mixture_experts_wavefront_amd as moe
     from sparse_mixture_experts_wavefront_amd.device_inputs import (floe_to_device, mwq_to_device,
@@ -165,8 +172,11 @@ def run_gpu(name, steps, warmup):
         sets.append((C.c_void_p * 7)(*hs))
     B = moe.lib()
     per = np.zeros((steps, 7))
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=x.device) if cold else None
     try:
-        for evs in sets:
+        for n, evs in enumerate(sets):
+            if cold:
+                flush.fill_(float(n))
             B.moe_set_stage_events(C.cast(evs, C.POINTER(C.c_void_p)), 7)
             call()
         B.moe_set_stage_events(None, 0)
@@ -196,7 +206,9 @@ def run_gpu(name, steps, warmup):
     timing = dict(event_ms_p10=round(float(np.percentile(layer_ms, 10)), 4),
                   event_ms_p50=round(float(np.percentile(layer_ms, 50)), 4),
                   event_ms_p90=round(float(np.percentile(layer_ms, 90)), 4))
-    return wl, dict(ms=ms, counts=counts, lis=lis, stages_us=stages, work=w, timing=timing)
+    del flush
+    return wl, dict(ms=ms, counts=counts, lis=lis, stages_us=stages, work=w, timing=timing,
+                    cold=cold, event_ms=float(layer_ms.mean()))
 
 
 def sources_sha256(kernel):
@@ -284,8 +296,9 @@ def run_atomic(name, steps, warmup):
                        "shared_mlp", "combine"], [round(v * 1000.0, 2) for v in st]))
     T, d, N, K = cfg.T, cfg.d, cfg.nr * cfg.nc, cfg.k
     dense_flops = 2.0 * T * N * d
+    method_flops = 2.0 * T * K * d     # per side: each kept (token, unit) pair, one d-long dot
     t_in = st[2] * 1e-3
-    ach = dense_flops / t_in / 1e12
+    ach = method_flops / t_in / 1e12
     return {"workload": name, "T": T, "d_model": d, "experts": N, "top_k": K,
             "tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
             "lis": float(runner.aux_t["lis"].cpu().numpy()[0]),
@@ -293,10 +306,14 @@ def run_atomic(name, steps, warmup):
             "stages_us": stages,
             "timing": dict(event_ms_p50=round(float(np.percentile(per[:, 6], 50)), 4)),
             "roofline": dict(kernel="grouped_gemm_tile<kAtomIn> (dense x . W_in^T, masked epilogue)",
-                             bound="mfma", achieved=round(ach, 1), peak=MFMA_BF16_PEAK_TFLOPS,
+                             bound="mfma", achieved=round(ach, 2), peak=MFMA_BF16_PEAK_TFLOPS,
                              unit="TFLOP/s", frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
                              traffic=None,
-                             per_launch=dict(flops=dense_flops, us=round(t_in * 1e6, 2)))}
+                             per_launch=dict(flops=method_flops, us=round(t_in * 1e6, 2)),
+                             dense_gemm_rate=dict(
+                                 flops=dense_flops, tflops=round(dense_flops / t_in / 1e12, 1),
+                                 note="all T x N cells computed; only the K kept per token "
+                                      "are used"))}
 
 
 def run_replica(name, steps, warmup):
@@ -351,6 +368,12 @@ def roofline(cfg, r):
                     achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
                     per_launch=dict(bytes=w["gu_bytes"], us=round(t * 1e6, 2)))
+    if cfg.dtype == "f32":             # fp32 layers run on the vector ALUs
+        ach = w["gu_flops"] / t / 1e12
+        return dict(kernel="ffn_f32_up (fp32 VALU gate/up)", bound="alu",
+                    achieved=round(ach, 3), peak=FP32_VALU_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(ach / FP32_VALU_PEAK_TFLOPS, 5), traffic=None,
+                    per_launch=dict(flops=w["gu_flops"], us=round(t * 1e6, 2)))
     if cfg.T * cfg.k >= 1024:          # many rows per expert: the GEMM is MFMA-bound
         ach = w["gu_flops"] / t / 1e12
         return dict(kernel="grouped_gemm gate/up (SwiGLU epilogue)", bound="mfma",
@@ -364,6 +387,17 @@ def roofline(cfg, r):
                 frac=round(ach / HBM_PEAK_GBS, 4),
                 traffic=measured_traffic(cfg.name, "stream_ffn"),
                 per_launch=dict(bytes=w["gu_bytes"], us=round(t * 1e6, 2)))
+
+
+def host_cpu_model():
+    """The host CPU's model name (lscpu's "Model name", read from /proc/cpuinfo)."""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.lower().startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(wl, target_s=15.0):
@@ -386,8 +420,47 @@ def cpu_baseline(wl, target_s=15.0):
         oracle.layer_forward(sample(S))
         dt = time.perf_counter() - t0
     return dict(value=round(S / dt, 3), unit="tokens/s", cores=threads, kind="oracle",
+                host=host_cpu_model(),
                 sample="first %d of %d tokens as one batch, whole layer (router, top-k, "
                        "permutation, FFN, combine), fp64 C oracle, %.1f s" % (S, cfg.T, dt))
+
+
+# HBM-bound workloads are timed from a cold cache (a 512 MB write before each
+# step); the Switch-shaped layer, whose 75 MB of weights fit in the MALL, is
+# reported both warm and cold
+COLD = {"mixtral_decode_bf16": ("cold",), "mixtral_int4_decode": ("cold",),
+        "mixtral_mwq_decode": ("cold",), "mixtral_floe_decode": ("cold",),
+        "mixtral_floe_decode_t1": ("cold",), "switch_bf16": ("warm", "cold")}
+
+
+def secondary_lines(name, steps, warmup, oracle_s):
+    """One line per cache state of a workload: tokens/s, stage times and the
+    gate/up roofline from the event-timed pass (cold) or the wall clock
+    (warm), plus the oracle timed on the host beside it."""
+    modes = COLD.get(name, ("warm",))
+    wl, r = run_gpu(name, steps, warmup, cold="cold" in modes)
+    rw = None
+    if "warm" in modes and "cold" in modes:
+        _, rw = run_gpu(name, steps, warmup, cold=False)
+    c = wl.cfg
+    lines = []
+    for mode in modes:
+        rr = rw if (mode == "warm" and rw is not None) else r
+        ms = rr["event_ms"] if mode == "cold" else rr["ms"]
+        gbs = rr["work"]["bytes"] / (ms * 1e-3) / 1e9
+        lines.append({"workload": name, "cache": mode, "T": c.T,
+                      "tokens_per_s": round(c.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+                      "lis": rr["lis"], "active_experts": rr["work"]["active"],
+                      "layer_tflops": round(rr["work"]["flops"] / (ms * 1e-3) / 1e12, 2),
+                      "layer_GBps": round(gbs, 1), "layer_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "stages_us": rr["stages_us"], "timing": rr["timing"],
+                      "roofline": roofline(c, rr)})
+    if oracle_s > 0:
+        base = cpu_baseline(wl, target_s=oracle_s)
+        for ln in lines:
+            ln["cpu_baseline"] = base
+    del wl
+    return lines
 
 
 def main():
@@ -396,8 +469,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill_bf16")
-    ap.add_argument("--secondary", default="mixtral_decode_bf16,mixtral_int4_decode",
+    ap.add_argument("--secondary",
+                    default="mixtral_decode_bf16,mixtral_int4_decode,deepseek_v2_lite_bf16,"
+                            "switch_bf16,tiny_fp32",
                     help="comma-separated extra workloads reported in the same line ('' for none)")
+    ap.add_argument("--oracle-seconds", type=float, default=4.0,
+                    help="CPU seconds of oracle work timed beside each secondary workload "
+                         "(0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--replica", default="switch_bf16,deepseek_v2_lite_bf16",
                     help="comma-separated workloads also run with an INT4 replica of their "
@@ -455,16 +533,7 @@ def main():
     }
     sec = []
     for name in [s for s in args.secondary.split(",") if s]:
-        wl2, r2 = run_gpu(name, args.steps, args.warmup)
-        c2 = wl2.cfg
-        sec.append({"workload": name, "T": c2.T, "tokens_per_s": round(c2.T / (r2["ms"] / 1e3), 1),
-                    "ms_per_step": round(r2["ms"], 4), "lis": r2["lis"],
-                    "layer_GBps": round(r2["work"]["bytes"] / (r2["ms"] * 1e-3) / 1e9, 1),
-                    "layer_hbm_frac": round(r2["work"]["bytes"] / (r2["ms"] * 1e-3) / 1e9
-                                            / HBM_PEAK_GBS, 4),
-                    "stages_us": r2["stages_us"], "timing": r2["timing"],
-                    "roofline": roofline(c2, r2)})
-        del wl2
+        sec.extend(secondary_lines(name, args.steps, args.warmup, args.oracle_seconds))
     if sec:
         out["secondary"] = sec
     mw = []
