@@ -196,6 +196,36 @@ def run_gpu(name, steps, warmup, cold=False):
                 hip.hipEventDestroy(evs[i])
     st = per[:, :6].mean(axis=0)
     layer_ms = per[:, 6]
+    if cold:
+        # the cold layer time from two events per step only (the stage events
+        # above add their own overhead between the stages)
+        ev = []
+        for _ in range(steps):
+            pair = []
+            for _ in range(2):
+                h = C.c_void_p()
+                assert hip.hipEventCreate(C.byref(h)) == 0
+                pair.append(h.value)
+            ev.append(pair)
+        hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+        try:
+            for n, (a, b) in enumerate(ev):
+                flush.fill_(float(n))
+                assert hip.hipEventRecord(C.c_void_p(a), stream) == 0
+                call()
+                assert hip.hipEventRecord(C.c_void_p(b), stream) == 0
+            torch.cuda.synchronize()
+            cold_ms = []
+            for a, b in ev:
+                f = C.c_float(0)
+                assert hip.hipEventElapsedTime(C.byref(f), C.c_void_p(a), C.c_void_p(b)) == 0
+                cold_ms.append(f.value)
+        finally:
+            for a, b in ev:
+                hip.hipEventDestroy(C.c_void_p(a))
+                hip.hipEventDestroy(C.c_void_p(b))
+        layer_ms = np.asarray(cold_ms)
     w = work(cfg, counts)
     if cfg.mwq:
         w.update(work_mwq(cfg, runner.aux_t["mwq_counts"].cpu().numpy()))
@@ -242,17 +272,28 @@ def measured_traffic(workload, kernel):
     return None
 
 
-def run_atomic(name, steps, warmup):
-    """The atomic-expert layer (router grid, exact top-K, expert grouping, masked
-    input GEMM, output GEMM, shared MLP), per-stage HIP events as in run_gpu."""
+_ATOMIC_WL = {}
+
+
+def run_atomic(spec, steps, warmup):
+    """The atomic-expert layer (router grid, exact top-K, expert grouping, then
+    the schedule's input and output sides, shared MLP, combine), per-stage HIP
+    events as in run_gpu.  `spec` is a workload name, optionally ':' and a
+    schedule (auto, dense, expert_centric)."""
     import torch
     import sparse_mixture_experts_wavefront_amd as moe
     from sparse_mixture_experts_wavefront_amd.device_inputs import atomic_to_device
     from workloads import make_workload
-    wl = make_workload(name)
+    name, _, schedule = spec.partition(":")
+    schedule = schedule or "auto"
+    if name not in _ATOMIC_WL:
+        _ATOMIC_WL.clear()
+        _ATOMIC_WL[name] = make_workload(name)
+    wl = _ATOMIC_WL[name]
     cfg = wl.cfg
-    layer, x = atomic_to_device(wl)
+    layer, x = atomic_to_device(wl, schedule=schedule)
     runner = moe.AtomicRunner(layer, cfg.T)
+    resolved = runner.schedule_used()
     for _ in range(warmup):
         runner(x)
     torch.cuda.synchronize()
@@ -292,28 +333,48 @@ def run_atomic(name, steps, warmup):
             for i in range(7):
                 hip.hipEventDestroy(evs[i])
     st = per[:, :6].mean(axis=0)
-    stages = dict(zip(["route_grid_topk", "permute", "input_gemm_masked", "output_gemm",
-                       "shared_mlp", "combine"], [round(v * 1000.0, 2) for v in st]))
+    ec = resolved == "expert_centric"
+    stages = dict(zip(["route_grid_topk", "permute",
+                       "input_expert_centric" if ec else "input_gemm_masked",
+                       "output_expert_centric" if ec else "output_gemm",
+                       "shared_mlp", "reduce" if ec else "combine"],
+                      [round(v * 1000.0, 2) for v in st]))
     T, d, N, K = cfg.T, cfg.d, cfg.nr * cfg.nc, cfg.k
+    counts = runner.aux_t["counts"].cpu().numpy()
+    active = int(np.count_nonzero(counts))
     dense_flops = 2.0 * T * N * d
     method_flops = 2.0 * T * K * d     # per side: each kept (token, unit) pair, one d-long dot
     t_in = st[2] * 1e-3
-    ach = method_flops / t_in / 1e12
-    return {"workload": name, "T": T, "d_model": d, "experts": N, "top_k": K,
+    line = {"workload": name, "schedule": resolved, "T": T, "d_model": d, "experts": N,
+            "top_k": K, "active_experts": active,
             "tokens_per_s": round(T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
             "lis": float(runner.aux_t["lis"].cpu().numpy()[0]),
             "useful_fraction_of_dense_gemm": round(K / N, 4),
             "stages_us": stages,
-            "timing": dict(event_ms_p50=round(float(np.percentile(per[:, 6], 50)), 4)),
-            "roofline": dict(kernel="grouped_gemm_tile<kAtomIn> (dense x . W_in^T, masked epilogue)",
-                             bound="mfma", achieved=round(ach, 2), peak=MFMA_BF16_PEAK_TFLOPS,
-                             unit="TFLOP/s", frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                             traffic=None,
-                             per_launch=dict(flops=method_flops, us=round(t_in * 1e6, 2)),
-                             dense_gemm_rate=dict(
-                                 flops=dense_flops, tflops=round(dense_flops / t_in / 1e12, 1),
+            "timing": dict(event_ms_p50=round(float(np.percentile(per[:, 6], 50)), 4))}
+    if ec:
+        # expert-centric input side: the input vectors of the experts some token
+        # kept, each read once, plus x
+        in_bytes = active * d * 2.0 + T * d * 2.0
+        ach = in_bytes / t_in / 1e9
+        line["roofline"] = dict(kernel="atomic_ec_in (kept experts' w_in read once, v_dot2)",
+                                bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS,
+                                unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                                per_launch=dict(bytes=in_bytes, us=round(t_in * 1e6, 2)),
+                                method_flops_rate=dict(
+                                    flops=method_flops,
+                                    tflops=round(method_flops / t_in / 1e12, 2)))
+    else:
+        ach = method_flops / t_in / 1e12
+        line["roofline"] = dict(
+            kernel="grouped_gemm_tile<kAtomIn> (dense x . W_in^T, masked epilogue)",
+            bound="mfma", achieved=round(ach, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+            frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None,
+            per_launch=dict(flops=method_flops, us=round(t_in * 1e6, 2)),
+            dense_gemm_rate=dict(flops=dense_flops, tflops=round(dense_flops / t_in / 1e12, 1),
                                  note="all T x N cells computed; only the K kept per token "
-                                      "are used"))}
+                                      "are used"))
+    return line
 
 
 def run_replica(name, steps, warmup):
@@ -486,8 +547,11 @@ def main():
     ap.add_argument("--floe", default="mixtral_floe_decode,mixtral_floe_decode_t1",
                     help="comma-separated sparse-down workloads reported in the same line "
                          "('' for none)")
-    ap.add_argument("--atomic", default="omni_atomic",
-                    help="comma-separated atomic-expert workloads reported in the same line "
+    ap.add_argument("--atomic",
+                    default="omni_atomic,omni_atomic:expert_centric,omni_atomic_decode,"
+                            "omni_atomic_decode:dense",
+                    help="comma-separated atomic-expert workloads, each optionally with "
+                         "':schedule' (auto, dense, expert_centric), reported in the same line "
                          "('' for none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (the known-size kernel "
@@ -565,6 +629,7 @@ def main():
     if fl:
         out["floe"] = fl
     atoms = [run_atomic(n, args.steps, args.warmup) for n in args.atomic.split(",") if n]
+    _ATOMIC_WL.clear()
     if atoms:
         out["atomic"] = atoms
     reps = [run_replica(n, args.steps, args.warmup) for n in args.replica.split(",") if n]

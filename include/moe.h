@@ -43,9 +43,9 @@
  *   - Limits: 1 <= E <= 64, 1 <= k <= min(E, 8), d and d_ff multiples of 8
  *     (multiples of 128 along K for INT4).  Out-of-range shapes return
  *     MOE_ERR_INVALID_ARG, in-range but unimplemented ones MOE_ERR_UNSUPPORTED.
- *   - Routing, counts, permutation and LIS are exact integer results.  Default
- *     outputs are bitwise run-to-run deterministic; MOE_F_NONDETERMINISTIC_COMBINE
- *     allows floating-point atomics in the combine.
+ *   - Routing, counts, permutation and LIS are exact integer results.  All
+ *     outputs are bitwise run-to-run deterministic (MOE_F_NONDETERMINISTIC_COMBINE
+ *     is reserved: accepted and ignored).
  *   - The library is stateless apart from a device-property cache and a
  *     thread-local error string; calls are thread-safe.
  */
@@ -73,7 +73,11 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU = 1 } moe_act;
 enum {
   MOE_F_LOGITS_GIVEN = 1u,   /* moe_route_topk / layer: `logits` is an input */
   MOE_F_VALIDATE_ONLY = 2u,  /* check arguments, enqueue nothing */
-  MOE_F_NONDETERMINISTIC_COMBINE = 4u /* fp32 atomics allowed in the combine */
+  MOE_F_NONDETERMINISTIC_COMBINE = 4u /* reserved: accepted and ignored; every path is
+                                         deterministic (the fused combine of decode
+                                         layers adds at most two rows onto a zeroed
+                                         output, which gives the same sum in either
+                                         order) */
 };
 
 /* Group-wise asymmetric INT4 weights of one projection, all experts.
@@ -399,6 +403,24 @@ moe_status moe_floe_workspace_size(const moe_layer_desc* L, int T, size_t* bytes
  *       + the shared SwiGLU MLP (n_shared > 0)
  * The kept (token, expert) pairs are grouped by expert (counts, offsets,
  * token-ordered rows, LIS = N * max_n count_n / (T * K)). */
+/* How the kept pairs are executed (OmniMoE -- What carries the argument,
+ * Figure 3: expert-centric scheduling).  Both give the same result within
+ * floating-point summation order.
+ *   MOE_ATOMIC_DENSE: one dense GEMM of x against all N input vectors whose
+ *     epilogue keeps only the kept cells (gate and SiLU applied, rounded to
+ *     bf16, zeros elsewhere), then one dense GEMM of that [T][N] matrix against
+ *     w_out.  Needs w_out.  At 4096 tokens every block of 256 consecutive
+ *     experts is kept by nearly every token, so this is the grouped product of
+ *     each expert group with its tokens, run as MFMA tiles.
+ *   MOE_ATOMIC_EXPERT_CENTRIC: the grouping drives the compute: each expert
+ *     with kept pairs reads w_in[n] once for all of its tokens, then w_out[n]
+ *     (from w_out_rows) once, adding h * w_out[n] into per-range partial sums
+ *     that are added in range order; experts no token kept are never read.
+ *     Needs w_out_rows and d_model a multiple of 512, at most 4096.
+ *   MOE_ATOMIC_AUTO: expert-centric for at most 64 tokens when w_out_rows is
+ *     given (or when w_out is NULL), dense otherwise. */
+enum { MOE_ATOMIC_AUTO = 0, MOE_ATOMIC_DENSE = 1, MOE_ATOMIC_EXPERT_CENTRIC = 2 };
+
 typedef struct {
   int d_model;
   int grid_rows, grid_cols;  /* nr, nc: N = nr * nc atomic experts */
@@ -406,9 +428,13 @@ typedef struct {
   const void* w_row;         /* bf16 [nr][d_model] */
   const void* w_col;         /* bf16 [nc][d_model] */
   const void* w_in;          /* bf16 [N][d_model] */
-  const void* w_out;         /* bf16 [d_model][N]: column n is w_out of expert n */
+  const void* w_out;         /* bf16 [d_model][N]: column n is w_out of expert n (dense
+                                schedule); may be NULL */
   int n_shared, d_ff_shared;
   moe_experts shared;        /* as in moe_layer_desc */
+  const void* w_out_rows;    /* bf16 [N][d_model]: row n is w_out of expert n, the same
+                                values expert-major (expert-centric schedule); may be NULL */
+  int schedule;              /* MOE_ATOMIC_AUTO, MOE_ATOMIC_DENSE or MOE_ATOMIC_EXPERT_CENTRIC */
 } moe_atomic_layer_desc;
 
 /* Optional outputs of moe_atomic_layer_forward; every pointer may be NULL. */
@@ -426,14 +452,17 @@ typedef struct {
 
 /* The atomic-expert layer.  x [T][d_model] bf16, y [T][d_model] in ydt.
  * Requires d_model % 128 == 0, nc % 32 == 0, nr, nc <= 1024, N % 128 == 0,
- * 1 <= K <= N.  The input side is one dense GEMM of x against all N input
- * vectors whose epilogue keeps only the selected cells (gate and SiLU applied,
- * rounded to bf16, zeros elsewhere); the output side is one dense GEMM of that
- * [T][N] matrix against w_out.  Workspace: moe_atomic_workspace_size. */
+ * 1 <= K <= N; the schedule's own needs are listed with moe_atomic_layer_desc
+ * (unmet: MOE_ERR_INVALID_ARG for a missing matrix, MOE_ERR_UNSUPPORTED for
+ * d_model).  Workspace: moe_atomic_workspace_size (it depends on the schedule
+ * the call resolves to). */
 moe_status moe_atomic_layer_forward(const moe_atomic_layer_desc* L, const void* x, int T, void* y,
                                     moe_dtype ydt, moe_atomic_aux* aux, void* ws, size_t ws_bytes,
                                     unsigned flags, void* stream);
 moe_status moe_atomic_workspace_size(const moe_atomic_layer_desc* L, int T, size_t* bytes);
+/* The schedule (MOE_ATOMIC_DENSE or MOE_ATOMIC_EXPERT_CENTRIC) a call of the
+ * atomic layer with T tokens runs (host only, pure; errors as the layer's). */
+moe_status moe_atomic_schedule(const moe_atomic_layer_desc* L, int T, int* schedule);
 
 /* Instrumentation (not part of the layer's arithmetic).  While set, every
  * moe_layer_forward call made on this thread records events[i] (hipEvent_t

@@ -19,6 +19,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_RELU = 0, 1
 MOE_F_LOGITS_GIVEN, MOE_F_VALIDATE_ONLY, MOE_F_NONDETERMINISTIC_COMBINE = 1, 2, 4
+MOE_ATOMIC_AUTO, MOE_ATOMIC_DENSE, MOE_ATOMIC_EXPERT_CENTRIC = 0, 1, 2
 
 EXPORTED = ("moe_route_topk", "moe_permute", "moe_permute_workspace_size", "moe_grouped_ffn",
             "moe_grouped_ffn_workspace_size", "moe_combine", "moe_layer_forward",
@@ -26,7 +27,7 @@ EXPORTED = ("moe_route_topk", "moe_permute", "moe_permute_workspace_size", "moe_
             "moe_replica_workspace_size", "moe_mwq_group", "moe_mwq_group_workspace_size",
             "moe_grouped_ffn_mwq", "moe_grouped_ffn_mwq_workspace_size", "moe_layer_forward_mwq",
             "moe_mwq_workspace_size", "moe_layer_forward_floe", "moe_floe_workspace_size",
-            "moe_atomic_layer_forward", "moe_atomic_workspace_size",
+            "moe_atomic_layer_forward", "moe_atomic_workspace_size", "moe_atomic_schedule",
             "moe_layer_forward_noalloc", "moe_noalloc_scratch_bytes",
             "moe_set_stage_events", "moe_status_string", "moe_last_error")
 
@@ -90,7 +91,8 @@ class AtomicLayerDesc(C.Structure):
     _fields_ = [("d_model", C.c_int), ("grid_rows", C.c_int), ("grid_cols", C.c_int),
                 ("top_k", C.c_int), ("w_row", C.c_void_p), ("w_col", C.c_void_p),
                 ("w_in", C.c_void_p), ("w_out", C.c_void_p), ("n_shared", C.c_int),
-                ("d_ff_shared", C.c_int), ("shared", Experts)]
+                ("d_ff_shared", C.c_int), ("shared", Experts), ("w_out_rows", C.c_void_p),
+                ("schedule", C.c_int)]
 
 
 class AtomicAux(C.Structure):
@@ -157,6 +159,7 @@ def lib():
                                                    C.POINTER(AtomicAux), p, sz, u, p]
             L.moe_atomic_workspace_size.argtypes = [C.POINTER(AtomicLayerDesc), i,
                                                     C.POINTER(sz)]
+            L.moe_atomic_schedule.argtypes = [C.POINTER(AtomicLayerDesc), i, C.POINTER(i)]
             L.moe_set_stage_events.argtypes = [C.POINTER(C.c_void_p), i]
             L.moe_set_stage_events.restype = C.c_int
             L.moe_status_string.argtypes = [i]
@@ -170,7 +173,7 @@ def lib():
                       "moe_mwq_group", "moe_grouped_ffn_mwq", "moe_layer_forward_mwq",
                       "moe_mwq_workspace_size", "moe_layer_forward_floe",
                       "moe_floe_workspace_size", "moe_atomic_layer_forward",
-                      "moe_atomic_workspace_size"):
+                      "moe_atomic_workspace_size", "moe_atomic_schedule"):
                 getattr(L, f).restype = C.c_int
             _lib = L
     return _lib

@@ -451,8 +451,10 @@ def grouped_ffn_mwq(x, E, k, act, experts: MwqExperts, offsets, row_assign, topk
 @dataclass
 class AtomicLayer:
     """Atomic experts on an nr x nc router grid (see moe_atomic_layer_forward):
-    w_row [nr][d], w_col [nc][d], w_in [N][d], w_out [d][N] bf16; optional
-    shared SwiGLU MLP."""
+    w_row [nr][d], w_col [nc][d], w_in [N][d], w_out [d][N] and/or w_out_rows
+    [N][d] bf16 (the same output vectors in the dense and the expert-centric
+    layout); optional shared SwiGLU MLP; schedule "auto", "dense" or
+    "expert_centric"."""
     d_model: int
     grid_rows: int
     grid_cols: int
@@ -460,10 +462,12 @@ class AtomicLayer:
     w_row: torch.Tensor
     w_col: torch.Tensor
     w_in: torch.Tensor
-    w_out: torch.Tensor
+    w_out: Optional[torch.Tensor]
     n_shared: int = 0
     d_ff_shared: int = 0
     shared: Optional[ExpertWeights] = None
+    w_out_rows: Optional[torch.Tensor] = None
+    schedule: str = "auto"
 
     def desc(self) -> B.AtomicLayerDesc:
         L = B.AtomicLayerDesc()
@@ -474,6 +478,9 @@ class AtomicLayer:
         L.n_shared, L.d_ff_shared = self.n_shared, self.d_ff_shared
         if self.shared is not None:
             L.shared = self.shared.struct(B.MOE_DT_BF16)
+        L.w_out_rows = _p(self.w_out_rows)
+        L.schedule = {"auto": B.MOE_ATOMIC_AUTO, "dense": B.MOE_ATOMIC_DENSE,
+                      "expert_centric": B.MOE_ATOMIC_EXPERT_CENTRIC}[self.schedule]
         return L
 
 
@@ -504,6 +511,13 @@ class AtomicRunner:
                 assign_row=torch.empty(max(T * K, 1), dtype=torch.int32, device=dev),
                 lis=torch.empty(1, dtype=torch.float64, device=dev))
             self.aux = B.AtomicAux(**{k: _p(v) for k, v in self.aux_t.items()})
+
+    def schedule_used(self) -> str:
+        """The schedule the library runs for this layer and T (moe_atomic_schedule)."""
+        v = C.c_int(-1)
+        B.check(B.lib().moe_atomic_schedule(C.byref(self.desc), self.T, C.byref(v)),
+                "moe_atomic_schedule")
+        return {B.MOE_ATOMIC_DENSE: "dense", B.MOE_ATOMIC_EXPERT_CENTRIC: "expert_centric"}[v.value]
 
     def __call__(self, x, flags=0):
         aux = C.byref(self.aux) if self.aux is not None else None

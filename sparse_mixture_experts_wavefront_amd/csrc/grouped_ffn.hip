@@ -1096,6 +1096,11 @@ hipError_t run_tiles(TileArgs a, hipStream_t s) {
 
 }  // namespace
 
+bool ffn_direct_applies(const FfnProblem& p) {
+  if (p.offsets && !p.row_assign) return false;
+  return stream_ffn_applies(p) && p.k <= 2 && p.down_splits <= 1;
+}
+
 size_t ffn_ws_bytes(int rows, int F, moe_dtype dt) {
   return (size_t)rows * F * (dt == MOE_DT_F32 ? 4 : 2);
 }
@@ -1126,6 +1131,7 @@ int ffn_down_splits(int T, int d, int F, int E, int k, moe_dtype dt, bool int4) 
 
 hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid) {
   if (p.rows == 0) return hipSuccess;
+  if (p.y_direct && !ffn_direct_applies(p)) return hipErrorInvalidValue;
   if (stream_ffn_applies(p)) return launch_stream_ffn(p, s, mid);
   const bool relu = p.act == MOE_ACT_RELU;
   const int E = p.offsets ? p.E : 1;

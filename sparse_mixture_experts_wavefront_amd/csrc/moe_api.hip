@@ -361,6 +361,28 @@ moe_status check_replica(const moe_layer_desc* L, const moe_replica* R) {
   return check_experts(&q, MOE_DT_BF16, L->d_model, L->d_ff, L->act, "replica");
 }
 
+// Routing and the permutation of a layer call (one workgroup for decode
+// sizes, else the route and permute kernels); stage event 1 between them.
+hipError_t route_and_permute(const moe_layer_desc* L, const void* x, int T, float* logits,
+                             int32_t* idx, float* gates, int32_t* counts, int32_t* offsets,
+                             int32_t* row_assign, int32_t* assign_row, double* lis, void* perm_ws,
+                             unsigned flags, hipStream_t st) {
+  const int E = L->n_experts, k = L->top_k, d = L->d_model;
+  const bool given = (flags & MOE_F_LOGITS_GIVEN) != 0;
+  if (route_permute_small_applies(L->act_dtype, T, E, k)) {
+    hipError_t e = launch_route_permute_small(x, L->w_router, L->b_router, T, d, E, k, logits, idx,
+                                              gates, given, counts, offsets, row_assign,
+                                              assign_row, lis, st);
+    stage(1, st);
+    return e;
+  }
+  hipError_t e = launch_route_topk(x, L->act_dtype, L->w_router, L->b_router, T, d, E, k, logits,
+                                   idx, gates, given, st);
+  if (e != hipSuccess) return e;
+  stage(1, st);
+  return launch_permute(idx, T, E, k, counts, offsets, row_assign, assign_row, lis, perm_ws, st);
+}
+
 // The layer; with R, expert R->expert's odd-ranked assignments run on the
 // replica as slot E.
 moe_status layer_forward_impl(const moe_layer_desc* L, const moe_replica* R, const void* x, int T,
@@ -407,13 +429,36 @@ moe_status layer_forward_impl(const moe_layer_desc* L, const moe_replica* R, con
   int32_t* assign_row = (!R && aux && aux->assign_row) ? aux->assign_row : w.assign_row;
   double* lis = R ? (lis_base ? lis_base : w.lis) : ((aux && aux->lis) ? aux->lis : w.lis);
 
+  FfnProblem p{};
+  p.T = T; p.d = d; p.F = L->d_ff; p.E = E; p.k = k; p.act = L->act;
+  p.dt = L->act_dtype; p.x = x; p.w = &L->routed;
+  p.gate = gates; p.y_rows = w.y_rows; p.H = w.H; p.rows = T * k;
+  p.down_splits = w.down_splits;
+  // decode sizes: route, top-k and permutation in one workgroup.  When every
+  // output element receives at most two gate-scaled rows (weight streaming
+  // with k <= 2, no shared experts), the down pass adds them straight into y,
+  // zeroed by the gate/up grid: fp32 addition of two terms onto zero gives
+  // the same value in either order, so y stays run-to-run deterministic and
+  // the combine launch goes away
+  const bool small = !R && route_permute_small_applies(L->act_dtype, T, E, k);
+  const bool direct = !R && ydt == MOE_DT_F32 && L->n_shared == 0 && ffn_direct_applies(p);
+  p.zero_y = direct ? (float*)y : nullptr;
   stage(0, st);
-  hipError_t e = launch_route_topk(x, L->act_dtype, L->w_router, L->b_router, T, d, E, k, logits,
-                                   idx, gates, (flags & MOE_F_LOGITS_GIVEN) != 0, st);
-  if (e != hipSuccess) return hip_status(e, "route_topk");
-  stage(1, st);
-  e = launch_permute(idx, T, E, k, counts, offsets, row_assign, assign_row, lis, w.perm_ws, st);
-  if (e != hipSuccess) return hip_status(e, "permute");
+  hipError_t e;
+  if (small) {
+    e = launch_route_permute_small(x, L->w_router, L->b_router, T, d, E, k, logits, idx, gates,
+                                   (flags & MOE_F_LOGITS_GIVEN) != 0, counts, offsets, row_assign,
+                                   assign_row, lis, st);
+    if (e != hipSuccess) return hip_status(e, "route and permute");
+    stage(1, st);
+  } else {
+    e = launch_route_topk(x, L->act_dtype, L->w_router, L->b_router, T, d, E, k, logits, idx,
+                          gates, (flags & MOE_F_LOGITS_GIVEN) != 0, st);
+    if (e != hipSuccess) return hip_status(e, "route_topk");
+    stage(1, st);
+    e = launch_permute(idx, T, E, k, counts, offsets, row_assign, assign_row, lis, w.perm_ws, st);
+    if (e != hipSuccess) return hip_status(e, "permute");
+  }
   // rows of expert-major order used by the FFN and the combine
   const int32_t* f_offsets = offsets;
   const int32_t* f_row_assign = row_assign;
@@ -432,11 +477,9 @@ moe_status layer_forward_impl(const moe_layer_desc* L, const moe_replica* R, con
     f_assign_row = ar2;
   }
   stage(2, st);
-  FfnProblem p{};
-  p.T = T; p.d = d; p.F = L->d_ff; p.E = E; p.k = k; p.act = L->act;
-  p.dt = L->act_dtype; p.x = x; p.w = &L->routed; p.offsets = f_offsets;
-  p.row_assign = f_row_assign; p.gate = gates; p.y_rows = w.y_rows; p.H = w.H; p.rows = T * k;
-  p.down_splits = w.down_splits;
+  p.offsets = f_offsets;
+  p.row_assign = f_row_assign;
+  p.y_direct = direct ? (float*)y : nullptr;
   e = launch_grouped_ffn(p, st, g_stage_on ? g_stage_ev[3] : nullptr);
   if (e != hipSuccess) return hip_status(e, "grouped_ffn");
   if (R) {
@@ -466,8 +509,9 @@ moe_status layer_forward_impl(const moe_layer_desc* L, const moe_replica* R, con
     if (e != hipSuccess) return hip_status(e, "shared experts");
   }
   stage(5, st);
-  e = launch_combine(w.y_rows, f_assign_row, T, k, d, w.y_shared, y, ydt, st, w.down_splits,
-                     (size_t)T * k * d);
+  if (!direct)
+    e = launch_combine(w.y_rows, f_assign_row, T, k, d, w.y_shared, y, ydt, st, w.down_splits,
+                       (size_t)T * k * d);
   stage(6, st);
   return hip_status(e, "combine");
 }
@@ -816,12 +860,9 @@ moe_status moe_layer_forward_mwq(const moe_layer_desc* L, const moe_mwq_experts*
   int32_t* assign_row3 = (groups && groups->assign_row) ? groups->assign_row : m.assign_row3;
 
   stage(0, st);
-  hipError_t e = launch_route_topk(x, L->act_dtype, L->w_router, L->b_router, T, d, E, k, logits,
-                                   idx, gates, (flags & MOE_F_LOGITS_GIVEN) != 0, st);
-  if (e != hipSuccess) return hip_status(e, "route_topk");
-  stage(1, st);
-  e = launch_permute(idx, T, E, k, counts, offsets, row_assign, assign_row, lis, w.perm_ws, st);
-  if (e != hipSuccess) return hip_status(e, "permute");
+  hipError_t e = route_and_permute(L, x, T, logits, idx, gates, counts, offsets, row_assign,
+                                   assign_row, lis, w.perm_ws, flags, st);
+  if (e != hipSuccess) return hip_status(e, "route and permute");
   e = launch_mwq_group_ids(idx, widths, T * k, gidx, st);
   if (e != hipSuccess) return hip_status(e, "mwq group ids");
   e = launch_permute(gidx, T, 3 * E, k, counts3, offsets3, row_assign3, assign_row3, nullptr,
@@ -974,12 +1015,9 @@ moe_status moe_layer_forward_floe(const moe_layer_desc* L, const moe_floe_expert
   double* lis = (aux && aux->lis) ? aux->lis : w.lis;
 
   stage(0, st);
-  hipError_t e = launch_route_topk(x, L->act_dtype, L->w_router, L->b_router, T, d, E, k, logits,
-                                   idx, gates, (flags & MOE_F_LOGITS_GIVEN) != 0, st);
-  if (e != hipSuccess) return hip_status(e, "route_topk");
-  stage(1, st);
-  e = launch_permute(idx, T, E, k, counts, offsets, row_assign, assign_row, lis, w.perm_ws, st);
-  if (e != hipSuccess) return hip_status(e, "permute");
+  hipError_t e = route_and_permute(L, x, T, logits, idx, gates, counts, offsets, row_assign,
+                                   assign_row, lis, w.perm_ws, flags, st);
+  if (e != hipSuccess) return hip_status(e, "route and permute");
   stage(2, st);
   FloeProblem p{};
   p.T = T; p.d = d; p.F = F; p.E = E; p.k = k; p.x = x; p.w = W; p.offsets = offsets;
@@ -1017,6 +1055,45 @@ moe_status moe_layer_forward_floe(const moe_layer_desc* L, const moe_floe_expert
 
 namespace {
 
+// At most this many tokens, the automatic schedule runs the atomic experts
+// expert-centric (when w_out_rows is given): each expert with kept pairs is
+// read once, so the layer streams only the experts some token kept, against
+// every expert's weights (and a [T][N] matrix) for the dense product.
+constexpr int kAtomicEcAutoMaxT = 64;
+
+// The schedule a call runs (MOE_ATOMIC_DENSE or MOE_ATOMIC_EXPERT_CENTRIC), or
+// -1 with the error set.
+int atomic_schedule(const moe_atomic_layer_desc* L, int T, moe_status* st) {
+  *st = MOE_OK;
+  const bool ec_ok = L->w_out_rows && atomic_ec_supported(L->d_model);
+  switch (L->schedule) {
+    case MOE_ATOMIC_DENSE:
+      if (!L->w_out) { *st = fail(MOE_ERR_INVALID_ARG, "the dense schedule needs w_out"); return -1; }
+      return MOE_ATOMIC_DENSE;
+    case MOE_ATOMIC_EXPERT_CENTRIC:
+      if (!L->w_out_rows) {
+        *st = fail(MOE_ERR_INVALID_ARG, "the expert-centric schedule needs w_out_rows");
+        return -1;
+      }
+      if (!ec_ok) {
+        *st = fail(MOE_ERR_UNSUPPORTED,
+                   "the expert-centric schedule needs d_model a multiple of 512, at most 4096");
+        return -1;
+      }
+      return MOE_ATOMIC_EXPERT_CENTRIC;
+    case MOE_ATOMIC_AUTO:
+      if (ec_ok && (T <= kAtomicEcAutoMaxT || !L->w_out)) return MOE_ATOMIC_EXPERT_CENTRIC;
+      if (L->w_out) return MOE_ATOMIC_DENSE;
+      *st = L->w_out_rows ? fail(MOE_ERR_UNSUPPORTED,
+                                 "only w_out_rows given, and the expert-centric schedule needs "
+                                 "d_model a multiple of 512, at most 4096")
+                          : fail(MOE_ERR_INVALID_ARG, "w_out and w_out_rows are both NULL");
+      return -1;
+  }
+  *st = fail(MOE_ERR_INVALID_ARG, "unknown atomic schedule %d", L->schedule);
+  return -1;
+}
+
 moe_status check_atomic(const moe_atomic_layer_desc* L, int T, unsigned flags) {
   REQUIRE(L, "layer descriptor must not be NULL");
   REQUIRE((flags & ~kKnownFlags) == 0, "unknown flag bits 0x%x", flags & ~kKnownFlags);
@@ -1035,7 +1112,10 @@ moe_status check_atomic(const moe_atomic_layer_desc* L, int T, unsigned flags) {
   REQUIRE_PTR(L->w_row, "w_row");
   REQUIRE_PTR(L->w_col, "w_col");
   REQUIRE_PTR(L->w_in, "w_in");
-  REQUIRE_PTR(L->w_out, "w_out");
+  OPT_PTR(L->w_out, "w_out");
+  OPT_PTR(L->w_out_rows, "w_out_rows");
+  moe_status st;
+  if (atomic_schedule(L, T, &st) < 0) return st;
   REQUIRE(L->n_shared >= 0, "n_shared must be >= 0");
   if (L->n_shared > 0) {
     REQUIRE(L->d_ff_shared >= 8 && L->d_ff_shared % 8 == 0,
@@ -1068,13 +1148,17 @@ struct AtomicWs {
   uint32_t* bits;
   double* lis;
   void *perm_ws, *H, *Hs;
+  void* ec;  // expert-centric schedule: h [T*K] bf16, then the partial sums
   int splits, rsplit, csplit;
   size_t total;
 };
 
-AtomicWs carve_atomic(const moe_atomic_layer_desc* L, int T, void* ws) {
+// `schedule` as atomic_schedule resolved it; the two schedules carve different
+// buffers after the shared routing and grouping ones
+AtomicWs carve_atomic(const moe_atomic_layer_desc* L, int T, void* ws, int schedule) {
   const int d = L->d_model, nr = L->grid_rows, nc = L->grid_cols, K = L->top_k;
   const size_t N = (size_t)nr * nc, n = (size_t)T * K, W = N / 32;
+  const bool ec = schedule == MOE_ATOMIC_EXPERT_CENTRIC;
   Carver c(ws);
   AtomicWs w;
   w.rsplit = atomic_router_splits(T, nr, d);
@@ -1094,10 +1178,19 @@ AtomicWs carve_atomic(const moe_atomic_layer_desc* L, int T, void* ws) {
   w.assign_row = (int32_t*)c.take(n * 4);
   w.lis = (double*)c.take(8);
   w.perm_ws = c.take(grid_permute_ws_bytes(T, (int)N));
-  w.H = c.take((size_t)T * N * 2);
-  w.splits = atomic_out_splits(T, d, (int)N);
-  w.y_rows = (float*)c.take((size_t)w.splits * T * d * 4);
-  w.iota = (int32_t*)c.take((size_t)T * 4);
+  w.H = nullptr;
+  w.y_rows = nullptr;
+  w.iota = nullptr;
+  w.ec = nullptr;
+  w.splits = 0;
+  if (ec) {
+    w.ec = c.take(atomic_ec_ws_bytes(T, d, (int)N, K));
+  } else {
+    w.H = c.take((size_t)T * N * 2);
+    w.splits = atomic_out_splits(T, d, (int)N);
+    w.y_rows = (float*)c.take((size_t)w.splits * T * d * 4);
+    w.iota = (int32_t*)c.take((size_t)T * 4);
+  }
   const int Fs = L->n_shared * L->d_ff_shared;
   w.Hs = L->n_shared ? c.take((size_t)T * Fs * 2) : nullptr;
   w.y_shared = L->n_shared ? (float*)c.take((size_t)T * d * 4) : nullptr;
@@ -1109,11 +1202,19 @@ AtomicWs carve_atomic(const moe_atomic_layer_desc* L, int T, void* ws) {
 
 extern "C" {
 
+moe_status moe_atomic_schedule(const moe_atomic_layer_desc* L, int T, int* schedule) {
+  REQUIRE(schedule, "schedule must not be NULL");
+  moe_status s = check_atomic(L, T, 0);
+  if (s != MOE_OK) return s;
+  *schedule = atomic_schedule(L, T, &s);
+  return ok();
+}
+
 moe_status moe_atomic_workspace_size(const moe_atomic_layer_desc* L, int T, size_t* bytes) {
   REQUIRE(bytes, "bytes must not be NULL");
   moe_status s = check_atomic(L, T, 0);
   if (s != MOE_OK) return s;
-  *bytes = carve_atomic(L, T, nullptr).total;
+  *bytes = carve_atomic(L, T, nullptr, atomic_schedule(L, T, &s)).total;
   return ok();
 }
 
@@ -1134,7 +1235,8 @@ moe_status moe_atomic_layer_forward(const moe_atomic_layer_desc* L, const void* 
     OPT_PTR(aux->row_assign, "aux.row_assign"); OPT_PTR(aux->assign_row, "aux.assign_row");
     OPT_PTR(aux->lis, "aux.lis");
   }
-  const size_t need = carve_atomic(L, T, nullptr).total;
+  const int sched = atomic_schedule(L, T, &s);
+  const size_t need = carve_atomic(L, T, nullptr, sched).total;
   if (!ws || ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "the atomic layer needs %zu workspace bytes (got %zu)", need,
                 ws ? ws_bytes : (size_t)0);
@@ -1143,7 +1245,7 @@ moe_status moe_atomic_layer_forward(const moe_atomic_layer_desc* L, const void* 
   if (T == 0) return ok();
 
   hipStream_t st = (hipStream_t)stream;
-  AtomicWs w = carve_atomic(L, T, ws);
+  AtomicWs w = carve_atomic(L, T, ws, sched);
   const int d = L->d_model, nr = L->grid_rows, nc = L->grid_cols, K = L->top_k;
   const int N = nr * nc;
   float* pr = (aux && aux->logp_row) ? aux->logp_row : w.pr;
@@ -1172,13 +1274,27 @@ moe_status moe_atomic_layer_forward(const moe_atomic_layer_desc* L, const void* 
                           w.perm_ws, st);
   if (e != hipSuccess) return hip_status(e, "grid permutation");
   stage(2, st);
-  e = launch_atomic_in(X, T, (const u16*)L->w_in, N, d, w.bits, w.bitpre, idx, gates, K, w.ukept,
-                       (u16*)w.H, st);
-  if (e != hipSuccess) return hip_status(e, "atomic input GEMM");
-  stage(3, st);
-  e = launch_gemm_bt((const u16*)w.H, N, T, (const u16*)L->w_out, d, N, w.y_rows, w.splits,
-                     (size_t)T * d, st);
-  if (e != hipSuccess) return hip_status(e, "atomic output GEMM");
+  const bool ec = sched == MOE_ATOMIC_EXPERT_CENTRIC;
+  u16* hrow = ec ? (u16*)w.ec : nullptr;
+  float* ypart = ec ? (float*)((char*)w.ec + align_up((size_t)T * K * 2)) : nullptr;
+  if (ec) {
+    // expert-centric: each expert with kept pairs reads its w_in / w_out once
+    e = launch_atomic_ec_in(X, T, d, (const u16*)L->w_in, N, offsets, row_assign, gates, K, hrow,
+                            st);
+    if (e != hipSuccess) return hip_status(e, "atomic expert-centric input");
+    stage(3, st);
+    e = launch_atomic_ec_out(hrow, offsets, row_assign, K, (const u16*)L->w_out_rows, N, d, T,
+                             ypart, st);
+    if (e != hipSuccess) return hip_status(e, "atomic expert-centric output");
+  } else {
+    e = launch_atomic_in(X, T, (const u16*)L->w_in, N, d, w.bits, w.bitpre, idx, gates, K,
+                         w.ukept, (u16*)w.H, st);
+    if (e != hipSuccess) return hip_status(e, "atomic input GEMM");
+    stage(3, st);
+    e = launch_gemm_bt((const u16*)w.H, N, T, (const u16*)L->w_out, d, N, w.y_rows, w.splits,
+                       (size_t)T * d, st);
+    if (e != hipSuccess) return hip_status(e, "atomic output GEMM");
+  }
   stage(4, st);
   if (L->n_shared > 0) {
     FfnProblem q{};
@@ -1190,10 +1306,14 @@ moe_status moe_atomic_layer_forward(const moe_atomic_layer_desc* L, const void* 
     if (e != hipSuccess) return hip_status(e, "shared experts");
   }
   stage(5, st);
-  e = launch_iota(w.iota, T, st);
-  if (e == hipSuccess)
-    e = launch_combine(w.y_rows, w.iota, T, 1, d, w.y_shared, y, ydt, st, w.splits,
-                       (size_t)T * d);
+  if (ec) {
+    e = launch_atomic_ec_reduce(ypart, T, d, N, w.y_shared, y, ydt, st);
+  } else {
+    e = launch_iota(w.iota, T, st);
+    if (e == hipSuccess)
+      e = launch_combine(w.y_rows, w.iota, T, 1, d, w.y_shared, y, ydt, st, w.splits,
+                         (size_t)T * d);
+  }
   stage(6, st);
   return hip_status(e, "combine");
 }

@@ -57,6 +57,15 @@ hipError_t launch_route_topk(const void* x, moe_dtype xdt, const void* w_router,
                              const float* b_router, int T, int d, int E, int k, float* logits,
                              int32_t* idx, float* gate, bool logits_given, hipStream_t s);
 
+// Small batches (bf16, T <= 64, ceil(T/16) * ceil(E/16) <= 4): route, top-k
+// and the permutation (counts, offsets, rows, LIS) in one workgroup.
+bool route_permute_small_applies(moe_dtype xdt, int T, int E, int k);
+hipError_t launch_route_permute_small(const void* x, const void* w_router, const float* b_router,
+                                      int T, int d, int E, int k, float* logits, int32_t* idx,
+                                      float* gate, bool logits_given, int32_t* counts,
+                                      int32_t* offsets, int32_t* row_assign, int32_t* assign_row,
+                                      double* lis, hipStream_t s);
+
 size_t permute_ws_bytes(int T, int E, int k);
 hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* counts,
                           int32_t* offsets, int32_t* row_assign, int32_t* assign_row,
@@ -87,6 +96,13 @@ struct FfnProblem {
   int rows;                      // T * k
   int down_splits;               // K slices of the down pass (0 or 1: none); slice s
                                  // writes its partial sums to y_rows + s * rows * d
+  float* y_direct;               // weight-streaming path only: if not NULL, the down
+                                 // pass adds each gate-scaled row into y_direct[token]
+                                 // [T][d] fp32 (zeroed by the caller) instead of
+                                 // writing y_rows: the combine, fused
+  float* zero_y;                 // weight-streaming path: if not NULL, the gate/up grid
+                                 // zeroes zero_y[0 .. T*d) first (the y that y_direct
+                                 // accumulates into)
 };
 size_t ffn_ws_bytes(int rows, int F, moe_dtype dt);
 // K slices for the down pass of a layer-sized problem: more, smaller tiles when
@@ -94,6 +110,12 @@ size_t ffn_ws_bytes(int rows, int F, moe_dtype dt);
 // the shapes (the workspace size depends on it).
 int ffn_down_splits(int T, int d, int F, int E, int k, moe_dtype dt, bool int4);
 hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid = nullptr);
+// Whether the down pass can add its rows straight into y (FfnProblem::y_direct)
+// with every y element receiving at most two of them: the weight-streaming
+// path with k <= 2 (one K slice).  (The tiled pass with k = 1 could do the same
+// with its two K slices; measured on the Switch-shaped layer, its fp32 atomics
+// cost more than the combine launch they replace, so it keeps the combine.)
+bool ffn_direct_applies(const FfnProblem& p);
 
 // Weight-streaming variant for few rows per expert (decode); same contract as
 // launch_grouped_ffn.
@@ -180,6 +202,28 @@ hipError_t launch_grid_permute(const uint32_t* bits, const int32_t* bitpre, int 
                                int32_t* counts, int32_t* offsets, int32_t* row_assign,
                                int32_t* assign_row, double* lis, void* ws, hipStream_t s);
 hipError_t launch_iota(int32_t* out, int n, hipStream_t s);
+
+// Expert-centric execution of atomic experts (atomic_ec.hip).  Rows of expert
+// n are offsets[n]..offsets[n+1]-1 (tokens ascending), row r is the kept pair
+// a = row_assign[r] (token a / K, gate gates[a]).
+// d a multiple of 512, at most 4096.
+bool atomic_ec_supported(int d);
+// expert ranges of the output side (partial sums [ranges][T][d] fp32)
+int atomic_ec_ranges(int T, int d, int N);
+// workspace: h [T*K] bf16 (256-byte aligned end), then the partial sums
+size_t atomic_ec_ws_bytes(int T, int d, int N, int K);
+// h[r] = bf16(gates[a] * silu(x[a / K] . w_in[n])) for every row r of every expert
+hipError_t launch_atomic_ec_in(const u16* x, int T, int d, const u16* w_in, int N,
+                               const int32_t* offsets, const int32_t* row_assign,
+                               const float* gates, int K, u16* h, hipStream_t s);
+// ypart[p][t] = sum over the experts n of range p, rows r of n with token t, of
+// h[r] * w_out_rows[n]   (w_out_rows [N][d] bf16)
+hipError_t launch_atomic_ec_out(const u16* h, const int32_t* offsets, const int32_t* row_assign,
+                                int K, const u16* w_out_rows, int N, int d, int T, float* ypart,
+                                hipStream_t s);
+// y[t] = sum over ranges in order of ypart[p][t] (+ y_shared[t]), in ydt
+hipError_t launch_atomic_ec_reduce(const float* ypart, int T, int d, int N,
+                                   const float* y_shared, void* y, moe_dtype ydt, hipStream_t s);
 
 // y[t] = sum over slots j, then over K slices s, of y_rows[s * split_stride +
 // assign_row[t*k+j] * d], plus y_shared[t]; fixed order, so deterministic.

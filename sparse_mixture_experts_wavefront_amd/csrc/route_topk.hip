@@ -162,7 +162,219 @@ __global__ __launch_bounds__(64 * NW) void route_topk_kernel(const void* __restr
   }
 }
 
+// ---- small batches: route, top-k and permutation in one workgroup ----------
+// For a decode step the three are latency, not work: one workgroup of 16 waves
+// computes the logits of up to 16*G tokens (the waves split d as above, each
+// covering all G token groups), selects each token's top-k, then builds the
+// stable expert-major permutation of the T*k <= 1024 assignments at once:
+// per-expert counts with LDS atomics, one wave scans them (offsets, LIS), and
+// an assignment's row is its expert's offset + the count of equal experts in
+// earlier waves + its rank among equal experts in its own wave (a match built
+// from log2(64) ballots).  Ranks are computed, never raced, so the order is the
+// stable one.
+
+__device__ __forceinline__ unsigned long long lanes_below() {
+  const int lane = threadIdx.x & 63;
+  return lane ? ((~0ull) >> (64 - lane)) : 0ull;
+}
+
+// lanes of this wave holding the same valid expert id as this lane
+__device__ __forceinline__ unsigned long long same_expert(int e, bool valid) {
+  unsigned long long m = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < 6; ++bit) {
+    const bool b = (e >> bit) & 1;
+    const unsigned long long bal = __ballot(valid && b);
+    m &= b ? bal : ~bal;
+  }
+  return m;
+}
+
+template <int EB, int G>
+__global__ __launch_bounds__(1024) void route_permute_small_kernel(
+    const u16* __restrict__ x, const u16* __restrict__ w, const float* __restrict__ bias, int T,
+    int d, int E, int k, int seg, float* __restrict__ logits, int32_t* __restrict__ idx,
+    float* __restrict__ gate, int logits_given, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_assign,
+    int32_t* __restrict__ assign_row, double* __restrict__ lis) {
+  constexpr int NW = 16, TG = 16 * G;
+  __shared__ float lt[TG][kMaxExperts + 1];
+  __shared__ f32x4 part[NW][G][EB][64];
+  __shared__ int s_idx[TG * kMaxTopK];
+  __shared__ int cnt[kMaxExperts], ebase[kMaxExperts];
+  __shared__ int wc[NW][kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  if (!logits_given) {
+    const int r = lane & 15, g = lane >> 4;
+    const u16* xr[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) xr[gi] = x + (size_t)min(gi * 16 + r, T - 1) * d + g * 8;
+    const u16* wr[EB];
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb) wr[eb] = w + (size_t)min(eb * 16 + r, E - 1) * d + g * 8;
+    f32x4 acc[G][EB];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+      for (int eb = 0; eb < EB; ++eb) acc[gi][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // all of a wave's K steps are independent: unrolled, their loads are in flight together
+#pragma unroll 8
+    for (int k0 = wv_id * 32; k0 < d; k0 += 32 * NW) {
+      const bool in = (k0 + g * 8) < d;  // d % 8 == 0: an 8-chunk is all in or all out
+      u32x4 av[G], bv[EB];
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) av[gi] = in ? *(const u32x4*)(xr[gi] + k0) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int eb = 0; eb < EB; ++eb) bv[eb] = in ? *(const u32x4*)(wr[eb] + k0) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb)
+          acc[gi][eb] = mfma16(as_bf16x8(av[gi]), as_bf16x8(bv[eb]), acc[gi][eb]);
+    }
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+      for (int eb = 0; eb < EB; ++eb) part[wv_id][gi][eb][lane] = acc[gi][eb];
+    __syncthreads();
+    // wave partials summed in wave order; C layout of the 16x16 MFMA: lane holds
+    // token rows 4*(lane/16)+i of its group, expert column lane%16
+    for (int q = tid; q < G * EB * 256; q += 64 * NW) {
+      const int gi = q / (EB * 256), eb = (q / 256) % EB, ln = (q >> 2) & 63, i = q & 3;
+      float sum = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) sum += part[ww][gi][eb][ln][i];
+      const int tr = gi * 16 + 4 * (ln >> 4) + i, e = eb * 16 + (ln & 15);
+      if (e < E) lt[tr][e] = sum + (bias ? bias[e] : 0.0f);
+    }
+    __syncthreads();
+    for (int q = tid; q < T * E; q += 64 * NW) logits[q] = lt[q / E][q % E];
+  } else {
+    for (int q = tid; q < T * E; q += 64 * NW) lt[q / E][q % E] = logits[q];
+  }
+  __syncthreads();
+
+  // ---- exact top-k, one token per segment of `seg` lanes (as route_topk_kernel)
+  const int per = 64 / seg;
+  const int ts = lane / seg, e = lane % seg;
+  for (int b0 = wv_id * per; b0 < TG; b0 += per * NW) {
+    const int t = b0 + ts;
+    const bool live = (ts < per) && (t < T);
+    unsigned long long key = 0ull;
+    if (live && e < E)
+      key = ((unsigned long long)order_key(lt[t][e]) << 32) | (uint32_t)(seg - 1 - e);
+    unsigned long long top[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k) {
+        unsigned long long m = key;
+        for (int o = 1; o < seg; o <<= 1) {
+          unsigned long long v = shfl_xor_u64(m, o);
+          m = v > m ? v : m;
+        }
+        top[j] = m;
+        const int win = seg - 1 - (int)(uint32_t)(m & 0xffffffffull);
+        if (e == win) key = 0ull;
+      }
+    }
+    if (live && e < k) {
+      const float lmax = order_key_inv((uint32_t)(top[0] >> 32));
+      float sum = 0.0f, mine = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        if (j < k) {
+          const float wj = expf(order_key_inv((uint32_t)(top[j] >> 32)) - lmax);
+          sum += wj;
+          if (j == e) mine = wj;
+        }
+      }
+      unsigned long long me = top[0];
+#pragma unroll
+      for (int j = 1; j < kMaxTopK; ++j)
+        if (j == e) me = top[j];
+      const int ex = seg - 1 - (int)(uint32_t)(me & 0xffffffffull);
+      idx[(size_t)t * k + e] = ex;
+      s_idx[t * k + e] = ex;
+      if (gate) gate[(size_t)t * k + e] = (k == 1) ? 1.0f : mine / sum;
+    }
+  }
+  if (tid < kMaxExperts) cnt[tid] = 0;
+  __syncthreads();
+
+  // ---- stable expert-major permutation of the n = T*k <= 1024 assignments
+  const int n = T * k;
+  const bool valid = tid < n;
+  const int ea = valid ? s_idx[tid] : 0;
+  if (valid) atomicAdd(&cnt[ea], 1);
+  __syncthreads();
+  if (tid < 64) {  // wave 0: exclusive scan and max over the experts
+    const int c = (tid < E) ? cnt[tid] : 0;
+    int incl = c;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (tid >= o) incl += v;
+    }
+    int mx = c;
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o, 64));
+    if (tid < E) {
+      counts[tid] = c;
+      offsets[tid] = incl - c;
+      ebase[tid] = incl - c;
+    }
+    if (tid == E - 1) offsets[E] = incl;
+    if (tid == 0 && lis)
+      *lis = (double)((long long)E * mx) / (double)((long long)T * k);
+  }
+  const unsigned long long m = same_expert(ea, valid);
+  const int rank = __popcll(m & lanes_below());
+  wc[wv_id][lane] = 0;
+  __syncthreads();
+  if (valid && rank == 0) wc[wv_id][ea] = __popcll(m);
+  __syncthreads();
+  if (valid) {
+    int row = ebase[ea] + rank;
+    for (int ww = 0; ww < wv_id; ++ww) row += wc[ww][ea];
+    if (row_assign) row_assign[row] = tid;
+    if (assign_row) assign_row[tid] = row;
+  }
+}
+
 }  // namespace
+
+bool route_permute_small_applies(moe_dtype xdt, int T, int E, int k) {
+  const int G = (T + 15) / 16, EB = (E + 15) / 16;
+  return xdt == MOE_DT_BF16 && T >= 1 && T <= 64 && G * EB <= 4 && T * k <= 1024;
+}
+
+hipError_t launch_route_permute_small(const void* x, const void* w_router, const float* b_router,
+                                      int T, int d, int E, int k, float* logits, int32_t* idx,
+                                      float* gate, bool logits_given, int32_t* counts,
+                                      int32_t* offsets, int32_t* row_assign, int32_t* assign_row,
+                                      double* lis, hipStream_t s) {
+  if (!route_permute_small_applies(MOE_DT_BF16, T, E, k)) return hipErrorInvalidValue;
+  int seg = 1;
+  while (seg < E) seg <<= 1;
+  const int G = (T + 15) / 16, EB = (E + 15) / 16;
+  const int lg = logits_given ? 1 : 0;
+  const u16* X = (const u16*)x;
+  const u16* W = (const u16*)w_router;
+#define MOE_RPS(EBV, GV)                                                                         hipLaunchKernelGGL((route_permute_small_kernel<EBV, GV>), dim3(1), dim3(1024), 0, s, X, W,                         b_router, T, d, E, k, seg, logits, idx, gate, lg, counts, offsets,                              row_assign, assign_row, lis)
+  switch (EB * 8 + G) {
+    case 1 * 8 + 1: MOE_RPS(1, 1); break;
+    case 1 * 8 + 2: MOE_RPS(1, 2); break;
+    case 1 * 8 + 3: MOE_RPS(1, 3); break;
+    case 1 * 8 + 4: MOE_RPS(1, 4); break;
+    case 2 * 8 + 1: MOE_RPS(2, 1); break;
+    case 2 * 8 + 2: MOE_RPS(2, 2); break;
+    case 3 * 8 + 1: MOE_RPS(3, 1); break;
+    case 4 * 8 + 1: MOE_RPS(4, 1); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_RPS
+  return hipGetLastError();
+}
 
 hipError_t launch_route_topk(const void* x, moe_dtype xdt, const void* w_router,
                              const float* b_router, int T, int d, int E, int k, float* logits,

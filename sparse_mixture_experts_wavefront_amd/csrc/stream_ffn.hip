@@ -64,11 +64,24 @@ struct StreamArgs {
   int rows;
   u16* H;                  // gate/up output [rows][N]
   float* Y;                // down output [rows][N]
+  float* Yacc;             // down: if not NULL, row r is added into Yacc[gate_map[r] / k][N]
   const int32_t* gate_map;
   const float* gate;
   int nblk_per_expert;
   uint32_t xbytes;         // bytes of X (register-direct kernel: buffer size)
+  int sz_vec;              // INT4: scales / zero points 16-byte aligned, K % 1024 == 0 and
+                           // R*K/1024 <= 2048: staged with 16-byte loads
+  f32x4* zero;             // gate/up: if not NULL, the grid zeroes zero[0 .. zero_n4) first
+  size_t zero_n4;          // (the output the down pass then accumulates into)
 };
+
+// the whole grid zeroes p.zero (spread over all blocks, before any exits)
+__device__ __forceinline__ void grid_zero(const StreamArgs& p) {
+  if (!p.zero) return;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < p.zero_n4;
+       i += (size_t)gridDim.x * blockDim.x)
+    p.zero[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
 
 // fp32(q) - z is exact for all q in 0..15 when z == 0 or |z| >= 2^-10 (finite).
 __device__ __forceinline__ bool zero_point_fma_exact(u16 z) {
@@ -139,6 +152,7 @@ __global__ __launch_bounds__(256) void stream_ffn_kernel(StreamArgs p) {
 
   __shared__ __align__(16) unsigned char sW0[CBYTES], sW1[CBYTES];
 
+  grid_zero(p);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int e = blockIdx.x / p.nblk_per_expert;
@@ -377,7 +391,11 @@ __global__ __launch_bounds__(256) void stream_ffn_kernel(StreamArgs p) {
         } else if constexpr (MODE == kSModeRelu) {
           p.H[orow * p.N + n0 + col] = f32_to_bf16(fmaxf(part(col), 0.0f));
         } else {
-          p.Y[orow * p.N + n0 + col] = gsm[mb * 16 + m] * part(col);
+          const float v = gsm[mb * 16 + m] * part(col);
+          if (p.Yacc)
+            unsafeAtomicAdd(p.Yacc + (size_t)(p.gate_map[orow] / p.k) * p.N + n0 + col, v);
+          else
+            p.Y[orow * p.N + n0 + col] = v;
         }
       }
     }
@@ -408,7 +426,8 @@ constexpr int stream_reg_rows(int mode, bool int4) {
 }
 
 template <int MODE, bool INT4, int MB, int D>
-__global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(INT4 ? 2 : 1)))
+void stream_reg_kernel(StreamArgs p) {
   // weight rows per block: gate/up 32 gate + 32 up rows (INT4: 64 + 64); down
   // and ReLU W_in 32 rows (INT4: 64).  More rows let each token fragment feed
   // more MFMAs, fewer token-operand loads per weight byte; the INT4 weight
@@ -426,6 +445,7 @@ __global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
   float* red = (float*)smem;                                 // [4][RB][64][4]
   uint32_t* sz = (uint32_t*)(smem + 4 * RB * 64 * 16);       // [R][G+1]: s | z << 16
 
+  grid_zero(p);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int e = blockIdx.x / p.nblk_per_expert;
@@ -477,15 +497,50 @@ __global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
   bool fused_ok = true;
   if constexpr (INT4) {
     bool ok = true;
-    for (int i = tid; i < R * G; i += 256) {
-      const int r = i / G, gi = i - r * G;
-      int n;
-      bool second;
-      wsel(r, n, second);
-      const size_t o = ((size_t)e * p.N + n) * G + gi;
-      const u16 s = (second ? p.s1 : p.s0)[o], z = (second ? p.z1 : p.z0)[o];
-      ok = ok && zero_point_fma_exact(z);
-      sz[r * GP + gi] = (uint32_t)s | ((uint32_t)z << 16);
+    if (p.sz_vec) {
+      // 8 groups (16 bytes of scales, 16 of zero points) per load; a thread's
+      // loads are issued together, so the staging costs one memory round trip
+      const int G8 = G >> 3;
+      constexpr int kMaxPer = 8;  // R * G / 8 / 256 <= 8 for K <= 16384
+      u32x4 sv[kMaxPer], zv[kMaxPer];
+#pragma unroll
+      for (int q = 0; q < kMaxPer; ++q) {
+        const int i = tid + q * 256;
+        if (i < R * G8) {
+          const int r = i / G8, j = i - r * G8;
+          int n;
+          bool second;
+          wsel(r, n, second);
+          const size_t o = ((size_t)e * p.N + n) * G + j * 8;
+          sv[q] = *(const u32x4*)((second ? p.s1 : p.s0) + o);
+          zv[q] = *(const u32x4*)((second ? p.z1 : p.z0) + o);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kMaxPer; ++q) {
+        const int i = tid + q * 256;
+        if (i < R * G8) {
+          const int r = i / G8, j = i - r * G8;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const uint32_t s2 = sv[q][h], z2 = zv[q][h];
+            ok = ok && zero_point_fma_exact((u16)(z2 & 0xffffu)) && zero_point_fma_exact((u16)(z2 >> 16));
+            sz[r * GP + j * 8 + 2 * h] = (s2 & 0xffffu) | (z2 << 16);
+            sz[r * GP + j * 8 + 2 * h + 1] = (s2 >> 16) | (z2 & 0xffff0000u);
+          }
+        }
+      }
+    } else {
+      for (int i = tid; i < R * G; i += 256) {
+        const int r = i / G, gi = i - r * G;
+        int n;
+        bool second;
+        wsel(r, n, second);
+        const size_t o = ((size_t)e * p.N + n) * G + gi;
+        const u16 s = (second ? p.s1 : p.s0)[o], z = (second ? p.z1 : p.z0)[o];
+        ok = ok && zero_point_fma_exact(z);
+        sz[r * GP + gi] = (uint32_t)s | ((uint32_t)z << 16);
+      }
     }
     // the fused decode when every zero point of the block allows it (the usual
     // case), else the two-operation form; uniform over the block
@@ -625,7 +680,11 @@ __global__ __launch_bounds__(256) void stream_reg_kernel(StreamArgs p) {
           } else if constexpr (MODE == kSModeRelu) {
             p.H[orow * p.N + n0 + col] = f32_to_bf16(fmaxf(part(col), 0.0f));
           } else {
-            p.Y[orow * p.N + n0 + col] = gsm[mb * 16 + m] * part(col);
+            const float v = gsm[mb * 16 + m] * part(col);
+            if (p.Yacc)
+              unsafeAtomicAdd(p.Yacc + (size_t)(p.gate_map[orow] / p.k) * p.N + n0 + col, v);
+            else
+              p.Y[orow * p.N + n0 + col] = v;
           }
         }
       }
@@ -653,6 +712,13 @@ hipError_t launch_reg_mode(const StreamArgs& a0, int E, int mb, hipStream_t s) {
   constexpr int NOUT = MODE == kSModeGateUp ? stream_reg_rows(MODE, INT4) / 2 : stream_reg_rows(MODE, INT4);
   StreamArgs a = a0;
   a.nblk_per_expert = (a.N + NOUT - 1) / NOUT;
+  a.sz_vec = 0;
+  if constexpr (INT4) {
+    constexpr int R = stream_reg_rows(MODE, INT4);
+    auto al16 = [](const void* q) { return q == nullptr || ((uintptr_t)q % 16) == 0; };
+    a.sz_vec = (a.K % 1024 == 0) && ((long long)R * (a.K / 1024) <= 2048) && al16(a.s0) &&
+               al16(a.z0) && (MODE != kSModeGateUp || (al16(a.s1) && al16(a.z1)));
+  }
   const dim3 grid((unsigned)(E * a.nblk_per_expert)), block(256);
   const size_t lds = stream_reg_lds_bytes<MODE, INT4>(a.K);
   // two register sets in flight: deeper prefetch measured no faster here
@@ -703,6 +769,8 @@ hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid)
   a.N = p.F;
   a.K = p.d;
   a.H = (u16*)p.H;
+  a.zero = (f32x4*)p.zero_y;
+  a.zero_n4 = p.zero_y ? (size_t)p.T * p.d / 4 : 0;
   a.nblk_per_expert = (p.F + 31) / 32;
   // the register-direct kernel addresses the token matrix (x, then H) and a
   // weight strip of up to 64 rows with 32-bit buffer offsets
@@ -746,6 +814,7 @@ hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid)
   b.N = p.d;
   b.K = p.F;
   b.Y = p.y_rows;
+  b.Yacc = p.y_direct;
   b.xbytes = (uint32_t)hb;
   b.gate_map = p.row_assign;
   b.gate = p.gate;

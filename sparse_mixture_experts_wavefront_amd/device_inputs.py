@@ -76,8 +76,10 @@ def floe_to_device(wl, device="cuda"):
                        torch.from_numpy(np.ascontiguousarray(wl.floe_thr)).to(device))
 
 
-def atomic_to_device(wl, device="cuda"):
-    """(AtomicLayer, x) for an atomic-expert ``workloads.Workload``."""
+def atomic_to_device(wl, device="cuda", schedule="auto", layouts=("dense", "rows")):
+    """(AtomicLayer, x) for an atomic-expert ``workloads.Workload``; ``layouts``
+    picks which copies of the output vectors go to the device: "dense" (w_out
+    [d][N]) and/or "rows" (w_out_rows [N][d])."""
     cfg = wl.cfg
     shared = None
     if cfg.n_shared:
@@ -85,5 +87,8 @@ def atomic_to_device(wl, device="cuda"):
                                w_down=_t(wl.ws_down, device, True))
     layer = AtomicLayer(cfg.d, cfg.nr, cfg.nc, cfg.k, _t(wl.w_router, device, True),
                         _t(wl.w_col, device, True), _t(wl.w_in, device, True),
-                        _t(wl.w_out_t, device, True), cfg.n_shared, cfg.F_shared, shared)
+                        _t(wl.w_out_t, device, True) if "dense" in layouts else None,
+                        cfg.n_shared, cfg.F_shared, shared,
+                        w_out_rows=_t(wl.w_out_rows, device, True) if "rows" in layouts else None,
+                        schedule=schedule)
     return layer, _t(wl.x, device, True)

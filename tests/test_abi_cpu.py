@@ -432,3 +432,50 @@ def test_atomic_validation_and_workspace(L, B):
     bad = desc()
     bad.w_in = None
     assert fwd(bad) == B.MOE_ERR_INVALID_ARG
+
+
+def test_atomic_schedule_resolution(L, B):
+    """Which schedule a call runs, and what each schedule needs, all on the host."""
+    VO = B.MOE_F_VALIDATE_ONLY
+
+    def desc(d=512, dense=True, rows=True, schedule=0):
+        Ld = B.AtomicLayerDesc()
+        Ld.d_model, Ld.grid_rows, Ld.grid_cols, Ld.top_k = d, 8, 32, 16
+        Ld.w_row, Ld.w_col, Ld.w_in = _addr(50), _addr(51), _addr(52)
+        Ld.w_out = _addr(53) if dense else None
+        Ld.w_out_rows = _addr(54) if rows else None
+        Ld.schedule = schedule
+        return Ld
+
+    def sched(Ld, T):
+        v = C.c_int(-1)
+        r = L.moe_atomic_schedule(C.byref(Ld), T, C.byref(v))
+        return r if r != B.MOE_OK else ("ec" if v.value == B.MOE_ATOMIC_EXPERT_CENTRIC else
+                                        "dense" if v.value == B.MOE_ATOMIC_DENSE else v.value)
+    assert sched(desc(), 1) == "ec"
+    assert sched(desc(), 64) == "ec"
+    assert sched(desc(), 65) == "dense"
+    assert sched(desc(dense=False), 4096) == "ec"          # only the expert-major copy
+    assert sched(desc(rows=False), 1) == "dense"
+    assert sched(desc(d=256), 1) == "dense"                # d % 512: expert-centric not built
+    assert sched(desc(d=256, dense=False), 1) == B.MOE_ERR_UNSUPPORTED
+    assert sched(desc(dense=False, rows=False), 1) == B.MOE_ERR_INVALID_ARG
+    assert sched(desc(schedule=B.MOE_ATOMIC_DENSE), 1) == "dense"
+    assert sched(desc(schedule=B.MOE_ATOMIC_EXPERT_CENTRIC), 4096) == "ec"
+    assert sched(desc(rows=False, schedule=B.MOE_ATOMIC_EXPERT_CENTRIC), 1) == \
+        B.MOE_ERR_INVALID_ARG
+    assert sched(desc(dense=False, schedule=B.MOE_ATOMIC_DENSE), 1) == B.MOE_ERR_INVALID_ARG
+    assert sched(desc(d=4608, schedule=B.MOE_ATOMIC_EXPERT_CENTRIC), 1) == B.MOE_ERR_UNSUPPORTED
+    assert sched(desc(schedule=7), 1) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_atomic_schedule(C.byref(desc()), 1, None) == B.MOE_ERR_INVALID_ARG
+    # the workspace follows the schedule (each is checked against its own size)
+    n_ec, n_dense = C.c_size_t(0), C.c_size_t(0)
+    assert L.moe_atomic_workspace_size(C.byref(desc(schedule=2)), 64, C.byref(n_ec)) == B.MOE_OK
+    assert L.moe_atomic_workspace_size(C.byref(desc(schedule=1)), 64, C.byref(n_dense)) == B.MOE_OK
+    assert n_ec.value != n_dense.value
+    ws = C.c_void_p(FAKE * 16)
+    for Ld, n in ((desc(schedule=2), n_ec.value), (desc(schedule=1), n_dense.value)):
+        assert L.moe_atomic_layer_forward(C.byref(Ld), _addr(1), 64, _addr(2), 0, None, ws, n,
+                                          VO, None) == B.MOE_OK
+        assert L.moe_atomic_layer_forward(C.byref(Ld), _addr(1), 64, _addr(2), 0, None, ws,
+                                          n - 1, VO, None) == B.MOE_ERR_WORKSPACE

@@ -36,10 +36,10 @@ def _workload(**over):
     return make_workload(get_config("omni_atomic", **over))
 
 
-def run_atomic(wl):
+def run_atomic(wl, schedule="auto", layouts=("dense", "rows")):
     import sparse_mixture_experts_wavefront_amd as moe
     from sparse_mixture_experts_wavefront_amd.device_inputs import atomic_to_device
-    layer, x = atomic_to_device(wl)
+    layer, x = atomic_to_device(wl, schedule=schedule, layouts=layouts)
     y, aux = moe.atomic_layer_forward(layer, x)
     torch.cuda.synchronize()
     g = {n: t.cpu().numpy() for n, t in aux.items()}
@@ -50,8 +50,9 @@ def run_atomic(wl):
     return g
 
 
-def check_atomic(wl, g, tokens=None, full_routing=True):
-    ref = oracle.atomic_layer_forward(wl, pr=g["logp_row"], pc=g["logp_col"], tokens=tokens)
+def check_atomic(wl, g, tokens=None, full_routing=True, ref=None):
+    if ref is None:
+        ref = oracle.atomic_layer_forward(wl, pr=g["logp_row"], pc=g["logp_col"], tokens=tokens)
     for a, b in (("logp_row", "pr"), ("logp_col", "pc")):
         dlp = np.abs(g[a].astype(np.float64) - ref[b].astype(np.float64)).max()
         assert dlp <= 1e-4, (a, dlp)
@@ -91,8 +92,48 @@ SMALL = {
 def test_atomic_layer_parity_small(case):
     _say("atomic layer %s %s" % (case, SMALL[case]))
     wl = _workload(**SMALL[case])
-    g = run_atomic(wl)
+    g = run_atomic(wl, schedule="dense")
     check_atomic(wl, g)
+
+
+# expert-centric schedule: d a multiple of 512 (one to eight 512-wide chunks per
+# lane); T > 16 exercises the token chunks of the output side, T = 1 and top-1
+# leave most experts without rows
+EC_SMALL = {
+    "ec_small": dict(T=48, d=512, nr=8, nc=32, E=256, k=16, F_shared=128),
+    "ec_one_token": dict(T=1, d=512, nr=8, nc=32, E=256, k=16, F_shared=128),
+    "ec_top1": dict(T=40, d=1024, nr=8, nc=32, E=256, k=1, n_shared=0),
+    "ec_all_cells": dict(T=20, d=512, nr=4, nc=32, E=128, k=128, F_shared=128),
+    "ec_ragged": dict(T=300, d=1024, nr=20, nc=64, E=1280, k=100, F_shared=256),
+    "ec_wide": dict(T=17, d=4096, nr=8, nc=32, E=256, k=24, F_shared=128),
+    "ec_sixteen": dict(T=16, d=2048, nr=12, nc=32, E=384, k=40, F_shared=128),
+}
+
+
+@pytest.mark.parametrize("case", list(EC_SMALL))
+def test_atomic_layer_expert_centric_small(case):
+    _say("atomic layer expert-centric %s %s" % (case, EC_SMALL[case]))
+    wl = _workload(**EC_SMALL[case])
+    g = run_atomic(wl, schedule="expert_centric", layouts=("rows",))
+    ref = oracle.atomic_layer_forward(wl, pr=g["logp_row"], pc=g["logp_col"])
+    check_atomic(wl, g, ref=ref)
+    # the dense schedule on the same inputs: the same routing, y within tolerance
+    gd = run_atomic(wl, schedule="dense", layouts=("dense",))
+    for n in ("idx", "counts", "offsets", "row_assign", "assign_row"):
+        assert np.array_equal(gd[n], g[n]), n
+    check_atomic(wl, gd, ref=ref)
+
+
+def test_atomic_auto_schedule_picks_by_tokens():
+    """auto: expert-centric up to 64 tokens when w_out_rows is given, dense above;
+    either layout alone forces its schedule; the results agree with the oracle."""
+    _say("atomic auto schedule")
+    base = dict(d=512, nr=8, nc=32, E=256, k=16, F_shared=128)
+    for T, layouts in ((64, ("dense", "rows")), (65, ("dense", "rows")), (65, ("rows",)),
+                       (30, ("dense",))):
+        wl = _workload(T=T, **base)
+        g = run_atomic(wl, schedule="auto", layouts=layouts)
+        check_atomic(wl, g)
 
 
 def test_atomic_layer_tied_scores():
@@ -124,3 +165,18 @@ def test_atomic_layer_full_size():
     rel = np.linalg.norm(gy - ry) / np.linalg.norm(ry)
     print("  LIS %.3f; y max-abs %.3e rel-L2 %.3e" % (g["lis"], d.max(), rel), flush=True)
     assert d.max() <= 2e-2 and rel <= 1e-2
+    # the expert-centric schedule at the same size (the bench times both)
+    _say("atomic layer full-size omni_atomic, expert-centric")
+    ge = run_atomic(wl, schedule="expert_centric", layouts=("rows",))
+    for n in ("idx", "counts", "offsets", "row_assign", "assign_row"):
+        assert np.array_equal(ge[n], g[n]), n
+    check_atomic(wl, ge, ref=ref)
+
+
+def test_atomic_layer_full_width_decode():
+    """The full grid (102,400 experts, top-4096, d 2048) at 16 tokens, where the
+    automatic schedule is expert-centric; every token checked."""
+    _say("atomic layer full width, 16 tokens (expert-centric)")
+    wl = make_workload(get_config("omni_atomic", T=16))
+    g = run_atomic(wl, schedule="auto", layouts=("rows",))
+    check_atomic(wl, g)

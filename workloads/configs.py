@@ -81,6 +81,11 @@ CONFIGS = {
         atomic=True, nr=320, nc=320, n_shared=1, F_shared=1536,
         notes="102,400 atomic experts on a 320 x 320 router grid, top-4096 per token, "
               "SiLU units, one shared SwiGLU MLP (d_ff 1536)"),
+    "omni_atomic_decode": WorkloadConfig(
+        "omni_atomic_decode", 7, T=16, d=2048, E=320 * 320, k=4096, F=1, act="silu",
+        dtype="bf16", atomic=True, nr=320, nc=320, n_shared=1, F_shared=1536,
+        notes="the atomic-expert layer above at 16 tokens (a decode step): only the "
+              "experts some token keeps need their parameters read"),
     "mixtral_floe_decode": WorkloadConfig(
         "mixtral_floe_decode", 6, T=16, d=4096, E=8, k=2, F=14336, act="swiglu",
         dtype="bf16", floe=True, sparsity=0.9, x_rows_of="mixtral_prefill_bf16",

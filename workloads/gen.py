@@ -236,6 +236,7 @@ class Workload:
     w_col: Optional[np.ndarray] = None     # [nc, d] column router (atomic configs; w_router = rows)
     w_in: Optional[np.ndarray] = None      # [N, d] atomic input vectors
     w_out_t: Optional[np.ndarray] = None   # [d, N] atomic output vectors as columns
+    w_out_rows: Optional[np.ndarray] = None  # [N, d] the same output vectors as rows
     u2_up: Optional[Int2Weights] = None    # INT2 up projection (floe configs)
     floe_thr: Optional[np.ndarray] = None  # [E] fp32 |up output| threshold per expert
 
@@ -280,9 +281,10 @@ def _make_atomic(cfg, threads):
         with ThreadPoolExecutor(max(1, min(threads, nch))) as ex:
             return np.concatenate(list(ex.map(one, range(nch))), axis=0)
     w_in = chunks(TID_WUP)
-    w_out_t = np.ascontiguousarray(chunks(TID_WDOWN).T)
+    w_out_rows = chunks(TID_WDOWN)                      # [N][d]: expert n's output vector
+    w_out_t = np.ascontiguousarray(w_out_rows.T)        # [d][N]: the same values transposed
     wl = Workload(cfg, x, w_row, np.zeros(cfg.nr, np.float32), None, w_in, w_out_t)
-    wl.w_col, wl.w_in, wl.w_out_t = w_col, w_in, w_out_t
+    wl.w_col, wl.w_in, wl.w_out_t, wl.w_out_rows = w_col, w_in, w_out_t, w_out_rows
     if cfg.n_shared:
         Fs = cfg.n_shared * cfg.F_shared
         wl.ws_gate = _normal(wid, TID_SGATE, 0, (Fs, d), W_STD, True)
