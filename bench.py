@@ -114,13 +114,15 @@ def work_floe(cfg, counts, nnz):
                 dense_bf16_bytes=float(active.sum()) * 3 * F * d * 2)
 
 
-FLUSH_BYTES = 512 << 20   # written before each cold step: more than the 256 MB MALL
+FLUSH_BYTES = 512 << 20   # read before each cold step: more than the 256 MB MALL
+# (read, not written: a written flush leaves dirty lines behind whose write-back
+# the first kernel of the step would pay for)
 
 
 def run_gpu(name, steps, warmup, cold=False):
     """Warm wall-clock timing of `steps` back-to-back layer calls, then one
     event-timed pass per step (per-stage HIP events).  With cold=True a 512 MB
-    buffer is written before each event-timed step, outside its events, so the
+    buffer is read before each event-timed step, outside its events, so the
     weights start from HBM rather than the MALL."""
     import torch
     import sparse_mixture_experts_wavefront_amd as moe
@@ -172,11 +174,15 @@ def run_gpu(name, steps, warmup, cold=False):
         sets.append((C.c_void_p * 7)(*hs))
     B = moe.lib()
     per = np.zeros((steps, 7))
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=x.device) if cold else None
+    flush = None
+    if cold:
+        flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=x.device)
+        flush.sum()
+        torch.cuda.synchronize()
     try:
         for n, evs in enumerate(sets):
             if cold:
-                flush.fill_(float(n))
+                flush.sum()
             B.moe_set_stage_events(C.cast(evs, C.POINTER(C.c_void_p)), 7)
             call()
         B.moe_set_stage_events(None, 0)
@@ -211,7 +217,7 @@ def run_gpu(name, steps, warmup, cold=False):
         stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
         try:
             for n, (a, b) in enumerate(ev):
-                flush.fill_(float(n))
+                flush.sum()
                 assert hip.hipEventRecord(C.c_void_p(a), stream) == 0
                 call()
                 assert hip.hipEventRecord(C.c_void_p(b), stream) == 0

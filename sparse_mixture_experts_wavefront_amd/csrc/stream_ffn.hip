@@ -41,6 +41,7 @@
 // sums over the same K set (the order of K inside one accumulation is free).
 // LDS rows keep 16-byte unit u of row r at position u ^ (r & 15), so the 16 rows
 // one read pass touches fall on 16 different bank groups.
+#include <mutex>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -103,6 +104,35 @@ __device__ __forceinline__ bf16x8 dq8_fma(uint32_t w, float s, float nzs) {
   o[1] = pk_bf16(__builtin_fmaf(ub1(lo), s, nzs), __builtin_fmaf(ub1(hi), s, nzs));
   o[2] = pk_bf16(__builtin_fmaf(ub2(lo), s, nzs), __builtin_fmaf(ub2(hi), s, nzs));
   o[3] = pk_bf16(__builtin_fmaf(ub3(lo), s, nzs), __builtin_fmaf(ub3(hi), s, nzs));
+  return as_bf16x8(o);
+}
+// The same fused decode with the int-to-float conversion folded into the fma:
+// a 16-bit half that holds a nibble q in bits 0-3 (or 4-7) and zeros elsewhere
+// is the fp16 subnormal q * 2^-24 (q * 2^-20), which v_fma_mix_f32 reads as an
+// exact fp32 operand; with the scale pre-multiplied by 2^24 (2^20), also exact,
+// fma(q * 2^-24, s * 2^24, nzs) is fma(q, s, nzs) rounded once.  Four masks and
+// one shift place all 8 nibbles (fp16 denormals are kept: the kernels run with
+// the default denormal mode).
+__device__ __forceinline__ float mix_lo(uint32_t m, float s, float c) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(m), "v"(s), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float mix_hi(uint32_t m, float s, float c) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(m), "v"(s), "v"(c));
+  return r;
+}
+__device__ __forceinline__ bf16x8 dq8_mix(uint32_t w, float s, float nzs) {
+  const float s24 = s * 16777216.0f, s20 = s * 1048576.0f;
+  const uint32_t w8 = w >> 8;
+  const uint32_t m0 = w & 0x000f000fu, m1 = w & 0x00f000f0u;    // nibbles 0, 4 / 1, 5
+  const uint32_t m2 = w8 & 0x000f000fu, m3 = w8 & 0x00f000f0u;  // nibbles 2, 6 / 3, 7
+  u32x4 o;
+  o[0] = pk_bf16(mix_lo(m0, s24, nzs), mix_lo(m1, s20, nzs));
+  o[1] = pk_bf16(mix_lo(m2, s24, nzs), mix_lo(m3, s20, nzs));
+  o[2] = pk_bf16(mix_hi(m0, s24, nzs), mix_hi(m1, s20, nzs));
+  o[3] = pk_bf16(mix_hi(m2, s24, nzs), mix_hi(m3, s20, nzs));
   return as_bf16x8(o);
 }
 // the defining two-operation form (any zero point)
@@ -621,7 +651,7 @@ void stream_reg_kernel(StreamArgs p) {
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
               if constexpr (decltype(fused)::value)
-                a[s] = dq8_fma(S.wv[rb][0][s], sf, nzs);
+                a[s] = dq8_mix(S.wv[rb][0][s], sf, nzs);
               else
                 a[s] = dq8_exact(S.wv[rb][0][s], sf, zf);
             }
@@ -701,6 +731,294 @@ void stream_reg_kernel(StreamArgs p) {
   }
 }
 
+// ---- row-split variant (gate/up and ReLU W_in, few token rows) ----------------
+// The K-split kernel above gives each wave a quarter of K for all of the
+// block's rows, so each wave loads its own token fragments and a token byte
+// feeds only the block's 64-128 rows.  Here each wave owns 64 weight rows
+// (gate/up: 32 gate + 32 up rows of the same 32 f-values) over the whole of K
+// and the four waves share the token fragments: each 128-K slice of the block's
+// token rows is loaded once per block (one 16-byte load per thread and 16-row
+// token block), stored to one of two LDS slots (row stride 272 bytes, so the 16
+// rows one MFMA operand read touches fall on 16 different bank groups) and read
+// by all four waves, one barrier per slice.  A block covers 128 f-values of
+// gate/up (256 weight rows; ReLU: 256 rows) for up to MB*16 token rows per
+// pass; no cross-wave reduction is needed, each wave applies the epilogue to
+// its own accumulators.  Weights and token slices are loaded D slices ahead
+// into registers.  K map inside a slice, INT4 scale table and out-of-range
+// loads as in the K-split kernel.
+constexpr int kRowsRBW = 4;                      // 16-row weight blocks per wave
+// LDS bytes per staged token row of a slice of 128*WQ K values (16 bytes of padding)
+constexpr int rows_xrow(int wq) { return 128 * wq * 2 + 16; }
+
+template <int MODE>
+constexpr int stream_rows_nout() { return MODE == kSModeGateUp ? 4 * kRowsRBW * 8 : 4 * kRowsRBW * 16; }
+
+template <int MODE, bool INT4, int MB, int D, int WQ>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void stream_rows_kernel(StreamArgs p) {
+  static_assert(MODE != kSModeDown, "gate/up and ReLU W_in only");
+  static_assert(INT4 || WQ == 1, "bf16 slices are 128 K values");
+  constexpr int RBW = kRowsRBW, KI = 128 * WQ, NS = 4;
+  constexpr int WL = INT4 ? WQ : NS;                  // 16-byte weight loads per row block
+  constexpr int IT_BYTES = INT4 ? KI / 2 : KI * 2;    // weight bytes per row per slice
+  constexpr int NWF = (MODE == kSModeGateUp) ? RBW * 8 : RBW * 16;  // output columns per wave
+  constexpr int NOUT = stream_rows_nout<MODE>();      // per block (= rows per weight strip)
+  constexpr int XROW = rows_xrow(WQ);
+  constexpr int XSLOT = MB * 16 * XROW;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* xs = smem;                                  // [2][MB*16][XROW]
+  uint32_t* sz = (uint32_t*)(smem + 2 * XSLOT);              // [4*RBW*16][G+1]: s | z << 16
+
+  grid_zero(p);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int e = blockIdx.x / p.nblk_per_expert;
+  const int nb = blockIdx.x - e * p.nblk_per_expert;
+  int row0 = 0, cnt = p.rows;
+  if (p.offsets) {
+    row0 = p.offsets[e];
+    cnt = p.offsets[e + 1] - row0;
+  }
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  cnt = __builtin_amdgcn_readfirstlane(cnt);
+  if (cnt <= 0) return;
+  const int n0 = nb * NOUT;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int iters = p.K / KI;
+  const int G = p.K >> 7, GP = G + 1;
+  const uint32_t row_bytes = INT4 ? (uint32_t)p.K / 2 : (uint32_t)p.K * 2;
+
+  // weight strips: rows n0 .. n0+NOUT of each matrix (gate/up: gate and up)
+  const uint32_t strip_bytes = (uint32_t)min(NOUT, p.N - n0) * row_bytes;
+  const __amdgpu_buffer_rsrc_t wres0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.W0 + ((size_t)e * p.N + n0) * row_bytes), (short)0, (int)strip_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wres1 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((MODE == kSModeGateUp ? p.W1 : p.W0) + ((size_t)e * p.N + n0) * row_bytes), (short)0,
+      (int)strip_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t xres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.X, (short)0, (int)p.xbytes, 0x00020000);
+  // strip row of row block rb of wave w (gate/up: blocks RBW/2.. are the up rows
+  // of the same f-values as blocks 0..)
+  auto strip_row = [&](int ww, int rb) {
+    return MODE == kSModeGateUp ? ww * NWF + (rb % (RBW / 2)) * 16 : ww * NWF + rb * 16;
+  };
+  auto second = [](int rb) { return MODE == kSModeGateUp && rb >= RBW / 2; };
+  uint32_t wvoff[RBW];
+#pragma unroll
+  for (int rb = 0; rb < RBW; ++rb)
+    wvoff[rb] = (uint32_t)(strip_row(w, rb) + r16) * row_bytes + (uint32_t)g * 16;
+
+  bool fused_ok = true;
+  if constexpr (INT4) {
+    // scale table row br = ww*RBW*16 + rb*16 + r: strip row strip_row(ww, rb) + r.
+    // 8 groups (16 bytes of scales, 16 of zero points) per load, all of a
+    // thread's loads issued together: one memory round trip (the launcher
+    // checks K % 1024 == 0, K <= 8192 and 16-byte aligned scales and zeros)
+    bool ok = true;
+    const int G8 = G >> 3;
+    constexpr int kMaxPer = 8;  // 256 rows * G/8 loads per array over 256 threads
+    u32x4 sv[kMaxPer], zv[kMaxPer];
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q) {
+      const int i = tid + q * 256;
+      sv[q] = zv[q] = u32x4{0u, 0u, 0u, 0u};
+      if (i < 4 * RBW * 16 * G8) {
+        const int br = i / G8, j = i - br * G8;
+        const int ww = br / (RBW * 16), rb = (br / 16) % RBW, r = br % 16;
+        const int n = n0 + strip_row(ww, rb) + r;
+        if (n < p.N) {
+          const size_t o = ((size_t)e * p.N + n) * G + j * 8;
+          sv[q] = *(const u32x4*)((second(rb) ? p.s1 : p.s0) + o);
+          zv[q] = *(const u32x4*)((second(rb) ? p.z1 : p.z0) + o);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q) {
+      const int i = tid + q * 256;
+      if (i < 4 * RBW * 16 * G8) {
+        const int br = i / G8, j = i - br * G8;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t s2 = sv[q][h], z2 = zv[q][h];
+          ok = ok && zero_point_fma_exact((u16)(z2 & 0xffffu)) && zero_point_fma_exact((u16)(z2 >> 16));
+          sz[br * GP + j * 8 + 2 * h] = (s2 & 0xffffu) | (z2 << 16);
+          sz[br * GP + j * 8 + 2 * h + 1] = (s2 >> 16) | (z2 & 0xffff0000u);
+        }
+      }
+    }
+    // the fused decode when every zero point of the block allows it (the usual
+    // case), else the two-operation form; uniform over the block
+    fused_ok = __syncthreads_and(ok) != 0;
+  }
+
+  auto body = [&](auto fused) {
+    for (int mbase = 0; mbase < cnt; mbase += MB * 16) {
+      const int mrows = min(MB * 16, cnt - mbase);
+      // token slice loads: thread (q, c, tid) copies 16-byte chunk c*16 + tid%16
+      // of token row q*16 + tid/16
+      uint32_t xv[MB];
+#pragma unroll
+      for (int q = 0; q < MB; ++q) {
+        const int rr = row0 + mbase + min(q * 16 + (tid >> 4), mrows - 1);  // clamped copies
+        const int src = p.gather ? p.gather[rr] / p.k : rr;
+        xv[q] = ((uint32_t)src * (uint32_t)p.ldx + (uint32_t)(tid & 15) * 8) * 2u;
+      }
+      f32x4 acc[RBW][MB];
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+      struct Set {
+        u32x4 wv[RBW][WL];
+      };
+      auto load = [&](Set& S, int it) {
+        const bool live = it < iters;  // uniform
+        const uint32_t wo = live ? (uint32_t)it * IT_BYTES : strip_bytes;
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+          for (int q = 0; q < WL; ++q)
+            S.wv[rb][q] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(second(rb) ? wres1 : wres0,
+                                                             (int)(wvoff[rb] + wo + q * 64), 0, 0));
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // the token slice (from L2) is loaded one slice ahead, ahead of the
+      // weight loads issued after it, so waiting for it never waits for them
+      u32x4 xr[MB][WQ];
+      auto load_x = [&](int it) {
+        const bool live = it < iters;  // uniform
+#pragma unroll
+        for (int q = 0; q < MB; ++q)
+#pragma unroll
+          for (int c = 0; c < WQ; ++c)
+            xr[q][c] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           xres, (int)(live ? xv[q] + (uint32_t)it * KI * 2 + c * 256 : p.xbytes),
+                           0, 0));
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto compute = [&](const Set& S, const unsigned char* slot, int it) {
+        // sub-slice q = 128 K values (one INT4 group); token fragments: lane (t, g),
+        // step s reads K q*128 + [g*32 + s*8, +8) (INT4) or [s*32 + g*8, +8) (bf16)
+        // of token row t, as the weight lanes do
+#pragma unroll
+        for (int q = 0; q < WQ; ++q) {
+          u32x4 xf[MB][NS];
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+              xf[mb][s] = *(const u32x4*)(slot + (mb * 16 + r16) * XROW +
+                                          (q * 128 + (INT4 ? g * 32 + s * 8 : s * 32 + g * 8)) * 2);
+          if constexpr (!INT4) {
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+              for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                  acc[rb][mb] = mfma16(as_bf16x8(S.wv[rb][s]), as_bf16x8(xf[mb][s]), acc[rb][mb]);
+          } else {
+            const int grp = min(it, iters - 1) * WQ + q;  // past the K range the tokens are zeros
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) {
+              const uint32_t v = sz[(w * RBW * 16 + rb * 16 + r16) * GP + grp];
+              const float sf = h2f((u16)(v & 0xffffu)), zf = h2f((u16)(v >> 16));
+              const float nzs = -(zf * sf);
+              bf16x8 a[NS];
+#pragma unroll
+              for (int s = 0; s < NS; ++s) {
+                if constexpr (decltype(fused)::value)
+                  a[s] = dq8_mix(S.wv[rb][q][s], sf, nzs);
+                else
+                  a[s] = dq8_exact(S.wv[rb][q][s], sf, zf);
+              }
+#pragma unroll
+              for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                  acc[rb][mb] = mfma16(a[s], as_bf16x8(xf[mb][s]), acc[rb][mb]);
+            }
+          }
+          // one sub-slice's token fragments live at a time
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+
+      // slice it: weight register set it % D (loaded D slices ahead), LDS slot
+      // it % 2.  Slot it % 2 was last read in slice it - 2, which every wave
+      // finished before the barrier of slice it - 1.
+      Set st[D];
+      load_x(0);
+#pragma unroll
+      for (int d = 0; d < D; ++d) load(st[d], d);
+      for (int it0 = 0; it0 < iters; it0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+          const int it = it0 + u;
+          unsigned char* slot = xs + (u & 1) * XSLOT;  // it0 is even when D is
+          if (D % 2 != 0) slot = xs + (it & 1) * XSLOT;
+#pragma unroll
+          for (int q = 0; q < MB; ++q)
+#pragma unroll
+            for (int c = 0; c < WQ; ++c)
+              *(u32x4*)(slot + (q * 16 + (tid >> 4)) * XROW + (c * 16 + (tid & 15)) * 16) = xr[q][c];
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+          block_barrier();
+          load_x(it + 1);
+          compute(st[u], slot, it);
+          load(st[u], it + D);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // epilogue from the accumulators: lane (t, g) holds weight rows 4g..4g+3
+      // of each row block for token row t (C layout of the 16x16 MFMA)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int row = mbase + mb * 16 + r16;
+        if (row >= cnt) continue;
+        const size_t orow = (size_t)(row0 + row);
+        constexpr int NOB = (MODE == kSModeGateUp) ? RBW / 2 : RBW;
+#pragma unroll
+        for (int ob = 0; ob < NOB; ++ob) {
+          const int f = n0 + w * NWF + ob * 16 + 4 * g;
+          if (f >= p.N) continue;
+          float o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (MODE == kSModeGateUp)
+              o[i] = silu_f32(acc[ob][mb][i]) * acc[ob + RBW / 2][mb][i];
+            else
+              o[i] = fmaxf(acc[ob][mb][i], 0.0f);
+          }
+          *(uint2*)(p.H + orow * p.N + f) = uint2{pk_bf16(o[0], o[1]), pk_bf16(o[2], o[3])};
+        }
+      }
+      // the next pass writes slot 0 again
+      if (mbase + MB * 16 < cnt) __syncthreads();
+    }
+  };
+  if constexpr (INT4) {
+    if (fused_ok)
+      body(std::true_type{});
+    else
+      body(std::false_type{});
+  } else {
+    body(std::true_type{});
+  }
+}
+
+template <int MODE, bool INT4, int MB, int WQ>
+size_t stream_rows_lds_bytes(int K) {
+  return (size_t)2 * MB * 16 * rows_xrow(WQ) +
+         (INT4 ? (size_t)4 * kRowsRBW * 16 * ((K >> 7) + 1) * 4 : 0);
+}
+
 template <int MODE, bool INT4>
 size_t stream_reg_lds_bytes(int K) {
   constexpr int R = stream_reg_rows(MODE, INT4);
@@ -726,6 +1044,47 @@ hipError_t launch_reg_mode(const StreamArgs& a0, int E, int mb, hipStream_t s) {
     hipLaunchKernelGGL((stream_reg_kernel<MODE, INT4, 1, 2>), grid, block, lds, s, a);
   else
     hipLaunchKernelGGL((stream_reg_kernel<MODE, INT4, 2, 2>), grid, block, lds, s, a);
+  return hipGetLastError();
+}
+
+constexpr int kRowsWQ = 1;                 // INT4: K groups per slice (measured: 2 is slower)
+constexpr size_t kRowsMaxLds = 80 * 1024;  // two blocks per CU
+
+template <int MODE, bool INT4>
+hipError_t launch_rows_mode(const StreamArgs& a0, int E, int mb, hipStream_t s) {
+  constexpr int NOUT = stream_rows_nout<MODE>();
+  constexpr int WQ = INT4 ? kRowsWQ : 1;
+  StreamArgs a = a0;
+  a.nblk_per_expert = (a.N + NOUT - 1) / NOUT;
+  const dim3 grid((unsigned)(E * a.nblk_per_expert)), block(256);
+  auto k1 = stream_rows_kernel<MODE, INT4, 1, 2, WQ>;
+  auto k2 = stream_rows_kernel<MODE, INT4, 2, 2, WQ>;
+  // the dynamic-LDS limit of both instantiations is raised once per device,
+  // under a lock, so concurrent first calls from several threads are safe
+  static std::mutex attr_mu;
+  static bool attr_set[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lk(attr_mu);
+    const bool cached = dev >= 0 && dev < 64;
+    if (!cached || !attr_set[dev]) {
+      e = hipFuncSetAttribute((const void*)k1, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kRowsMaxLds);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)k2, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)kRowsMaxLds);
+      if (e != hipSuccess) return e;
+      if (cached) attr_set[dev] = true;
+    }
+  }
+  const size_t lds1 = stream_rows_lds_bytes<MODE, INT4, 1, WQ>(a.K);
+  const size_t lds2 = stream_rows_lds_bytes<MODE, INT4, 2, WQ>(a.K);
+  if (mb <= 1)
+    hipLaunchKernelGGL(k1, grid, block, lds1, s, a);
+  else
+    hipLaunchKernelGGL(k2, grid, block, lds2, s, a);
   return hipGetLastError();
 }
 
@@ -777,6 +1136,15 @@ hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid)
   const size_t xb = (size_t)p.T * p.d * 2, hb = (size_t)p.rows * p.F * 2;
   const size_t strip = 64 * (size_t)(p.d > p.F ? p.d : p.F) * (int4 ? 1 : 4) / 2;
   const bool reg = xb < (1u << 31) && hb < (1u << 31) && strip < (1u << 31);
+  // INT4 gate/up and ReLU W_in: the row-split kernel when its token slices and
+  // scale table fit its LDS limit and the table stages with 16-byte loads
+  // (d % 1024 == 0 and, for the limit, d <= 5120)
+  auto al16 = [](const void* q) { return q == nullptr || ((uintptr_t)q % 16) == 0; };
+  const moe_w4* g4 = int4 ? (relu ? p.w->q_up : p.w->q_gate) : nullptr;
+  const moe_w4* u4 = int4 ? p.w->q_up : nullptr;
+  const bool rows = reg && int4 && p.d % 1024 == 0 &&
+                    p.d <= 8192 && stream_rows_lds_bytes<kSModeGateUp, true, 2, kRowsWQ>(p.d) <= kRowsMaxLds &&
+                    al16(g4->scale) && al16(g4->zero) && al16(u4->scale) && al16(u4->zero);
   a.xbytes = (uint32_t)xb;
   if (int4) {
     const moe_w4* g = relu ? p.w->q_up : p.w->q_gate;
@@ -789,13 +1157,15 @@ hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid)
   }
   hipError_t e;
   if (relu)
-    e = int4 ? (reg ? launch_reg_mode<kSModeRelu, true>(a, E, mb, s)
-                    : launch_mode<kSModeRelu, true>(a, E, mb, s))
+    e = int4 ? (rows  ? launch_rows_mode<kSModeRelu, true>(a, E, mb, s)
+                : reg ? launch_reg_mode<kSModeRelu, true>(a, E, mb, s)
+                      : launch_mode<kSModeRelu, true>(a, E, mb, s))
              : (reg ? launch_reg_mode<kSModeRelu, false>(a, E, mb, s)
                     : launch_mode<kSModeRelu, false>(a, E, mb, s));
   else
-    e = int4 ? (reg ? launch_reg_mode<kSModeGateUp, true>(a, E, mb, s)
-                    : launch_mode<kSModeGateUp, true>(a, E, mb, s))
+    e = int4 ? (rows  ? launch_rows_mode<kSModeGateUp, true>(a, E, mb, s)
+                : reg ? launch_reg_mode<kSModeGateUp, true>(a, E, mb, s)
+                      : launch_mode<kSModeGateUp, true>(a, E, mb, s))
              : (reg ? launch_reg_mode<kSModeGateUp, false>(a, E, mb, s)
                     : launch_mode<kSModeGateUp, false>(a, E, mb, s));
   if (e != hipSuccess) return e;
