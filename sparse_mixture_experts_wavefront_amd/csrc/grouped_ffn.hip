@@ -1105,10 +1105,17 @@ size_t ffn_ws_bytes(int rows, int F, moe_dtype dt) {
   return (size_t)rows * F * (dt == MOE_DT_F32 ? 4 : 2);
 }
 
-int ffn_down_splits(int T, int d, int F, int E, int k, moe_dtype dt, bool int4) {
-  if (dt != MOE_DT_BF16 || int4 || T <= 0) return 1;
+int ffn_down_splits(int T, int d, int F, int E, int k, moe_dtype dt, const moe_experts* w) {
+  const bool int4 = w && w->q_up;
+  if (dt != MOE_DT_BF16 || T <= 0) return 1;
   FfnProblem q{};
-  q.T = T; q.d = d; q.F = F; q.dt = dt; q.rows = T * k;
+  q.T = T; q.d = d; q.F = F; q.dt = dt; q.rows = T * k; q.w = w;
+  if (int4) {
+    // weight streaming: K parts of the row-split down kernel
+    if (!stream_ffn_applies(q) || !w->q_down) return 1;
+    const int P = stream_down_parts(d, F, E);
+    return (P > 1 && stream_rows_applies(F, P, w->q_down, w->q_down)) ? P : 1;
+  }
   if (stream_ffn_applies(q)) return 1;
   // tiles of one slice (upper bound, as the launcher sizes the grid), in rounds
   // of one tile per CU (256 CUs); a slice costs 1/S of a full-K tile, and each

@@ -156,7 +156,7 @@ LayerWs carve_layer(const moe_layer_desc* L, int T, void* ws, bool replica = fal
   w.H = c.take(n * F * esz);
   // a replica layer runs its slot E through a separate (INT4) pass, which
   // writes whole rows: no K slices there
-  w.down_splits = replica ? 1 : ffn_down_splits(T, d, F, E, k, L->act_dtype, L->routed.q_up != nullptr);
+  w.down_splits = replica ? 1 : ffn_down_splits(T, d, F, E, k, L->act_dtype, &L->routed);
   w.y_rows = (float*)c.take(n * d * 4 * w.down_splits);
   const int Fs = L->n_shared * L->d_ff_shared;
   w.Hs = L->n_shared ? c.take((size_t)T * Fs * esz) : nullptr;

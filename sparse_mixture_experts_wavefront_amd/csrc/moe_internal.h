@@ -106,9 +106,10 @@ struct FfnProblem {
 };
 size_t ffn_ws_bytes(int rows, int F, moe_dtype dt);
 // K slices for the down pass of a layer-sized problem: more, smaller tiles when
-// one slice would leave the last round of tiles mostly idle.  Pure function of
-// the shapes (the workspace size depends on it).
-int ffn_down_splits(int T, int d, int F, int E, int k, moe_dtype dt, bool int4);
+// one slice would leave the last round of tiles mostly idle; for INT4 weight
+// streaming, K parts of the row-split down kernel.  A function of the shapes and
+// of the weights' alignment (the workspace size depends on it).
+int ffn_down_splits(int T, int d, int F, int E, int k, moe_dtype dt, const moe_experts* w);
 hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid = nullptr);
 // Whether the down pass can add its rows straight into y (FfnProblem::y_direct)
 // with every y element receiving at most two of them: the weight-streaming
@@ -121,6 +122,11 @@ bool ffn_direct_applies(const FfnProblem& p);
 // launch_grouped_ffn.
 bool stream_ffn_applies(const FfnProblem& p);
 hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid = nullptr);
+// Row-split INT4 streaming kernel over K / parts of a K-long reduction with
+// projections a and b (a == b for one projection), and the K parts its down
+// pass takes for d_model d, d_ff F and E experts (1: the K-split kernel).
+bool stream_rows_applies(int K, int parts, const moe_w4* a, const moe_w4* b);
+int stream_down_parts(int d, int F, int E);
 
 // (expert, width) group of each assignment: 3 * idx + clamp(width, 2, 4) - 2.
 hipError_t launch_mwq_group_ids(const int32_t* idx, const int32_t* widths, int n, int32_t* out,

@@ -74,6 +74,8 @@ struct StreamArgs {
                            // R*K/1024 <= 2048: staged with 16-byte loads
   f32x4* zero;             // gate/up: if not NULL, the grid zeroes zero[0 .. zero_n4) first
   size_t zero_n4;          // (the output the down pass then accumulates into)
+  int kparts;              // row-split down: K parts; part q writes its partial rows
+  size_t ystride;          // to Y + q * ystride (summed by the combine)
 };
 
 // the whole grid zeroes p.zero (spread over all blocks, before any exits)
@@ -743,9 +745,13 @@ void stream_reg_kernel(StreamArgs p) {
 // by all four waves, one barrier per slice.  A block covers 128 f-values of
 // gate/up (256 weight rows; ReLU: 256 rows) for up to MB*16 token rows per
 // pass; no cross-wave reduction is needed, each wave applies the epilogue to
-// its own accumulators.  Weights and token slices are loaded D slices ahead
-// into registers.  K map inside a slice, INT4 scale table and out-of-range
-// loads as in the K-split kernel.
+// its own accumulators.  Weights are loaded D slices ahead into registers,
+// token slices one slice ahead.  K map inside a slice, INT4 scale table and
+// out-of-range loads as in the K-split kernel.  The down pass (N = d_model is
+// short: 256-row strips would give too few blocks) also splits K into
+// p.kparts parts, one block each; a block writes its gate-scaled partial rows
+// to Y + part * ystride and the combine adds the parts in part order, so the
+// result does not depend on block timing.
 constexpr int kRowsRBW = 4;                      // 16-row weight blocks per wave
 // LDS bytes per staged token row of a slice of 128*WQ K values (16 bytes of padding)
 constexpr int rows_xrow(int wq) { return 128 * wq * 2 + 16; }
@@ -756,7 +762,6 @@ constexpr int stream_rows_nout() { return MODE == kSModeGateUp ? 4 * kRowsRBW * 
 template <int MODE, bool INT4, int MB, int D, int WQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void stream_rows_kernel(StreamArgs p) {
-  static_assert(MODE != kSModeDown, "gate/up and ReLU W_in only");
   static_assert(INT4 || WQ == 1, "bf16 slices are 128 K values");
   constexpr int RBW = kRowsRBW, KI = 128 * WQ, NS = 4;
   constexpr int WL = INT4 ? WQ : NS;                  // 16-byte weight loads per row block
@@ -769,12 +774,14 @@ void stream_rows_kernel(StreamArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* xs = smem;                                  // [2][MB*16][XROW]
   uint32_t* sz = (uint32_t*)(smem + 2 * XSLOT);              // [4*RBW*16][G+1]: s | z << 16
+  __shared__ float gsm[MB * 16];                             // down: gates of the pass's rows
 
   grid_zero(p);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int e = blockIdx.x / p.nblk_per_expert;
-  const int nb = blockIdx.x - e * p.nblk_per_expert;
+  const int nbk = blockIdx.x - e * p.nblk_per_expert;
+  const int kp = nbk % p.kparts, nb = nbk / p.kparts;     // K part, column strip
   int row0 = 0, cnt = p.rows;
   if (p.offsets) {
     row0 = p.offsets[e];
@@ -785,9 +792,11 @@ void stream_rows_kernel(StreamArgs p) {
   if (cnt <= 0) return;
   const int n0 = nb * NOUT;
   const int r16 = lane & 15, g = lane >> 4;
-  const int iters = p.K / KI;
-  const int G = p.K >> 7, GP = G + 1;
+  const int KP = p.K / p.kparts, K0 = kp * KP;            // this block's K range
+  const int iters = KP / KI;
+  const int G = KP >> 7, GP = G + 1, g0 = K0 >> 7, Gall = p.K >> 7;
   const uint32_t row_bytes = INT4 ? (uint32_t)p.K / 2 : (uint32_t)p.K * 2;
+  const uint32_t k0_bytes = INT4 ? (uint32_t)K0 / 2 : (uint32_t)K0 * 2;
 
   // weight strips: rows n0 .. n0+NOUT of each matrix (gate/up: gate and up)
   const uint32_t strip_bytes = (uint32_t)min(NOUT, p.N - n0) * row_bytes;
@@ -807,47 +816,57 @@ void stream_rows_kernel(StreamArgs p) {
   uint32_t wvoff[RBW];
 #pragma unroll
   for (int rb = 0; rb < RBW; ++rb)
-    wvoff[rb] = (uint32_t)(strip_row(w, rb) + r16) * row_bytes + (uint32_t)g * 16;
+    wvoff[rb] = (uint32_t)(strip_row(w, rb) + r16) * row_bytes + k0_bytes + (uint32_t)g * 16;
 
   bool fused_ok = true;
   if constexpr (INT4) {
-    // scale table row br = ww*RBW*16 + rb*16 + r: strip row strip_row(ww, rb) + r.
-    // 8 groups (16 bytes of scales, 16 of zero points) per load, all of a
-    // thread's loads issued together: one memory round trip (the launcher
-    // checks K % 1024 == 0, K <= 8192 and 16-byte aligned scales and zeros)
+    // scale table row br = ww*RBW*16 + rb*16 + r: strip row strip_row(ww, rb) + r,
+    // the G groups of this block's K range.  VG groups (2*VG bytes of scales,
+    // as many of zero points) per load, all of a thread's loads issued
+    // together: one memory round trip.  VG = 8 when p.sz_vec (G % 8 == 0 and
+    // 16-byte aligned arrays), else 4 (the launcher checks G % 4 == 0, G <= 64
+    // and 8-byte alignment)
     bool ok = true;
-    const int G8 = G >> 3;
-    constexpr int kMaxPer = 8;  // 256 rows * G/8 loads per array over 256 threads
-    u32x4 sv[kMaxPer], zv[kMaxPer];
+    auto stage = [&](auto vg) {
+      constexpr int VG = decltype(vg)::value;
+      typedef uint32_t vec_t __attribute__((ext_vector_type(VG / 2)));
+      const int GV = G / VG;
+      constexpr int kMaxPer = 64 / VG;  // 256 rows * G/VG loads per array over 256 threads
+      vec_t sv[kMaxPer], zv[kMaxPer];
 #pragma unroll
-    for (int q = 0; q < kMaxPer; ++q) {
-      const int i = tid + q * 256;
-      sv[q] = zv[q] = u32x4{0u, 0u, 0u, 0u};
-      if (i < 4 * RBW * 16 * G8) {
-        const int br = i / G8, j = i - br * G8;
-        const int ww = br / (RBW * 16), rb = (br / 16) % RBW, r = br % 16;
-        const int n = n0 + strip_row(ww, rb) + r;
-        if (n < p.N) {
-          const size_t o = ((size_t)e * p.N + n) * G + j * 8;
-          sv[q] = *(const u32x4*)((second(rb) ? p.s1 : p.s0) + o);
-          zv[q] = *(const u32x4*)((second(rb) ? p.z1 : p.z0) + o);
+      for (int q = 0; q < kMaxPer; ++q) {
+        const int i = tid + q * 256;
+        sv[q] = zv[q] = vec_t{};
+        if (i < 4 * RBW * 16 * GV) {
+          const int br = i / GV, j = i - br * GV;
+          const int ww = br / (RBW * 16), rb = (br / 16) % RBW, r = br % 16;
+          const int n = n0 + strip_row(ww, rb) + r;
+          if (n < p.N) {
+            const size_t o = ((size_t)e * p.N + n) * Gall + g0 + j * VG;
+            sv[q] = *(const vec_t*)((second(rb) ? p.s1 : p.s0) + o);
+            zv[q] = *(const vec_t*)((second(rb) ? p.z1 : p.z0) + o);
+          }
         }
       }
-    }
 #pragma unroll
-    for (int q = 0; q < kMaxPer; ++q) {
-      const int i = tid + q * 256;
-      if (i < 4 * RBW * 16 * G8) {
-        const int br = i / G8, j = i - br * G8;
+      for (int q = 0; q < kMaxPer; ++q) {
+        const int i = tid + q * 256;
+        if (i < 4 * RBW * 16 * GV) {
+          const int br = i / GV, j = i - br * GV;
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const uint32_t s2 = sv[q][h], z2 = zv[q][h];
-          ok = ok && zero_point_fma_exact((u16)(z2 & 0xffffu)) && zero_point_fma_exact((u16)(z2 >> 16));
-          sz[br * GP + j * 8 + 2 * h] = (s2 & 0xffffu) | (z2 << 16);
-          sz[br * GP + j * 8 + 2 * h + 1] = (s2 >> 16) | (z2 & 0xffff0000u);
+          for (int h = 0; h < VG / 2; ++h) {
+            const uint32_t s2 = sv[q][h], z2 = zv[q][h];
+            ok = ok && zero_point_fma_exact((u16)(z2 & 0xffffu)) && zero_point_fma_exact((u16)(z2 >> 16));
+            sz[br * GP + j * VG + 2 * h] = (s2 & 0xffffu) | (z2 << 16);
+            sz[br * GP + j * VG + 2 * h + 1] = (s2 >> 16) | (z2 & 0xffff0000u);
+          }
         }
       }
-    }
+    };
+    if (p.sz_vec)
+      stage(std::integral_constant<int, 8>{});
+    else
+      stage(std::integral_constant<int, 4>{});
     // the fused decode when every zero point of the block allows it (the usual
     // case), else the two-operation form; uniform over the block
     fused_ok = __syncthreads_and(ok) != 0;
@@ -863,7 +882,14 @@ void stream_rows_kernel(StreamArgs p) {
       for (int q = 0; q < MB; ++q) {
         const int rr = row0 + mbase + min(q * 16 + (tid >> 4), mrows - 1);  // clamped copies
         const int src = p.gather ? p.gather[rr] / p.k : rr;
-        xv[q] = ((uint32_t)src * (uint32_t)p.ldx + (uint32_t)(tid & 15) * 8) * 2u;
+        xv[q] = ((uint32_t)src * (uint32_t)p.ldx + (uint32_t)K0 + (uint32_t)(tid & 15) * 8) * 2u;
+      }
+      if constexpr (MODE == kSModeDown) {
+        // gates of this pass's rows, published by the first slice's barrier
+        if (tid < MB * 16) {
+          const int rr = row0 + mbase + min(tid, mrows - 1);
+          gsm[tid] = p.gate ? p.gate[p.gate_map ? p.gate_map[rr] : rr] : 1.0f;
+        }
       }
       f32x4 acc[RBW][MB];
 #pragma unroll
@@ -988,6 +1014,13 @@ void stream_rows_kernel(StreamArgs p) {
         for (int ob = 0; ob < NOB; ++ob) {
           const int f = n0 + w * NWF + ob * 16 + 4 * g;
           if (f >= p.N) continue;
+          if constexpr (MODE == kSModeDown) {
+            const float gv = gsm[mb * 16 + r16];
+            const f32x4 a = acc[ob][mb];
+            *(f32x4*)(p.Y + (size_t)kp * p.ystride + orow * p.N + f) =
+                f32x4{gv * a[0], gv * a[1], gv * a[2], gv * a[3]};
+            continue;
+          }
           float o[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -999,7 +1032,7 @@ void stream_rows_kernel(StreamArgs p) {
           *(uint2*)(p.H + orow * p.N + f) = uint2{pk_bf16(o[0], o[1]), pk_bf16(o[2], o[3])};
         }
       }
-      // the next pass writes slot 0 again
+      // the next pass writes slot 0 and the gates again
       if (mbase + MB * 16 < cnt) __syncthreads();
     }
   };
@@ -1013,6 +1046,7 @@ void stream_rows_kernel(StreamArgs p) {
   }
 }
 
+// K: the K range of one block (K / parts)
 template <int MODE, bool INT4, int MB, int WQ>
 size_t stream_rows_lds_bytes(int K) {
   return (size_t)2 * MB * 16 * rows_xrow(WQ) +
@@ -1051,11 +1085,15 @@ constexpr int kRowsWQ = 1;                 // INT4: K groups per slice (measured
 constexpr size_t kRowsMaxLds = 80 * 1024;  // two blocks per CU
 
 template <int MODE, bool INT4>
-hipError_t launch_rows_mode(const StreamArgs& a0, int E, int mb, hipStream_t s) {
+hipError_t launch_rows_mode(const StreamArgs& a0, int E, int mb, int parts, hipStream_t s) {
   constexpr int NOUT = stream_rows_nout<MODE>();
   constexpr int WQ = INT4 ? kRowsWQ : 1;
   StreamArgs a = a0;
-  a.nblk_per_expert = (a.N + NOUT - 1) / NOUT;
+  a.kparts = parts;
+  a.nblk_per_expert = (a.N + NOUT - 1) / NOUT * parts;
+  auto al16 = [](const void* q) { return q == nullptr || ((uintptr_t)q % 16) == 0; };
+  a.sz_vec = INT4 && ((a.K / parts) >> 7) % 8 == 0 && al16(a.s0) && al16(a.z0) && al16(a.s1) &&
+             al16(a.z1);
   const dim3 grid((unsigned)(E * a.nblk_per_expert)), block(256);
   auto k1 = stream_rows_kernel<MODE, INT4, 1, 2, WQ>;
   auto k2 = stream_rows_kernel<MODE, INT4, 2, 2, WQ>;
@@ -1079,8 +1117,8 @@ hipError_t launch_rows_mode(const StreamArgs& a0, int E, int mb, hipStream_t s) 
       if (cached) attr_set[dev] = true;
     }
   }
-  const size_t lds1 = stream_rows_lds_bytes<MODE, INT4, 1, WQ>(a.K);
-  const size_t lds2 = stream_rows_lds_bytes<MODE, INT4, 2, WQ>(a.K);
+  const size_t lds1 = stream_rows_lds_bytes<MODE, INT4, 1, WQ>(a.K / parts);
+  const size_t lds2 = stream_rows_lds_bytes<MODE, INT4, 2, WQ>(a.K / parts);
   if (mb <= 1)
     hipLaunchKernelGGL(k1, grid, block, lds1, s, a);
   else
@@ -1101,13 +1139,31 @@ hipError_t launch_mode(const StreamArgs& a, int E, int mb, hipStream_t s) {
 
 }  // namespace
 
+// The row-split INT4 kernel over K range K / parts: its token slices and scale
+// table fit the LDS limit, the table stages with 8-byte loads (4 groups: the
+// range is a multiple of 512), scales and zero points 8-byte aligned
+bool stream_rows_applies(int K, int parts, const moe_w4* a, const moe_w4* b) {
+  if (parts < 1 || K % parts != 0) return false;
+  const int KP = K / parts;
+  auto al8 = [](const void* q) { return q != nullptr && ((uintptr_t)q % 8) == 0; };
+  return KP % 512 == 0 && KP <= 8192 &&
+         stream_rows_lds_bytes<kSModeGateUp, true, 2, kRowsWQ>(KP) <= kRowsMaxLds && a && b &&
+         al8(a->scale) && al8(a->zero) && al8(b->scale) && al8(b->zero);
+}
+
+int stream_down_parts(int d, int F, int E) {
+  // about two blocks per CU: E * ceil(d / 256) strips times the parts
+  const long long strips = (long long)E * ((d + 255) / 256);
+  for (int P = 8; P > 1; P /= 2)
+    if (F % (512 * P) == 0 && strips * P <= 2 * 256 && F / P <= 8192) return P;
+  return 1;
+}
+
 bool stream_ffn_applies(const FfnProblem& p) {
   if (p.dt != MOE_DT_BF16) return false;
   // few rows per expert: every expert has at most T rows (a token picks an
   // expert once); beyond 64 the tiled kernels win
   if (p.T > 64) return false;
-  const bool int4 = p.w->q_up != nullptr;
-  (void)int4;
   // chunking needs both reduction lengths to be multiples of 512
   return (p.d % 512) == 0 && (p.F % 512) == 0;
 }
@@ -1136,15 +1192,9 @@ hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid)
   const size_t xb = (size_t)p.T * p.d * 2, hb = (size_t)p.rows * p.F * 2;
   const size_t strip = 64 * (size_t)(p.d > p.F ? p.d : p.F) * (int4 ? 1 : 4) / 2;
   const bool reg = xb < (1u << 31) && hb < (1u << 31) && strip < (1u << 31);
-  // INT4 gate/up and ReLU W_in: the row-split kernel when its token slices and
-  // scale table fit its LDS limit and the table stages with 16-byte loads
-  // (d % 1024 == 0 and, for the limit, d <= 5120)
-  auto al16 = [](const void* q) { return q == nullptr || ((uintptr_t)q % 16) == 0; };
-  const moe_w4* g4 = int4 ? (relu ? p.w->q_up : p.w->q_gate) : nullptr;
-  const moe_w4* u4 = int4 ? p.w->q_up : nullptr;
-  const bool rows = reg && int4 && p.d % 1024 == 0 &&
-                    p.d <= 8192 && stream_rows_lds_bytes<kSModeGateUp, true, 2, kRowsWQ>(p.d) <= kRowsMaxLds &&
-                    al16(g4->scale) && al16(g4->zero) && al16(u4->scale) && al16(u4->zero);
+  // INT4 gate/up and ReLU W_in: the row-split kernel (see stream_rows_applies)
+  const bool rows = reg && int4 &&
+                    stream_rows_applies(p.d, 1, relu ? p.w->q_up : p.w->q_gate, p.w->q_up);
   a.xbytes = (uint32_t)xb;
   if (int4) {
     const moe_w4* g = relu ? p.w->q_up : p.w->q_gate;
@@ -1157,13 +1207,13 @@ hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid)
   }
   hipError_t e;
   if (relu)
-    e = int4 ? (rows  ? launch_rows_mode<kSModeRelu, true>(a, E, mb, s)
+    e = int4 ? (rows  ? launch_rows_mode<kSModeRelu, true>(a, E, mb, 1, s)
                 : reg ? launch_reg_mode<kSModeRelu, true>(a, E, mb, s)
                       : launch_mode<kSModeRelu, true>(a, E, mb, s))
              : (reg ? launch_reg_mode<kSModeRelu, false>(a, E, mb, s)
                     : launch_mode<kSModeRelu, false>(a, E, mb, s));
   else
-    e = int4 ? (rows  ? launch_rows_mode<kSModeGateUp, true>(a, E, mb, s)
+    e = int4 ? (rows  ? launch_rows_mode<kSModeGateUp, true>(a, E, mb, 1, s)
                 : reg ? launch_reg_mode<kSModeGateUp, true>(a, E, mb, s)
                       : launch_mode<kSModeGateUp, true>(a, E, mb, s))
              : (reg ? launch_reg_mode<kSModeGateUp, false>(a, E, mb, s)
@@ -1196,6 +1246,14 @@ hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid)
   }
   // bf16 down rows are long (K = d_ff): whole contiguous row pieces staged
   // through LDS stream faster there than MFMA-shaped register loads
+  if (int4 && reg && p.down_splits > 1) {
+    // K split into parts: partial rows to y_rows + part * rows * d, which the
+    // combine adds (the layer sized y_rows and chose the parts for this)
+    if (!stream_rows_applies(p.F, p.down_splits, p.w->q_down, p.w->q_down))
+      return hipErrorInvalidValue;
+    b.ystride = (size_t)p.rows * p.d;
+    return launch_rows_mode<kSModeDown, true>(b, E, mb, p.down_splits, s);
+  }
   if (int4 && reg) return launch_reg_mode<kSModeDown, true>(b, E, mb, s);
   return int4 ? launch_mode<kSModeDown, true>(b, E, mb, s) : launch_mode<kSModeDown, false>(b, E, mb, s);
 }
