@@ -8,6 +8,8 @@
 #include <mutex>
 #include <string>
 
+#include <algorithm>
+
 #include "moe_internal.h"
 
 using namespace moe;
@@ -138,6 +140,13 @@ struct LayerWs {
   size_t total;
 };
 
+// scratch of the routing step: the permutation's block counts, or for the
+// one-workgroup path the router GEMM's block partials (never both)
+size_t route_ws_bytes(const moe_layer_desc* L, int T) {
+  const int E = L->n_experts, k = L->top_k;
+  return std::max(permute_ws_bytes(T, E, k), route_part_bytes(L->act_dtype, T, L->d_model, E, k));
+}
+
 LayerWs carve_layer(const moe_layer_desc* L, int T, void* ws, bool replica = false) {
   const int E = L->n_experts, k = L->top_k, d = L->d_model, F = L->d_ff;
   const size_t n = (size_t)T * k;
@@ -152,7 +161,7 @@ LayerWs carve_layer(const moe_layer_desc* L, int T, void* ws, bool replica = fal
   w.row_assign = (int32_t*)c.take(n * 4);
   w.assign_row = (int32_t*)c.take(n * 4);
   w.lis = (double*)c.take(8);
-  w.perm_ws = c.take(permute_ws_bytes(T, E, k));
+  w.perm_ws = c.take(route_ws_bytes(L, T));
   w.H = c.take(n * F * esz);
   // a replica layer runs its slot E through a separate (INT4) pass, which
   // writes whole rows: no K slices there
@@ -372,7 +381,7 @@ hipError_t route_and_permute(const moe_layer_desc* L, const void* x, int T, floa
   if (route_permute_small_applies(L->act_dtype, T, E, k)) {
     hipError_t e = launch_route_permute_small(x, L->w_router, L->b_router, T, d, E, k, logits, idx,
                                               gates, given, counts, offsets, row_assign,
-                                              assign_row, lis, st);
+                                              assign_row, lis, (float*)perm_ws, st);
     stage(1, st);
     return e;
   }
@@ -448,7 +457,7 @@ moe_status layer_forward_impl(const moe_layer_desc* L, const moe_replica* R, con
   if (small) {
     e = launch_route_permute_small(x, L->w_router, L->b_router, T, d, E, k, logits, idx, gates,
                                    (flags & MOE_F_LOGITS_GIVEN) != 0, counts, offsets, row_assign,
-                                   assign_row, lis, st);
+                                   assign_row, lis, (float*)w.perm_ws, st);
     if (e != hipSuccess) return hip_status(e, "route and permute");
     stage(1, st);
   } else {
@@ -692,7 +701,7 @@ MwqLayerWs carve_mwq_layer(const moe_layer_desc* L, int T, void* ws) {
   w.row_assign = (int32_t*)c.take(n * 4);
   w.assign_row = (int32_t*)c.take(n * 4);
   w.lis = (double*)c.take(8);
-  w.perm_ws = c.take(permute_ws_bytes(T, E, k));
+  w.perm_ws = c.take(route_ws_bytes(L, T));
   w.H = c.take(n * F * 2);
   w.down_splits = 1;
   w.y_rows = (float*)c.take(n * d * 4);
@@ -933,7 +942,7 @@ FloeLayerWs carve_floe_layer(const moe_layer_desc* L, int T, void* ws) {
   w.row_assign = (int32_t*)c.take(n * 4);
   w.assign_row = (int32_t*)c.take(n * 4);
   w.lis = (double*)c.take(8);
-  w.perm_ws = c.take(permute_ws_bytes(T, E, k));
+  w.perm_ws = c.take(route_ws_bytes(L, T));
   w.H = nullptr;
   w.down_splits = floe_down_splits(d, E);
   w.y_rows = (float*)c.take(n * d * 4 * w.down_splits);

@@ -60,11 +60,14 @@ hipError_t launch_route_topk(const void* x, moe_dtype xdt, const void* w_router,
 // Small batches (bf16, T <= 64, ceil(T/16) * ceil(E/16) <= 4): route, top-k
 // and the permutation (counts, offsets, rows, LIS) in one workgroup.
 bool route_permute_small_applies(moe_dtype xdt, int T, int E, int k);
+// part_ws: route_part_bytes(...) bytes for the router GEMM split over d (NULL
+// or 0 bytes: the workgroup computes the logits itself)
+size_t route_part_bytes(moe_dtype xdt, int T, int d, int E, int k);
 hipError_t launch_route_permute_small(const void* x, const void* w_router, const float* b_router,
                                       int T, int d, int E, int k, float* logits, int32_t* idx,
                                       float* gate, bool logits_given, int32_t* counts,
                                       int32_t* offsets, int32_t* row_assign, int32_t* assign_row,
-                                      double* lis, hipStream_t s);
+                                      double* lis, float* part_ws, hipStream_t s);
 
 size_t permute_ws_bytes(int T, int E, int k);
 hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* counts,

@@ -190,13 +190,66 @@ __device__ __forceinline__ unsigned long long same_expert(int e, bool valid) {
   return m;
 }
 
+// Router logits of a small batch, split over K.  One workgroup pulls the
+// batch's token rows from memory slowly (measured ~25 GB/s for one CU: 19 us of
+// GEMM for T = 64, d = 4096), so the GEMM first runs over d / KS blocks: block
+// b computes the partial logits of all T tokens over K [b*KS, +KS) (4 waves,
+// each taking 32-wide K steps KS/128 apart, 16x16x32 MFMA as above; wave
+// partials added in wave order), and the routing workgroup adds the block
+// partials in block order, so the logits do not depend on block timing.
+template <int EB, int G>
+__global__ __launch_bounds__(256) void router_partial_kernel(const u16* __restrict__ x,
+                                                            const u16* __restrict__ w, int T, int d,
+                                                            int E, int KS, float* __restrict__ part) {
+  __shared__ f32x4 red[4][G][EB][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  f32x4 acc[G][EB];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb) acc[gi][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int steps = KS / 128;  // 1 or 2
+#pragma unroll 2
+  for (int j = 0; j < steps; ++j) {
+    const int k0 = blockIdx.x * KS + j * 128 + wv * 32 + g * 8;
+    u32x4 av[G], bv[EB];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+      av[gi] = *(const u32x4*)(x + (size_t)min(gi * 16 + r, T - 1) * d + k0);
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb)
+      bv[eb] = *(const u32x4*)(w + (size_t)min(eb * 16 + r, E - 1) * d + k0);
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+      for (int eb = 0; eb < EB; ++eb)
+        acc[gi][eb] = mfma16(as_bf16x8(av[gi]), as_bf16x8(bv[eb]), acc[gi][eb]);
+  }
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb) red[wv][gi][eb][lane] = acc[gi][eb];
+  __syncthreads();
+  // C layout: lane holds token rows 4*(lane/16)+i of its group, expert lane%16
+  for (int q = tid; q < G * EB * 256; q += 256) {
+    const int gi = q / (EB * 256), eb = (q / 256) % EB, ln = (q >> 2) & 63, i = q & 3;
+    const float v = ((red[0][gi][eb][ln][i] + red[1][gi][eb][ln][i]) + red[2][gi][eb][ln][i]) +
+                    red[3][gi][eb][ln][i];
+    const int tr = gi * 16 + 4 * (ln >> 4) + i, e = eb * 16 + (ln & 15);
+    if (tr < T && e < E) part[((size_t)blockIdx.x * T + tr) * E + e] = v;
+  }
+}
+
 template <int EB, int G>
 __global__ __launch_bounds__(1024) void route_permute_small_kernel(
     const u16* __restrict__ x, const u16* __restrict__ w, const float* __restrict__ bias, int T,
     int d, int E, int k, int seg, float* __restrict__ logits, int32_t* __restrict__ idx,
     float* __restrict__ gate, int logits_given, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_assign,
-    int32_t* __restrict__ assign_row, double* __restrict__ lis) {
+    int32_t* __restrict__ assign_row, double* __restrict__ lis, const float* __restrict__ lpart,
+    int nparts) {
   constexpr int NW = 16, TG = 16 * G;
   __shared__ float lt[TG][kMaxExperts + 1];
   __shared__ f32x4 part[NW][G][EB][64];
@@ -206,7 +259,26 @@ __global__ __launch_bounds__(1024) void route_permute_small_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv_id = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  if (!logits_given) {
+  if (!logits_given && lpart) {
+    // partial logits of router_partial_kernel, added in block order; a thread's
+    // loads are issued together (16 per round)
+    for (int q = tid; q < T * E; q += 64 * NW) {
+      const int t = q / E, e = q - t * E;
+      float sum = 0.0f;
+      for (int b0 = 0; b0 < nparts; b0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          v[j] = (b0 + j < nparts) ? lpart[((size_t)(b0 + j) * T + t) * E + e] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (b0 + j < nparts) sum += v[j];
+      }
+      const float l = sum + (bias ? bias[e] : 0.0f);
+      lt[t][e] = l;
+      logits[q] = l;
+    }
+  } else if (!logits_given) {
     const int r = lane & 15, g = lane >> 4;
     const u16* xr[G];
 #pragma unroll
@@ -348,11 +420,21 @@ bool route_permute_small_applies(moe_dtype xdt, int T, int E, int k) {
   return xdt == MOE_DT_BF16 && T >= 1 && T <= 64 && G * EB <= 4 && T * k <= 1024;
 }
 
+// K per block of the split router GEMM (0: not split, the routing workgroup
+// computes the logits itself)
+static int route_part_ks(int d) { return d % 256 == 0 ? 256 : d % 128 == 0 ? 128 : 0; }
+
+size_t route_part_bytes(moe_dtype xdt, int T, int d, int E, int k) {
+  if (!route_permute_small_applies(xdt, T, E, k)) return 0;
+  const int ks = route_part_ks(d);
+  return ks ? (size_t)(d / ks) * T * E * sizeof(float) : 0;
+}
+
 hipError_t launch_route_permute_small(const void* x, const void* w_router, const float* b_router,
                                       int T, int d, int E, int k, float* logits, int32_t* idx,
                                       float* gate, bool logits_given, int32_t* counts,
                                       int32_t* offsets, int32_t* row_assign, int32_t* assign_row,
-                                      double* lis, hipStream_t s) {
+                                      double* lis, float* part_ws, hipStream_t s) {
   if (!route_permute_small_applies(MOE_DT_BF16, T, E, k)) return hipErrorInvalidValue;
   int seg = 1;
   while (seg < E) seg <<= 1;
@@ -360,7 +442,34 @@ hipError_t launch_route_permute_small(const void* x, const void* w_router, const
   const int lg = logits_given ? 1 : 0;
   const u16* X = (const u16*)x;
   const u16* W = (const u16*)w_router;
-#define MOE_RPS(EBV, GV)                                                                         hipLaunchKernelGGL((route_permute_small_kernel<EBV, GV>), dim3(1), dim3(1024), 0, s, X, W,                         b_router, T, d, E, k, seg, logits, idx, gate, lg, counts, offsets,                              row_assign, assign_row, lis)
+  // the router GEMM over d / ks blocks first (part_ws holds
+  // route_part_bytes(...) bytes); without a buffer the workgroup computes it
+  const int ks = route_part_ks(d);
+  const float* part = (!logits_given && part_ws && ks) ? part_ws : nullptr;
+  const int nparts = part ? d / ks : 0;
+  if (part) {
+#define MOE_RPART(EBV, GV)                                                                      \
+  hipLaunchKernelGGL((router_partial_kernel<EBV, GV>), dim3(nparts), dim3(256), 0, s, X, W, T, d, \
+                     E, ks, part_ws)
+    switch (EB * 8 + G) {
+      case 1 * 8 + 1: MOE_RPART(1, 1); break;
+      case 1 * 8 + 2: MOE_RPART(1, 2); break;
+      case 1 * 8 + 3: MOE_RPART(1, 3); break;
+      case 1 * 8 + 4: MOE_RPART(1, 4); break;
+      case 2 * 8 + 1: MOE_RPART(2, 1); break;
+      case 2 * 8 + 2: MOE_RPART(2, 2); break;
+      case 3 * 8 + 1: MOE_RPART(3, 1); break;
+      case 4 * 8 + 1: MOE_RPART(4, 1); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef MOE_RPART
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+#define MOE_RPS(EBV, GV)                                                                         \
+  hipLaunchKernelGGL((route_permute_small_kernel<EBV, GV>), dim3(1), dim3(1024), 0, s, X, W,     \
+                     b_router, T, d, E, k, seg, logits, idx, gate, lg, counts, offsets,          \
+                     row_assign, assign_row, lis, part, nparts)
   switch (EB * 8 + G) {
     case 1 * 8 + 1: MOE_RPS(1, 1); break;
     case 1 * 8 + 2: MOE_RPS(1, 2); break;
