@@ -137,6 +137,8 @@ struct LayerWs {
   int32_t *counts2, *offsets2, *row_assign2, *assign_row2;
   double* lis2;
   float* y_shared;
+  // replica layer with many rows: the replica's projections decoded to bf16
+  void *rep_gate, *rep_up, *rep_down;
   size_t total;
 };
 
@@ -146,6 +148,13 @@ size_t route_ws_bytes(const moe_layer_desc* L, int T) {
   const int E = L->n_experts, k = L->top_k;
   return std::max(permute_ws_bytes(T, E, k), route_part_bytes(L->act_dtype, T, L->d_model, E, k));
 }
+
+// A replica slot with many rows (the tiled path) runs the bf16 tile kernels on
+// its projections decoded once per call into the workspace (the INT4 tile
+// kernel stages weights through registers and is several times slower; the
+// decoded copy is a few MB per projection); decode sizes stream the INT4
+// weights directly.
+bool replica_decoded(int T) { return T > 64; }
 
 LayerWs carve_layer(const moe_layer_desc* L, int T, void* ws, bool replica = false) {
   const int E = L->n_experts, k = L->top_k, d = L->d_model, F = L->d_ff;
@@ -172,6 +181,12 @@ LayerWs carve_layer(const moe_layer_desc* L, int T, void* ws, bool replica = fal
   w.y_shared = L->n_shared ? (float*)c.take((size_t)T * d * 4) : nullptr;
   w.counts2 = w.offsets2 = w.row_assign2 = w.assign_row2 = nullptr;
   w.lis2 = nullptr;
+  w.rep_gate = w.rep_up = w.rep_down = nullptr;
+  if (replica && replica_decoded(T)) {
+    if (L->act == MOE_ACT_SWIGLU) w.rep_gate = c.take((size_t)F * d * 2);
+    w.rep_up = c.take((size_t)F * d * 2);
+    w.rep_down = c.take((size_t)d * F * 2);
+  }
   if (replica) {
     w.counts2 = (int32_t*)c.take((size_t)(E + 1) * 4);
     w.offsets2 = (int32_t*)c.take((size_t)(E + 2) * 4);
@@ -496,9 +511,23 @@ moe_status layer_forward_impl(const moe_layer_desc* L, const moe_replica* R, con
     // same H and y_rows buffers), INT4 weights of the replica
     moe_experts q{};
     q.dtype = MOE_DT_BF16;
-    q.q_gate = R->q_gate;
-    q.q_up = R->q_up;
-    q.q_down = R->q_down;
+    if (w.rep_up) {
+      const int F = L->d_ff;
+      if (w.rep_gate) {
+        e = launch_dequant_int4(R->q_gate, F, d, w.rep_gate, st);
+        if (e != hipSuccess) return hip_status(e, "replica decode");
+      }
+      e = launch_dequant_int4(R->q_up, F, d, w.rep_up, st);
+      if (e == hipSuccess) e = launch_dequant_int4(R->q_down, d, F, w.rep_down, st);
+      if (e != hipSuccess) return hip_status(e, "replica decode");
+      q.w_gate = w.rep_gate;
+      q.w_up = w.rep_up;
+      q.w_down = w.rep_down;
+    } else {
+      q.q_gate = R->q_gate;
+      q.q_up = R->q_up;
+      q.q_down = R->q_down;
+    }
     FfnProblem r = p;
     r.E = 1;
     r.w = &q;

@@ -130,6 +130,9 @@ hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid 
 // pass takes for d_model d, d_ff F and E experts (1: the K-split kernel).
 bool stream_rows_applies(int K, int parts, const moe_w4* a, const moe_w4* b);
 int stream_down_parts(int d, int F, int E);
+// INT4 projection w ([rows][K], decoded as documented for moe_w4) to bf16 out
+// [rows][K], bit-identical to the weights the GEMM kernels decode in registers
+hipError_t launch_dequant_int4(const moe_w4* w, int rows, int K, void* out, hipStream_t s);
 
 // (expert, width) group of each assignment: 3 * idx + clamp(width, 2, 4) - 2.
 hipError_t launch_mwq_group_ids(const int32_t* idx, const int32_t* widths, int n, int32_t* out,

@@ -1137,6 +1137,27 @@ hipError_t launch_mode(const StreamArgs& a, int E, int mb, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- INT4 -> bf16 decode of whole projections ---------------------------------
+// The many-row replica slot runs the bf16 tile kernels on a decoded copy of its
+// INT4 weights: one thread decodes one word (8 weights) with the same rule as
+// the GEMM kernels (fused form when the group's zero point allows it, else the
+// two-operation form) and writes 16 bytes.
+__global__ __launch_bounds__(256) void dequant_int4_kernel(const uint32_t* __restrict__ q,
+                                                           const u16* __restrict__ s,
+                                                           const u16* __restrict__ z, size_t words,
+                                                           int K, u16* __restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= words) return;
+  const size_t kw = (size_t)K / 8;
+  const size_t row = i / kw, kk = (i - row * kw) * 8;
+  const size_t gi = row * (size_t)(K >> 7) + (kk >> 7);
+  const u16 zh = z[gi];
+  const float sf = h2f(s[gi]), zf = h2f(zh);
+  const uint32_t w = q[i];
+  const bf16x8 v = zero_point_fma_exact(zh) ? dq8_mix(w, sf, -(zf * sf)) : dq8_exact(w, sf, zf);
+  *(bf16x8*)(out + i * 8) = v;
+}
+
 }  // namespace
 
 // The row-split INT4 kernel over K range K / parts: its token slices and scale
@@ -1157,6 +1178,15 @@ int stream_down_parts(int d, int F, int E) {
   for (int P = 8; P > 1; P /= 2)
     if (F % (512 * P) == 0 && strips * P <= 2 * 256 && F / P <= 8192) return P;
   return 1;
+}
+
+hipError_t launch_dequant_int4(const moe_w4* w, int rows, int K, void* out, hipStream_t s) {
+  if (K % 128 != 0) return hipErrorInvalidValue;
+  const size_t words = (size_t)rows * (K / 8);
+  if (words == 0) return hipSuccess;
+  hipLaunchKernelGGL(dequant_int4_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s,
+                     (const uint32_t*)w->q, w->scale, w->zero, words, K, (u16*)out);
+  return hipGetLastError();
 }
 
 bool stream_ffn_applies(const FfnProblem& p) {
