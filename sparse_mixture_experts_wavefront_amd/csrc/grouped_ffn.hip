@@ -69,6 +69,9 @@ struct TileArgs {
   int m_tiles_max, n_tiles;
   int ksplit;              // K slices (down only): slice s covers K [s*K/ksplit, +K/ksplit)
   size_t ystride;          // elements between the partial outputs of two slices
+  const u16* xB0;          // if not NULL, expert xslot takes its weights from xB0 (and
+  const u16* xB1;          // xB1, up for SwiGLU), [N][K] each, instead of B0/B1 (256x256 path)
+  int xslot;
   const uint32_t* bits;    // kAtomIn: [rows][wpr] kept cells, bit c%32 of word c/32
   const int32_t* bitpre;   // kAtomIn: [rows][wpr] kept cells of the row before the word
   int wpr;                 // kAtomIn: words per row (N / 32)
@@ -457,6 +460,10 @@ void grouped_gemm_tile_kernel(TileArgs p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) srow[j] = gv[j] / p.k;
   }
+  // the extra slot (a replica's decoded weights) reads its own [N][K] matrices
+  const bool xs = p.xB0 != nullptr && expert == p.xslot;
+  const u16* B0 = xs ? p.xB0 : p.B0 + (size_t)expert * wstride;
+  const u16* B1 = MODE != kGateUpSwiglu ? nullptr : xs ? p.xB1 : p.B1 + (size_t)expert * wstride;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int r = (wid * 8 + j) * 8 + (lane >> 3);
@@ -465,14 +472,14 @@ void grouped_gemm_tile_kernel(TileArgs p) {
     const u16* Bm;
     int n;
     if constexpr (MODE == kGateUpSwiglu) {
-      Bm = (r < 128) ? p.B0 : p.B1;
+      Bm = (r < 128) ? B0 : B1;
       n = n_tile * 128 + (r & 127);
     } else {
-      Bm = p.B0;
+      Bm = B0;
       n = n_tile * 256 + r;
     }
     n = min(n, p.N - 1);
-    src[8 + j] = Bm + (size_t)expert * wstride + (size_t)n * p.K + c * 8;
+    src[8 + j] = Bm + (size_t)n * p.K + c * 8;
   }
 #pragma unroll
   for (int j = 0; j < 16; ++j) src[j] += (size_t)ks * kslice;
@@ -1139,6 +1146,7 @@ int ffn_down_splits(int T, int d, int F, int E, int k, moe_dtype dt, const moe_e
 hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid) {
   if (p.rows == 0) return hipSuccess;
   if (p.y_direct && !ffn_direct_applies(p)) return hipErrorInvalidValue;
+  if (p.xw && stream_ffn_applies(p)) return hipErrorInvalidValue;  // tiled path only
   if (stream_ffn_applies(p)) return launch_stream_ffn(p, s, mid);
   const bool relu = p.act == MOE_ACT_RELU;
   const int E = p.offsets ? p.E : 1;
@@ -1184,6 +1192,13 @@ hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid
   }
   hipError_t e;
   const bool v2_gu = !int4 && (p.d % 128 == 0);
+  if (p.xw) {
+    // the extra slot runs only on the 256x256 path
+    if (int4 || !v2_gu || p.F % 128 != 0 || p.xw->q_up) return hipErrorInvalidValue;
+    a.xB0 = (const u16*)(relu ? p.xw->w_up : p.xw->w_gate);
+    a.xB1 = (const u16*)p.xw->w_up;
+    a.xslot = p.xslot;
+  }
   if (relu)
     e = int4 ? run_tiles<128, 128, kUpRelu, true>(a, s)
              : (v2_gu ? run_tiles_v2<kUpRelu>(a, s) : run_tiles<128, 128, kUpRelu, false>(a, s));
@@ -1217,6 +1232,10 @@ hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid
     return run_tiles<128, 128, kDown, true>(b, s);
   }
   b.B0 = (const u16*)p.w->w_down;
+  if (p.xw) {
+    b.xB0 = (const u16*)p.xw->w_down;
+    b.xslot = p.xslot;
+  }
   if (p.F % 128 == 0) return run_tiles_v2<kDown>(b, s);
   if (b.ksplit > 1) return hipErrorInvalidValue;  // slices exist only on the 256x256 path
   return run_tiles<128, 128, kDown, false>(b, s);

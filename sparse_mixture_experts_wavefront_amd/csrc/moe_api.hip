@@ -172,9 +172,11 @@ LayerWs carve_layer(const moe_layer_desc* L, int T, void* ws, bool replica = fal
   w.lis = (double*)c.take(8);
   w.perm_ws = c.take(route_ws_bytes(L, T));
   w.H = c.take(n * F * esz);
-  // a replica layer runs its slot E through a separate (INT4) pass, which
-  // writes whole rows: no K slices there
-  w.down_splits = replica ? 1 : ffn_down_splits(T, d, F, E, k, L->act_dtype, &L->routed);
+  // a replica layer at decode sizes runs its slot E through a separate INT4
+  // pass that writes whole rows: no K slices there
+  w.down_splits = (replica && !replica_decoded(T))
+                      ? 1
+                      : ffn_down_splits(T, d, F, E, k, L->act_dtype, &L->routed);
   w.y_rows = (float*)c.take(n * d * 4 * w.down_splits);
   const int Fs = L->n_shared * L->d_ff_shared;
   w.Hs = L->n_shared ? c.take((size_t)T * Fs * esz) : nullptr;
@@ -504,35 +506,46 @@ moe_status layer_forward_impl(const moe_layer_desc* L, const moe_replica* R, con
   p.offsets = f_offsets;
   p.row_assign = f_row_assign;
   p.y_direct = direct ? (float*)y : nullptr;
+  // the replica (slot E): with many rows its INT4 projections are decoded to
+  // bf16 and it runs as one more expert of the same tiled launches, so its
+  // tiles share the chip with the others'; at decode sizes (or shapes off the
+  // 256x256 path) it runs as a second pass over its rows with the INT4 weights
+  moe_experts q{};
+  q.dtype = MOE_DT_BF16;
+  bool rep_joined = false;
+  if (R && w.rep_up) {
+    const int F = L->d_ff;
+    if (w.rep_gate) {
+      e = launch_dequant_int4(R->q_gate, F, d, w.rep_gate, st);
+      if (e != hipSuccess) return hip_status(e, "replica decode");
+    }
+    e = launch_dequant_int4(R->q_up, F, d, w.rep_up, st);
+    if (e == hipSuccess) e = launch_dequant_int4(R->q_down, d, F, w.rep_down, st);
+    if (e != hipSuccess) return hip_status(e, "replica decode");
+    q.w_gate = w.rep_gate;
+    q.w_up = w.rep_up;
+    q.w_down = w.rep_down;
+    // (the tile map scans the experts' row counts with one wave: E + 1 <= 64)
+    rep_joined = d % 128 == 0 && F % 128 == 0 && E + 1 <= 64;
+  } else if (R) {
+    q.q_gate = R->q_gate;
+    q.q_up = R->q_up;
+    q.q_down = R->q_down;
+  }
+  if (rep_joined) {
+    p.E = E + 1;
+    p.xw = &q;
+    p.xslot = E;
+  }
   e = launch_grouped_ffn(p, st, g_stage_on ? g_stage_ev[3] : nullptr);
   if (e != hipSuccess) return hip_status(e, "grouped_ffn");
-  if (R) {
+  if (R && !rep_joined) {
     // slot E: one expert whose rows start at offsets[E] (absolute rows, so the
-    // same H and y_rows buffers), INT4 weights of the replica
-    moe_experts q{};
-    q.dtype = MOE_DT_BF16;
-    if (w.rep_up) {
-      const int F = L->d_ff;
-      if (w.rep_gate) {
-        e = launch_dequant_int4(R->q_gate, F, d, w.rep_gate, st);
-        if (e != hipSuccess) return hip_status(e, "replica decode");
-      }
-      e = launch_dequant_int4(R->q_up, F, d, w.rep_up, st);
-      if (e == hipSuccess) e = launch_dequant_int4(R->q_down, d, F, w.rep_down, st);
-      if (e != hipSuccess) return hip_status(e, "replica decode");
-      q.w_gate = w.rep_gate;
-      q.w_up = w.rep_up;
-      q.w_down = w.rep_down;
-    } else {
-      q.q_gate = R->q_gate;
-      q.q_up = R->q_up;
-      q.q_down = R->q_down;
-    }
+    // same H and y_rows buffers and K slices)
     FfnProblem r = p;
     r.E = 1;
     r.w = &q;
     r.offsets = f_offsets + E;
-    r.down_splits = 1;
     e = launch_grouped_ffn(r, st);
     if (e != hipSuccess) return hip_status(e, "replica ffn");
   }

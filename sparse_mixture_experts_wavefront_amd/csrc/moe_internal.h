@@ -103,6 +103,8 @@ struct FfnProblem {
                                  // pass adds each gate-scaled row into y_direct[token]
                                  // [T][d] fp32 (zeroed by the caller) instead of
                                  // writing y_rows: the combine, fused
+  const moe_experts* xw;         // if not NULL: expert xslot uses these bf16 weights
+  int xslot;                     // ([N][K] per projection) instead of w's (tiled path)
   float* zero_y;                 // weight-streaming path: if not NULL, the gate/up grid
                                  // zeroes zero_y[0 .. T*d) first (the y that y_direct
                                  // accumulates into)
