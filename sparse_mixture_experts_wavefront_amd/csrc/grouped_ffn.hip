@@ -382,23 +382,33 @@ void grouped_gemm_tile_kernel(TileArgs p) {
   // contiguous eighth of the real tiles (equal work, and neighbouring tiles
   // share A and B slices in that XCD's L2); blocks past them exit at once.
   if (wid == 0) {
-    int cnt = 0, first = 0;
+    // up to 128 experts: lane holds experts lane and lane + 64 (the second only
+    // when a replica slot makes E = 65)
+    int cnt[2] = {0, 0}, first[2] = {0, 0}, tiles[2], excl[2];
     if (p.offsets) {
-      if (lane < p.E) {
-        first = p.offsets[lane];
-        cnt = p.offsets[lane + 1] - first;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int ex = lane + 64 * c;
+        if (ex < p.E) {
+          first[c] = p.offsets[ex];
+          cnt[c] = p.offsets[ex + 1] - first[c];
+        }
       }
     } else if (lane == 0) {
-      cnt = p.rows;
+      cnt[0] = p.rows;
     }
-    const int tiles = (cnt + BM - 1) / BM;
-    int incl = tiles;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
+    int m_real = 0;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      tiles[c] = (cnt[c] + BM - 1) / BM;
+      int incl = tiles[c];
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      excl[c] = m_real + incl - tiles[c];
+      m_real += __shfl(incl, 63, 64);
     }
-    const int excl = incl - tiles;
-    const int m_real = __shfl(incl, 63, 64);
     const int slice_tiles = m_real * p.n_tiles;
     const int total = slice_tiles * p.ksplit;
     const int per_xcd = (total + 7) >> 3;
@@ -408,19 +418,22 @@ void grouped_gemm_tile_kernel(TileArgs p) {
     if (loc < per_xcd && t < total) {
       const int ksl = t / slice_tiles;
       t -= ksl * slice_tiles;
-      const int u = t - excl * p.n_tiles;  // tile index inside this lane's expert
-      if (u >= 0 && u < tiles * p.n_tiles) {  // exactly one lane
-        const int per_group = kV2GroupM * p.n_tiles;
-        const int g = u / per_group;
-        const int first_m = g * kV2GroupM;
-        const int gm = min(tiles - first_m, kV2GroupM);
-        const int in_g = u - g * per_group;
-        const int m_loc = first_m + in_g % gm;
-        s_tile[0] = lane;
-        s_tile[1] = first + m_loc * BM;
-        s_tile[2] = min(BM, cnt - m_loc * BM);
-        s_tile[3] = in_g / gm;
-        s_tile[4] = ksl;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int u = t - excl[c] * p.n_tiles;  // tile index inside expert lane + 64c
+        if (u >= 0 && u < tiles[c] * p.n_tiles) {  // exactly one (lane, c)
+          const int per_group = kV2GroupM * p.n_tiles;
+          const int g = u / per_group;
+          const int first_m = g * kV2GroupM;
+          const int gm = min(tiles[c] - first_m, kV2GroupM);
+          const int in_g = u - g * per_group;
+          const int m_loc = first_m + in_g % gm;
+          s_tile[0] = lane + 64 * c;
+          s_tile[1] = first[c] + m_loc * BM;
+          s_tile[2] = min(BM, cnt[c] - m_loc * BM);
+          s_tile[3] = in_g / gm;
+          s_tile[4] = ksl;
+        }
       }
     }
   }

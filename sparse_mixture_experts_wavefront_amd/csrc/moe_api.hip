@@ -525,8 +525,8 @@ moe_status layer_forward_impl(const moe_layer_desc* L, const moe_replica* R, con
     q.w_gate = w.rep_gate;
     q.w_up = w.rep_up;
     q.w_down = w.rep_down;
-    // (the tile map scans the experts' row counts with one wave: E + 1 <= 64)
-    rep_joined = d % 128 == 0 && F % 128 == 0 && E + 1 <= 64;
+    // (the 256x256 tile map scans up to 128 experts' row counts)
+    rep_joined = d % 128 == 0 && F % 128 == 0 && E + 1 <= 128;
   } else if (R) {
     q.q_gate = R->q_gate;
     q.q_up = R->q_up;

@@ -110,10 +110,10 @@ def check_replica(wl, rep, g, tokens=None):
 
 SMALL = {
     # T > 64: the replica's projections decoded to bf16; it runs as expert E of
-    # the main tiled launches when E + 1 <= 64 and d, F are multiples of 128
+    # the main tiled launches (E + 1 = 65 for the DeepSeek shape: the tile map's
+    # second 64-expert chunk)
     "switch_small": ("switch_bf16", dict(T=300, d=256, F=384)),
     "mixtral_small": ("mixtral_prefill_bf16", dict(T=333, d=512, F=640)),
-    # ... else (E = 64) as a second tiled pass over its rows
     "deepseek_small": ("deepseek_v2_lite_bf16", dict(T=257, d=256, F=256, F_shared=64)),
     # T <= 64: the replica runs through the weight-streaming INT4 kernel
     "decode_small": ("mixtral_decode_bf16", dict(T=16, d=512, F=1024, x_rows_of=None,
