@@ -2,12 +2,13 @@
 // the weight-read patterns of the decode kernels on MI355X.
 //
 // 470 MB of 2048-byte rows (the INT4 gate/up weights of the Mixtral decode
-// workload), 256 rows per block of 4 waves, each wave 64 rows as 4 blocks of
-// 16.  "pat L, D": lane (r, g) of a load reads 16 bytes of row r at offset
-// g*16 + j*64 of the current visit (the MFMA operand layout); one visit reads
-// L*64 contiguous bytes of each row (L loads per row block issued together),
-// D visits in flight.  "lin D": each wave instruction reads 1 KB contiguous.
-// Before every timed launch a 512 MB buffer is read, so the rows come from HBM.
+// workload).  "pat L D RW": blocks of 4 waves, each wave RW blocks of 16 rows
+// (a block owns 64*RW rows); lane (r, g) of a load reads 16 bytes of row r at
+// offset g*16 + j*64 of the current visit (the MFMA operand layout); one visit
+// reads L*64 contiguous bytes of each row (L loads per row block issued
+// together), D visits in flight.  "lin D": each wave instruction reads 1 KB
+// contiguous, 256 rows per block.  Before every timed launch a 512 MB buffer is
+// read, so the rows come from HBM.
 //
 //   hipcc -O3 --offload-arch=gfx950 -Xclang -target-feature -Xclang -packed-fp32-ops \
 //       sparse_mixture_experts_wavefront_amd/csrc/probe/stream_pattern.hip -o stream_pattern
@@ -18,22 +19,22 @@
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <int L, int D>
+template <int L, int D, int RW = 4>
 __global__ __launch_bounds__(256) void pat_kernel(const unsigned char* W, int row_bytes, uint32_t* out) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const size_t strip = (size_t)blockIdx.x * 256 * row_bytes;
+  const size_t strip = (size_t)blockIdx.x * 64 * RW * row_bytes;
   const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + strip), (short)0, 256 * row_bytes, 0x00020000);
-  uint32_t off[4];
-  for (int rb = 0; rb < 4; ++rb) off[rb] = (uint32_t)((w * 64 + rb * 16 + r16) * row_bytes + g * 16);
+      (void*)(W + strip), (short)0, 64 * RW * row_bytes, 0x00020000);
+  uint32_t off[RW];
+  for (int rb = 0; rb < RW; ++rb) off[rb] = (uint32_t)((w * 16 * RW + rb * 16 + r16) * row_bytes + g * 16);
   const int visits = row_bytes / (64 * L);
   u32x4 acc = {0, 0, 0, 0};
-  u32x4 st[D][4][L];
+  u32x4 st[D][RW][L];
   auto load = [&](int d, int v) {
-    const uint32_t vo = v < visits ? (uint32_t)v * 64 * L : 256u * row_bytes;
+    const uint32_t vo = v < visits ? (uint32_t)v * 64 * L : 64u * RW * row_bytes;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < RW; ++rb)
 #pragma unroll
       for (int j = 0; j < L; ++j)
         st[d][rb][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(res, (int)(off[rb] + vo + j * 64), 0, 0));
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(256) void pat_kernel(const unsigned char* W, int ro
 #pragma unroll
     for (int u = 0; u < D; ++u) {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < RW; ++rb)
 #pragma unroll
         for (int j = 0; j < L; ++j) acc ^= st[u][rb][j];
       load(u, v0 + u + D);
@@ -96,19 +97,20 @@ int main() {
   unsigned char* W; uint32_t* out; unsigned char* flush;
   const size_t fbytes = 512u << 20;
   CHECK(hipMalloc(&W, bytes));
-  CHECK(hipMalloc(&out, (size_t)blocks * 256 * 4));
+  CHECK(hipMalloc(&out, (size_t)(rows / 64) * 256 * 4));
   CHECK(hipMalloc(&flush, fbytes));
   CHECK(hipMemset(W, 1, bytes));
   CHECK(hipMemset(flush, 2, fbytes));
   uint32_t* fo; CHECK(hipMalloc(&fo, (size_t)(fbytes / row_bytes / 256) * 256 * 4));
   hipEvent_t a, b; CHECK(hipEventCreate(&a)); CHECK(hipEventCreate(&b));
-  auto run = [&](const char* name, auto kern, int reps) -> int {
+  auto run = [&](const char* name, auto kern, int reps, int nblocks = 0) -> int {
+    const int gb = nblocks ? nblocks : blocks;
     float best = 1e9, sum = 0;
     for (int i = 0; i < reps + 1; ++i) {
       // read-flush the MALL with the linear kernel over the 512 MB buffer
       hipLaunchKernelGGL((lin_kernel<2>), dim3(fbytes / row_bytes / 256), dim3(256), 0, 0, flush, row_bytes, fo);
       CHECK(hipEventRecord(a, 0));
-      hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, 0, W, row_bytes, out);
+      hipLaunchKernelGGL(kern, dim3(gb), dim3(256), 0, 0, W, row_bytes, out);
       CHECK(hipEventRecord(b, 0));
       CHECK(hipEventSynchronize(b));
       float ms; CHECK(hipEventElapsedTime(&ms, a, b));
@@ -119,15 +121,13 @@ int main() {
     return 0;
   };
   run("lin D2", lin_kernel<2>, 5);
-  run("lin D4", lin_kernel<4>, 5);
-  run("pat L1 D2", pat_kernel<1, 2>, 5);
-  run("pat L1 D4", pat_kernel<1, 4>, 5);
-  run("pat L1 D8", pat_kernel<1, 8>, 5);
-  run("pat L2 D2", pat_kernel<2, 2>, 5);
-  run("pat L2 D4", pat_kernel<2, 4>, 5);
-  run("pat L4 D2", pat_kernel<4, 2>, 5);
-  run("pat L4 D4", pat_kernel<4, 4>, 5);
-  run("pat L8 D2", pat_kernel<8, 2>, 5);
-  run("pat L8 D1", pat_kernel<8, 1>, 5);
+  run("pat L1 D4 RW4", pat_kernel<1, 4, 4>, 5);
+  run("pat L4 D2 RW4", pat_kernel<4, 2, 4>, 5);
+  run("pat L1 D4 RW1", pat_kernel<1, 4, 1>, 5, rows / 64);
+  run("pat L1 D8 RW1", pat_kernel<1, 8, 1>, 5, rows / 64);
+  run("pat L4 D2 RW1", pat_kernel<4, 2, 1>, 5, rows / 64);
+  run("pat L4 D4 RW1", pat_kernel<4, 4, 1>, 5, rows / 64);
+  run("pat L1 D4 RW2", pat_kernel<1, 4, 2>, 5, rows / 128);
+  run("pat L4 D2 RW2", pat_kernel<4, 2, 2>, 5, rows / 128);
   return 0;
 }

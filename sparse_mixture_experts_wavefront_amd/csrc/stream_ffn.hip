@@ -733,41 +733,41 @@ void stream_reg_kernel(StreamArgs p) {
   }
 }
 
-// ---- row-split variant (gate/up and ReLU W_in, few token rows) ----------------
+// ---- row-split variant (INT4 gate/up, ReLU W_in and down, few token rows) -----
 // The K-split kernel above gives each wave a quarter of K for all of the
 // block's rows, so each wave loads its own token fragments and a token byte
-// feeds only the block's 64-128 rows.  Here each wave owns 64 weight rows
-// (gate/up: 32 gate + 32 up rows of the same 32 f-values) over the whole of K
-// and the four waves share the token fragments: each 128-K slice of the block's
-// token rows is loaded once per block (one 16-byte load per thread and 16-row
-// token block), stored to one of two LDS slots (row stride 272 bytes, so the 16
-// rows one MFMA operand read touches fall on 16 different bank groups) and read
-// by all four waves, one barrier per slice.  A block covers 128 f-values of
-// gate/up (256 weight rows; ReLU: 256 rows) for up to MB*16 token rows per
-// pass; no cross-wave reduction is needed, each wave applies the epilogue to
-// its own accumulators.  Weights are loaded D slices ahead into registers,
-// token slices one slice ahead.  K map inside a slice, INT4 scale table and
-// out-of-range loads as in the K-split kernel.  The down pass (N = d_model is
-// short: 256-row strips would give too few blocks) also splits K into
-// p.kparts parts, one block each; a block writes its gate-scaled partial rows
-// to Y + part * ystride and the combine adds the parts in part order, so the
-// result does not depend on block timing.
-constexpr int kRowsRBW = 4;                      // 16-row weight blocks per wave
+// feeds only the block's 64-128 rows.  Here each wave owns RBW 16-row blocks of
+// weight rows (gate/up: RBW/2 blocks of gate rows and the matching up rows)
+// over the whole of K and the four waves share the token fragments: each
+// 128-K slice of the block's token rows is loaded once per block (one 16-byte
+// load per thread and 16-row token block), stored to one of two LDS slots (row
+// stride 272 bytes, so the 16 rows one MFMA operand read touches fall on 16
+// different bank groups) and read by all four waves, one barrier per slice.  A
+// block covers 4*RBW*16 weight rows of each matrix's strip for up to MB*16
+// token rows per pass; no cross-wave reduction is needed, each wave applies
+// the epilogue to its own accumulators.  Weights are loaded D slices ahead
+// into registers, token slices one slice ahead.  K map inside a slice, INT4
+// scale table and out-of-range loads as in the K-split kernel.  The down pass
+// (N = d_model is short: strips alone would give too few blocks) also splits K
+// into p.kparts parts, one block each; a block writes its gate-scaled partial
+// rows to Y + part * ystride and the combine adds the parts in part order, so
+// the result does not depend on block timing.
+constexpr int kRowsRBW = 4;                      // 16-row weight blocks per wave (default)
 // LDS bytes per staged token row of a slice of 128*WQ K values (16 bytes of padding)
 constexpr int rows_xrow(int wq) { return 128 * wq * 2 + 16; }
 
-template <int MODE>
-constexpr int stream_rows_nout() { return MODE == kSModeGateUp ? 4 * kRowsRBW * 8 : 4 * kRowsRBW * 16; }
+template <int MODE, int RBW>
+constexpr int stream_rows_nout() { return MODE == kSModeGateUp ? 4 * RBW * 8 : 4 * RBW * 16; }
 
-template <int MODE, bool INT4, int MB, int D, int WQ>
+template <int MODE, bool INT4, int MB, int D, int WQ, int RBW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void stream_rows_kernel(StreamArgs p) {
   static_assert(INT4 || WQ == 1, "bf16 slices are 128 K values");
-  constexpr int RBW = kRowsRBW, KI = 128 * WQ, NS = 4;
+  constexpr int KI = 128 * WQ, NS = 4;
   constexpr int WL = INT4 ? WQ : NS;                  // 16-byte weight loads per row block
   constexpr int IT_BYTES = INT4 ? KI / 2 : KI * 2;    // weight bytes per row per slice
   constexpr int NWF = (MODE == kSModeGateUp) ? RBW * 8 : RBW * 16;  // output columns per wave
-  constexpr int NOUT = stream_rows_nout<MODE>();      // per block (= rows per weight strip)
+  constexpr int NOUT = stream_rows_nout<MODE, RBW>(); // per block (= rows per weight strip)
   constexpr int XROW = rows_xrow(WQ);
   constexpr int XSLOT = MB * 16 * XROW;
 
@@ -1047,10 +1047,10 @@ void stream_rows_kernel(StreamArgs p) {
 }
 
 // K: the K range of one block (K / parts)
-template <int MODE, bool INT4, int MB, int WQ>
+template <int MODE, bool INT4, int MB, int WQ, int RBW = kRowsRBW>
 size_t stream_rows_lds_bytes(int K) {
   return (size_t)2 * MB * 16 * rows_xrow(WQ) +
-         (INT4 ? (size_t)4 * kRowsRBW * 16 * ((K >> 7) + 1) * 4 : 0);
+         (INT4 ? (size_t)4 * RBW * 16 * ((K >> 7) + 1) * 4 : 0);
 }
 
 template <int MODE, bool INT4>
@@ -1082,11 +1082,13 @@ hipError_t launch_reg_mode(const StreamArgs& a0, int E, int mb, hipStream_t s) {
 }
 
 constexpr int kRowsWQ = 1;                 // INT4: K groups per slice (measured: 2 is slower)
+constexpr int kRowsRBWUp = 2;              // 16-row weight blocks per wave: gate/up, ReLU W_in (2: measured ~5% faster than 4)
+constexpr int kRowsRBWDown = 4;            // and down
 constexpr size_t kRowsMaxLds = 80 * 1024;  // two blocks per CU
 
-template <int MODE, bool INT4>
+template <int MODE, bool INT4, int RBW>
 hipError_t launch_rows_mode(const StreamArgs& a0, int E, int mb, int parts, hipStream_t s) {
-  constexpr int NOUT = stream_rows_nout<MODE>();
+  constexpr int NOUT = stream_rows_nout<MODE, RBW>();
   constexpr int WQ = INT4 ? kRowsWQ : 1;
   StreamArgs a = a0;
   a.kparts = parts;
@@ -1095,8 +1097,8 @@ hipError_t launch_rows_mode(const StreamArgs& a0, int E, int mb, int parts, hipS
   a.sz_vec = INT4 && ((a.K / parts) >> 7) % 8 == 0 && al16(a.s0) && al16(a.z0) && al16(a.s1) &&
              al16(a.z1);
   const dim3 grid((unsigned)(E * a.nblk_per_expert)), block(256);
-  auto k1 = stream_rows_kernel<MODE, INT4, 1, 2, WQ>;
-  auto k2 = stream_rows_kernel<MODE, INT4, 2, 2, WQ>;
+  auto k1 = stream_rows_kernel<MODE, INT4, 1, 2, WQ, RBW>;
+  auto k2 = stream_rows_kernel<MODE, INT4, 2, 2, WQ, RBW>;
   // the dynamic-LDS limit of both instantiations is raised once per device,
   // under a lock, so concurrent first calls from several threads are safe
   static std::mutex attr_mu;
@@ -1117,8 +1119,8 @@ hipError_t launch_rows_mode(const StreamArgs& a0, int E, int mb, int parts, hipS
       if (cached) attr_set[dev] = true;
     }
   }
-  const size_t lds1 = stream_rows_lds_bytes<MODE, INT4, 1, WQ>(a.K / parts);
-  const size_t lds2 = stream_rows_lds_bytes<MODE, INT4, 2, WQ>(a.K / parts);
+  const size_t lds1 = stream_rows_lds_bytes<MODE, INT4, 1, WQ, RBW>(a.K / parts);
+  const size_t lds2 = stream_rows_lds_bytes<MODE, INT4, 2, WQ, RBW>(a.K / parts);
   if (mb <= 1)
     hipLaunchKernelGGL(k1, grid, block, lds1, s, a);
   else
@@ -1173,8 +1175,9 @@ bool stream_rows_applies(int K, int parts, const moe_w4* a, const moe_w4* b) {
 }
 
 int stream_down_parts(int d, int F, int E) {
-  // about two blocks per CU: E * ceil(d / 256) strips times the parts
-  const long long strips = (long long)E * ((d + 255) / 256);
+  // about two blocks per CU: E * ceil(d / strip rows) strips times the parts
+  constexpr int NOUT = stream_rows_nout<kSModeDown, kRowsRBWDown>();
+  const long long strips = (long long)E * ((d + NOUT - 1) / NOUT);
   for (int P = 8; P > 1; P /= 2)
     if (F % (512 * P) == 0 && strips * P <= 2 * 256 && F / P <= 8192) return P;
   return 1;
@@ -1237,13 +1240,13 @@ hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid)
   }
   hipError_t e;
   if (relu)
-    e = int4 ? (rows  ? launch_rows_mode<kSModeRelu, true>(a, E, mb, 1, s)
+    e = int4 ? (rows  ? launch_rows_mode<kSModeRelu, true, kRowsRBWUp>(a, E, mb, 1, s)
                 : reg ? launch_reg_mode<kSModeRelu, true>(a, E, mb, s)
                       : launch_mode<kSModeRelu, true>(a, E, mb, s))
              : (reg ? launch_reg_mode<kSModeRelu, false>(a, E, mb, s)
                     : launch_mode<kSModeRelu, false>(a, E, mb, s));
   else
-    e = int4 ? (rows  ? launch_rows_mode<kSModeGateUp, true>(a, E, mb, 1, s)
+    e = int4 ? (rows  ? launch_rows_mode<kSModeGateUp, true, kRowsRBWUp>(a, E, mb, 1, s)
                 : reg ? launch_reg_mode<kSModeGateUp, true>(a, E, mb, s)
                       : launch_mode<kSModeGateUp, true>(a, E, mb, s))
              : (reg ? launch_reg_mode<kSModeGateUp, false>(a, E, mb, s)
@@ -1282,7 +1285,7 @@ hipError_t launch_stream_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid)
     if (!stream_rows_applies(p.F, p.down_splits, p.w->q_down, p.w->q_down))
       return hipErrorInvalidValue;
     b.ystride = (size_t)p.rows * p.d;
-    return launch_rows_mode<kSModeDown, true>(b, E, mb, p.down_splits, s);
+    return launch_rows_mode<kSModeDown, true, kRowsRBWDown>(b, E, mb, p.down_splits, s);
   }
   if (int4 && reg) return launch_reg_mode<kSModeDown, true>(b, E, mb, s);
   return int4 ? launch_mode<kSModeDown, true>(b, E, mb, s) : launch_mode<kSModeDown, false>(b, E, mb, s);
