@@ -116,6 +116,15 @@ SMALL = {
     "int4_prefill_small": ("mixtral_int4_decode", dict(T=300, d=256, F=384, x_rows_of=None,
                                                        weights_of=None)),
     "single_token": ("mixtral_prefill_bf16", dict(T=1, d=512, F=640)),
+    # small-batch routing: router GEMM split in 128-wide K blocks (d % 256 != 0),
+    # and not split at all (d % 128 != 0: the routing workgroup's own GEMM)
+    "route_split_128": ("mixtral_decode_bf16", dict(T=24, d=384, F=512, x_rows_of=None,
+                                                    weights_of=None)),
+    "route_unsplit": ("mixtral_decode_bf16", dict(T=8, d=200, F=256, x_rows_of=None,
+                                                  weights_of=None)),
+    # INT4 row-split down with 8 K parts of 512 (4 groups each: 8-byte scale staging)
+    "int4_down_8parts": ("mixtral_int4_decode", dict(T=32, d=1024, F=4096, x_rows_of=None,
+                                                     weights_of=None)),
 }
 
 
