@@ -1083,7 +1083,7 @@ hipError_t launch_reg_mode(const StreamArgs& a0, int E, int mb, hipStream_t s) {
 
 constexpr int kRowsWQ = 1;                 // INT4: K groups per slice (measured: 2 is slower)
 constexpr int kRowsRBWUp = 2;              // 16-row weight blocks per wave: gate/up, ReLU W_in (2: measured ~5% faster than 4)
-constexpr int kRowsRBWDown = 4;            // and down
+constexpr int kRowsRBWDown = 2;            // and down (2 with 4 K parts: ~5% faster than 4)
 constexpr size_t kRowsMaxLds = 80 * 1024;  // two blocks per CU
 
 template <int MODE, bool INT4, int RBW>
@@ -1175,11 +1175,11 @@ bool stream_rows_applies(int K, int parts, const moe_w4* a, const moe_w4* b) {
 }
 
 int stream_down_parts(int d, int F, int E) {
-  // about two blocks per CU: E * ceil(d / strip rows) strips times the parts
+  // about four blocks per CU: E * ceil(d / strip rows) strips times the parts
   constexpr int NOUT = stream_rows_nout<kSModeDown, kRowsRBWDown>();
   const long long strips = (long long)E * ((d + NOUT - 1) / NOUT);
   for (int P = 8; P > 1; P /= 2)
-    if (F % (512 * P) == 0 && strips * P <= 2 * 256 && F / P <= 8192) return P;
+    if (F % (512 * P) == 0 && strips * P <= 4 * 256 && F / P <= 8192) return P;
   return 1;
 }
 
