@@ -116,9 +116,10 @@ SMALL = {
     "int4_prefill_small": ("mixtral_int4_decode", dict(T=300, d=256, F=384, x_rows_of=None,
                                                        weights_of=None)),
     "single_token": ("mixtral_prefill_bf16", dict(T=1, d=512, F=640)),
-    # small-batch routing: router GEMM split in 128-wide K blocks (d % 256 != 0),
-    # and not split at all (d % 128 != 0: the routing workgroup's own GEMM)
-    "route_split_128": ("mixtral_decode_bf16", dict(T=24, d=384, F=512, x_rows_of=None,
+    # small-batch routing: router GEMM split in 128-wide K blocks
+    # (d % 256 != 0), and not split at all (d % 128 != 0: the routing
+    # workgroup's own GEMM)
+    "route_split_128": ("mixtral_decode_bf16", dict(T=48, d=1664, F=512, x_rows_of=None,
                                                     weights_of=None)),
     "route_unsplit": ("mixtral_decode_bf16", dict(T=8, d=200, F=256, x_rows_of=None,
                                                   weights_of=None)),
