@@ -119,7 +119,7 @@ FLUSH_BYTES = 512 << 20   # read before each cold step: more than the 256 MB MAL
 # the first kernel of the step would pay for)
 
 
-def run_gpu(name, steps, warmup, cold=False):
+def run_gpu(name, steps, warmup, cold=False, flags=0):
     """Warm wall-clock timing of `steps` back-to-back layer calls, then one
     event-timed pass per step (per-stage HIP events).  With cold=True a 512 MB
     buffer is read before each event-timed step, outside its events, so the
@@ -147,7 +147,7 @@ def run_gpu(name, steps, warmup, cold=False):
         runner = moe.LayerRunner(layer, cfg.T)
 
         def call():
-            return runner(x)
+            return runner(x, flags)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -544,6 +544,9 @@ def main():
                     help="CPU seconds of oracle work timed beside each secondary workload "
                          "(0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bf16-rows", default="deepseek_v2_lite_bf16",
+                    help="comma-separated workloads also run with MOE_F_BF16_ROWS (warm; '' for "
+                         "none)")
     ap.add_argument("--replica", default="switch_bf16,deepseek_v2_lite_bf16",
                     help="comma-separated workloads also run with an INT4 replica of their "
                          "heaviest expert ('' for none)")
@@ -641,6 +644,18 @@ def main():
     reps = [run_replica(n, args.steps, args.warmup) for n in args.replica.split(",") if n]
     if reps:
         out["replica"] = reps
+    rows16 = []
+    for n in [n for n in args.bf16_rows.split(",") if n]:
+        import sparse_mixture_experts_wavefront_amd as moe
+        w32, r32 = run_gpu(n, args.steps, args.warmup)
+        w16, r16 = run_gpu(n, args.steps, args.warmup, flags=moe.MOE_F_BF16_ROWS)
+        rows16.append({"workload": n, "cache": "warm", "ms_fp32_rows": round(r32["ms"], 4),
+                       "ms_bf16_rows": round(r16["ms"], 4),
+                       "tokens_per_s_bf16_rows": round(w16.cfg.T / (r16["ms"] / 1000.0), 1),
+                       "stages_us_fp32_rows": r32["stages_us"],
+                       "stages_us_bf16_rows": r16["stages_us"]})
+    if rows16:
+        out["bf16_rows"] = rows16
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     else:

@@ -73,11 +73,18 @@ typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU = 1 } moe_act;
 enum {
   MOE_F_LOGITS_GIVEN = 1u,   /* moe_route_topk / layer: `logits` is an input */
   MOE_F_VALIDATE_ONLY = 2u,  /* check arguments, enqueue nothing */
-  MOE_F_NONDETERMINISTIC_COMBINE = 4u /* reserved: accepted and ignored; every path is
-                                         deterministic (the fused combine of decode
-                                         layers adds at most two rows onto a zeroed
-                                         output, which gives the same sum in either
-                                         order) */
+  MOE_F_NONDETERMINISTIC_COMBINE = 4u, /* reserved: accepted and ignored; every path is
+                                          deterministic (the fused combine of decode
+                                          layers adds at most two rows onto a zeroed
+                                          output, which gives the same sum in either
+                                          order) */
+  MOE_F_BF16_ROWS = 8u /* layer calls with bf16 activations on the tiled path (T > 64,
+                          dense experts, d_ff a multiple of 128): the gate-scaled expert
+                          rows between the down pass and the combine are stored as bf16
+                          (RNE) instead of fp32, halving that traffic (the k rows per
+                          token of k = 6 layers); each row then carries one more bf16
+                          rounding before the fixed-order fp32 sum.  Ignored elsewhere
+                          (weight streaming writes y directly or keeps fp32 rows). */
 };
 
 /* Group-wise asymmetric INT4 weights of one projection, all experts.

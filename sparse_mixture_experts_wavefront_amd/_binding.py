@@ -18,7 +18,7 @@ LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 MOE_ACT_SWIGLU, MOE_ACT_RELU = 0, 1
-MOE_F_LOGITS_GIVEN, MOE_F_VALIDATE_ONLY, MOE_F_NONDETERMINISTIC_COMBINE = 1, 2, 4
+MOE_F_LOGITS_GIVEN, MOE_F_VALIDATE_ONLY, MOE_F_NONDETERMINISTIC_COMBINE, MOE_F_BF16_ROWS = 1, 2, 4, 8
 MOE_ATOMIC_AUTO, MOE_ATOMIC_DENSE, MOE_ATOMIC_EXPERT_CENTRIC = 0, 1, 2
 
 EXPORTED = ("moe_route_topk", "moe_permute", "moe_permute_workspace_size", "moe_grouped_ffn",

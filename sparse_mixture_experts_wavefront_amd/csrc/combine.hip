@@ -12,7 +12,8 @@
 // access, so a decode step of a few tokens still spreads over many CUs.  When
 // the down pass split its reduction, each row arrives as nsplit partial rows and
 // the combine adds them too (slot-major, slice-minor order); the partial rows of
-// one slot are loaded four at a time and added in that order.
+// one slot are loaded four at a time and added in that order.  Rows may be bf16
+// (MOE_F_BF16_ROWS): widened to fp32 exactly before the same sum.
 #include "moe_internal.h"
 
 namespace moe {
@@ -24,9 +25,21 @@ __device__ __forceinline__ void add4(float4& s, const float4 v) {
   s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
 }
 
+// four values of a row: fp32, or bf16 rows (MOE_F_BF16_ROWS) widened exactly
+template <bool BF16ROWS>
+__device__ __forceinline__ float4 load_row4(const float* rows, size_t idx) {
+  if constexpr (BF16ROWS) {
+    const uint2 v = *(const uint2*)((const u16*)rows + idx);
+    return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                       __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+  } else {
+    return *(const float4*)(rows + idx);
+  }
+}
+
 // y[t][i..i+3]: the k rows of token t (each as nsplit partial rows), then the
 // shared term, added in that fixed order
-template <bool BF16OUT>
+template <bool BF16OUT, bool BF16ROWS>
 __device__ __forceinline__ void combine_one(const float* __restrict__ y_rows,
                                             const int32_t* __restrict__ assign_row, int k, int d,
                                             const float* __restrict__ y_shared, void* yv,
@@ -42,16 +55,16 @@ __device__ __forceinline__ void combine_one(const float* __restrict__ y_rows,
     }
   };
   for (int j = 0; j < k; ++j) {
-    const float* base = y_rows + (size_t)assign_row[t * k + j] * d + i;
+    const size_t base = (size_t)assign_row[t * k + j] * d + i;
     int sp = 0;
     for (; sp + 4 <= nsplit; sp += 4) {
       float4 v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = *(const float4*)(base + (size_t)(sp + q) * split_stride);
+      for (int q = 0; q < 4; ++q) v[q] = load_row4<BF16ROWS>(y_rows, base + (size_t)(sp + q) * split_stride);
 #pragma unroll
       for (int q = 0; q < 4; ++q) add(v[q]);
     }
-    for (; sp < nsplit; ++sp) add(*(const float4*)(base + (size_t)sp * split_stride));
+    for (; sp < nsplit; ++sp) add(load_row4<BF16ROWS>(y_rows, base + (size_t)sp * split_stride));
   }
   if (y_shared) add4(s, *(const float4*)(y_shared + t * d + i));
   if constexpr (BF16OUT) {
@@ -65,7 +78,7 @@ __device__ __forceinline__ void combine_one(const float* __restrict__ y_rows,
 }
 
 // work item b = (token b / nchunk, columns of chunk b % nchunk); grid-stride
-template <bool BF16OUT>
+template <bool BF16OUT, bool BF16ROWS>
 __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y_rows,
                                                      const int32_t* __restrict__ assign_row,
                                                      int k, int d,
@@ -77,7 +90,8 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y
     const size_t t = b / nchunk;
     const int i = (int)(b - t * nchunk) * kCombCols + threadIdx.x * 4;
     if (i < d)
-      combine_one<BF16OUT>(y_rows, assign_row, k, d, y_shared, yv, nsplit, split_stride, t, i);
+      combine_one<BF16OUT, BF16ROWS>(y_rows, assign_row, k, d, y_shared, yv, nsplit, split_stride,
+                                     t, i);
   }
 }
 
@@ -85,17 +99,20 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ y
 
 hipError_t launch_combine(const float* y_rows, const int32_t* assign_row, int T, int k, int d,
                           const float* y_shared, void* y, moe_dtype ydt, hipStream_t s,
-                          int nsplit, size_t split_stride) {
+                          int nsplit, size_t split_stride, bool rows_bf16) {
   if (T == 0) return hipSuccess;
   // one block per (token, 256 columns), at most 2^20 blocks (grid-stride beyond)
   const size_t items = (size_t)((d + kCombCols - 1) / kCombCols) * (size_t)T;
   const dim3 grid((unsigned)(items < (1u << 20) ? items : (1u << 20)));
-  if (ydt == MOE_DT_BF16)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(64), 0, s, y_rows, assign_row, k, d,
-                       y_shared, y, nsplit, split_stride, items);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(64), 0, s, y_rows, assign_row, k, d,
-                       y_shared, y, nsplit, split_stride, items);
+#define MOE_COMBINE(O, R)                                                                    \
+  hipLaunchKernelGGL((combine_kernel<O, R>), grid, dim3(64), 0, s, y_rows, assign_row, k, d, \
+                     y_shared, y, nsplit, split_stride, items)
+  if (ydt == MOE_DT_BF16) {
+    if (rows_bf16) MOE_COMBINE(true, true); else MOE_COMBINE(true, false);
+  } else {
+    if (rows_bf16) MOE_COMBINE(false, true); else MOE_COMBINE(false, false);
+  }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

@@ -69,6 +69,7 @@ struct TileArgs {
   int m_tiles_max, n_tiles;
   int ksplit;              // K slices (down only): slice s covers K [s*K/ksplit, +K/ksplit)
   size_t ystride;          // elements between the partial outputs of two slices
+  int ybf16;               // down (256x256 path): Y holds bf16 rows (RNE), not fp32
   const u16* xB0;          // if not NULL, expert xslot takes its weights from xB0 (and
   const u16* xB1;          // xB1, up for SwiGLU), [N][K] each, instead of B0/B1 (256x256 path)
   int xslot;
@@ -620,30 +621,41 @@ void grouped_gemm_tile_kernel(TileArgs p) {
         float* gsc = (float*)sA0;
         gsc[tid] = gpre;
         __syncthreads();
+        const int esz = p.ybf16 ? 2 : 4;  // bytes per output element
         const __amdgpu_buffer_rsrc_t yres = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(p.Y + (size_t)ks * p.ystride + (size_t)row0 * p.N), (short)0, rvalid * p.N * 4,
-            0x00020000);
+            (void*)((const char*)p.Y + ((size_t)ks * p.ystride + (size_t)row0 * p.N) * esz),
+            (short)0, rvalid * p.N * esz, 0x00020000);
         const int wcol0 = n_tile * 256 + wq * 64;
-        auto rows = [&](auto whole) __attribute__((always_inline)) {
+        auto rows = [&](auto whole, auto bf16) __attribute__((always_inline)) {
           constexpr bool WHOLE = decltype(whole)::value;  // the wave's 64 columns all < N
+          constexpr bool BF = decltype(bf16)::value;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int row = i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
               const float g = gsc[row];
-              const int off = (row * p.N + wcol0 + fr) * 4;
+              const int off = (row * p.N + wcol0 + fr) * (BF ? 2 : 4);
 #pragma unroll
               for (int j = 0; j < 2; ++j)
-                if (WHOLE || wcol0 + j * 32 + fr < p.N)
-                  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g * hacc[i][j][r]), yres,
-                                                        off + j * 128, 0, 0);
+                if (WHOLE || wcol0 + j * 32 + fr < p.N) {
+                  if constexpr (BF)
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(g * hacc[i][j][r]), yres,
+                                                          off + j * 64, 0, 0);
+                  else
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g * hacc[i][j][r]),
+                                                          yres, off + j * 128, 0, 0);
+                }
             }
         };
-        if (wcol0 + 64 <= p.N)
-          rows(std::true_type{});
-        else
-          rows(std::false_type{});
+        const bool whole = wcol0 + 64 <= p.N;
+        if (p.ybf16) {
+          if (whole) rows(std::true_type{}, std::true_type{});
+          else rows(std::false_type{}, std::true_type{});
+        } else {
+          if (whole) rows(std::true_type{}, std::false_type{});
+          else rows(std::false_type{}, std::false_type{});
+        }
       }
       return;
     }
@@ -903,30 +915,41 @@ void grouped_gemm_tile_kernel(TileArgs p) {
     float* gsc = (float*)sA0;
     gsc[tid] = gpre;
     __syncthreads();
+    const int esz = p.ybf16 ? 2 : 4;  // bytes per output element
     const __amdgpu_buffer_rsrc_t yres = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.Y + (size_t)ks * p.ystride + (size_t)row0 * p.N), (short)0, rvalid * p.N * 4,
-        0x00020000);
+        (void*)((const char*)p.Y + ((size_t)ks * p.ystride + (size_t)row0 * p.N) * esz), (short)0,
+        rvalid * p.N * esz, 0x00020000);
     const int wcol0 = n_tile * 256 + __builtin_amdgcn_readfirstlane(wn) * 128;
-    auto rows = [&](auto whole) __attribute__((always_inline)) {
+    auto rows = [&](auto whole, auto bf16) __attribute__((always_inline)) {
       constexpr bool WHOLE = decltype(whole)::value;  // all of the wave's 128 columns < N
+      constexpr bool BF = decltype(bf16)::value;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
           const float g = gsc[row];
-          const int off = (row * p.N + wcol0 + fr) * 4;
+          const int off = (row * p.N + wcol0 + fr) * (BF ? 2 : 4);
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (WHOLE || wcol0 + j * 32 + fr < p.N)
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g * acc[i][j][r]), yres,
-                                                    off + j * 128, 0, 0);
+            if (WHOLE || wcol0 + j * 32 + fr < p.N) {
+              if constexpr (BF)
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(g * acc[i][j][r]), yres,
+                                                      off + j * 64, 0, 0);
+              else
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g * acc[i][j][r]), yres,
+                                                      off + j * 128, 0, 0);
+            }
         }
     };
-    if (wcol0 + 128 <= p.N)
-      rows(std::true_type{});
-    else
-      rows(std::false_type{});
+    const bool whole = wcol0 + 128 <= p.N;
+    if (p.ybf16) {
+      if (whole) rows(std::true_type{}, std::true_type{});
+      else rows(std::false_type{}, std::true_type{});
+    } else {
+      if (whole) rows(std::true_type{}, std::false_type{});
+      else rows(std::false_type{}, std::false_type{});
+    }
     return;
   }
   if constexpr (MODE == kUpRelu) {
@@ -1116,6 +1139,11 @@ hipError_t run_tiles(TileArgs a, hipStream_t s) {
 
 }  // namespace
 
+bool ffn_rows_bf16_applies(const FfnProblem& p) {
+  // the 256x256 down path of the tiled launch with dense bf16 experts
+  return p.dt == MOE_DT_BF16 && p.w && !p.w->q_up && !stream_ffn_applies(p) && p.F % 128 == 0;
+}
+
 bool ffn_direct_applies(const FfnProblem& p) {
   if (p.offsets && !p.row_assign) return false;
   return stream_ffn_applies(p) && p.k <= 2 && p.down_splits <= 1;
@@ -1245,6 +1273,10 @@ hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid
     return run_tiles<128, 128, kDown, true>(b, s);
   }
   b.B0 = (const u16*)p.w->w_down;
+  if (p.rows_bf16) {
+    if (!ffn_rows_bf16_applies(p)) return hipErrorInvalidValue;
+    b.ybf16 = 1;
+  }
   if (p.xw) {
     b.xB0 = (const u16*)p.xw->w_down;
     b.xslot = p.xslot;

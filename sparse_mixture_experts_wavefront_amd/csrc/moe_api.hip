@@ -46,7 +46,7 @@ moe_status hip_status(hipError_t e, const char* what) {
 }
 
 constexpr unsigned kKnownFlags =
-    MOE_F_LOGITS_GIVEN | MOE_F_VALIDATE_ONLY | MOE_F_NONDETERMINISTIC_COMBINE;
+    MOE_F_LOGITS_GIVEN | MOE_F_VALIDATE_ONLY | MOE_F_NONDETERMINISTIC_COMBINE | MOE_F_BF16_ROWS;
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -506,6 +506,7 @@ moe_status layer_forward_impl(const moe_layer_desc* L, const moe_replica* R, con
   p.offsets = f_offsets;
   p.row_assign = f_row_assign;
   p.y_direct = direct ? (float*)y : nullptr;
+  p.rows_bf16 = (flags & MOE_F_BF16_ROWS) != 0 && !direct && ffn_rows_bf16_applies(p);
   // the replica (slot E): with many rows its INT4 projections are decoded to
   // bf16 and it runs as one more expert of the same tiled launches, so its
   // tiles share the chip with the others'; at decode sizes (or shapes off the
@@ -562,7 +563,7 @@ moe_status layer_forward_impl(const moe_layer_desc* L, const moe_replica* R, con
   stage(5, st);
   if (!direct)
     e = launch_combine(w.y_rows, f_assign_row, T, k, d, w.y_shared, y, ydt, st, w.down_splits,
-                       (size_t)T * k * d);
+                       (size_t)T * k * d, p.rows_bf16);
   stage(6, st);
   return hip_status(e, "combine");
 }

@@ -103,6 +103,8 @@ struct FfnProblem {
                                  // pass adds each gate-scaled row into y_direct[token]
                                  // [T][d] fp32 (zeroed by the caller) instead of
                                  // writing y_rows: the combine, fused
+  bool rows_bf16;                // y_rows holds bf16 rows (tiled bf16 path only: see
+                                 // ffn_rows_bf16_applies)
   const moe_experts* xw;         // if not NULL: expert xslot uses these bf16 weights
   int xslot;                     // ([N][K] per projection) instead of w's (tiled path)
   float* zero_y;                 // weight-streaming path: if not NULL, the gate/up grid
@@ -122,6 +124,9 @@ hipError_t launch_grouped_ffn(const FfnProblem& p, hipStream_t s, hipEvent_t mid
 // with its two K slices; measured on the Switch-shaped layer, its fp32 atomics
 // cost more than the combine launch they replace, so it keeps the combine.)
 bool ffn_direct_applies(const FfnProblem& p);
+// Whether the down pass can store its gate-scaled rows as bf16 (the 256x256
+// tile path with dense bf16 experts)
+bool ffn_rows_bf16_applies(const FfnProblem& p);
 
 // Weight-streaming variant for few rows per expert (decode); same contract as
 // launch_grouped_ffn.
@@ -243,6 +248,6 @@ hipError_t launch_atomic_ec_reduce(const float* ypart, int T, int d, int N,
 // assign_row[t*k+j] * d], plus y_shared[t]; fixed order, so deterministic.
 hipError_t launch_combine(const float* y_rows, const int32_t* assign_row, int T, int k, int d,
                           const float* y_shared, void* y, moe_dtype ydt, hipStream_t s,
-                          int nsplit = 1, size_t split_stride = 0);
+                          int nsplit = 1, size_t split_stride = 0, bool rows_bf16 = false);
 
 }  // namespace moe

@@ -45,12 +45,12 @@ def _tol(wl):
     return (1e-5, 1e-5, 1e-5) if wl.cfg.dtype == "f32" else (1e-4, 2e-2, 1e-2)
 
 
-def run_layer(wl, logits=None):
+def run_layer(wl, logits=None, flags=0):
     from sparse_mixture_experts_wavefront_amd.device_inputs import to_device
     moe = _moe()
     layer, x = to_device(wl)
     lg = None if logits is None else torch.from_numpy(logits).cuda()
-    y, aux = moe.layer_forward(layer, x, logits=lg)
+    y, aux = moe.layer_forward(layer, x, logits=lg, flags=flags)
     torch.cuda.synchronize()
     T, k = wl.cfg.T, wl.cfg.k
     out = {n: t.cpu().numpy() for n, t in aux.items()}
@@ -137,6 +137,33 @@ def test_layer_parity_small(case):
     g = run_layer(wl)
     check_routing(wl, g)
     check_y(wl, g)
+
+
+BF16_ROWS = {
+    "switch_small": ("switch_bf16", dict(T=300, d=256, F=384)),
+    "mixtral_small": ("mixtral_prefill_bf16", dict(T=333, d=512, F=640)),
+    "deepseek_small": ("deepseek_v2_lite_bf16", dict(T=257, d=256, F=256, F_shared=64)),
+    "deepseek_full": ("deepseek_v2_lite_bf16", {}),
+}
+
+
+@pytest.mark.parametrize("case", list(BF16_ROWS))
+def test_bf16_rows_flag(case):
+    """MOE_F_BF16_ROWS (tiled path, d_ff a multiple of 128): the gate-scaled
+    expert rows travel as bf16 between the down pass and the combine (one more
+    rounding per row, the same tolerance); the result stays run-to-run
+    deterministic and differs from the fp32-row one (the flag took effect)."""
+    name, over = BF16_ROWS[case]
+    _say("bf16 rows %s %s" % (case, over))
+    moe = _moe()
+    wl = _workload(name, **over)
+    g = run_layer(wl, flags=moe.MOE_F_BF16_ROWS)
+    check_routing(wl, g)
+    check_y(wl, g)
+    g2 = run_layer(wl, flags=moe.MOE_F_BF16_ROWS)
+    assert np.array_equal(g["y"], g2["y"])
+    g32 = run_layer(wl)
+    assert not np.array_equal(g["y"], g32["y"])
 
 
 def test_int4_fractional_zero_point():
