@@ -33,6 +33,7 @@ namespace {
 constexpr int kGateChMax = 32;  // listed channels per gate block (16 or 32)
 constexpr int kDownCols = 1024; // output columns per down block (4 per lane)
 constexpr int kDownJc = 64;     // channels staged in LDS per down step
+constexpr int kCompactSeg = 128;  // flags per thread of the list kernel (d_ff <= 32768)
 
 // ---- 2. per-expert list of kept channels ------------------------------------
 // Thread tid owns a segment of seg flags (a multiple of 8, read as 8-byte words;
@@ -49,14 +50,17 @@ __global__ __launch_bounds__(256) void floe_compact_kernel(const int32_t* __rest
     if (tid == 0) nnz[e] = 0;
     return;
   }
-  const int seg = (((F + 255) / 256) + 7) & ~7;
+  const int seg = (((F + 255) / 256) + 7) & ~7;  // <= kCompactSeg (F <= 32768)
   const int f0 = min(tid * seg, F), f1 = min(f0 + seg, F);
   const uint8_t* fl = flags + (size_t)e * F;
+  // the segment's flag words, all loads issued before the first use
+  uint2 v[kCompactSeg / 8];
+#pragma unroll
+  for (int i = 0; i < kCompactSeg / 8; ++i)
+    v[i] = f0 + 8 * i < f1 ? *(const uint2*)(fl + f0 + 8 * i) : make_uint2(0u, 0u);
   int c = 0;
-  for (int f = f0; f < f1; f += 8) {
-    const uint2 v = *(const uint2*)(fl + f);
-    c += __popc(v.x) + __popc(v.y);
-  }
+#pragma unroll
+  for (int i = 0; i < kCompactSeg / 8; ++i) c += __popc(v[i].x) + __popc(v[i].y);
   // inclusive scan inside the wave, then across the 4 waves
   int incl = c;
   for (int o = 1; o < 64; o <<= 1) {
@@ -69,12 +73,11 @@ __global__ __launch_bounds__(256) void floe_compact_kernel(const int32_t* __rest
   for (int w = 0; w < wv; ++w) base += wsum[w];
   int pos = base + incl - c;
   int32_t* out = list + (size_t)e * F;
-  for (int f = f0; f < f1; f += 8) {
-    const uint2 v = *(const uint2*)(fl + f);
+#pragma unroll
+  for (int i = 0; i < kCompactSeg / 8; ++i)
 #pragma unroll
     for (int b = 0; b < 8; ++b)
-      if (((b < 4 ? v.x : v.y) >> (8 * (b & 3))) & 1u) out[pos++] = f + b;
-  }
+      if (((b < 4 ? v[i].x : v[i].y) >> (8 * (b & 3))) & 1u) out[pos++] = f0 + 8 * i + b;
   if (tid == 255) nnz[e] = base + incl;
 }
 
@@ -91,89 +94,107 @@ struct GateArgs {
   const float* U;          // [rows][F]
   const float* thr;        // [E]
   u16* Hc;                 // [rows][F], column j = j-th listed channel
-  int nchunk;              // F / CH
+  int E;                   // experts (E <= 64)
 };
 
-// Each wave owns a quarter of K; lane (r, g) feeds MFMA step s with K values
-// [s*32 + g*8, +8) of an iteration of 128 (channel row r of its 16-row block,
-// token row r of the B operand), loads two iterations ahead.
-template <int CH>
+// Work items are chunks of CH consecutive listed channels, numbered over the
+// experts in id order (an expert without rows has none); blocks take chunks
+// blockIdx.x, + gridDim.x, ... so the grid is sized to the chip, not to the
+// largest possible list.  Each wave owns a quarter of K; lane (r, g) feeds MFMA
+// step s with K values [s*32 + g*8, +8) of an iteration of 128 (channel row r
+// of its 16-row block, token row r of the B operand), loads D iterations ahead.
+template <int CH, int D>
 __global__ __launch_bounds__(256) void floe_gate_kernel(GateArgs p) {
-  constexpr int RB = CH / 16, NS = 4, D = 2;
+  constexpr int RB = CH / 16, NS = 4;
   __shared__ f32x4 red[4][RB][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int e = blockIdx.x / p.nchunk;
-  const int j0 = (blockIdx.x - e * p.nchunk) * CH;
-  const int nz = __builtin_amdgcn_readfirstlane(p.nnz[e]);
-  if (j0 >= nz) return;
-  const int row0 = __builtin_amdgcn_readfirstlane(p.offsets[e]);
-  const int cnt = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]) - row0;
-  if (cnt <= 0) return;
+  // chunk counts per expert (lane = expert), inclusive scan over the wave
+  int nch = 0;
+  if (lane < p.E && p.offsets[lane + 1] > p.offsets[lane]) nch = (p.nnz[lane] + CH - 1) / CH;
+  int incl = nch;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  const int total = __shfl(incl, 63, 64);
   const int r16 = lane & 15, g = lane >> 4;
   const int Kq = p.K >> 2, kw0 = w * Kq, iters = Kq / 128;
-  const int32_t* lst = p.list + (size_t)e * p.F;
-  const u16* wrow[RB];
+  for (int ci = blockIdx.x; ci < total; ci += gridDim.x) {
+    const int e = __builtin_amdgcn_readfirstlane(__builtin_ctzll(__ballot(incl > ci)));
+    const int j0 = __builtin_amdgcn_readfirstlane((ci - __shfl(incl - nch, e, 64)) * CH);
+    const int nz = __builtin_amdgcn_readfirstlane(p.nnz[e]);
+    const int row0 = __builtin_amdgcn_readfirstlane(p.offsets[e]);
+    const int cnt = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]) - row0;
+    const int32_t* lst = p.list + (size_t)e * p.F;
+    const u16* wrow[RB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int j = min(j0 + rb * 16 + r16, nz - 1);  // past the list: a listed row, unused
-    wrow[rb] = p.Wg + ((size_t)e * p.F + lst[j]) * p.K + kw0 + g * 8;
-  }
-  for (int mbase = 0; mbase < cnt; mbase += 16) {
-    const int mrows = min(16, cnt - mbase);
-    const int tr = row0 + mbase + min(r16, mrows - 1);
-    const u16* xr = p.X + (size_t)(p.gather[tr] / p.k) * p.K + kw0 + g * 8;
-    struct Set {
-      u32x4 w[RB][NS];
-      u32x4 x[NS];
-    };
-    auto load = [&](Set& S, int it) __attribute__((always_inline)) {
-      it = min(it, iters - 1);  // past the end: reload the last iteration (unused)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int s = 0; s < NS; ++s) S.w[rb][s] = *(const u32x4*)(wrow[rb] + it * 128 + s * 32);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) S.x[s] = *(const u32x4*)(xr + it * 128 + s * 32);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    f32x4 acc[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Set st[D];
-#pragma unroll
-    for (int u = 0; u < D; ++u) load(st[u], u);
-    for (int it0 = 0; it0 < iters; it0 += D) {
-#pragma unroll
-      for (int u = 0; u < D; ++u) {
-        if (it0 + u < iters) {
-#pragma unroll
-          for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-              acc[rb] = mfma16(as_bf16x8(st[u].w[rb][s]), as_bf16x8(st[u].x[s]), acc[rb]);
-        }
-        load(st[u], it0 + u + D);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int rb = 0; rb < RB; ++rb) {
+      const int j = min(j0 + rb * 16 + r16, nz - 1);  // past the list: a listed row, unused
+      wrow[rb] = p.Wg + ((size_t)e * p.F + lst[j]) * p.K + kw0 + g * 8;
     }
-    __syncthreads();
+    for (int mbase = 0; mbase < cnt; mbase += 16) {
+      const int mrows = min(16, cnt - mbase);
+      const int tr = row0 + mbase + min(r16, mrows - 1);
+      const u16* xr = p.X + (size_t)(p.gather[tr] / p.k) * p.K + kw0 + g * 8;
+      struct Set {
+        u32x4 w[RB][NS];
+        u32x4 x[NS];
+      };
+      auto load = [&](Set& S, int it) __attribute__((always_inline)) {
+        it = min(it, iters - 1);  // past the end: reload the last iteration (unused)
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) red[w][rb][lane] = acc[rb];
-    __syncthreads();
-    for (int o = tid; o < 16 * CH; o += 256) {
-      const int m = o / CH, col = o % CH;
-      const int j = j0 + col;
-      if (mbase + m >= cnt || j >= nz) continue;
-      // C layout of the 16x16 MFMA: channel row 4*(lane/16)+i, token column lane%16
-      const int rb = col >> 4, rr = col & 15;
-      const int ln = (rr >> 2) * 16 + m, i = rr & 3;
-      float gv = 0.0f;
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) gv += red[ww][rb][ln][i];
-      const size_t orow = (size_t)(row0 + mbase + m);
-      const float u = p.U[orow * p.F + lst[j]];
-      p.Hc[orow * p.F + j] = fabsf(u) > p.thr[e] ? f32_to_bf16(silu_f32(gv) * u) : (u16)0;
+          for (int s = 0; s < NS; ++s) S.w[rb][s] = *(const u32x4*)(wrow[rb] + it * 128 + s * 32);
+        // token lanes past the pass's rows take zeros and fetch nothing
+        if (r16 < mrows) {
+#pragma unroll
+          for (int s = 0; s < NS; ++s) S.x[s] = *(const u32x4*)(xr + it * 128 + s * 32);
+        } else {
+#pragma unroll
+          for (int s = 0; s < NS; ++s) S.x[s] = u32x4{0u, 0u, 0u, 0u};
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      f32x4 acc[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      Set st[D];
+#pragma unroll
+      for (int u = 0; u < D; ++u) load(st[u], u);
+      for (int it0 = 0; it0 < iters; it0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+          if (it0 + u < iters) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+              for (int rb = 0; rb < RB; ++rb)
+                acc[rb] = mfma16(as_bf16x8(st[u].w[rb][s]), as_bf16x8(st[u].x[s]), acc[rb]);
+          }
+          load(st[u], it0 + u + D);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) red[w][rb][lane] = acc[rb];
+      __syncthreads();
+      for (int o = tid; o < 16 * CH; o += 256) {
+        const int m = o / CH, col = o % CH;
+        const int j = j0 + col;
+        if (mbase + m >= cnt || j >= nz) continue;
+        // C layout of the 16x16 MFMA: channel row 4*(lane/16)+i, token column lane%16
+        const int rb = col >> 4, rr = col & 15;
+        const int ln = (rr >> 2) * 16 + m, i = rr & 3;
+        float gv = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) gv += red[ww][rb][ln][i];
+        const size_t orow = (size_t)(row0 + mbase + m);
+        const float u = p.U[orow * p.F + lst[j]];
+        p.Hc[orow * p.F + j] = fabsf(u) > p.thr[e] ? f32_to_bf16(silu_f32(gv) * u) : (u16)0;
+      }
     }
   }
 }
@@ -190,9 +211,12 @@ struct DownArgs {
   const float* gate;
   float* Y;                // [S][rows][d]
   int S, ncc, rows;
+  int E;                   // experts (E <= 64)
 };
 
-// Block (expert, 1024-column chunk, channel slice); lane owns 4 consecutive
+// Block (expert with rows, 1024-column chunk, channel slice), experts with rows
+// numbered in id order so the grid covers only as many as the call can have;
+// lane owns 4 consecutive
 // output columns (one 8-byte load per channel) and runs fp32 FMAs over the
 // slice's channels, 8 at a time, the hidden values of up to MR token rows
 // broadcast from LDS.
@@ -203,7 +227,9 @@ __global__ __launch_bounds__(256) void floe_down_kernel(DownArgs p) {
   const int tid = threadIdx.x;
   const int s = blockIdx.x % p.S;
   const int cc = (blockIdx.x / p.S) % p.ncc;
-  const int e = blockIdx.x / (p.S * p.ncc);
+  const int e = __builtin_amdgcn_readfirstlane(
+      active_expert(p.offsets, 1, p.E, blockIdx.x / (p.S * p.ncc)));
+  if (e < 0) return;
   const int row0 = __builtin_amdgcn_readfirstlane(p.offsets[e]);
   const int cnt = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]) - row0;
   if (cnt <= 0) return;
@@ -294,6 +320,7 @@ int floe_down_splits(int d, int E) {
 const char* floe_unsupported(int T, int d, int F, int k) {
   if (const char* why = mwq_ffn_unsupported(T, d, F, k)) return why;
   if (F % kGateChMax != 0) return "sparse down-projection needs d_ff a multiple of 32";
+  if (F > 256 * kCompactSeg) return "sparse down-projection needs d_ff <= 32768";
   return nullptr;
 }
 
@@ -319,13 +346,15 @@ hipError_t launch_floe_ffn(const FloeProblem& p, hipStream_t s, hipEvent_t mid) 
   g.thr = p.w->threshold;
   g.Hc = p.Hc;
   // few rows (a one- or two-token step): few experts are active, so narrower
-  // blocks give the gather more of them
+  // blocks, each with more loads in flight, give the gather more of them
+  g.E = p.E;
+  const int eact = p.rows < p.E ? p.rows : p.E;  // experts that can have rows
   if (p.rows <= 4) {
-    g.nchunk = p.F / 16;
-    hipLaunchKernelGGL(floe_gate_kernel<16>, dim3(p.E * g.nchunk), dim3(256), 0, s, g);
+    const int grid = std::min(eact * (p.F / 16), 512);
+    hipLaunchKernelGGL((floe_gate_kernel<16, 4>), dim3(grid), dim3(256), 0, s, g);
   } else {
-    g.nchunk = p.F / 32;
-    hipLaunchKernelGGL(floe_gate_kernel<32>, dim3(p.E * g.nchunk), dim3(256), 0, s, g);
+    const int grid = std::min(eact * (p.F / 32), 2048);
+    hipLaunchKernelGGL((floe_gate_kernel<32, 2>), dim3(grid), dim3(256), 0, s, g);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (mid) {
@@ -346,7 +375,8 @@ hipError_t launch_floe_ffn(const FloeProblem& p, hipStream_t s, hipEvent_t mid) 
   dn.S = p.splits;
   dn.ncc = (p.d + kDownCols - 1) / kDownCols;
   dn.rows = p.rows;
-  hipLaunchKernelGGL(floe_down_kernel, dim3(p.E * dn.ncc * dn.S), dim3(256), 0, s, dn);
+  dn.E = p.E;
+  hipLaunchKernelGGL(floe_down_kernel, dim3(eact * dn.ncc * dn.S), dim3(256), 0, s, dn);
   return hipGetLastError();
 }
 

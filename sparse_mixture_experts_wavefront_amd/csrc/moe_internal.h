@@ -45,6 +45,20 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// The ai-th expert (in id order) among those with rows, -1 past the last one.
+// Blocks are numbered over the experts that have rows, so a step with few
+// active experts launches few blocks and none waits only to find itself idle.
+// Each wave computes it on its own (lane = expert, E <= kMaxExperts = 64).
+__device__ __forceinline__ int active_expert(const int32_t* offsets, int gpe, int E, int ai) {
+  const int lane = threadIdx.x & 63;
+  bool has = false;
+  if (lane < E) has = offsets[gpe * (lane + 1)] > offsets[gpe * lane];
+  unsigned long long act = __ballot(has);
+  if (ai >= __popcll(act)) return -1;
+  for (int i = 0; i < ai; ++i) act &= act - 1ull;
+  return __builtin_ctzll(act);
+}
+
 // g / (1 + e^-g) with the hardware reciprocal (about 1 ulp of fp32): every
 // caller rounds the product with the up value to bf16, 2^14 times coarser
 __device__ __forceinline__ float silu_f32(float g) {

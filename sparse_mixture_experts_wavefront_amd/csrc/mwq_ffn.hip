@@ -73,6 +73,7 @@ struct MwqArgs {
   const int32_t* gate_map; // down: row -> flat assignment (gate index)
   const float* gate;
   int nblk_per_expert;
+  int E;                   // experts (E <= 64)
   uint32_t xbytes;         // bytes of X (buffer resource size)
 };
 
@@ -158,8 +159,10 @@ void mwq_stream_kernel(MwqArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int e = blockIdx.x / p.nblk_per_expert;
-  const int nb = blockIdx.x - e * p.nblk_per_expert;
+  const int ai = blockIdx.x / p.nblk_per_expert;
+  const int nb = blockIdx.x - ai * p.nblk_per_expert;
+  const int e = __builtin_amdgcn_readfirstlane(active_expert(p.offsets, p.gpe, p.E, ai));
+  if (e < 0) return;
   const int* off = p.offsets + p.gpe * e;
   const int row0 = __builtin_amdgcn_readfirstlane(off[0]);
   const int cnt = __builtin_amdgcn_readfirstlane(off[p.gpe]) - row0;
@@ -231,9 +234,10 @@ void mwq_stream_kernel(MwqArgs p) {
   auto pass = [&](auto wmc, int mbase) __attribute__((always_inline)) {
     constexpr int WM = decltype(wmc)::value;
     const int mrows = min(16, cnt - mbase);
-    const int tr = row0 + mbase + min(r16, mrows - 1);  // rows past the count: clamped copies
+    const int tr = row0 + mbase + min(r16, mrows - 1);  // rows past the count: clamped (no load)
     const int src = p.gather ? p.gather[tr] / p.k : tr;
     const uint32_t xoff = ((uint32_t)src * (uint32_t)p.ldx + (uint32_t)g * 128u) * 2u;
+    const bool xrow = r16 < mrows;  // token lanes past the pass's rows read zeros, fetch nothing
 
     f32x4 acc2[RB], acc3[RB], acc4[RB];
 #pragma unroll
@@ -274,7 +278,7 @@ void mwq_stream_kernel(MwqArgs p) {
       for (int s = 0; s < 4; ++s)
         S.x[s] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                       xres, (int)(live ? xoff + (kq + (uint32_t)s * 8u) * 2u : p.xbytes), 0, 0));
+                       xres, (int)(live && xrow ? xoff + (kq + (uint32_t)s * 8u) * 2u : p.xbytes), 0, 0));
       // sets are issued whole and in order, so the oldest set is complete once
       // vmcnt <= the loads of the younger set
       __builtin_amdgcn_sched_barrier(0);
@@ -429,12 +433,16 @@ size_t mwq_lds_bytes(int K) {
 constexpr size_t kMwqMaxLds = 64 * 1024;
 constexpr int kRmGateUp = MWQ_RM_GU, kRmDown = MWQ_RM_DN;
 
+// rows: routed rows of the call, so at most min(E, rows) experts have any
 template <int MODE, int RM>
-hipError_t launch_mwq_mode(MwqArgs a, int E, hipStream_t s) {
+hipError_t launch_mwq_mode(MwqArgs a, int E, int rows, hipStream_t s) {
   const size_t lds = mwq_lds_bytes<MODE, RM>(a.K);
-  if (lds > kMwqMaxLds) return hipErrorInvalidValue;
+  if (lds > kMwqMaxLds || E > kMaxExperts) return hipErrorInvalidValue;
   a.nblk_per_expert = a.N / RM;
-  hipLaunchKernelGGL((mwq_stream_kernel<MODE, RM>), dim3((unsigned)(E * a.nblk_per_expert)),
+  a.E = E;
+  const int eact = rows < E ? rows : E;
+  if (eact <= 0) return hipSuccess;
+  hipLaunchKernelGGL((mwq_stream_kernel<MODE, RM>), dim3((unsigned)(eact * a.nblk_per_expert)),
                      dim3(256), lds, s, a);
   return hipGetLastError();
 }
@@ -467,8 +475,8 @@ hipError_t launch_mwq_ffn(const MwqProblem& p, hipStream_t s, hipEvent_t mid) {
   a.gpe = 3;
   a.H = (u16*)p.H;
   a.xbytes = (uint32_t)((size_t)p.T * p.d * 2);
-  hipError_t e = relu ? launch_mwq_mode<kMModeRelu, kRmGateUp>(a, p.E, s)
-                      : launch_mwq_mode<kMModeGateUp, kRmGateUp>(a, p.E, s);
+  hipError_t e = relu ? launch_mwq_mode<kMModeRelu, kRmGateUp>(a, p.E, p.rows, s)
+                      : launch_mwq_mode<kMModeGateUp, kRmGateUp>(a, p.E, p.rows, s);
   if (e != hipSuccess) return e;
   if (mid) {
     e = hipEventRecord(mid, s);
@@ -489,7 +497,7 @@ hipError_t launch_mwq_ffn(const MwqProblem& p, hipStream_t s, hipEvent_t mid) {
   b.gate_map = p.row_assign;
   b.gate = p.gate;
   b.xbytes = (uint32_t)((size_t)p.rows * p.F * 2);
-  return launch_mwq_mode<kMModeDown, kRmDown>(b, p.E, s);
+  return launch_mwq_mode<kMModeDown, kRmDown>(b, p.E, p.rows, s);
 }
 
 hipError_t launch_int2_up(const void* x, int T, int d, int F, int E, int k, const moe_wmwq* w,
@@ -511,7 +519,7 @@ hipError_t launch_int2_up(const void* x, int T, int d, int F, int E, int k, cons
   a.thr = thr;
   a.flags = flags;
   a.xbytes = (uint32_t)((size_t)T * d * 2);
-  return launch_mwq_mode<kMModeUp, kRmDown>(a, E, s);
+  return launch_mwq_mode<kMModeUp, kRmDown>(a, E, T * k, s);
 }
 
 }  // namespace moe
