@@ -98,6 +98,9 @@ SMALL = {
     "many_rows": lambda: _small(T=64, E=4),
     # K ranges that leave waves idle in the INT2 up pass (d: 3 iterations of 512)
     "ragged": lambda: _small(T=24, d=1536, F=2560),
+    # a few active experts among 64: blocks are numbered over the active ones
+    # (lane = expert up to 63) and the gate chunks over their lists
+    "few_of_many": lambda: _small(T=3, E=64),
     "shared_experts": lambda: _workload("deepseek_v2_lite_bf16", T=40, d=512, F=512, E=16, k=4,
                                         F_shared=256, floe=True, sparsity=0.9),
 }

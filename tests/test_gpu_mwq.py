@@ -114,6 +114,8 @@ SMALL = {
     "many_rows": lambda: _small(T=64, E=4),
     # K ranges that leave waves with nothing (d: 3 iterations of 512, F: 5)
     "ragged_k": lambda: _small(T=24, d=1536, F=2560),
+    # T*k = 4 of 20 experts: the grid covers four experts, numbered over those with rows
+    "few_of_many": lambda: _small(T=2, E=20),
     "relu_k1": lambda: _workload("switch_bf16", T=40, d=512, F=1024, mwq=True),
     "shared_experts": lambda: _workload("deepseek_v2_lite_bf16", T=48, d=512, F=512, E=16, k=4,
                                         F_shared=256, mwq=True),
