@@ -1072,15 +1072,12 @@ __global__ __launch_bounds__(256) void ffn_f32_up_kernel(const float* __restrict
   const int t = gather ? gather[r] / k : r;
   const float* xr = x + (size_t)t * d;
   const float* wur = wu + ((size_t)e * F + f) * d;
-  float u = 0.0f;
-  for (int i = 0; i < d; ++i) u = fmaf(xr[i], wur[i], u);
+  const float u = dot_f32(xr, wur, d);
   float h;
   if (relu) {
     h = fmaxf(u, 0.0f);
   } else {
-    const float* wgr = wg + ((size_t)e * F + f) * d;
-    float g = 0.0f;
-    for (int i = 0; i < d; ++i) g = fmaf(xr[i], wgr[i], g);
+    const float g = dot_f32(xr, wg + ((size_t)e * F + f) * d, d);
     h = (g / (1.0f + expf(-g))) * u;
   }
   H[(size_t)r * F + f] = h;
@@ -1100,8 +1097,7 @@ __global__ __launch_bounds__(256) void ffn_f32_down_kernel(const float* __restri
     while (e + 1 < E && offsets[e + 1] <= r) ++e;
   const float* hr = H + (size_t)r * F;
   const float* wr = wd + ((size_t)e * d + i) * F;
-  float s = 0.0f;
-  for (int f = 0; f < F; ++f) s = fmaf(hr[f], wr[f], s);
+  const float s = dot_f32(hr, wr, F);
   const float g = gate ? gate[gmap ? gmap[r] : r] : 1.0f;
   Y[(size_t)r * d + i] = g * s;
 }

@@ -45,6 +45,28 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// sum over i < n of a[i] * b[i], one fmaf per term in index order (so the
+// result does not depend on how the loads are grouped), with 16-byte loads
+// when both rows are 16-byte aligned and n % 4 == 0
+__device__ __forceinline__ float dot_f32(const float* a, const float* b, int n) {
+  float s = 0.0f;
+  if ((((uintptr_t)a | (uintptr_t)b) & 15u) == 0 && (n & 3) == 0) {
+    const float4* a4 = (const float4*)a;
+    const float4* b4 = (const float4*)b;
+#pragma unroll 4
+    for (int i = 0; i < (n >> 2); ++i) {
+      const float4 x = a4[i], y = b4[i];
+      s = fmaf(x.x, y.x, s);
+      s = fmaf(x.y, y.y, s);
+      s = fmaf(x.z, y.z, s);
+      s = fmaf(x.w, y.w, s);
+    }
+  } else {
+    for (int i = 0; i < n; ++i) s = fmaf(a[i], b[i], s);
+  }
+  return s;
+}
+
 // The ai-th expert (in id order) among those with rows, -1 past the last one.
 // Blocks are numbered over the experts that have rows, so a step with few
 // active experts launches few blocks and none waits only to find itself idle.

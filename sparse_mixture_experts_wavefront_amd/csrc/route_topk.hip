@@ -97,10 +97,7 @@ __global__ __launch_bounds__(64 * NW) void route_topk_kernel(const void* __restr
       for (int p = tid; p < kTokPerWave * E; p += 64 * NW) {
         const int tr = p / E, e = p % E;
         const int tok = min(t0 + tr, T - 1);
-        const float* xr = x + (size_t)tok * d;
-        const float* wr = w + (size_t)e * d;
-        float s = 0.0f;
-        for (int i = 0; i < d; ++i) s = fmaf(xr[i], wr[i], s);
+        const float s = dot_f32(x + (size_t)tok * d, w + (size_t)e * d, d);
         lt[tr][e] = s + (bias ? bias[e] : 0.0f);
       }
     }
