@@ -530,6 +530,68 @@ def secondary_lines(name, steps, warmup, oracle_s):
     return lines
 
 
+def vendor_gate_up(name, steps, warmup, lib_gate_up_us=None):
+    """The same gate/up work through the vendor GEMM library, for comparison.
+
+    torch's bf16 F.linear (hipBLASLt) on the rows the library's own routing
+    gives: one GEMM per expert with its gate and up rows concatenated ([2F][d],
+    built once, not timed), alone, and as a pipeline doing the step's whole
+    work -- gather of the expert-major rows, the GEMMs, silu(g) * u to bf16.
+    Beside them the library's fused gate/up launch (stage events of the same
+    layer), all warm wall-clock means on the same box."""
+    import torch
+    import torch.nn.functional as Fn
+    import sparse_mixture_experts_wavefront_amd as moe
+    from sparse_mixture_experts_wavefront_amd.device_inputs import to_device
+    from workloads import make_workload
+    wl = make_workload(name)
+    cfg = wl.cfg
+    if cfg.act != "swiglu" or cfg.dtype != "bf16" or cfg.int4:
+        return None
+    layer, x = to_device(wl)
+    runner = moe.LayerRunner(layer, cfg.T)
+    runner(x)
+    torch.cuda.synchronize()
+    offs = runner.aux_t["offsets"].cpu().tolist()
+    tok = (runner.aux_t["row_assign"][:cfg.T * cfg.k].long() // cfg.k).contiguous()
+    wg, wu = layer.routed.w_gate, layer.routed.w_up
+    wc = [torch.cat([wg[e], wu[e]], 0).contiguous() for e in range(cfg.E)]
+    F = cfg.F
+
+    def gemms():
+        for e in range(cfg.E):
+            a, b = offs[e], offs[e + 1]
+            if b > a:
+                Fn.linear(x[:b - a], wc[e])
+
+    def pipeline():
+        xs = x.index_select(0, tok)
+        for e in range(cfg.E):
+            a, b = offs[e], offs[e + 1]
+            if b > a:
+                gu = Fn.linear(xs[a:b], wc[e])
+                Fn.silu(gu[:, :F]) * gu[:, F:]
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1000.0 / steps
+
+    g_ms, p_ms = timed(gemms), timed(pipeline)
+    del wc
+    if lib_gate_up_us is None:  # not the headline workload: time the library's launch here
+        lib_gate_up_us = run_gpu(name, steps, warmup)[1]["stages_us"]["gate_up_gemm"]
+    return {"workload": name, "vendor_gemms_ms": round(g_ms, 4), "vendor_pipeline_ms": round(p_ms, 4),
+            "library_gate_up_ms": round(lib_gate_up_us / 1000.0, 4),
+            "note": "torch F.linear (hipBLASLt) per expert, gate and up rows concatenated; "
+                    "pipeline = gather + GEMMs + silu(g)*u; library = the fused gate/up launch"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -562,6 +624,9 @@ def main():
                     help="comma-separated atomic-expert workloads, each optionally with "
                          "':schedule' (auto, dense, expert_centric), reported in the same line "
                          "('' for none)")
+    ap.add_argument("--vendor", default="mixtral_prefill_bf16",
+                    help="workloads whose gate/up step is also timed through the vendor GEMM "
+                         "library (comma-separated; '' for none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (the known-size kernel "
                          "that scales the FETCH_SIZE/WRITE_SIZE counters)")
@@ -656,6 +721,11 @@ def main():
                        "stages_us_bf16_rows": r16["stages_us"]})
     if rows16:
         out["bf16_rows"] = rows16
+    vend = [v for v in (vendor_gate_up(n, args.steps, args.warmup,
+                                       r["stages_us"]["gate_up_gemm"] if n == args.workload else None)
+                        for n in args.vendor.split(",") if n) if v]
+    if vend:
+        out["vendor_gate_up"] = vend
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     else:
