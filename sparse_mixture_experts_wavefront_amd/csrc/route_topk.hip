@@ -69,13 +69,32 @@ __global__ __launch_bounds__(64 * NW) void route_topk_kernel(const void* __restr
       f32x4 acc[EB];
 #pragma unroll
       for (int eb = 0; eb < EB; ++eb) acc[eb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int k0 = wv_id * 32; k0 < d; k0 += 32 * NW) {
-        const bool in = (k0 + g * 8) < d;  // d % 8 == 0: an 8-chunk is all in or all out
-        u32x4 av = in ? *(const u32x4*)(xr + k0) : u32x4{0, 0, 0, 0};
+      // U K steps per trip, all their loads issued before the first MFMA (a
+      // load per step behind its own wait made this loop a chain of memory
+      // round trips: the DeepSeek-shaped router went 55 -> 43 us); one with 16
+      // waves, which split K finer already (two or four measured no faster).
+      // d % 8 == 0: an 8-chunk is all in or all out; a lane past d loads its
+      // row's first chunk (in bounds) and feeds zeros, as before, so the
+      // MFMA sequence and the logits are unchanged.
+      constexpr int U = NW >= 16 ? 1 : 4;
+      for (int k0 = wv_id * 32; k0 < d; k0 += 32 * NW * U) {
+        u32x4 av[U], bv[U][EB];
 #pragma unroll
-        for (int eb = 0; eb < EB; ++eb) {
-          u32x4 bv = in ? *(const u32x4*)(wr[eb] + k0) : u32x4{0, 0, 0, 0};
-          acc[eb] = mfma16(as_bf16x8(av), as_bf16x8(bv), acc[eb]);
+        for (int u = 0; u < U; ++u) {
+          const int kk = k0 + u * 32 * NW;
+          const int kc = (kk + g * 8) < d ? kk : -g * 8;
+          av[u] = *(const u32x4*)(xr + kc);
+#pragma unroll
+          for (int eb = 0; eb < EB; ++eb) bv[u][eb] = *(const u32x4*)(wr[eb] + kc);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const bool in = (k0 + u * 32 * NW + g * 8) < d;
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          const u32x4 a = in ? av[u] : z;
+#pragma unroll
+          for (int eb = 0; eb < EB; ++eb)
+            acc[eb] = mfma16(as_bf16x8(a), as_bf16x8(in ? bv[u][eb] : z), acc[eb]);
         }
       }
 #pragma unroll
