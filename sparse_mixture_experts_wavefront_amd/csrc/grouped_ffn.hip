@@ -203,6 +203,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(TileArgs p) {
 
   u32x4 ra[AJ];
   u32x4 rb[NMAT][BJ];
+  // INT4: the stage's raw word, scale and zero point; decoded in store_stage,
+  // after the current stage's MFMAs, so the loads of the next stage are in
+  // flight under them rather than waited for at once
+  uint32_t rq[INT4 ? NMAT : 1][INT4 ? BJ : 1];
+  u16 rs[INT4 ? NMAT : 1][INT4 ? BJ : 1], rz[INT4 ? NMAT : 1][INT4 ? BJ : 1];
+  bool rkin = false;
   const int nk = (p.K + kBK - 1) / kBK;
 
   auto load_stage = [&](int kt) {
@@ -218,17 +224,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(TileArgs p) {
         if constexpr (!INT4) {
           rb[m][j] = kin ? *(const u32x4*)(b_ptr[m][j] + k0) : u32x4{0, 0, 0, 0};
         } else {
-          if (kin) {
-            const uint32_t w = (uint32_t)q_ptr[m][j][k0 >> 3];
-            const int g = k0 >> 7;
-            const float s = fp16_to_f32(sz_ptr[m][j][0][g]);
-            const float z = fp16_to_f32(sz_ptr[m][j][1][g]);
-            rb[m][j] = dequant8(w, s, z);
-          } else {
-            rb[m][j] = u32x4{0, 0, 0, 0};
-          }
+          // past K: the stage's first word and group (in bounds), decoded to zeros
+          const int kq = kin ? k0 : 0;
+          rq[m][j] = (uint32_t)q_ptr[m][j][kq >> 3];
+          rs[m][j] = sz_ptr[m][j][0][kq >> 7];
+          rz[m][j] = sz_ptr[m][j][1][kq >> 7];
         }
       }
+    rkin = kin;
   };
   auto store_stage = [&](int buf) {
     u16* as = As + buf * BM * kBK;
@@ -238,7 +241,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(TileArgs p) {
     for (int m = 0; m < NMAT; ++m) {
       u16* bs = Bs + (buf * NMAT + m) * BN * kBK;
 #pragma unroll
-      for (int j = 0; j < BJ; ++j) *(u32x4*)(bs + swz((tid >> 3) + 32 * j, kc)) = rb[m][j];
+      for (int j = 0; j < BJ; ++j) {
+        if constexpr (INT4)
+          rb[m][j] = rkin ? dequant8(rq[m][j], fp16_to_f32(rs[m][j]), fp16_to_f32(rz[m][j]))
+                          : u32x4{0, 0, 0, 0};
+        *(u32x4*)(bs + swz((tid >> 3) + 32 * j, kc)) = rb[m][j];
+      }
     }
   };
 
