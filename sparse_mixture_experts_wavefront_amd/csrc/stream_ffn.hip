@@ -760,7 +760,7 @@ template <int MODE, int RBW>
 constexpr int stream_rows_nout() { return MODE == kSModeGateUp ? 4 * RBW * 8 : 4 * RBW * 16; }
 
 template <int MODE, bool INT4, int MB, int D, int WQ, int RBW>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 void stream_rows_kernel(StreamArgs p) {
   static_assert(INT4 || WQ == 1, "bf16 slices are 128 K values");
   constexpr int KI = 128 * WQ, NS = 4;
@@ -875,163 +875,172 @@ void stream_rows_kernel(StreamArgs p) {
   auto body = [&](auto fused) {
     for (int mbase = 0; mbase < cnt; mbase += MB * 16) {
       const int mrows = min(MB * 16, cnt - mbase);
-      // token slice loads: thread (q, c, tid) copies 16-byte chunk c*16 + tid%16
-      // of token row q*16 + tid/16
-      uint32_t xv[MB];
+      // a pass of at most 16 rows runs its first 16-row token block only (MBE = 1):
+      // no loads, LDS traffic or MFMAs for the clamped copies
+      auto pass = [&](auto mbe_c) {
+        constexpr int MBE = decltype(mbe_c)::value;
+        // token slice loads: thread (q, c, tid) copies 16-byte chunk c*16 + tid%16
+        // of token row q*16 + tid/16
+        uint32_t xv[MBE];
 #pragma unroll
-      for (int q = 0; q < MB; ++q) {
-        const int rr = row0 + mbase + min(q * 16 + (tid >> 4), mrows - 1);  // clamped copies
-        const int src = p.gather ? p.gather[rr] / p.k : rr;
-        xv[q] = ((uint32_t)src * (uint32_t)p.ldx + (uint32_t)K0 + (uint32_t)(tid & 15) * 8) * 2u;
-      }
-      if constexpr (MODE == kSModeDown) {
-        // gates of this pass's rows, published by the first slice's barrier
-        if (tid < MB * 16) {
-          const int rr = row0 + mbase + min(tid, mrows - 1);
-          gsm[tid] = p.gate ? p.gate[p.gate_map ? p.gate_map[rr] : rr] : 1.0f;
+        for (int q = 0; q < MBE; ++q) {
+          const int rr = row0 + mbase + min(q * 16 + (tid >> 4), mrows - 1);  // clamped copies
+          const int src = p.gather ? p.gather[rr] / p.k : rr;
+          xv[q] = ((uint32_t)src * (uint32_t)p.ldx + (uint32_t)K0 + (uint32_t)(tid & 15) * 8) * 2u;
         }
-      }
-      f32x4 acc[RBW][MB];
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-      struct Set {
-        u32x4 wv[RBW][WL];
-      };
-      auto load = [&](Set& S, int it) {
-        const bool live = it < iters;  // uniform
-        const uint32_t wo = live ? (uint32_t)it * IT_BYTES : strip_bytes;
+        if constexpr (MODE == kSModeDown) {
+          // gates of this pass's rows, published by the first slice's barrier
+          if (tid < MB * 16) {
+            const int rr = row0 + mbase + min(tid, mrows - 1);
+            gsm[tid] = p.gate ? p.gate[p.gate_map ? p.gate_map[rr] : rr] : 1.0f;
+          }
+        }
+        f32x4 acc[RBW][MBE];
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-          for (int q = 0; q < WL; ++q)
-            S.wv[rb][q] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(second(rb) ? wres1 : wres0,
-                                                             (int)(wvoff[rb] + wo + q * 64), 0, 0));
-        __builtin_amdgcn_sched_barrier(0);
-      };
-      // the token slice (from L2) is loaded one slice ahead, ahead of the
-      // weight loads issued after it, so waiting for it never waits for them
-      u32x4 xr[MB][WQ];
-      auto load_x = [&](int it) {
-        const bool live = it < iters;  // uniform
-#pragma unroll
-        for (int q = 0; q < MB; ++q)
-#pragma unroll
-          for (int c = 0; c < WQ; ++c)
-            xr[q][c] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                           xres, (int)(live ? xv[q] + (uint32_t)it * KI * 2 + c * 256 : p.xbytes),
-                           0, 0));
-        __builtin_amdgcn_sched_barrier(0);
-      };
-      auto compute = [&](const Set& S, const unsigned char* slot, int it) {
-        // sub-slice q = 128 K values (one INT4 group); token fragments: lane (t, g),
-        // step s reads K q*128 + [g*32 + s*8, +8) (INT4) or [s*32 + g*8, +8) (bf16)
-        // of token row t, as the weight lanes do
-#pragma unroll
-        for (int q = 0; q < WQ; ++q) {
-          u32x4 xf[MB][NS];
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-              xf[mb][s] = *(const u32x4*)(slot + (mb * 16 + r16) * XROW +
-                                          (q * 128 + (INT4 ? g * 32 + s * 8 : s * 32 + g * 8)) * 2);
-          if constexpr (!INT4) {
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-              for (int s = 0; s < NS; ++s)
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                  acc[rb][mb] = mfma16(as_bf16x8(S.wv[rb][s]), as_bf16x8(xf[mb][s]), acc[rb][mb]);
-          } else {
-            const int grp = min(it, iters - 1) * WQ + q;  // past the K range the tokens are zeros
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) {
-              const uint32_t v = sz[(w * RBW * 16 + rb * 16 + r16) * GP + grp];
-              const float sf = h2f((u16)(v & 0xffffu)), zf = h2f((u16)(v >> 16));
-              const float nzs = -(zf * sf);
-              bf16x8 a[NS];
-#pragma unroll
-              for (int s = 0; s < NS; ++s) {
-                if constexpr (decltype(fused)::value)
-                  a[s] = dq8_mix(S.wv[rb][q][s], sf, nzs);
-                else
-                  a[s] = dq8_exact(S.wv[rb][q][s], sf, zf);
-              }
-#pragma unroll
-              for (int s = 0; s < NS; ++s)
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                  acc[rb][mb] = mfma16(a[s], as_bf16x8(xf[mb][s]), acc[rb][mb]);
-            }
-          }
-          // one sub-slice's token fragments live at a time
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      };
+          for (int mb = 0; mb < MBE; ++mb) acc[rb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-      // slice it: weight register set it % D (loaded D slices ahead), LDS slot
-      // it % 2.  Slot it % 2 was last read in slice it - 2, which every wave
-      // finished before the barrier of slice it - 1.
-      Set st[D];
-      load_x(0);
+        struct Set {
+          u32x4 wv[RBW][WL];
+        };
+        auto load = [&](Set& S, int it) {
+          const bool live = it < iters;  // uniform
+          const uint32_t wo = live ? (uint32_t)it * IT_BYTES : strip_bytes;
 #pragma unroll
-      for (int d = 0; d < D; ++d) load(st[d], d);
-      for (int it0 = 0; it0 < iters; it0 += D) {
+          for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-        for (int u = 0; u < D; ++u) {
-          const int it = it0 + u;
-          unsigned char* slot = xs + (u & 1) * XSLOT;  // it0 is even when D is
-          if (D % 2 != 0) slot = xs + (it & 1) * XSLOT;
+            for (int q = 0; q < WL; ++q)
+              S.wv[rb][q] = __builtin_bit_cast(
+                  u32x4, __builtin_amdgcn_raw_buffer_load_b128(second(rb) ? wres1 : wres0,
+                                                               (int)(wvoff[rb] + wo + q * 64), 0, 0));
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        // the token slice (from L2) is loaded one slice ahead, ahead of the
+        // weight loads issued after it, so waiting for it never waits for them
+        u32x4 xr[MBE][WQ];
+        auto load_x = [&](int it) {
+          const bool live = it < iters;  // uniform
 #pragma unroll
-          for (int q = 0; q < MB; ++q)
+          for (int q = 0; q < MBE; ++q)
 #pragma unroll
             for (int c = 0; c < WQ; ++c)
-              *(u32x4*)(slot + (q * 16 + (tid >> 4)) * XROW + (c * 16 + (tid & 15)) * 16) = xr[q][c];
-          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
-          block_barrier();
-          load_x(it + 1);
-          compute(st[u], slot, it);
-          load(st[u], it + D);
+              xr[q][c] = __builtin_bit_cast(
+                  u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                             xres, (int)(live ? xv[q] + (uint32_t)it * KI * 2 + c * 256 : p.xbytes),
+                             0, 0));
           __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+        };
+        auto compute = [&](const Set& S, const unsigned char* slot, int it) {
+          // sub-slice q = 128 K values (one INT4 group); token fragments: lane (t, g),
+          // step s reads K q*128 + [g*32 + s*8, +8) (INT4) or [s*32 + g*8, +8) (bf16)
+          // of token row t, as the weight lanes do
+#pragma unroll
+          for (int q = 0; q < WQ; ++q) {
+            u32x4 xf[MBE][NS];
+#pragma unroll
+            for (int mb = 0; mb < MBE; ++mb)
+#pragma unroll
+              for (int s = 0; s < NS; ++s)
+                xf[mb][s] = *(const u32x4*)(slot + (mb * 16 + r16) * XROW +
+                                            (q * 128 + (INT4 ? g * 32 + s * 8 : s * 32 + g * 8)) * 2);
+            if constexpr (!INT4) {
+#pragma unroll
+              for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                for (int s = 0; s < NS; ++s)
+#pragma unroll
+                  for (int mb = 0; mb < MBE; ++mb)
+                    acc[rb][mb] = mfma16(as_bf16x8(S.wv[rb][s]), as_bf16x8(xf[mb][s]), acc[rb][mb]);
+            } else {
+              const int grp = min(it, iters - 1) * WQ + q;  // past the K range the tokens are zeros
+#pragma unroll
+              for (int rb = 0; rb < RBW; ++rb) {
+                const uint32_t v = sz[(w * RBW * 16 + rb * 16 + r16) * GP + grp];
+                const float sf = h2f((u16)(v & 0xffffu)), zf = h2f((u16)(v >> 16));
+                const float nzs = -(zf * sf);
+                bf16x8 a[NS];
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                  if constexpr (decltype(fused)::value)
+                    a[s] = dq8_mix(S.wv[rb][q][s], sf, nzs);
+                  else
+                    a[s] = dq8_exact(S.wv[rb][q][s], sf, zf);
+                }
+#pragma unroll
+                for (int s = 0; s < NS; ++s)
+#pragma unroll
+                  for (int mb = 0; mb < MBE; ++mb)
+                    acc[rb][mb] = mfma16(a[s], as_bf16x8(xf[mb][s]), acc[rb][mb]);
+              }
+            }
+            // one sub-slice's token fragments live at a time
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        };
 
-      // epilogue from the accumulators: lane (t, g) holds weight rows 4g..4g+3
-      // of each row block for token row t (C layout of the 16x16 MFMA)
+        // slice it: weight register set it % D (loaded D slices ahead), LDS slot
+        // it % 2.  Slot it % 2 was last read in slice it - 2, which every wave
+        // finished before the barrier of slice it - 1.
+        Set st[D];
+        load_x(0);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int row = mbase + mb * 16 + r16;
-        if (row >= cnt) continue;
-        const size_t orow = (size_t)(row0 + row);
-        constexpr int NOB = (MODE == kSModeGateUp) ? RBW / 2 : RBW;
+        for (int d = 0; d < D; ++d) load(st[d], d);
+        for (int it0 = 0; it0 < iters; it0 += D) {
 #pragma unroll
-        for (int ob = 0; ob < NOB; ++ob) {
-          const int f = n0 + w * NWF + ob * 16 + 4 * g;
-          if (f >= p.N) continue;
-          if constexpr (MODE == kSModeDown) {
-            const float gv = gsm[mb * 16 + r16];
-            const f32x4 a = acc[ob][mb];
-            *(f32x4*)(p.Y + (size_t)kp * p.ystride + orow * p.N + f) =
-                f32x4{gv * a[0], gv * a[1], gv * a[2], gv * a[3]};
-            continue;
+          for (int u = 0; u < D; ++u) {
+            const int it = it0 + u;
+            unsigned char* slot = xs + (u & 1) * XSLOT;  // it0 is even when D is
+            if (D % 2 != 0) slot = xs + (it & 1) * XSLOT;
+#pragma unroll
+            for (int q = 0; q < MBE; ++q)
+#pragma unroll
+              for (int c = 0; c < WQ; ++c)
+                *(u32x4*)(slot + (q * 16 + (tid >> 4)) * XROW + (c * 16 + (tid & 15)) * 16) = xr[q][c];
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+            block_barrier();
+            load_x(it + 1);
+            compute(st[u], slot, it);
+            load(st[u], it + D);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          float o[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if constexpr (MODE == kSModeGateUp)
-              o[i] = silu_f32(acc[ob][mb][i]) * acc[ob + RBW / 2][mb][i];
-            else
-              o[i] = fmaxf(acc[ob][mb][i], 0.0f);
-          }
-          *(uint2*)(p.H + orow * p.N + f) = uint2{pk_bf16(o[0], o[1]), pk_bf16(o[2], o[3])};
         }
-      }
+
+        // epilogue from the accumulators: lane (t, g) holds weight rows 4g..4g+3
+        // of each row block for token row t (C layout of the 16x16 MFMA)
+#pragma unroll
+        for (int mb = 0; mb < MBE; ++mb) {
+          const int row = mbase + mb * 16 + r16;
+          if (row >= cnt) continue;
+          const size_t orow = (size_t)(row0 + row);
+          constexpr int NOB = (MODE == kSModeGateUp) ? RBW / 2 : RBW;
+#pragma unroll
+          for (int ob = 0; ob < NOB; ++ob) {
+            const int f = n0 + w * NWF + ob * 16 + 4 * g;
+            if (f >= p.N) continue;
+            if constexpr (MODE == kSModeDown) {
+              const float gv = gsm[mb * 16 + r16];
+              const f32x4 a = acc[ob][mb];
+              *(f32x4*)(p.Y + (size_t)kp * p.ystride + orow * p.N + f) =
+                  f32x4{gv * a[0], gv * a[1], gv * a[2], gv * a[3]};
+              continue;
+            }
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if constexpr (MODE == kSModeGateUp)
+                o[i] = silu_f32(acc[ob][mb][i]) * acc[ob + RBW / 2][mb][i];
+              else
+                o[i] = fmaxf(acc[ob][mb][i], 0.0f);
+            }
+            *(uint2*)(p.H + orow * p.N + f) = uint2{pk_bf16(o[0], o[1]), pk_bf16(o[2], o[3])};
+          }
+        }
+      };
+      if (MB > 1 && mrows <= 16)
+        pass(std::integral_constant<int, 1>{});
+      else
+        pass(std::integral_constant<int, MB>{});
       // the next pass writes slot 0 and the gates again
       if (mbase + MB * 16 < cnt) __syncthreads();
     }
