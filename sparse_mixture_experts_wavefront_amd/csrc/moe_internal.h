@@ -20,6 +20,7 @@ constexpr int kMaxExperts = 64;
 constexpr int kMaxTopK = 8;
 constexpr int kPermChunk = 2048;      // assignments per block in the multi-block permutation
 constexpr int kPermFusedMax = 2048;  // up to this many assignments: one fused block
+constexpr int kPermFusedBigMax = 8192;  // up to this many: one 1024-thread block
 
 __device__ __forceinline__ float bf16_to_f32(u16 b) {
   return __uint_as_float((uint32_t)b << 16);

@@ -18,7 +18,9 @@
 //               match-any built out of log2(64) ballots, earlier waves of the
 //               round add their per-expert counts from LDS.
 // Assignments of at most kPermFusedMax entries take one fused block (decode
-// latency); larger ones take the three-kernel path.
+// latency); up to kPermFusedBigMax one 1024-thread block that ranks every
+// 64-assignment chunk at once (prefill latency); larger ones the three-kernel
+// path.
 #include <math.h>
 
 #include "moe_internal.h"
@@ -121,6 +123,92 @@ __global__ __launch_bounds__(kBlock) void permute_fused_kernel(
   scatter_range(idx, 0, n, E, run, wc, row_assign, assign_row);
 }
 
+// One 1024-thread block for kPermFusedMax < n <= kPermFusedBigMax.  Chunk c
+// holds assignments [64c, 64c + 64) and belongs to wave c % 16.  (1) each wave
+// ranks its chunks' lanes among equal experts (match-any from ballots) and the
+// lane of rank 0 records the chunk's count of that expert; (2) per expert, an
+// exclusive scan over chunks in chunk order (16 parts of consecutive chunks,
+// lane = expert) turns the counts into each chunk's first row inside the
+// expert; (3) wave 0 scans the expert totals into offsets, counts and LIS;
+// (4) row = offsets[e] + chunk base + rank.  Rows inside an expert therefore
+// follow the flat order a, as in the other paths.
+constexpr int kBigBlock = 1024;
+constexpr int kBigWaves = kBigBlock / 64;
+constexpr int kBigChunks = kPermFusedBigMax / 64;
+constexpr int kBigPer = kBigChunks / kBigWaves;  // chunks per wave
+
+__global__ __launch_bounds__(kBigBlock) void permute_fused_big_kernel(
+    const int32_t* __restrict__ idx, int T, int E, int k, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_assign,
+    int32_t* __restrict__ assign_row, double* __restrict__ lis) {
+  __shared__ int cc[kBigChunks][kMaxExperts];  // chunk counts, then chunk bases
+  __shared__ int part[kBigWaves][kMaxExperts];  // per-part sums
+  __shared__ int off[kMaxExperts];              // expert totals, then offsets
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int n = T * k, nch = (n + 63) >> 6;
+  int ev[kBigPer];
+#pragma unroll
+  for (int j = 0; j < kBigPer; ++j) {
+    const int a = (w + j * kBigWaves) * 64 + lane;
+    ev[j] = a < n ? idx[a] : -1;
+  }
+  for (int i = tid; i < nch * kMaxExperts; i += kBigBlock) cc[i / kMaxExperts][i % kMaxExperts] = 0;
+  __syncthreads();
+  int rk[kBigPer];
+#pragma unroll
+  for (int j = 0; j < kBigPer; ++j) {
+    const bool valid = ev[j] >= 0 && ev[j] < E;
+    const int e = valid ? ev[j] : 0;
+    const unsigned long long m = match_expert(e, valid);
+    rk[j] = __popcll(m & lanemask_lt());
+    if (valid && rk[j] == 0) cc[w + j * kBigWaves][e] = __popcll(m);
+    if (!valid) ev[j] = -1;
+  }
+  __syncthreads();
+  // part w = chunks [c0, c1); lane = expert
+  const int S = (nch + kBigWaves - 1) / kBigWaves;
+  const int c0 = min(nch, w * S), c1 = min(nch, c0 + S);
+  int sum = 0;
+  for (int c = c0; c < c1; ++c) sum += cc[c][lane];
+  part[w][lane] = sum;
+  __syncthreads();
+  int base = 0;
+  for (int q = 0; q < w; ++q) base += part[q][lane];
+  for (int c = c0; c < c1; ++c) {
+    const int v = cc[c][lane];
+    cc[c][lane] = base;
+    base += v;
+  }
+  if (w == kBigWaves - 1) off[lane] = base;  // the expert's total
+  __syncthreads();
+  if (w == 0) {
+    const int c = (lane < E) ? off[lane] : 0;
+    int incl = c;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    int mx = c;
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o, 64));
+    off[lane] = incl - c;
+    if (lane < E) {
+      counts[lane] = c;
+      offsets[lane] = incl - c;
+    }
+    if (lane == E - 1) offsets[E] = incl;
+    if (lane == 0) write_lis(lis, T, E, k, mx);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kBigPer; ++j) {
+    if (ev[j] < 0) continue;
+    const int c = w + j * kBigWaves, a = c * 64 + lane;
+    const int row = off[ev[j]] + cc[c][ev[j]] + rk[j];
+    if (row_assign) row_assign[row] = a;
+    if (assign_row) assign_row[a] = row;
+  }
+}
+
 __global__ __launch_bounds__(kBlock) void permute_hist_kernel(const int32_t* __restrict__ idx,
                                                               int n, int E,
                                                               int32_t* __restrict__ blk_counts) {
@@ -184,7 +272,7 @@ __global__ __launch_bounds__(kBlock) void permute_scatter_kernel(
 
 size_t permute_ws_bytes(int T, int E, int k) {
   const long long n = (long long)T * k;
-  if (n <= kPermFusedMax) return 0;
+  if (n <= kPermFusedBigMax) return 0;
   const long long nblk = (n + kPermChunk - 1) / kPermChunk;
   return (size_t)(2 * nblk * E * sizeof(int32_t));
 }
@@ -196,6 +284,11 @@ hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* coun
   if (n <= kPermFusedMax) {
     hipLaunchKernelGGL(permute_fused_kernel, dim3(1), dim3(kBlock), 0, s, idx, T, E, k, counts,
                        offsets, row_assign, assign_row, lis);
+    return hipGetLastError();
+  }
+  if (n <= kPermFusedBigMax) {
+    hipLaunchKernelGGL(permute_fused_big_kernel, dim3(1), dim3(kBigBlock), 0, s, idx, T, E, k,
+                       counts, offsets, row_assign, assign_row, lis);
     return hipGetLastError();
   }
   const int nblk = (n + kPermChunk - 1) / kPermChunk;

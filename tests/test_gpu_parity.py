@@ -270,6 +270,22 @@ def test_permute_multiblock_path():
         assert float(lis.cpu()[0]) == rlis
 
 
+def test_permute_single_block_mid_sizes():
+    _say("permute: one 1024-thread block (fused limit < T*k <= 8192), skewed and edge sizes")
+    moe = _moe()
+    rng = np.random.default_rng(17)
+    for T, E, k in ((2049, 8, 1), (4096, 8, 1), (4096, 64, 2), (1365, 64, 6), (3000, 1, 2),
+                    (2730, 3, 3), (1100, 37, 2)):
+        p = rng.zipf(1.3, size=(T, E)).astype(np.float64)
+        idx = np.argsort(-p + rng.random((T, E)) * 1e-3, axis=1)[:, :k].astype(np.int32)
+        c, o, ra, ar, lis = moe.permute(torch.from_numpy(idx).cuda(), E)
+        torch.cuda.synchronize()
+        rc, ro, rra, rar, rlis = oracle.permute(idx, E)
+        assert np.array_equal(c.cpu().numpy(), rc) and np.array_equal(o.cpu().numpy(), ro)
+        assert np.array_equal(ra.cpu().numpy(), rra) and np.array_equal(ar.cpu().numpy(), rar)
+        assert float(lis.cpu()[0]) == rlis
+
+
 def test_grouped_ffn_single_dense_expert_and_combine():
     _say("grouped_ffn with offsets NULL (one dense expert), combine alone")
     moe = _moe()
