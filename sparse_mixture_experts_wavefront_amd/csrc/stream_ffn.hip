@@ -831,13 +831,15 @@ void stream_rows_kernel(StreamArgs p) {
       constexpr int VG = decltype(vg)::value;
       typedef uint32_t vec_t __attribute__((ext_vector_type(VG / 2)));
       const int GV = G / VG;
-      constexpr int kMaxPer = 64 / VG;  // 256 rows * G/VG loads per array over 256 threads
+      const int nload = 4 * RBW * 16 * GV;  // loads per array (uniform)
+      constexpr int kMaxPer = RBW * 16 / VG;  // 64*RBW rows * (G <= 64)/VG loads over 256 threads
       vec_t sv[kMaxPer], zv[kMaxPer];
 #pragma unroll
       for (int q = 0; q < kMaxPer; ++q) {
+        if (q * 256 >= nload) break;
         const int i = tid + q * 256;
         sv[q] = zv[q] = vec_t{};
-        if (i < 4 * RBW * 16 * GV) {
+        if (i < nload) {
           const int br = i / GV, j = i - br * GV;
           const int ww = br / (RBW * 16), rb = (br / 16) % RBW, r = br % 16;
           const int n = n0 + strip_row(ww, rb) + r;
@@ -850,8 +852,9 @@ void stream_rows_kernel(StreamArgs p) {
       }
 #pragma unroll
       for (int q = 0; q < kMaxPer; ++q) {
+        if (q * 256 >= nload) break;
         const int i = tid + q * 256;
-        if (i < 4 * RBW * 16 * GV) {
+        if (i < nload) {
           const int br = i / GV, j = i - br * GV;
 #pragma unroll
           for (int h = 0; h < VG / 2; ++h) {
