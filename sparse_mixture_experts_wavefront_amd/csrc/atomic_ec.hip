@@ -16,9 +16,8 @@
 // slice of output columns.  It lists the experts of its range that have rows
 // in its token chunk, streams each listed expert's output vector once (from
 // the unit-major copy w_out_rows [N][d], 16 bytes per lane, D experts ahead)
-// and adds h * w_out[n] into per-token fp32 accumulators held in registers
-// (the token of a row is uniform across the block, so the accumulator is
-// selected by a uniform branch).  Each range leaves partial sums of its
+// and adds h * w_out[n] into per-token fp32 accumulators in LDS (each thread
+// its own 8 columns of every token).  Each range leaves partial sums of its
 // experts; the reduce kernel adds the ranges in range order, then the shared
 // MLP's rows, so the result is run-to-run deterministic.
 #include <type_traits>
