@@ -80,26 +80,44 @@ __device__ __forceinline__ int block_exscan(int v, int* red, int* total = nullpt
 }
 
 // ---- log-probabilities ---------------------------------------------------------
-// one wave per token; the logits may arrive as nsplit partial sums (K slices of
-// the router GEMM, split_stride floats apart) that are added here in slice order
-__global__ __launch_bounds__(64) void log_softmax_kernel(const float* __restrict__ l, int n,
-                                                         int nsplit, size_t split_stride,
-                                                         float* __restrict__ out) {
+// one 256-thread block per token; the logits may arrive as NS partial sums (K
+// slices of the router GEMM, split_stride floats apart), added here in slice
+// order.  A thread's NS loads of an element are all issued before the adds (the
+// partial sums come from another launch, so each load is a full memory round
+// trip; a runtime-length loop waited for each in turn).
+constexpr int kLsThreads = 256;
+
+template <int NS>
+__global__ __launch_bounds__(kLsThreads) void log_softmax_kernel(const float* __restrict__ l,
+                                                                 int n, size_t split_stride,
+                                                                 float* __restrict__ out) {
   __shared__ float row[kGridMax];
+  __shared__ float red[kLsThreads / 64];
   const float* r = l + (size_t)blockIdx.x * n;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float m = -INFINITY;
-  for (int i = threadIdx.x; i < n; i += 64) {
-    float v = r[i];
-    for (int q = 1; q < nsplit; ++q) v += r[(size_t)q * split_stride + i];
+  for (int i = tid; i < n; i += kLsThreads) {
+    float p[NS];
+#pragma unroll
+    for (int q = 0; q < NS; ++q) p[q] = r[(size_t)q * split_stride + i];
+    float v = p[0];
+#pragma unroll
+    for (int q = 1; q < NS; ++q) v += p[q];
     row[i] = v;
     m = fmaxf(m, v);
   }
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  float s = 0.0f;
-  for (int i = threadIdx.x; i < n; i += 64) s += expf(row[i] - m);
-  s = wave_sum_f(s);
-  const float lse = m + logf(s);
-  for (int i = threadIdx.x; i < n; i += 64) out[(size_t)blockIdx.x * n + i] = row[i] - lse;
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();  // red is reused below
+  float sum = 0.0f;
+  for (int i = tid; i < n; i += kLsThreads) sum += expf(row[i] - m);  // this thread's own elements
+  sum = wave_sum_f(sum);
+  if (lane == 0) red[w] = sum;
+  __syncthreads();
+  const float lse = m + logf(((red[0] + red[1]) + red[2]) + red[3]);
+  for (int i = tid; i < n; i += kLsThreads) out[(size_t)blockIdx.x * n + i] = row[i] - lse;
 }
 
 // ---- exact top-K over the grid -----------------------------------------------
@@ -534,8 +552,16 @@ __global__ void iota_kernel_zero(int32_t* out, int n) {
 hipError_t launch_log_softmax_rows(const float* l, int T, int n, float* out, hipStream_t s,
                                    int nsplit, size_t split_stride) {
   if (T == 0) return hipSuccess;
-  if (n > kGridMax || nsplit < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(log_softmax_kernel, dim3(T), dim3(64), 0, s, l, n, nsplit, split_stride, out);
+  if (n > kGridMax) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)T), block(kLsThreads);
+  switch (nsplit) {
+    case 1: hipLaunchKernelGGL(log_softmax_kernel<1>, grid, block, 0, s, l, n, split_stride, out); break;
+    case 2: hipLaunchKernelGGL(log_softmax_kernel<2>, grid, block, 0, s, l, n, split_stride, out); break;
+    case 4: hipLaunchKernelGGL(log_softmax_kernel<4>, grid, block, 0, s, l, n, split_stride, out); break;
+    case 8: hipLaunchKernelGGL(log_softmax_kernel<8>, grid, block, 0, s, l, n, split_stride, out); break;
+    case 16: hipLaunchKernelGGL(log_softmax_kernel<16>, grid, block, 0, s, l, n, split_stride, out); break;
+    default: return hipErrorInvalidValue;  // the router GEMM splits are powers of two up to 16
+  }
   return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ constexpr int kEcOutThreads = 64;       // output side: threads per block (one w
 constexpr int kEcOutCols = 8;           // columns per thread (one 16-byte bf16 load)
 constexpr int kEcOutSlice = kEcOutThreads * kEcOutCols;   // 512 columns per block
 constexpr int kEcTok = 16;              // tokens per output-side block
-constexpr int kEcList = 512;            // experts listed per round of the output side
+constexpr int kEcList = 256;            // experts listed per round of the output side
 constexpr int kEcAhead = 32;            // output vectors in flight per thread
 constexpr int kEcOutRows = 1024;        // rows of a listing round staged in LDS (T <= 16)
 
