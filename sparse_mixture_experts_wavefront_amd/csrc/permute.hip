@@ -231,14 +231,24 @@ __global__ __launch_bounds__(64) void permute_scan_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ blk_base,
                                                           double* __restrict__ lis) {
+  // lane e = expert: its per-block counts, 16 loads in flight per batch (the
+  // counts come from the previous launch: a memory round trip per batch, not
+  // per block).  Pass 1 totals them, pass 2 (after the scan over experts)
+  // reads them again and writes each block's first row.
+  constexpr int kBatch = 16;
   const int e = threadIdx.x;
+  auto batch = [&](int b0, int (&v)[kBatch]) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      v[j] = (e < E && b0 + j < nblk) ? blk_counts[(size_t)(b0 + j) * E + e] : 0;
+  };
   int c = 0;
-  if (e < E)
-    for (int b = 0; b < nblk; ++b) {
-      const int v = blk_counts[(size_t)b * E + e];
-      blk_base[(size_t)b * E + e] = c;
-      c += v;
-    }
+  for (int b0 = 0; b0 < nblk; b0 += kBatch) {
+    int v[kBatch];
+    batch(b0, v);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) c += v[j];
+  }
   int incl = c;
   for (int o = 1; o < 64; o <<= 1) {
     const int v = __shfl_up(incl, o, 64);
@@ -250,7 +260,16 @@ __global__ __launch_bounds__(64) void permute_scan_kernel(const int32_t* __restr
   if (e < E) {
     counts[e] = c;
     offsets[e] = excl;
-    for (int b = 0; b < nblk; ++b) blk_base[(size_t)b * E + e] += excl;
+    int run = excl;
+    for (int b0 = 0; b0 < nblk; b0 += kBatch) {
+      int v[kBatch];
+      batch(b0, v);
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (b0 + j < nblk) blk_base[(size_t)(b0 + j) * E + e] = run;
+        run += v[j];
+      }
+    }
   }
   if (e == E - 1) offsets[E] = incl;
   if (e == 0) write_lis(lis, T, E, k, mx);
