@@ -29,6 +29,7 @@ constexpr int kGridMax = 1024;   // nr, nc limit
 constexpr int kPermChunkT = 64;  // tokens per counting chunk
 constexpr int kRowsTok = 256;    // tokens staged per round of grid_rows_kernel
 constexpr int kRowsSpan = 1024;  // tokens per grid_rows_kernel block (a multiple of both)
+constexpr int kTopkWideMaxT = 64;  // up to this many tokens: 1024-thread top-K blocks
 
 __device__ __forceinline__ uint32_t fkey(float f) {
   uint32_t u = __float_as_uint(f);
@@ -52,17 +53,22 @@ __device__ __forceinline__ float wave_sum_f(float v) {
 }
 
 // block (256 threads) sum; every thread gets the total
+template <int NW = 4>
 __device__ __forceinline__ int block_sum(int v, int* red) {
   const int tid = threadIdx.x;
   v = wave_sum(v);
   __syncthreads();
   if ((tid & 63) == 0) red[tid >> 6] = v;
   __syncthreads();
-  return red[0] + red[1] + red[2] + red[3];
+  int s = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) s += red[i];
+  return s;
 }
 
-// exclusive scan of one value per thread over the block (256 threads); the
+// exclusive scan of one value per thread over the block (NW waves); the
 // block total goes to *total
+template <int NW = 4>
 __device__ __forceinline__ int block_exscan(int v, int* red, int* total = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int incl = v;
@@ -75,7 +81,12 @@ __device__ __forceinline__ int block_exscan(int v, int* red, int* total = nullpt
   __syncthreads();
   int base = 0;
   for (int i = 0; i < w; ++i) base += red[i];
-  if (total) *total = red[0] + red[1] + red[2] + red[3];
+  if (total) {
+    int s = red[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) s += red[i];
+    *total = s;
+  }
   return base + incl - v;
 }
 
@@ -125,12 +136,16 @@ __global__ __launch_bounds__(kLsThreads) void log_softmax_kernel(const float* __
 // the cells at or above any key form a prefix of that order, found by binary
 // search, so theta (the K-th largest key) comes from a binary search over the
 // 32-bit keys with one such count per row.  Emission then walks the grid in
-// rounds of 256 consecutive 32-cell words (one word per thread): a cell is kept
+// rounds of NT consecutive 32-cell words (one word per thread): a cell is kept
 // if its key is above theta, or equal to it while the ties before it (in id
 // order, a block scan per round) are fewer than the ties needed; positions come
 // from a block scan of the kept counts, so ids and gates leave in ascending id
 // order and the bitmap words and their prefixes in coalesced stores.
-__global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict__ pr,
+// NT threads per block: 256 when many tokens fill the chip, 1024 at decode
+// sizes, where each token's block is alone on its CU and the search and the
+// walk over the grid are its latency
+template <int NT>
+__global__ __launch_bounds__(NT) void grid_topk_kernel(const float* __restrict__ pr,
                                                         const float* __restrict__ pc, int nr,
                                                         int nc, int K, int32_t* __restrict__ idx,
                                                         float* __restrict__ gate,
@@ -138,13 +153,14 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
                                                         int32_t* __restrict__ bitpre) {
   __shared__ float a[kGridMax], b[kGridMax], bv[kGridMax];
   __shared__ unsigned long long bk[kGridMax];  // sort keys: fkey(b) << 32 | ~column
-  __shared__ int red[4];
-  __shared__ float redf[4];
+  constexpr int NW = NT / 64;
+  __shared__ int red[NW];
+  __shared__ float redf[NW];
   const int t = blockIdx.x, tid = threadIdx.x;
   int ncp = 1;
   while (ncp < nc) ncp <<= 1;
-  for (int i = tid; i < nr; i += 256) a[i] = pr[(size_t)t * nr + i];
-  for (int j = tid; j < ncp; j += 256) {
+  for (int i = tid; i < nr; i += NT) a[i] = pr[(size_t)t * nr + i];
+  for (int j = tid; j < ncp; j += NT) {
     unsigned long long key = 0ull;  // padding sorts last
     if (j < nc) {
       const float v = pc[(size_t)t * nc + j];
@@ -157,7 +173,7 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
   // bitonic sort of bk, descending
   for (int size = 2; size <= ncp; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int q = tid; q < ncp / 2; q += 256) {
+      for (int q = tid; q < ncp / 2; q += NT) {
         const int lo = 2 * q - (q & (stride - 1));
         const int hi = lo + stride;
         const bool desc = (lo & size) == 0;
@@ -170,12 +186,12 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
       __syncthreads();
     }
   }
-  for (int j = tid; j < nc; j += 256) bv[j] = b[~(uint32_t)bk[j]];
+  for (int j = tid; j < nc; j += NT) bv[j] = b[~(uint32_t)bk[j]];
   __syncthreads();
   auto count_ge = [&](uint32_t kt) {
     const float th = kf(kt);
     int c = 0;
-    for (int i = tid; i < nr; i += 256) {
+    for (int i = tid; i < nr; i += NT) {
       const float ai = a[i];
       int lo = 0, hi = nc;
       while (lo < hi) {
@@ -187,11 +203,11 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
       }
       c += lo;
     }
-    return block_sum(c, red);
+    return block_sum<NW>(c, red);
   };
   // the largest and smallest cell scores: row extreme plus column extreme
   float am = -INFINITY, an = INFINITY;
-  for (int i = tid; i < nr; i += 256) {
+  for (int i = tid; i < nr; i += NT) {
     am = fmaxf(am, a[i]);
     an = fminf(an, a[i]);
   }
@@ -199,24 +215,30 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
     am = fmaxf(am, __shfl_xor(am, o, 64));
     an = fminf(an, __shfl_xor(an, o, 64));
   }
-  __shared__ float redn[4];
+  __shared__ float redn[NW];
   if ((tid & 63) == 0) {
     redf[tid >> 6] = am;
     redn[tid >> 6] = an;
   }
   __syncthreads();
-  const float smax = fmaxf(fmaxf(redf[0], redf[1]), fmaxf(redf[2], redf[3])) + bv[0];
-  const float smin = fminf(fminf(redn[0], redn[1]), fminf(redn[2], redn[3])) + bv[nc - 1];
+  float rmax = redf[0], rmin = redn[0];
+#pragma unroll
+  for (int q = 1; q < NW; ++q) {
+    rmax = fmaxf(rmax, redf[q]);
+    rmin = fminf(rmin, redn[q]);
+  }
+  const float smax = rmax + bv[0];
+  const float smin = rmin + bv[nc - 1];
   // theta: the largest key with at least K cells at or above it.  A probe with
   // exactly K cells at or above it ends the search early: those cells are the
   // selection (kept: key >= probe, no ties to break).
-  // Per row i of this thread (i = tid + 256*s), the count of its cells at or
+  // Per row i of this thread (i = tid + NT*s), the count of its cells at or
   // above a key is a prefix length of the sorted column order; the search keeps
   // that length at lo (rub) and at the last probe that fell short (rlb) and
   // looks for the next probe's length only between them.
   uint32_t lo = fkey(smin), hi = fkey(smax);
   int c_lo = nr * nc;  // cells at or above key lo
-  constexpr int kRowsPer = kGridMax / 256;
+  constexpr int kRowsPer = kGridMax / NT;
   int rlb[kRowsPer], rub[kRowsPer], rl[kRowsPer];
 #pragma unroll
   for (int s = 0; s < kRowsPer; ++s) {
@@ -229,7 +251,7 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
     int cpart = 0;
 #pragma unroll
     for (int s = 0; s < kRowsPer; ++s) {
-      const int i = tid + 256 * s;
+      const int i = tid + NT * s;
       rl[s] = 0;
       if (i < nr) {
         const float ai = a[i];
@@ -245,7 +267,7 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
         cpart += l;
       }
     }
-    const int c = block_sum(cpart, red);
+    const int c = block_sum<NW>(cpart, red);
     if (c >= K) {
       lo = mid;
       c_lo = c;
@@ -271,7 +293,7 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
   float wsum = 0.0f;
   int32_t* out = idx + (size_t)t * K;
   float* gout = gate + (size_t)t * K;
-  for (int w0 = 0; w0 < W; w0 += 256) {
+  for (int w0 = 0; w0 < W; w0 += NT) {
     const int w = w0 + tid;
     uint32_t word = 0u;
     int i = 0, j0 = 0;
@@ -301,7 +323,7 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
       // ties before this word in id order, then keep as many as are still needed
       const int nt = __popc(tiew);
       int tsum;
-      const int tb = ties + block_exscan(nt, red, &tsum);
+      const int tb = ties + block_exscan<NW>(nt, red, &tsum);
       int room = min(max(m_tie - tb, 0), nt);
       while (room > 0) {  // lowest tie columns first
         const uint32_t low = tiew & (0u - tiew);
@@ -313,7 +335,7 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
     }
     const int nk = __popc(word);
     int ksum;
-    const int pos = base + block_exscan(nk, red, &ksum);
+    const int pos = base + block_exscan<NW>(nk, red, &ksum);
     if (w < W) {
       bits[(size_t)t * W + w] = word;
       bitpre[(size_t)t * W + w] = pos;
@@ -337,8 +359,16 @@ __global__ __launch_bounds__(256) void grid_topk_kernel(const float* __restrict_
   __syncthreads();
   if ((tid & 63) == 0) redf[tid >> 6] = wsum;
   __syncthreads();
-  const float total = (redf[0] + redf[1]) + (redf[2] + redf[3]);
-  for (int p = tid; p < K; p += 256) gout[p] = gout[p] / total;
+  // pairwise in wave order (NW = 4: (0 + 1) + (2 + 3))
+  float part[NW];
+#pragma unroll
+  for (int q = 0; q < NW; ++q) part[q] = redf[q];
+#pragma unroll
+  for (int h = 1; h < NW; h <<= 1)
+#pragma unroll
+    for (int q = 0; q + h < NW; q += 2 * h) part[q] = part[q] + part[q + h];
+  const float total = part[0];
+  for (int p = tid; p < K; p += NT) gout[p] = gout[p] / total;
 }
 
 // ---- counting sort of the kept pairs by expert ---------------------------------
@@ -570,7 +600,11 @@ hipError_t launch_grid_topk(const float* pr, const float* pc, int T, int nr, int
                             hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (nr > kGridMax || nc > kGridMax || nc % 32 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(grid_topk_kernel, dim3(T), dim3(256), 0, s, pr, pc, nr, nc, K, idx, gate,
+if (T <= kTopkWideMaxT)
+    hipLaunchKernelGGL(grid_topk_kernel<1024>, dim3(T), dim3(1024), 0, s, pr, pc, nr, nc, K, idx, gate,
+                     bits, bitpre);
+  else
+    hipLaunchKernelGGL(grid_topk_kernel<256>, dim3(T), dim3(256), 0, s, pr, pc, nr, nc, K, idx, gate,
                      bits, bitpre);
   return hipGetLastError();
 }
