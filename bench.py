@@ -492,7 +492,7 @@ def cpu_baseline(wl, target_s=15.0):
                        "permutation, FFN, combine), fp64 C oracle, %.1f s" % (S, cfg.T, dt))
 
 
-# HBM-bound workloads are timed from a cold cache (a 512 MB write before each
+# HBM-bound workloads are timed from a cold cache (a 512 MB read before each
 # step); the Switch-shaped layer, whose 75 MB of weights fit in the MALL, is
 # reported both warm and cold
 COLD = {"mixtral_decode_bf16": ("cold",), "mixtral_int4_decode": ("cold",),
