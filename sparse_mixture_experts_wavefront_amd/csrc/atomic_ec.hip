@@ -35,7 +35,7 @@ constexpr int kEcOutSlice = kEcOutThreads * kEcOutCols;   // 512 columns per blo
 constexpr int kEcTok = 16;              // tokens per output-side block
 constexpr int kEcList = 256;            // experts listed per round of the output side
 constexpr int kEcAhead = 32;            // output vectors in flight per thread
-constexpr int kEcOutRows = 1024;        // rows of a listing round staged in LDS (T <= 16)
+constexpr int kEcOutRows = 512;         // rows of a listing round staged in LDS (T <= 16)
 
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 

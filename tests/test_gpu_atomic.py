@@ -107,6 +107,9 @@ EC_SMALL = {
     "ec_ragged": dict(T=300, d=1024, nr=20, nc=64, E=1280, k=100, F_shared=256),
     "ec_wide": dict(T=17, d=4096, nr=8, nc=32, E=256, k=24, F_shared=128),
     "ec_sixteen": dict(T=16, d=2048, nr=12, nc=32, E=384, k=40, F_shared=128),
+    # 16 tokens x 64 units = 1024 rows in one 256-unit range: more than a round
+    # stages in LDS, so the output side reads rows and tokens from memory
+    "ec_unstaged": dict(T=16, d=512, nr=8, nc=32, E=256, k=64, F_shared=128),
 }
 
 
