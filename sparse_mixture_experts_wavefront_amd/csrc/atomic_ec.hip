@@ -27,8 +27,8 @@
 namespace moe {
 namespace {
 
-constexpr int kEcInUnits = 64;         // consecutive experts per block (input side)
-constexpr int kEcInRows = 1024;        // their rows staged in LDS (64 experts x 16 tokens)
+constexpr int kEcInUnits = 32;         // consecutive experts per block (input side)
+constexpr int kEcInRows = 512;         // their rows staged in LDS (32 experts x 16 tokens)
 constexpr int kEcOutThreads = 64;       // output side: threads per block (one wave)
 constexpr int kEcOutCols = 8;           // columns per thread (one 16-byte bf16 load)
 constexpr int kEcOutSlice = kEcOutThreads * kEcOutCols;   // 512 columns per block
