@@ -134,6 +134,50 @@ __global__ __launch_bounds__(64 * NW) void route_topk_kernel(const void* __restr
   __syncthreads();
 
   // ---- exact top-k, one token per segment of `seg` lanes ----
+  if (seg == 64) {
+    // a whole wave per token: radix select of the k-th largest key from
+    // ballots (the keys of valid lanes are distinct and above 0; only bits
+    // 63..32 and 5..0 can be set), then each winner's rank among the winners
+    // from k broadcast keys -- no cross-lane shuffles in a dependent chain
+    for (int tr = wv_id; tr < kTokPerWave; tr += NW) {
+      const int t = t0 + tr;
+      if (t >= T) break;  // uniform
+      const unsigned long long key =
+          lane < E ? ((unsigned long long)order_key(lt[tr][lane]) << 32) | (uint32_t)(63 - lane) : 0ull;
+      unsigned long long th = 0ull;
+      auto probe = [&](int b) {
+        const unsigned long long c = th | (1ull << b);
+        if (__popcll(__ballot(key >= c)) >= k) th = c;
+      };
+      for (int b = 63; b >= 32; --b) probe(b);
+      for (int b = 5; b >= 0; --b) probe(b);
+      const bool win = key >= th;  // exactly k lanes
+      const uint32_t khi = (uint32_t)(key >> 32), klo = (uint32_t)key;
+      int rank = 0;
+      for (unsigned long long rest = __ballot(win); rest; rest &= rest - 1ull) {
+        const int l = __builtin_ctzll(rest);
+        const unsigned long long kl =
+            ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)khi, l) << 32) |
+            (uint32_t)__builtin_amdgcn_readlane((int)klo, l);
+        rank += kl > key ? 1 : 0;
+      }
+      // weights in slot order (slot 0 the largest), as below
+      float lmax = 0.0f, sum = 0.0f, mine = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        const int l = __builtin_ctzll(__ballot(win && rank == j));
+        const float v = order_key_inv((uint32_t)__builtin_amdgcn_readlane((int)khi, l));
+        if (j == 0) lmax = v;
+        const float w = expf(v - lmax);
+        sum += w;
+        if (win && rank == j) mine = w;
+      }
+      if (win) {
+        idx[(size_t)t * k + rank] = lane;
+        if (gate) gate[(size_t)t * k + rank] = (k == 1) ? 1.0f : mine / sum;
+      }
+    }
+    return;
+  }
   const int per = 64 / seg;
   const int ts = lane / seg, e = lane % seg;
   for (int base = wv_id * per; base < kTokPerWave; base += per * NW) {
