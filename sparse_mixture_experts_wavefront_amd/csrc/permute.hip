@@ -136,6 +136,8 @@ constexpr int kBigBlock = 1024;
 constexpr int kBigWaves = kBigBlock / 64;
 constexpr int kBigChunks = kPermFusedBigMax / 64;
 constexpr int kBigPer = kBigChunks / kBigWaves;  // chunks per wave
+static_assert(kBigChunks % kBigWaves == 0 && kMaxExperts == 64,
+              "chunks split evenly over the waves; one lane per expert");
 
 __global__ __launch_bounds__(kBigBlock) void permute_fused_big_kernel(
     const int32_t* __restrict__ idx, int T, int E, int k, int32_t* __restrict__ counts,
