@@ -519,7 +519,11 @@ hipError_t launch_int2_up(const void* x, int T, int d, int F, int E, int k, cons
   a.thr = thr;
   a.flags = flags;
   a.xbytes = (uint32_t)((size_t)T * d * 2);
-  return launch_mwq_mode<kMModeUp, 64>(a, E, T * k, s);
+  // 64-column strips where their group metadata fits the LDS (faster at 16
+  // tokens), else the down pass's 32
+  if (mwq_lds_bytes<kMModeUp, 64>(d) <= kMwqMaxLds)
+    return launch_mwq_mode<kMModeUp, 64>(a, E, T * k, s);
+  return launch_mwq_mode<kMModeUp, kRmDown>(a, E, T * k, s);
 }
 
 }  // namespace moe
